@@ -1,0 +1,230 @@
+/*
+ * Plain C encoder and bit-serial decoder for the chunked, lane-interleaved
+ * canonical-Huffman stream ("ECW v1").  TEST INFRASTRUCTURE ONLY: part of the
+ * CPU oracle, used by the tests and by the benchmark's CPU baseline.  It
+ * shares no code with the GPU library.
+ *
+ * What the pages fix: encoded weights are split into independent chunks that
+ * keep the tensor's structure and are decoded concurrently (EntroLLM,
+ * gist.science technical summary, Methodology item 3); codes are Huffman-coded
+ * losslessly in interleaved lanes and decoded bit-exactly (LazyWeights
+ * abstract, arXiv 2611.17108).  The layout is the reading spelled out in
+ * oracle/ecw.py; this file implements the same steps without tables:
+ *
+ *   - canonical codes from lengths (codes of one length consecutive in symbol
+ *     order, shorter codes first, first code zero; MSB-first);
+ *   - lane j of a chunk holds symbols k = j (mod W); its codewords are cut
+ *     into 32-bit words, first bit in bit 31, last word zero-padded;
+ *   - a lane takes its next word at the step whose codeword is longer than
+ *     its count of loaded, unconsumed bits; words are stored in the order they
+ *     are taken, lanes of one step in increasing lane index;
+ *   - chunk_bit_off[c] = 32 * (words before chunk c), plus a final entry.
+ *
+ * The decoder reads one bit at a time and compares against the canonical
+ * first code of each length; a lane that runs out of bits takes the chunk's
+ * next word.  It never builds a lookup table.
+ *
+ * Plain C99, no intrinsics, no threads (callers run chunk ranges in parallel).
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OC_OK 0
+#define OC_E_PARAM 1
+#define OC_E_CODEBOOK 2
+#define OC_E_STREAM 3
+#define OC_E_NOMEM 4
+#define OC_MAXLEN 32
+
+static int check_params(uint32_t chunk, uint32_t lanes) {
+  if (lanes < 1 || lanes > 64 || (lanes & (lanes - 1))) return OC_E_PARAM;
+  if (chunk < 1 || chunk % lanes) return OC_E_PARAM;
+  return OC_OK;
+}
+
+/* Canonical codes; returns max length or -1 on bad lengths. */
+static int canonical(const uint8_t *len, uint32_t nsym, uint32_t *code) {
+  uint32_t bl_count[OC_MAXLEN + 1], next[OC_MAXLEN + 1];
+  int max_len = 0;
+  uint32_t s, l, c;
+  memset(bl_count, 0, sizeof bl_count);
+  for (s = 0; s < nsym; s++) {
+    if (len[s] > OC_MAXLEN) return -1;
+    if (len[s]) bl_count[len[s]]++;
+    if (len[s] > max_len) max_len = len[s];
+  }
+  c = 0;
+  next[0] = 0;
+  for (l = 1; l <= OC_MAXLEN; l++) {
+    c = (c + (l >= 2 ? bl_count[l - 1] : 0)) << 1;
+    next[l] = c;
+  }
+  for (s = 0; s < nsym; s++) {
+    code[s] = 0;
+    if (len[s]) code[s] = next[len[s]]++;
+  }
+  return max_len;
+}
+
+/* Words of one chunk = sum over lanes of ceil(bits / 32). */
+static uint64_t chunk_words(const uint8_t *q, uint64_t cc, const uint8_t *len, uint32_t lanes) {
+  uint64_t total = 0, k;
+  uint32_t j;
+  for (j = 0; j < lanes; j++) {
+    uint64_t bits = 0;
+    for (k = j; k < cc; k += lanes) bits += len[q[k]];
+    total += (bits + 31) / 32;
+  }
+  return total;
+}
+
+/* Number of words the whole stream takes; fills chunk_bit_off[0..n_chunks]. */
+int oc_layout(const uint8_t *q, uint64_t n, const uint8_t *len, uint32_t nsym,
+              uint32_t chunk, uint32_t lanes, uint64_t *chunk_bit_off, uint64_t *n_words) {
+  uint64_t nc, c, acc = 0, i;
+  if (check_params(chunk, lanes)) return OC_E_PARAM;
+  for (i = 0; i < n; i++)
+    if (q[i] >= nsym || len[q[i]] == 0) return OC_E_CODEBOOK;
+  nc = (n + chunk - 1) / chunk;
+  chunk_bit_off[0] = 0;
+  for (c = 0; c < nc; c++) {
+    uint64_t beg = c * chunk, cc = n - beg < chunk ? n - beg : chunk;
+    acc += chunk_words(q + beg, cc, len, lanes);
+    chunk_bit_off[c + 1] = 32 * acc;
+  }
+  *n_words = acc;
+  return OC_OK;
+}
+
+/* Encode chunks [c0, c1) into words; chunk_bit_off must come from oc_layout. */
+int oc_encode(const uint8_t *q, uint64_t n, const uint8_t *len, uint32_t nsym,
+              uint32_t chunk, uint32_t lanes, const uint64_t *chunk_bit_off,
+              uint32_t *words, uint64_t c0, uint64_t c1) {
+  uint32_t code[256];
+  uint64_t c, k;
+  uint32_t j;
+  uint64_t lane_cap;
+  uint32_t *lane_buf;
+  uint64_t lane_n[64], taken[64];
+  int32_t avail[64];
+  if (check_params(chunk, lanes) || nsym > 256) return OC_E_PARAM;
+  if (canonical(len, nsym, code) < 0) return OC_E_CODEBOOK;
+  /* per-lane word buffer: at most ceil(chunk/lanes) codewords of <= 32 bits */
+  lane_cap = ((uint64_t)chunk / lanes) + 2;
+  lane_buf = (uint32_t *)calloc((size_t)(lane_cap * lanes), sizeof(uint32_t));
+  if (!lane_buf) return OC_E_NOMEM;
+  for (c = c0; c < c1; c++) {
+    uint64_t beg = c * chunk, cc = n - beg < chunk ? n - beg : chunk;
+    uint64_t out = chunk_bit_off[c] / 32, steps;
+    uint32_t t;
+    /* 1. each lane's bit sequence, MSB-first, into its own word buffer */
+    memset(lane_buf, 0, (size_t)(lane_cap * lanes) * sizeof(uint32_t));
+    for (j = 0; j < lanes; j++) {
+      uint64_t bitpos = 0;
+      uint32_t *lw = lane_buf + (uint64_t)j * lane_cap;
+      for (k = j; k < cc; k += lanes) {
+        uint32_t s = q[beg + k], l = len[s], b;
+        if (l == 0) { free(lane_buf); return OC_E_CODEBOOK; }
+        for (b = 0; b < l; b++) {
+          uint32_t bit = (code[s] >> (l - 1 - b)) & 1u;
+          if (bit) lw[bitpos / 32] |= 1u << (31 - (bitpos % 32));
+          bitpos++;
+        }
+      }
+      lane_n[j] = (bitpos + 31) / 32;
+      taken[j] = 0;
+      avail[j] = 0;
+    }
+    /* 2. store the words in the order the lanes take them */
+    steps = (cc + lanes - 1) / lanes;
+    for (t = 0; t < steps; t++) {
+      for (j = 0; j < lanes; j++) {
+        uint64_t kk = (uint64_t)t * lanes + j;
+        int32_t l;
+        if (kk >= cc) continue;
+        l = len[q[beg + kk]];
+        if (l > avail[j]) {
+          if (taken[j] >= lane_n[j]) { free(lane_buf); return OC_E_STREAM; }
+          words[out++] = lane_buf[(uint64_t)j * lane_cap + taken[j]++];
+          avail[j] += 32;
+        }
+        avail[j] -= l;
+      }
+    }
+    for (j = 0; j < lanes; j++)
+      if (taken[j] != lane_n[j]) { free(lane_buf); return OC_E_STREAM; }
+    if (out != chunk_bit_off[c + 1] / 32) { free(lane_buf); return OC_E_STREAM; }
+  }
+  free(lane_buf);
+  return OC_OK;
+}
+
+/* Decode chunks [c0, c1) bit by bit into out[c*chunk ...]. */
+int oc_decode(const uint32_t *words, uint64_t n_words, const uint64_t *chunk_bit_off,
+              uint64_t n, const uint8_t *len, uint32_t nsym, uint32_t chunk, uint32_t lanes,
+              uint8_t *out, uint64_t c0, uint64_t c1) {
+  uint32_t count[OC_MAXLEN + 1], first[OC_MAXLEN + 1], offset[OC_MAXLEN + 1];
+  uint8_t sorted_syms[256];
+  uint32_t cur[64];      /* current word of each lane */
+  int32_t left[64];      /* unread bits of cur */
+  int max_len = 0;
+  uint32_t s, l, code, acc, j;
+  uint64_t c;
+  if (check_params(chunk, lanes) || nsym > 256) return OC_E_PARAM;
+  memset(count, 0, sizeof count);
+  for (s = 0; s < nsym; s++) {
+    if (len[s] > OC_MAXLEN) return OC_E_CODEBOOK;
+    if (len[s]) count[len[s]]++;
+    if (len[s] > max_len) max_len = len[s];
+  }
+  code = 0;
+  acc = 0;
+  for (l = 1; l <= (uint32_t)max_len; l++) {
+    code = (code + (l >= 2 ? count[l - 1] : 0)) << 1;
+    first[l] = code;
+    offset[l] = acc;
+    acc += count[l];
+  }
+  acc = 0;
+  for (l = 1; l <= (uint32_t)max_len; l++)
+    for (s = 0; s < nsym; s++)
+      if (len[s] == l) sorted_syms[acc++] = (uint8_t)s;
+  for (c = c0; c < c1; c++) {
+    uint64_t beg = c * chunk, cc = n - beg < chunk ? n - beg : chunk;
+    uint64_t pos = chunk_bit_off[c] / 32, end = chunk_bit_off[c + 1] / 32, t, steps;
+    if (chunk_bit_off[c] % 32 || end < pos || end > n_words) return OC_E_STREAM;
+    for (j = 0; j < lanes; j++) { left[j] = 0; cur[j] = 0; }
+    steps = (cc + lanes - 1) / lanes;
+    for (t = 0; t < steps; t++) {
+      for (j = 0; j < lanes; j++) {
+        uint64_t k = t * lanes + j;
+        int found = 0;
+        if (k >= cc) continue;
+        code = 0;
+        for (l = 1; l <= (uint32_t)max_len; l++) {
+          uint32_t bit;
+          if (left[j] == 0) {
+            if (pos >= end) return OC_E_STREAM;
+            cur[j] = words[pos++];
+            left[j] = 32;
+          }
+          bit = (cur[j] >> (left[j] - 1)) & 1u;
+          left[j]--;
+          code = (code << 1) | bit;
+          if (code >= first[l] && code - first[l] < count[l]) {
+            out[beg + k] = sorted_syms[offset[l] + code - first[l]];
+            found = 1;
+            break;
+          }
+        }
+        if (!found) return OC_E_STREAM;
+      }
+    }
+    if (pos != end) return OC_E_STREAM;
+    for (j = 0; j < lanes; j++)
+      if (left[j] && (cur[j] & ((left[j] == 32) ? 0xFFFFFFFFu : ((1u << left[j]) - 1u))))
+        return OC_E_STREAM;
+  }
+  return OC_OK;
+}

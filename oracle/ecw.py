@@ -1,0 +1,168 @@
+"""Chunked, lane-interleaved canonical-Huffman stream, "ECW v1"
+(oracle; pure Python, small inputs; test infrastructure only).
+
+What the pages fix: EntroLLM splits the encoded weights into independent
+chunks that keep the tensor's structure and decodes them concurrently
+(gist.science technical summary, Methodology item 3); LazyWeights Huffman-codes
+the integer codes in interleaved lanes and decodes them bit-exactly (LazyWeights
+abstract, arXiv 2611.17108).  The layout below is the reading of those two
+statements; nothing in it is printed on the pages.
+
+Layout
+------
+1. The tensor is flattened row-major (``N`` symbols).
+2. Chunk ``c`` holds symbols ``[c*C, min((c+1)*C, N))``; the last may be short.
+3. Inside a chunk of ``C_c`` symbols, symbol ``k`` belongs to lane
+   ``j = k mod W`` and is decoded at step ``t = k div W``.
+4. Lane ``j``'s bit sequence is its codewords in step order, first bit first,
+   cut into 32-bit words whose first bit is bit 31; the last word is padded
+   with zero bits.
+5. Word order inside a chunk: each lane keeps a count ``n`` of loaded but
+   unconsumed bits (0 at the start).  At step ``t`` a lane takes its next word
+   exactly when its codeword for this step is longer than ``n`` (then
+   ``n += 32``), and then consumes the codeword (``n -= l``).  The chunk's
+   words are stored in the order they are taken, lanes of one step in
+   increasing lane index.
+6. Chunks are concatenated; ``chunk_bit_off[c]`` = 32 x (words before chunk c),
+   with a final entry for the end.  Words are little-endian uint32 in memory.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .canonical import canonical_codes, codeword_str
+
+
+def n_chunks(n_symbols: int, chunk: int) -> int:
+    return -(-n_symbols // chunk)
+
+
+def _check_params(chunk: int, lanes: int) -> None:
+    if lanes < 1 or lanes > 64 or (lanes & (lanes - 1)):
+        raise ValueError("lanes must be a power of two in [1, 64]")
+    if chunk < 1 or chunk % lanes:
+        raise ValueError("chunk must be a positive multiple of lanes")
+
+
+def encode(q: np.ndarray, lengths: np.ndarray, chunk: int, lanes: int):
+    """Encode codes ``q`` (any shape, row-major) -> ``(words uint32, chunk_bit_off uint64)``."""
+    _check_params(chunk, lanes)
+    q = np.asarray(q, dtype=np.uint8).ravel()
+    lengths = np.asarray(lengths, dtype=np.int64)
+    codes = canonical_codes(lengths)
+    if len(q) and (lengths[q] == 0).any():
+        raise ValueError("a code value present in the tensor has no codeword")
+    words: list[int] = []
+    offs = [0]
+    for c in range(n_chunks(len(q), chunk)):
+        sl = q[c * chunk: min((c + 1) * chunk, len(q))]
+        cc = len(sl)
+        lane_words = []
+        for j in range(lanes):
+            bits = "".join(codeword_str(int(codes[s]), int(lengths[s])) for s in sl[j::lanes])
+            lane_words.append([int(bits[i:i + 32].ljust(32, "0"), 2) for i in range(0, len(bits), 32)])
+        n = [0] * lanes
+        taken = [0] * lanes
+        for t in range(-(-cc // lanes)):
+            for j in range(lanes):
+                k = t * lanes + j
+                if k >= cc:
+                    continue
+                l = int(lengths[sl[k]])
+                if l > n[j]:
+                    words.append(lane_words[j][taken[j]])
+                    taken[j] += 1
+                    n[j] += 32
+                n[j] -= l
+        assert all(taken[j] == len(lane_words[j]) for j in range(lanes))
+        offs.append(32 * len(words))
+    return np.array(words, dtype=np.uint32), np.array(offs, dtype=np.uint64)
+
+
+class StreamError(ValueError):
+    """The stream does not decode under the given codebook and layout."""
+
+
+def _canonical_tables(lengths: np.ndarray):
+    ls = [int(x) for x in lengths]
+    max_len = max(ls)
+    count = [0] * (max_len + 1)
+    for l in ls:
+        if l > 0:
+            count[l] += 1
+    first = [0] * (max_len + 1)
+    code = 0
+    for l in range(1, max_len + 1):
+        code = (code + count[l - 1]) << 1
+        first[l] = code
+    offset = [0] * (max_len + 1)
+    acc = 0
+    for l in range(1, max_len + 1):
+        offset[l] = acc
+        acc += count[l]
+    sorted_syms = [s for l in range(1, max_len + 1) for s in range(len(ls)) if ls[s] == l]
+    return max_len, count, first, offset, sorted_syms
+
+
+def decode(words: np.ndarray, chunk_bit_off: np.ndarray, lengths: np.ndarray,
+           n_symbols: int, chunk: int, lanes: int) -> np.ndarray:
+    """Bit-serial canonical decoder: reads one bit at a time, never a table.
+
+    A lane that needs a bit and has none left takes the chunk's next word.
+    Because a lane only runs dry inside a codeword it could not finish, this
+    reproduces the encoder's word order without computing it.  Raises
+    ``StreamError`` on an undecodable prefix, on running past the chunk's
+    words, on unused words, or on nonzero padding bits.
+    """
+    _check_params(chunk, lanes)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    max_len, count, first, offset, sorted_syms = _canonical_tables(lengths)
+    words = [int(w) for w in np.asarray(words, dtype=np.uint32)]
+    offs = [int(o) for o in np.asarray(chunk_bit_off, dtype=np.uint64)]
+    out = np.zeros(n_symbols, dtype=np.uint8)
+    nc = n_chunks(n_symbols, chunk)
+    if len(offs) != nc + 1 or offs[0] != 0 or offs[-1] != 32 * len(words):
+        raise StreamError("chunk offsets do not span the word array")
+    for c in range(nc):
+        if offs[c] % 32 or offs[c + 1] < offs[c]:
+            raise StreamError("chunk offsets must be ascending multiples of 32")
+        pos = offs[c] // 32
+        end = offs[c + 1] // 32
+        cc = min(chunk, n_symbols - c * chunk)
+        pending = [[] for _ in range(lanes)]   # unconsumed bits of each lane, first bit first
+
+        def next_bit(j):
+            nonlocal pos
+            if not pending[j]:
+                if pos >= end:
+                    raise StreamError(f"chunk {c}: lane {j} runs past the chunk's words")
+                w = words[pos]
+                pos += 1
+                pending[j].extend((w >> (31 - i)) & 1 for i in range(32))
+            return pending[j].pop(0)
+
+        for t in range(-(-cc // lanes)):
+            for j in range(lanes):
+                k = t * lanes + j
+                if k >= cc:
+                    continue
+                code = 0
+                for l in range(1, max_len + 1):
+                    code = (code << 1) | next_bit(j)
+                    d = code - first[l]
+                    if 0 <= d < count[l]:
+                        out[c * chunk + k] = sorted_syms[offset[l] + d]
+                        break
+                else:
+                    raise StreamError(f"chunk {c}: lane {j} step {t}: no codeword matches")
+        if pos != end:
+            raise StreamError(f"chunk {c}: {end - pos} words left unused")
+        for j in range(lanes):
+            if any(pending[j]):
+                raise StreamError(f"chunk {c}: lane {j} has nonzero padding bits")
+    return out
+
+
+def stream_bits(words: np.ndarray, n_chunks_: int) -> int:
+    """Coded size in bits: stream words plus one 64-bit offset per chunk boundary."""
+    return 32 * int(len(words)) + 64 * (n_chunks_ + 1)

@@ -1,0 +1,123 @@
+"""Pins for oracle.quant: hand-derived fixture, error bounds, torch's quantizer,
+and the pages' qualitative entropy claim (tensor-level codes are spikier than
+block-wise ones)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import quant
+from synth import TensorSpec, weights
+from tests._golden import load
+
+
+def test_golden_tiny():
+    g, _ = load("quant_tiny.txt")
+    w = np.array([float(x) for x in g["w"][0]], dtype=np.float32)
+    bits = int(g["bits"][0][0])
+    a = quant.quantize_asymmetric(w, bits)
+    assert a.zero_point == int(g["asym_zp"][0][0])
+    assert a.q.tolist() == [int(x) for x in g["asym_q"][0]]
+    assert a.scale == np.float32(2.0 / 15.0)
+    u = quant.quantize_unsigned(w, bits)
+    assert u.zero_point == int(g["unsigned_zp"][0][0])
+    assert u.q.tolist() == [int(x) for x in g["unsigned_q"][0]]
+    assert u.scale == np.float32(1.0 / 7.0)
+    assert quant.quantize_mixed(w, bits).scheme == g["mixed"][0][0]
+
+
+def _rand_w(seed, n=200_000, dist="normal"):
+    rng = np.random.default_rng(seed)
+    if dist == "normal":
+        return rng.normal(0, 0.02, n).astype(np.float32)
+    if dist == "laplace":
+        return rng.laplace(0.003, 0.015, n).astype(np.float32)
+    return (rng.standard_t(4, n) * 0.02).astype(np.float32)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("dist", ["normal", "laplace", "t"])
+def test_codes_in_range_and_round_off_bound(bits, dist):
+    w = _rand_w(bits, dist=dist)
+    Q = (1 << bits) - 1
+    for qz in (quant.quantize_asymmetric(w, bits), quant.quantize_unsigned(w, bits)):
+        assert qz.q.dtype == np.uint8 and int(qz.q.max()) <= Q
+        err = np.abs(w.astype(np.float64) - quant.dequant_f64(qz))
+        s = float(qz.scale)
+        clamped = (qz.q == 0) | (qz.q == Q)
+        assert (err[~clamped] <= 0.5 * s * (1 + 1e-6)).all()
+        # clamping only trims the very ends of the range
+        assert (err <= s * (1 + 1e-6)).all()
+    u = quant.quantize_unsigned(w, bits)
+    assert int(u.q.min()) >= 1  # the symmetric range never reaches code 0
+    a = quant.quantize_asymmetric(w, bits)
+    assert int(a.q.min()) == 0  # the minimum maps to code 0
+
+
+def test_asymmetric_8bit_agrees_with_torch_quantize_per_tensor():
+    w = _rand_w(3, n=500_000)
+    a = quant.quantize_asymmetric(w, 8)
+    tq = torch.quantize_per_tensor(torch.from_numpy(w), float(a.scale), a.zero_point, torch.quint8)
+    tcodes = tq.int_repr().numpy()
+    diff = np.abs(tcodes.astype(np.int64) - a.q.astype(np.int64))
+    assert diff.max() <= 1
+    # torch scales by a reciprocal; only rounding ties can land differently
+    assert (diff != 0).mean() < 1e-3
+
+
+def test_unsigned_clip_saturates():
+    w = _rand_w(5, dist="t")
+    c = 1.4 * float(np.std(w.astype(np.float64)))
+    u = quant.quantize_unsigned(w, 4, clip=c)
+    assert u.scale == np.float32(c / 7)
+    big = np.abs(w) > 8 * c / 7
+    assert (u.q[w > 8 * c / 7] == 15).all() and (u.q[w < -8.5 * c / 7] == 0).all()
+    assert big.any()
+
+
+def test_degenerate_tensor():
+    w = np.full(100, 0.5, dtype=np.float32)
+    a = quant.quantize_asymmetric(w, 8)
+    assert a.scale == 1.0 and a.zero_point == 0 and len(set(a.q.tolist())) == 1
+    z = np.zeros(50, dtype=np.float32)
+    u = quant.quantize_unsigned(z, 4)
+    assert u.scale == 1.0 and u.zero_point == 8 and set(u.q.tolist()) == {8}
+
+
+def test_entropy_closed_forms():
+    assert quant.entropy_bits(np.array([5, 5, 5, 5])) == pytest.approx(2.0)
+    assert quant.entropy_bits(np.array([7, 0, 0])) == 0.0
+    assert quant.entropy_bits(np.array([2, 1, 1])) == pytest.approx(1.5)
+
+
+def test_mixed_picks_lower_entropy():
+    for seed, dist in ((1, "normal"), (2, "laplace"), (3, "t")):
+        w = _rand_w(seed, dist=dist)
+        for bits in (4, 8):
+            a = quant.quantize_asymmetric(w, bits)
+            u = quant.quantize_unsigned(w, bits)
+            ha = quant.entropy_bits(quant.histogram(a.q, bits))
+            hu = quant.entropy_bits(quant.histogram(u.q, bits))
+            m = quant.quantize_mixed(w, bits)
+            assert m.scheme == ("unsigned" if hu < ha else "asymmetric")
+
+
+def _blockwise_entropy(w, bits, group):
+    """Entropy of the codes of a group-wise min-max quantizer (each group its own scale)."""
+    Q = (1 << bits) - 1
+    g = w.astype(np.float64).reshape(-1, group)
+    lo = g.min(axis=1, keepdims=True)
+    hi = g.max(axis=1, keepdims=True)
+    s = np.where(hi > lo, (hi - lo) / Q, 1.0)
+    q = np.clip(np.rint((g - lo) / s), 0, Q).astype(np.uint8)
+    return quant.entropy_bits(quant.histogram(q, bits))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_tensor_level_codes_have_lower_entropy_than_blockwise(bits):
+    """EntroLLM: block-based quantization flattens the code histogram and raises
+    its entropy; tensor-level quantization keeps it spiky (gist.science
+    technical summary, Methodology item 1)."""
+    w = weights(TensorSpec("tensor_2048", 0, -1, "w", 2048, 2048, "w"))[:512]
+    h_tensor = quant.entropy_bits(quant.histogram(quant.quantize_mixed(w, bits).q, bits))
+    for group in (32, 128):
+        assert h_tensor < _blockwise_entropy(w.ravel(), bits, group)
