@@ -1,0 +1,52 @@
+// Constants and launch descriptors shared by the host code and the HIP
+// kernels of the library (not part of the public ABI).
+#pragma once
+
+#include <stdint.h>
+
+namespace entro {
+
+constexpr uint32_t kLutMagic = 0x31574345u;   // "ECW1", little-endian
+constexpr uint32_t kLutHeaderWords = 4;
+constexpr uint32_t kLutMaxEntries = 4096;     // 16 KiB of LDS per workgroup
+constexpr uint32_t kMaxCodeLen = 16;
+constexpr uint32_t kSingleLevelMax = 12;      // codes up to 12 bits: one level
+constexpr uint32_t kFirstLevelBits = 11;      // longer codes: 11-bit first level
+constexpr uint32_t kEntryPointer = 0x80u;
+constexpr uint32_t kMaxChunk = 1u << 20;
+
+// status bits (mirror ENTRO_F_* of entro.h)
+constexpr uint32_t kFOverrun = 0x01u, kFUnderrun = 0x02u, kFBadCode = 0x04u,
+                   kFPadding = 0x08u, kFOffsets = 0x10u, kFLut = 0x20u;
+
+enum Mode : int { kModeU8 = 0, kModeBf16 = 1, kModeGemv = 2 };
+
+// One tensor of a launch.
+struct TensorArg {
+  const uint32_t *lut;     // header + entries
+  const uint32_t *words;
+  const uint64_t *offs;
+  void *out;               // u8 / bf16 codes, or fp32 y for the GEMV
+  const uint16_t *x;       // GEMV activations, bf16 [batch][cols]
+  uint32_t *status;
+  uint64_t n_words;
+  uint64_t n_symbols;
+  uint32_t n_chunks;
+  uint32_t chunk;
+  uint32_t rows, cols;     // GEMV shape
+  uint32_t expect_hdr;     // sym_bits << 8 | max_len << 16 (header word 1 without K)
+  uint32_t lut_words;      // readable uint32 words at lut
+};
+
+constexpr int kMaxTensorsPerLaunch = 32;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlockThreads = 64 * kWavesPerBlock;
+
+struct LaunchArgs {
+  TensorArg t[kMaxTensorsPerLaunch];
+  uint32_t block_begin[kMaxTensorsPerLaunch + 1];  // first block of each tensor
+  uint32_t n_tensors;
+  uint32_t batch;                                  // GEMV rows of x / y
+};
+
+}  // namespace entro

@@ -1,0 +1,172 @@
+// Host side of the decode table (LUT): codebook validation, canonical codes,
+// table layout, bf16 dequantized values, status strings.
+//
+// Method: EntroLLM builds one Huffman code per weight tensor from the value
+// frequencies of its quantized codes (gist.science technical summary,
+// Methodology item 2) and dequantizes with the tensor's scale and zero point
+// (tensor-level unsigned/asymmetric quantization, abstract).  The canonical
+// assignment of codewords to lengths and the bf16 rounding are readings (the
+// pages are silent): codes of one length are consecutive in symbol order,
+// shorter codes first, first code zero, MSB-first; bf16 = RNE(f32 product).
+//
+// Table layout (uint32 words):
+//   [0] magic "ECW1"            [1] K | sym_bits << 8 | max_len << 16
+//   [2] number of entries E     [3] 2^K (first-level entries)
+//   [4 .. 4+E) entries.  Entry bits: [4:0] code length (0 = no codeword),
+//   [7] second-level pointer, [15:8] code value (pointer: index bits of the
+//   subtable), [31:16] bf16 value (pointer: absolute entry index of the
+//   subtable).  First level is indexed by the next K stream bits; a code of
+//   length l <= K fills the 2^(K-l) entries that start with it.  A K-bit
+//   prefix of codes longer than K points to a subtable indexed by the next
+//   (longest length under the prefix - K) bits.
+#include <cstring>
+#include <vector>
+
+#include "entro.h"
+#include "entro_internal.h"
+
+namespace entro {
+
+static uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+struct Plan {
+  uint32_t K = 0;
+  uint32_t entries = 0;
+  uint32_t codes[256] = {};
+  uint32_t max_used = 0;
+};
+
+// Validate a codebook and compute its canonical codes and table size.
+static entro_status plan_lut(const entro_codebook *cb, Plan *p) {
+  if (!cb || !cb->code_len) return ENTRO_E_INVAL;
+  if (cb->sym_bits != 4 && cb->sym_bits != 8) return ENTRO_E_FORMAT;
+  if (cb->max_len < 1 || cb->max_len > kMaxCodeLen) return ENTRO_E_FORMAT;
+  const uint32_t nsym = 1u << cb->sym_bits;
+  uint32_t count[kMaxCodeLen + 1] = {};
+  uint32_t used = 0;
+  for (uint32_t s = 0; s < nsym; ++s) {
+    uint32_t l = cb->code_len[s];
+    if (l > cb->max_len) return ENTRO_E_CODEBOOK;
+    if (l) {
+      count[l]++;
+      used++;
+      if (l > p->max_used) p->max_used = l;
+    }
+  }
+  if (!used) return ENTRO_E_CODEBOOK;
+  // Kraft sum <= 1, in units of 2^-16 (exact).
+  uint64_t kraft = 0;
+  for (uint32_t l = 1; l <= kMaxCodeLen; ++l) kraft += (uint64_t)count[l] << (kMaxCodeLen - l);
+  if (kraft > (1ull << kMaxCodeLen)) return ENTRO_E_CODEBOOK;
+  // canonical codes: first code of each length, then symbols in order
+  uint32_t next[kMaxCodeLen + 2] = {};
+  uint32_t code = 0;
+  for (uint32_t l = 1; l <= kMaxCodeLen; ++l) {
+    code = (code + count[l - 1]) << 1;
+    next[l] = code;
+  }
+  for (uint32_t s = 0; s < nsym; ++s)
+    if (cb->code_len[s]) p->codes[s] = next[cb->code_len[s]]++;
+  p->K = p->max_used <= kSingleLevelMax ? p->max_used : kFirstLevelBits;
+  uint32_t entries = 1u << p->K;
+  if (p->max_used > p->K) {
+    // one subtable per K-bit prefix shared by codes longer than K
+    std::vector<uint32_t> deepest(1u << p->K, 0);
+    for (uint32_t s = 0; s < nsym; ++s) {
+      uint32_t l = cb->code_len[s];
+      if (l > p->K) {
+        uint32_t pre = p->codes[s] >> (l - p->K);
+        if (l > deepest[pre]) deepest[pre] = l;
+      }
+    }
+    for (uint32_t pre = 0; pre < (1u << p->K); ++pre)
+      if (deepest[pre]) entries += 1u << (deepest[pre] - p->K);
+  }
+  if (entries > kLutMaxEntries) return ENTRO_E_UNSUPPORTED;
+  p->entries = entries;
+  return ENTRO_OK;
+}
+
+}  // namespace entro
+
+using namespace entro;
+
+extern "C" size_t entro_lut_bytes(const entro_codebook *cb) {
+  Plan p;
+  if (plan_lut(cb, &p) != ENTRO_OK) return 0;
+  return sizeof(uint32_t) * (kLutHeaderWords + p.entries);
+}
+
+extern "C" entro_status entro_lut_build(const entro_codebook *cb, void *host_lut, size_t cap) {
+  Plan p;
+  entro_status st = plan_lut(cb, &p);
+  if (st != ENTRO_OK) return st;
+  if (!host_lut || ((uintptr_t)host_lut & 3u)) return ENTRO_E_INVAL;
+  const size_t bytes = sizeof(uint32_t) * (kLutHeaderWords + p.entries);
+  if (cap < bytes) return ENTRO_E_INVAL;
+  uint32_t *out = (uint32_t *)host_lut;
+  std::memset(out, 0, bytes);
+  out[0] = kLutMagic;
+  out[1] = p.K | (cb->sym_bits << 8) | (cb->max_len << 16);
+  out[2] = p.entries;
+  out[3] = 1u << p.K;
+  uint32_t *e = out + kLutHeaderWords;
+  const uint32_t nsym = 1u << cb->sym_bits;
+  const uint32_t K = p.K;
+  // value field of every code: bf16 of f32(scale) * f32(q - zp), one rounding each
+  auto value = [&](uint32_t s) -> uint32_t {
+    float v = (float)((int32_t)s - cb->zero_point);
+    float prod = cb->scale * v;
+    return (uint32_t)f32_to_bf16_rne(prod);
+  };
+  // subtable placement
+  std::vector<uint32_t> deepest(1u << K, 0), base(1u << K, 0);
+  for (uint32_t s = 0; s < nsym; ++s) {
+    uint32_t l = cb->code_len[s];
+    if (l > K) {
+      uint32_t pre = p.codes[s] >> (l - K);
+      if (l > deepest[pre]) deepest[pre] = l;
+    }
+  }
+  uint32_t cursor = 1u << K;
+  for (uint32_t pre = 0; pre < (1u << K); ++pre) {
+    if (!deepest[pre]) continue;
+    const uint32_t sb = deepest[pre] - K;
+    base[pre] = cursor;
+    e[pre] = kEntryPointer | (sb << 8) | (cursor << 16);
+    cursor += 1u << sb;
+  }
+  for (uint32_t s = 0; s < nsym; ++s) {
+    const uint32_t l = cb->code_len[s];
+    if (!l) continue;
+    const uint32_t entry = l | (s << 8) | (value(s) << 16);
+    if (l <= K) {
+      const uint32_t first = p.codes[s] << (K - l);
+      for (uint32_t i = 0; i < (1u << (K - l)); ++i) e[first + i] = entry;
+    } else {
+      const uint32_t pre = p.codes[s] >> (l - K);
+      const uint32_t sb = deepest[pre] - K;
+      const uint32_t low = p.codes[s] & ((1u << (l - K)) - 1u);
+      const uint32_t first = low << (sb - (l - K));
+      for (uint32_t i = 0; i < (1u << (sb - (l - K))); ++i) e[base[pre] + first + i] = entry;
+    }
+  }
+  return ENTRO_OK;
+}
+
+extern "C" const char *entro_status_str(entro_status s) {
+  switch (s) {
+    case ENTRO_OK: return "ok";
+    case ENTRO_E_INVAL: return "invalid argument";
+    case ENTRO_E_CODEBOOK: return "invalid codebook";
+    case ENTRO_E_FORMAT: return "stream layout parameters out of range";
+    case ENTRO_E_UNSUPPORTED: return "unsupported configuration";
+    case ENTRO_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}

@@ -1,0 +1,163 @@
+/*
+ * entro.h - C ABI of the entropy-coded weight library for MI355X (gfx950).
+ *
+ * The library decodes per-tensor quantized LLM weight codes (4-bit or 8-bit)
+ * that were compressed with a length-limited canonical Huffman code laid out
+ * in independent chunks of lane-interleaved 32-bit words, and optionally
+ * dequantizes them to bf16 or multiplies them with activation vectors on the
+ * fly.  Method: EntroLLM (arXiv 2505.02380) - tensor-level mixed quantization,
+ * Huffman coding of the codes, chunks decoded in parallel; LazyWeights
+ * (arXiv 2611.17108) - codes Huffman-coded in interleaved lanes and decoded on
+ * demand so that memory moves only coded bytes.
+ *
+ * Stream layout ("ECW v1") for a tensor of N codes, chunk size C, lanes W:
+ *   - the tensor is flattened row-major; chunk c holds codes [c*C, min((c+1)*C, N));
+ *   - inside a chunk, code k belongs to lane k mod W and is decoded at step k / W;
+ *   - each lane's codewords (canonical: codes of one length are consecutive in
+ *     symbol order, shorter codes first, first code zero; MSB-first) are packed
+ *     into 32-bit words, first bit in bit 31, the last word zero-padded;
+ *   - a lane takes its next word at the step whose codeword is longer than the
+ *     number of loaded, unconsumed bits it holds; words are stored in the order
+ *     they are taken, lanes of one step in increasing lane order;
+ *   - chunk_bit_off[c] = 32 * (words before chunk c); chunk_bit_off[n_chunks]
+ *     = 32 * n_words.  Words are little-endian uint32.
+ *
+ * Conventions
+ *   - Pointers named d_* are DEVICE pointers (hipMalloc'd or torch CUDA/HIP
+ *     tensors on the current device); all others are host pointers.  Every
+ *     buffer is owned by the caller and only read (or written, for outputs)
+ *     during the call or the work it enqueues.
+ *   - Device entry points validate their host-side arguments synchronously
+ *     and return a nonzero status before enqueuing anything.  They enqueue on
+ *     the caller's stream (0 = the null stream) and return without waiting.
+ *   - Problems found in the data itself (offsets, LUT header, the bitstream)
+ *     are reported by OR-ing ENTRO_F_* bits into the caller-zeroed
+ *     d_status[i] of tensor i; read it after synchronizing.  Kernels never
+ *     read outside [d_words, d_words + n_words) or outside the chunk-offset
+ *     array, and never abort.  Outputs of a flagged tensor are unspecified.
+ *   - The library allocates no device memory and keeps no state between
+ *     calls; calls on different streams may run concurrently.
+ */
+#ifndef ENTRO_H
+#define ENTRO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ENTRO_ABI_VERSION 1
+
+typedef enum {
+  ENTRO_OK = 0,
+  ENTRO_E_INVAL = 1,        /* null pointer, bad size, inconsistent descriptor  */
+  ENTRO_E_CODEBOOK = 2,     /* lengths over the cap, Kraft sum > 1, no symbols  */
+  ENTRO_E_FORMAT = 3,       /* chunk/lane/shape parameters outside the layout   */
+  ENTRO_E_UNSUPPORTED = 4,  /* valid but not handled (e.g. LUT larger than LDS) */
+  ENTRO_E_HIP = 5           /* the HIP runtime reported an error                */
+} entro_status;
+
+/* Per-tensor data faults OR-ed into d_status[i] by the device entry points. */
+#define ENTRO_F_OVERRUN 0x01u   /* a lane needed a word past its chunk's end     */
+#define ENTRO_F_UNDERRUN 0x02u  /* a chunk ended with words left unused          */
+#define ENTRO_F_BADCODE 0x04u   /* bits matched no codeword                       */
+#define ENTRO_F_PADDING 0x08u   /* nonzero bits after a lane's last codeword      */
+#define ENTRO_F_OFFSETS 0x10u   /* chunk offsets not ascending multiples of 32,
+                                   or past n_words; such a chunk is skipped      */
+#define ENTRO_F_LUT 0x20u       /* LUT header does not match the descriptor;
+                                   the tensor is skipped                          */
+
+/* A per-tensor codebook (host memory, read during the call only).
+ * Defined by: EntroLLM - Huffman code built per layer/tensor from the value
+ * frequencies of the quantized weights (gist.science technical summary,
+ * Methodology item 2), tensor-level unsigned/asymmetric quantization (abstract).
+ * dequantized value of code q: bf16 = RNE(f32(scale) * f32(q - zero_point)). */
+typedef struct {
+  uint32_t sym_bits;        /* 4 or 8: the alphabet is 2^sym_bits codes            */
+  uint32_t max_len;         /* 1..16: cap on the code lengths used when encoding   */
+  const uint8_t *code_len;  /* [1 << sym_bits] code lengths; 0 = code value absent */
+  float scale;              /* per-tensor scale                                    */
+  int32_t zero_point;       /* per-tensor zero point                               */
+} entro_codebook;
+
+/* One coded tensor as the device entry points read it. */
+typedef struct {
+  const void *d_lut;              /* entro_lut_build bytes, copied to the device by the caller */
+  const uint32_t *d_words;        /* [n_words] ECW v1 stream                            */
+  const uint64_t *d_chunk_bit_off;/* [n_chunks + 1], n_chunks = ceil(n_symbols / chunk) */
+  uint64_t n_words;
+  uint64_t n_symbols;             /* codes in the tensor; 0 = empty tensor (skipped)   */
+  uint32_t chunk_symbols;         /* C >= 1, a multiple of lanes, <= 2^20               */
+  uint32_t lanes;                 /* W in {1, 2, 4, 8, 16, 32, 64}                      */
+  uint32_t sym_bits;              /* must equal the codebook the LUT was built from    */
+  uint32_t max_len;               /* likewise                                           */
+  uint64_t lut_bytes;             /* bytes readable at d_lut (entro_lut_bytes); a table
+                                     whose header claims more is rejected (ENTRO_F_LUT) */
+} entro_tensor;
+
+/* Operands of the fused GEMV for one tensor, read as a [rows][cols] row-major
+ * matrix (rows = output features, cols = input features). */
+typedef struct {
+  uint32_t rows, cols;      /* rows * cols == n_symbols; cols % lanes == 0;
+                               chunk_symbols % cols == 0 (chunks hold whole rows)   */
+  const uint16_t *d_x;      /* bf16 activations [batch][cols]                        */
+  float *d_y;               /* fp32 outputs [batch][rows], overwritten              */
+} entro_gemv_item;
+
+/* Size in bytes of the decode table built from cb (0 if cb is invalid).
+ * The table holds a 16-byte header and 4-byte entries: one level indexed by
+ * the next K stream bits (K = longest code if <= 12, else 11) and, for codes
+ * longer than K, second-level tables indexed by the following bits.  Each
+ * entry carries the code length, the code value and its bf16 dequantized
+ * value.  Defined by: canonical Huffman codes (reading of EntroLLM's Huffman
+ * step, see the stream layout above) and the dequantization rule of
+ * entro_codebook. */
+size_t entro_lut_bytes(const entro_codebook *cb);
+
+/* Build the decode table of cb into host_lut (cap bytes, 4-byte aligned).
+ * Errors: ENTRO_E_INVAL (null pointers, cap too small), ENTRO_E_CODEBOOK
+ * (a length > max_len, Kraft sum > 1, or no code value present),
+ * ENTRO_E_FORMAT (sym_bits not 4/8, max_len not in 1..16),
+ * ENTRO_E_UNSUPPORTED (table larger than 16 KiB of entries). */
+entro_status entro_lut_build(const entro_codebook *cb, void *host_lut, size_t cap);
+
+/* Decode n tensors to their codes: d_out[i] receives t[i].n_symbols bytes.
+ * Defined by: EntroLLM's parallel decoding of independent chunks
+ * (gist.science technical summary, Methodology item 3) and LazyWeights'
+ * interleaved-lane Huffman decoding (abstract).  One wavefront decodes
+ * 64 / lanes chunks in lockstep.  t and d_out are host arrays of n entries;
+ * d_status is a device array of n uint32 that the caller zeroes first. */
+entro_status entro_decode(const entro_tensor *t, size_t n, uint8_t *const *d_out,
+                          uint32_t *d_status, hipStream_t stream);
+
+/* Decode n tensors and dequantize: d_out_bf16[i] receives t[i].n_symbols bf16
+ * values, RNE(f32(scale) * f32(q - zero_point)), the scale and zero point
+ * being those the LUT was built with.  Defined by: EntroLLM's tensor-level
+ * unsigned/asymmetric quantization (abstract; gist.science technical summary,
+ * Methodology item 1) undone after decoding. */
+entro_status entro_decode_dequant(const entro_tensor *t, size_t n, uint16_t *const *d_out_bf16,
+                                  uint32_t *d_status, hipStream_t stream);
+
+/* Fused decode + dequant + GEMV: for each tensor i,
+ *   g[i].d_y[b][o] = sum_k deq(W_i[o][k]) * x_i[b][k]   for b < batch,
+ * fp32 accumulation; the weights never reach memory in decoded form.
+ * Defined by: LazyWeights' decode on demand, where memory moves only coded
+ * bytes and the consuming matrix-vector work is unchanged (abstract);
+ * EntroLLM's note that token generation is bandwidth-bound (gist.science
+ * technical summary, Problem statement).  batch in 1..8; g is a host array
+ * of n items. */
+entro_status entro_decode_gemv(const entro_tensor *t, size_t n, const entro_gemv_item *g,
+                               uint32_t batch, uint32_t *d_status, hipStream_t stream);
+
+/* Static English text for a status code. */
+const char *entro_status_str(entro_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENTRO_H */

@@ -1,0 +1,95 @@
+"""Coded test cases built only by the oracle (code lengths, stream, expected
+values) plus the library's own decode table, and helpers that run the device
+entry points through the C ABI."""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+import entropy_coded_weight_canonical_amd as ent
+from oracle import ccodec, huffman, quant
+from oracle.dequant import dequant_bf16
+
+
+@dataclass
+class Case:
+    q: np.ndarray            # flattened uint8 codes (the expected decode)
+    bits: int
+    max_len: int
+    lengths: np.ndarray
+    scale: np.float32
+    zp: int
+    chunk: int
+    lanes: int
+    words: np.ndarray
+    offs: np.ndarray
+    lut: np.ndarray
+    rows: int = 0
+    cols: int = 0
+
+    @property
+    def n(self) -> int:
+        return int(self.q.size)
+
+    def expected_bf16(self) -> np.ndarray:
+        return dequant_bf16(self.q, self.scale, self.zp)
+
+
+def make_case(q, bits, chunk, lanes, scale=0.0123, zp=None, max_len=None, lengths=None,
+              rows=0, cols=0) -> Case:
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.uint8).ravel())
+    max_len = max_len or (16 if bits == 8 else 12)
+    if lengths is None:
+        lengths = huffman.code_lengths(quant.histogram(q, bits), max_len) if q.size else None
+    if lengths is None:  # empty tensor: any valid codebook
+        lengths = np.zeros(1 << bits, dtype=np.int64)
+        lengths[0] = 1
+    zp = (1 << (bits - 1)) if zp is None else zp
+    words, offs = ccodec.encode(q, lengths, chunk, lanes, threads=8)
+    lut = ent.lut_build(lengths, bits, max_len, np.float32(scale), zp)
+    return Case(q, bits, max_len, np.asarray(lengths, dtype=np.uint8), np.float32(scale), int(zp), chunk,
+                lanes, words, offs, lut, rows, cols)
+
+
+def upload(case: Case, device="cuda"):
+    return ent.DeviceTensor.upload(case.lut, case.words, case.offs, case.n, case.chunk, case.lanes, case.bits,
+                                   case.max_len, device=device)
+
+
+def run_decode(cases, mode="u8", device="cuda"):
+    """Decode ``cases`` in one call; returns (outputs as numpy, status numpy)."""
+    import torch
+
+    dts = [upload(c, device) for c in cases]
+    dtype = torch.uint8 if mode == "u8" else torch.int16
+    outs = [torch.empty(max(c.n, 1), dtype=dtype, device=device) for c in cases]
+    if mode == "u8":
+        for o in outs:
+            o.fill_(0xA5)
+    else:
+        for o in outs:
+            o.fill_(0x5A5A)
+    status = torch.zeros(len(cases), dtype=torch.int32, device=device)
+    fn = ent.decode if mode == "u8" else ent.decode_dequant
+    fn([d.desc for d in dts], [o.data_ptr() for o in outs], status.data_ptr())
+    torch.cuda.synchronize()
+    res = []
+    for c, o in zip(cases, outs):
+        a = o.cpu().numpy()[: c.n]
+        res.append(a if mode == "u8" else a.view(np.uint16))
+    return res, status.cpu().numpy().view(np.uint32)
+
+
+def run_gemv(cases, xs, batch, device="cuda"):
+    """Fused GEMV of ``cases`` (each with rows/cols) on bf16 inputs ``xs``."""
+    import torch
+
+    dts = [upload(c, device) for c in cases]
+    dx = [torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device) for x in xs]
+    dy = [torch.full((batch, max(c.rows, 1)), float("nan"), dtype=torch.float32, device=device) for c in cases]
+    items = [ent.GemvItem(c.rows, c.cols, x.data_ptr(), y.data_ptr()) for c, x, y in zip(cases, dx, dy)]
+    status = torch.zeros(len(cases), dtype=torch.int32, device=device)
+    ent.decode_gemv([d.desc for d in dts], items, batch, status.data_ptr())
+    torch.cuda.synchronize()
+    return [y.cpu().numpy()[:, : c.rows] for c, y in zip(cases, dy)], status.cpu().numpy().view(np.uint32)

@@ -1,0 +1,231 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Codes and bf16 values must be bit-exact; fused GEMV outputs within a
+floor-guarded relative error of 1e-2 of the float64 oracle (fp32
+accumulation gives ~1e-5).  Streams, code lengths and expected values come
+from the oracle only; the library contributes its decode table builder and
+the kernels under test.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import gemv as ogemv
+from oracle import quant
+from synth import CODE_KINDS, TensorSpec, activations_bf16, fuzz_codes, weights
+from tests._cases import make_case, run_decode, run_gemv
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import entropy_coded_weight_canonical_amd as ent
+
+    ent.load()
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+LANE_GRID = [(1, 16), (2, 8), (4, 4), (8, 2), (16, 3), (32, 1), (32, 4), (64, 1), (64, 3)]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("lanes,mult", LANE_GRID)
+def test_fuzz_grid_u8_and_bf16(bits, lanes, mult):
+    cases = []
+    for i, kind in enumerate(CODE_KINDS):
+        chunk = lanes * mult * 8
+        n = chunk * (3 + i) + (17 * i + 5) % chunk   # several chunks and a ragged tail
+        q = fuzz_codes(1000 * lanes + 10 * mult + i, n, bits, kind)
+        cases.append(make_case(q, bits, chunk, lanes, scale=0.0031 * (i + 1), zp=(7 * i) % (1 << bits)))
+    say(f"fuzz bits={bits} lanes={lanes} mult={mult}")
+    outs, st = run_decode(cases, "u8")
+    assert (st == 0).all(), st
+    for c, o in zip(cases, outs):
+        assert np.array_equal(o, c.q)
+    outs, st = run_decode(cases, "bf16")
+    assert (st == 0).all(), st
+    for c, o in zip(cases, outs):
+        assert np.array_equal(o, c.expected_bf16())
+
+
+def test_longest_codes_use_second_level():
+    counts = np.zeros(256, dtype=np.int64)
+    counts[:40] = (2.0 ** np.arange(40, 0, -1)).astype(np.int64) // 2 + 1
+    rng = np.random.default_rng(3)
+    q = rng.choice(256, size=200_000, p=counts / counts.sum()).astype(np.uint8)
+    # force the rarest symbols in so that 16-bit codes occur in the stream
+    q[rng.choice(q.size, 40, replace=False)] = np.arange(40, dtype=np.uint8)
+    c = make_case(q, 8, 4096, 32)
+    assert c.lengths.max() >= 15
+    say("two-level table")
+    outs, st = run_decode([c], "u8")
+    assert st[0] == 0 and np.array_equal(outs[0], c.q)
+    outs, st = run_decode([c], "bf16")
+    assert st[0] == 0 and np.array_equal(outs[0], c.expected_bf16())
+
+
+def test_edge_cases_in_one_batch():
+    cases = [
+        make_case(np.zeros(0, dtype=np.uint8), 4, 64, 64),                 # empty tensor
+        make_case(np.full(1000, 9, dtype=np.uint8), 4, 256, 32),           # single symbol
+        make_case(fuzz_codes(1, 1, 8, "skewed"), 8, 4096, 64),             # one symbol total
+        make_case(fuzz_codes(2, 63, 8, "skewed"), 8, 4096, 64),            # fewer symbols than lanes
+        make_case(fuzz_codes(3, 4096 * 3, 4, "uniform"), 4, 4096, 64),     # exact multiple
+        make_case(fuzz_codes(4, 100_000, 4, "two"), 4, 64, 64),            # 1-bit codes, short chunks
+    ]
+    say("edge cases")
+    for mode in ("u8", "bf16"):
+        outs, st = run_decode(cases, mode)
+        assert (st == 0).all(), st
+        for c, o in zip(cases, outs):
+            exp = c.q if mode == "u8" else c.expected_bf16()
+            assert np.array_equal(o, exp)
+
+
+def test_more_tensors_than_one_launch_and_mixed_lanes():
+    cases = []
+    for i in range(45):
+        lanes = [64, 32, 64, 8][i % 4]
+        bits = 8 if i % 3 else 4
+        q = fuzz_codes(50 + i, 5000 + 37 * i, bits, CODE_KINDS[i % len(CODE_KINDS)])
+        cases.append(make_case(q, bits, lanes * 32, lanes, scale=0.001 * (i + 1), zp=i % 16))
+    say("45 tensors")
+    outs, st = run_decode(cases, "bf16")
+    assert (st == 0).all(), st
+    for c, o in zip(cases, outs):
+        assert np.array_equal(o, c.expected_bf16())
+
+
+def test_faults_are_flagged_not_fatal():
+    import entropy_coded_weight_canonical_amd as ent
+
+    base = make_case(fuzz_codes(9, 50_000, 8, "skewed"), 8, 4096, 32)
+    cases = []
+    # 1. bit flips in the stream
+    c = make_case(base.q, 8, 4096, 32)
+    rng = np.random.default_rng(0)
+    flip = rng.choice(c.words.size, 50, replace=False)
+    c.words = c.words.copy()
+    c.words[flip] ^= np.uint32(0x00400000)
+    cases.append(c)
+    # 2. chunk offsets pointing past the stream
+    c = make_case(base.q, 8, 4096, 32)
+    c.offs = c.offs.copy()
+    c.offs[-1] += np.uint64(32 * 1000)
+    cases.append(c)
+    # 3. offsets not multiples of 32
+    c = make_case(base.q, 8, 4096, 32)
+    c.offs = c.offs.copy()
+    c.offs[3] += np.uint64(5)
+    cases.append(c)
+    # 4. table built for another code width
+    c = make_case(base.q, 8, 4096, 32)
+    c.lut = ent.lut_build(np.r_[np.ones(2), np.zeros(14)].astype(np.uint8), 4, 12, 1.0, 0)
+    cases.append(c)
+    # 5. a word missing from the end (offsets still consistent)
+    c = make_case(base.q, 8, 4096, 32)
+    c.words = c.words[:-1].copy()
+    c.offs = c.offs.copy()
+    c.offs[-1] -= np.uint64(32)
+    cases.append(c)
+    # 6. a clean tensor after the faulty ones
+    cases.append(make_case(base.q, 8, 4096, 32))
+    say("fault injection")
+    outs, st = run_decode(cases, "u8")
+    assert st[0] != 0
+    assert st[1] & ent.FLAGS["offsets"]
+    assert st[2] & ent.FLAGS["offsets"]
+    assert st[3] == ent.FLAGS["lut"]
+    assert st[4] & (ent.FLAGS["overrun"] | ent.FLAGS["badcode"] | ent.FLAGS["padding"])
+    assert st[5] == 0 and np.array_equal(outs[5], base.q)
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, in the launch configuration the benchmark uses
+# --------------------------------------------------------------------------
+
+def _spec(workload):
+    return {"tensor_2048": TensorSpec("tensor_2048", 0, -1, "w", 2048, 2048, "w"),
+            "tensor_4096": TensorSpec("tensor_4096", 0, -1, "w", 4096, 4096, "w")}[workload]
+
+
+def test_tensor_2048_asymmetric_8bit_full_size():
+    qz = quant.quantize_asymmetric(weights(_spec("tensor_2048")), 8)
+    cases = [make_case(qz.q, 8, 4096, 32, scale=qz.scale, zp=qz.zero_point),
+             make_case(qz.q, 8, 4096, 64, scale=qz.scale, zp=qz.zero_point),
+             make_case(qz.q, 8, 4096, 1, scale=qz.scale, zp=qz.zero_point)]
+    say("tensor_2048 W=32/64/1")
+    outs, st = run_decode(cases, "u8")
+    assert (st == 0).all()
+    for c, o in zip(cases, outs):
+        assert np.array_equal(o, qz.q.ravel())
+    outs, st = run_decode(cases, "bf16")
+    assert (st == 0).all()
+    for c, o in zip(cases, outs):
+        assert np.array_equal(o, c.expected_bf16())
+
+
+def test_tensor_4096_unsigned_4bit_full_size_replicated():
+    qz = quant.quantize_unsigned(weights(_spec("tensor_4096")), 4)
+    c = make_case(qz.q, 4, 8192, 32, scale=qz.scale, zp=qz.zero_point)
+    say("tensor_4096 x16 replicas")
+    outs, st = run_decode([c] * 16, "bf16")
+    assert (st == 0).all()
+    exp = c.expected_bf16()
+    for o in outs:
+        assert np.array_equal(o, exp)
+
+
+# --------------------------------------------------------------------------
+# fused GEMV
+# --------------------------------------------------------------------------
+
+def _gemv_case(rows, cols, bits, seed, rows_per_chunk=1, lanes=64, scheme="mixed"):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_t(4, size=(rows, cols)) * 0.02).astype(np.float32)
+    qz = {"mixed": quant.quantize_mixed, "asymmetric": quant.quantize_asymmetric,
+          "unsigned": quant.quantize_unsigned}[scheme](w, bits)
+    return make_case(qz.q, bits, cols * rows_per_chunk, lanes, scale=qz.scale, zp=qz.zero_point,
+                     rows=rows, cols=cols)
+
+
+@pytest.mark.parametrize("batch", [1, 3, 8])
+def test_gemv_small_shapes(batch):
+    cases = [_gemv_case(37, 128, 4, 1), _gemv_case(64, 192, 8, 2, rows_per_chunk=3),
+             _gemv_case(100, 64, 4, 3, rows_per_chunk=7), _gemv_case(9, 320, 8, 4, lanes=32),
+             _gemv_case(33, 48, 4, 5, lanes=16, rows_per_chunk=2), _gemv_case(5, 8, 8, 6, lanes=1)]
+    xs = [activations_bf16("phi3_stack", i, c.cols, batch) for i, c in enumerate(cases)]
+    say(f"gemv small batch={batch}")
+    ys, st = run_gemv(cases, xs, batch)
+    assert (st == 0).all(), st
+    for c, x, y in zip(cases, xs, ys):
+        ref = ogemv.gemv_f64(c.expected_bf16().reshape(c.rows, c.cols), x)
+        assert ogemv.rel_err(y, ref) <= 1e-2
+        assert ogemv.rel_err(y, ref) <= 1e-4   # fp32 accumulation
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_gemv_mistral_shapes_sampled_layer(batch):
+    """One layer of the 4-bit Mistral-shaped stack at full size (row-aligned
+    chunks, 64 lanes), every output checked against the float64 oracle."""
+    specs = [s for s in __import__("synth").tensor_specs("mistral_stack") if s.layer == 0]
+    cases, xs = [], []
+    for gi, s in enumerate(specs):
+        qz = quant.quantize_mixed(weights(s), 4)
+        chunk = s.cols * max(1, round(8192 / s.cols))
+        cases.append(make_case(qz.q, 4, chunk, 64, scale=qz.scale, zp=qz.zero_point, rows=s.rows, cols=s.cols))
+        xs.append(activations_bf16("mistral_stack", gi, s.cols, batch))
+    say(f"gemv mistral layer0 batch={batch}")
+    ys, st = run_gemv(cases, xs, batch)
+    assert (st == 0).all(), st
+    for c, x, y in zip(cases, xs, ys):
+        ref = ogemv.gemv_f64(c.expected_bf16().reshape(c.rows, c.cols), x)
+        assert ogemv.rel_err(y, ref) <= 1e-2
