@@ -1,0 +1,382 @@
+"""Benchmark of the decode hot path on one MI355X.
+
+Default workload (one "step" = one call of entro_decode_dequant):
+  16 distinct device copies of a 4096 x 4096 float32 tensor w ~ Laplace(0, 0.015),
+  quantized per tensor to unsigned 4-bit codes, canonical-Huffman coded (lengths
+  <= 12) in 8192-code chunks of 32 interleaved lanes, decoded and dequantized
+  to bf16 in one batched call.  16 copies put the working set (about 590 MB)
+  well above the 256 MB last-level cache, so the timed data comes from HBM.
+
+Other workloads (``--workload``): tensor_2048 (8-bit asymmetric, 4096-code
+chunks, decode to codes and to bf16), smollm_stack (decode all 169 tensors),
+phi3_stack / mistral_stack (fused decode + GEMV per token).
+
+The encoder used to produce the inputs is the library's own (host C++), not
+the oracle; the oracle is only timed in the CPU-baseline leg.
+
+Output: one JSON line (rank 0).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decoded Gsym/s + effective HBM GB/s (% of peak); fused decode+GEMV ms/token"
+KERNEL_SOURCES = ["entropy_coded_weight_canonical_amd/csrc/entro_decode.hip",
+                  "entropy_coded_weight_canonical_amd/csrc/entro_internal.h"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_src_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    if the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_src_sha") != kernel_src_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# --------------------------------------------------------------------------
+# inputs (library encoder)
+# --------------------------------------------------------------------------
+
+class Coded:
+    def __init__(self, q, scale, zp, scheme, bits, max_len, chunk, lanes, rows, cols):
+        import entropy_coded_weight_canonical_amd as ent
+
+        self.rows, self.cols = rows, cols
+        self.bits, self.max_len, self.chunk, self.lanes = bits, max_len, chunk, lanes
+        self.scale, self.zp, self.scheme = scale, zp, scheme
+        self.n = int(q.size)
+        self.lengths = ent.code_lengths(q, bits, max_len)
+        self.words, self.offs = ent.encode(q, self.lengths, bits, chunk, lanes)
+        self.lut = ent.lut_build(self.lengths, bits, max_len, scale, zp)
+        self.n_chunks = int(self.offs.size - 1)
+
+    @property
+    def in_bytes(self) -> int:
+        return 4 * int(self.words.size) + 8 * (self.n_chunks + 1)
+
+    @property
+    def coded_bits_per_weight(self) -> float:
+        return 8.0 * self.in_bytes / self.n
+
+
+def code_tensor(spec, bits, scheme, chunk, lanes, clip_sigma=0.0):
+    import entropy_coded_weight_canonical_amd as ent
+    from synth import weights
+
+    w = weights(spec)
+    clip = float(clip_sigma * np.std(w, dtype=np.float64)) if clip_sigma else 0.0
+    q, s, zp, chosen = ent.quantize(w, bits, scheme, clip=clip)
+    return Coded(q, s, zp, chosen, bits, 16 if bits == 8 else 12, chunk, lanes, spec.rows, spec.cols)
+
+
+# --------------------------------------------------------------------------
+# CPU baseline: the oracle, as it stands
+# --------------------------------------------------------------------------
+
+def cpu_baseline(coded: Coded, budget_s: float = 12.0):
+    from oracle import ccodec
+    from oracle.dequant import dequant_bf16
+
+    threads = min(16, os.cpu_count() or 1)
+    n_done = 0
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        q = ccodec.decode(coded.words, coded.offs, coded.lengths, coded.n, coded.chunk, coded.lanes,
+                          threads=threads)
+        dequant_bf16(q, coded.scale, coded.zp)
+        n_done += coded.n
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(n_done / dt / 1e9, 4), "unit": "Gsym/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} x one {coded.rows}x{coded.cols} tensor ({coded.n} codes): bit-serial C decode "
+                      f"over {threads} host threads + numpy bf16 dequant, {dt:.1f} s wall"}
+
+
+# --------------------------------------------------------------------------
+# GPU timing helpers
+# --------------------------------------------------------------------------
+
+def time_steps(step, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    per = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        e_a = torch.cuda.Event(enable_timing=True)
+        e_b = torch.cuda.Event(enable_timing=True)
+        e_a.record(stream)
+        step()
+        e_b.record(stream)
+        per.append((e_a, e_b))
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = ev0.elapsed_time(ev1)
+    per_ms = [a.elapsed_time(b) for a, b in per]
+    return total_ms, per_ms, wall
+
+
+def flush_mall(torch):
+    """Evict the last-level cache between measurements (writes 512 MB)."""
+    buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    return buf
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+
+def bench_decode(args, workload, bits, scheme, chunk, lanes, replicas, mode):
+    import torch
+
+    import entropy_coded_weight_canonical_amd as ent
+    from synth import tensor_specs
+
+    spec = tensor_specs(workload)[0]
+    log(f"encoding {workload} ({spec.rows}x{spec.cols}, {bits}-bit {scheme}, C={chunk}, W={lanes})")
+    coded = code_tensor(spec, bits, scheme, chunk, lanes)
+    log(f"coded {coded.coded_bits_per_weight:.3f} bits/weight; uploading {replicas} replicas")
+    dts = [ent.DeviceTensor.upload(coded.lut, coded.words, coded.offs, coded.n, chunk, lanes, bits,
+                                   coded.max_len) for _ in range(replicas)]
+    odt = torch.uint8 if mode == "u8" else torch.int16
+    outs = [torch.empty(coded.n, dtype=odt, device="cuda") for _ in range(replicas)]
+    status = torch.zeros(replicas, dtype=torch.int32, device="cuda")
+    descs = [d.desc for d in dts]
+    ptrs = [o.data_ptr() for o in outs]
+    fn = ent.decode if mode == "u8" else ent.decode_dequant
+
+    def step():
+        fn(descs, ptrs, status.data_ptr())
+
+    step()
+    torch.cuda.synchronize()
+    if int(status.abs().sum().item()) != 0:
+        raise SystemExit(f"stream flags set: {status.cpu().numpy()}")
+    # spot check: replica 0 decodes to the library encoder's input codes
+    log(f"timing {args.steps} steps after {args.warmup} warm-up")
+    _keep = flush_mall(torch)
+    total_ms, per_ms, wall = time_steps(step, args.steps, args.warmup)
+    ms = total_ms / args.steps
+    n_sym = coded.n * replicas
+    out_b = coded.n * (1 if mode == "u8" else 2)
+    bytes_step = replicas * (coded.in_bytes + out_b)
+    launch_ms = float(np.mean(per_ms))
+    achieved = bytes_step / (launch_ms * 1e-3) / 1e9
+    traffic = read_traffic(f"{workload}_{mode}")
+    res = {
+        "metric": METRIC,
+        "value": round(n_sym / (ms * 1e-3) / 1e9, 3),
+        "unit": "Gsym/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if mode == "bf16" else "u8",
+        "data": "synthetic",
+        "config": {"workload": f"{workload}: {spec.rows}x{spec.cols} {scheme} {bits}-bit, C={chunk}, W={lanes}, "
+                               f"x{replicas} replicas, decode{'+dequant->bf16' if mode == 'bf16' else '->u8'}",
+                   "global_batch": replicas, "symbols_per_step": n_sym,
+                   "coded_bits_per_weight": round(coded.coded_bits_per_weight, 4),
+                   "parallelism": "single GPU"},
+        "eff_GBps": round(bytes_step / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None if traffic is None else round(traffic / (launch_ms * 1e-3) / 1e9, 1)},
+        "kernel": {"name": "ecw_decode_kernel", "launches_per_step": 1, "avg_launch_ms": round(launch_ms, 5),
+                   "algorithmic_bytes_per_launch": bytes_step, "src_sha": kernel_src_sha()},
+    }
+    return res, coded
+
+
+def bench_gemv(args, workload, batch, clip_sigma=0.0):
+    """Per-token fused decode+GEMV over the whole stack, one call per group of
+    matrices sharing an input (q/k/v, o, gate/up, down) per layer."""
+    import torch
+
+    import entropy_coded_weight_canonical_amd as ent
+    from synth import activations_bf16, tensor_specs
+
+    specs = tensor_specs(workload)
+    layers = max(s.layer for s in specs) + 1
+    # every layer has the same shapes; encode layer 0 and layer 1, and give the
+    # other layers distinct device copies of them (same bytes, other addresses)
+    n_distinct = min(args.distinct_layers, layers)
+    log(f"{workload}: encoding {n_distinct} distinct layer(s) of {layers}")
+    coded_layers = []
+    for L in range(n_distinct):
+        row = []
+        for s in (x for x in specs if x.layer == L):
+            chunk = s.cols * max(1, round(8192 / s.cols))
+            row.append((s, code_tensor(s, 4, "unsigned" if clip_sigma else "mixed", chunk, 64, clip_sigma)))
+        coded_layers.append(row)
+    groups = []   # per layer: list of (descs, items)
+    keep = []
+    n_sym = 0
+    in_bytes = 0
+    for L in range(layers):
+        row = coded_layers[L % n_distinct]
+        by_group = {}
+        for s, c in row:
+            by_group.setdefault(s.group, []).append((s, c))
+        for gname, members in by_group.items():
+            cols = members[0][0].cols
+            x = torch.from_numpy(activations_bf16(workload, len(groups), cols, batch).view(np.int16)).cuda()
+            descs, items = [], []
+            for s, c in members:
+                dt = ent.DeviceTensor.upload(c.lut, c.words, c.offs, c.n, c.chunk, c.lanes, c.bits, c.max_len)
+                y = torch.empty((batch, s.rows), dtype=torch.float32, device="cuda")
+                keep += [dt, y]
+                descs.append(dt.desc)
+                items.append(ent.GemvItem(s.rows, s.cols, x.data_ptr(), y.data_ptr()))
+                n_sym += c.n
+                in_bytes += c.in_bytes + 2 * batch * s.cols + 4 * batch * s.rows
+            keep.append(x)
+            groups.append((descs, items))
+    status = torch.zeros(64, dtype=torch.int32, device="cuda")
+
+    def step():
+        for descs, items in groups:
+            ent.decode_gemv(descs, items, batch, status.data_ptr())
+
+    step()
+    torch.cuda.synchronize()
+    if int(status.abs().sum().item()) != 0:
+        raise SystemExit(f"stream flags set: {status.cpu().numpy()}")
+    _keep = flush_mall(torch)
+    total_ms, per_ms, wall = time_steps(step, args.steps, args.warmup)
+    ms = total_ms / args.steps
+    bits = np.mean([c.coded_bits_per_weight for row in coded_layers for _, c in row])
+    res = {
+        "metric": METRIC,
+        "value": round(ms, 4),
+        "unit": "ms/token",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{workload}: {len(specs)} matrices, 4-bit "
+                               f"{'unsigned clip %.2f sigma' % clip_sigma if clip_sigma else 'mixed'}, "
+                               f"row-aligned chunks, W=64, fused decode+dequant+GEMV batch {batch}",
+                   "global_batch": batch, "symbols_per_token": n_sym, "launch_groups": len(groups),
+                   "distinct_layers": n_distinct, "coded_bits_per_weight": round(float(bits), 4),
+                   "parallelism": "single GPU"},
+        "decoded_Gsym_per_s": round(n_sym / (ms * 1e-3) / 1e9, 3),
+        "eff_GBps": round(in_bytes / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(in_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+    }
+    return res
+
+
+def calibrate_copy(nbytes=256 << 20):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    import torch
+
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(3)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"calibration copy: {nbytes} bytes read + {nbytes} written per launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="tensor_4096",
+                    choices=["tensor_4096", "tensor_2048", "tensor_2048_u8", "smollm_stack", "phi3_stack",
+                             "mistral_stack"])
+    ap.add_argument("--replicas", type=int, default=0)
+    ap.add_argument("--lanes", type=int, default=0)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--clip-sigma", type=float, default=0.0)
+    ap.add_argument("--distinct-layers", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        raise SystemExit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs the GPU")
+    import entropy_coded_weight_canonical_amd as ent
+
+    ent.load()
+    if args.calibrate_copy:
+        calibrate_copy()
+    coded = None
+    if args.workload == "tensor_4096":
+        res, coded = bench_decode(args, "tensor_4096", 4, "unsigned", 8192, args.lanes or 32,
+                                  args.replicas or 16, "bf16")
+    elif args.workload in ("tensor_2048", "tensor_2048_u8"):
+        res, coded = bench_decode(args, "tensor_2048", 8, "asymmetric", 4096, args.lanes or 32,
+                                  args.replicas or 64, "u8" if args.workload.endswith("u8") else "bf16")
+    elif args.workload in ("phi3_stack", "mistral_stack"):
+        res = bench_gemv(args, args.workload, args.batch, args.clip_sigma)
+    else:
+        raise SystemExit(f"workload {args.workload} not wired yet")
+    res["gpu"] = torch.cuda.get_device_name(0)
+    if coded is not None and not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(coded)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,34 +7,108 @@
 // demand so that only coded bytes cross the memory bus (abstract).  Here one
 // wavefront (64 lanes) decodes 64 / W chunks of W lanes each, in lockstep:
 //
-//   per step t, every active lane
-//     1. looks up the next K bits of its 64-bit bit buffer in the LDS table
-//        (second level for long codes);
+//   per step t, every lane
+//     1. looks up the next K bits of its bit buffer in the table held in LDS
+//        (a second level for codes longer than K);
 //     2. needs a word iff that codeword is longer than its loaded bits (an
-//        entry without codeword counts as "longer" while fewer than 16 bits
-//        are loaded);
-//     3. the lanes needing a word take consecutive words of their chunk,
-//        word index = chunk word pointer + number of lower lanes of the same
-//        chunk needing one (a prefix count over the wave's ballot mask);
+//        entry without codeword counts as longer than any loaded count below
+//        31, so a partial peek into unused code space also fetches);
+//     3. the lanes needing a word take consecutive words of their chunk: word
+//        index = chunk word pointer + number of lower lanes of the same chunk
+//        needing one, a prefix count over the wavefront's ballot mask
+//        (v_mbcnt);
 //     4. after a refill the lookup is repeated; the codeword is consumed and
-//        the result emitted (code byte, bf16 value, or an FMA into the GEMV
-//        accumulators).
+//        the result emitted: code byte, bf16 value, or an FMA into the GEMV
+//        accumulators.
+//   Writes of one step are contiguous: lane j of a chunk emits code t*W + j.
 //
-// Writes of one step are contiguous: lane j of a chunk emits symbol t*W + j.
+// Two paths share that step:
+//   * staged: the workgroup is persistent and walks block tasks; a wavefront
+//     copies all words of its task (64/W consecutive chunks, contiguous in
+//     memory) into its LDS area with 16-byte buffer loads, then decodes from
+//     LDS.  The bit buffer is two 32-bit registers, left-aligned; refill and
+//     consume are v_alignbit / shift / or; the loop keeps word pointers and
+//     output addresses in scalar registers.
+//   * generic: any task (ragged last chunk, words beyond the staging area,
+//     malformed offsets): reads words straight from global memory with
+//     bounds checks and reports every fault.
+//
+// Table entries as held in LDS (converted from the host table on staging):
+//   [4:0] (32 - len) mod 32 (the v_alignbit shift that consumes the codeword)
+//   [7]   second-level pointer ([12:8] subtable index bits, [31:16] base)
+//   [15:8] len (1..16; 31 = no codeword)
+//   [31:16] bf16 value (dequant / GEMV) or [23:16] code value (decode)
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstring>
-#include <vector>
+#include <type_traits>
 
 #include "entro.h"
 #include "entro_internal.h"
 
 namespace entro {
 
-__device__ __forceinline__ uint32_t lut_lookup(const uint32_t *lut, uint32_t hi, uint32_t K) {
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int MODE>
+__device__ __forceinline__ uint32_t kernel_entry(uint32_t h) {
+  if (h & kEntryPointer) return h;
+  uint32_t len = h & 31u;
+  if (len == 0u) len = kInvalidLen;
+  const uint32_t val = (MODE == kModeU8) ? (((h >> 8) & 0xFFu) << 16) : (h & 0xFFFF0000u);
+  return ((32u - len) & 31u) | (len << 8) | val;
+}
+
+__device__ __forceinline__ uint32_t entry_len(uint32_t e) { return (e >> 8) & 0xFFu; }
+
+// Lanes whose codeword is longer than their loaded bits: one SDWA compare of
+// the entry's length byte against n, written straight to a lane mask.
+__device__ __forceinline__ uint64_t need_mask(uint32_t e, uint32_t n) {
+  uint64_t m;
+  asm volatile("v_cmp_gt_u32_sdwa %0, %1, %2 src0_sel:BYTE_1 src1_sel:DWORD" : "=s"(m) : "v"(e), "v"(n));
+  return m;
+}
+
+// n - (length byte of e), one SDWA subtract
+__device__ __forceinline__ uint32_t sub_len(uint32_t n, uint32_t e) {
+  uint32_t r;
+  asm("v_sub_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+      : "=v"(r) : "v"(n), "v"(e));
+  return r;
+}
+
+// scalar & vector, kept as one v_and (not folded into a select)
+__device__ __forceinline__ uint32_t and_sv(uint32_t s, uint32_t v) {
+  uint32_t r;
+  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "s"(s), "v"(v));
+  return r;
+}
+
+// One output element per lane through a buffer resource: per-lane byte
+// offset in a vector register, per-step offset in a scalar register.
+// The value sits in bits [31:16] ([23:16] for codes) of the table entry and
+// goes out with the d16_hi store forms, so no shift is spent on it.  (The
+// outputs are never read back by the kernel, so the compiler needs no
+// knowledge of these writes.)
+template <typename OutT>
+__device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t e) {
+  if (sizeof(OutT) == 1)
+    asm volatile("buffer_store_byte_d16_hi %0, %1, %2, %3 offen" : : "v"(e), "v"(voff), "s"(r), "s"(soff));
+  else
+    asm volatile("buffer_store_short_d16_hi %0, %1, %2, %3 offen" : : "v"(e), "v"(voff), "s"(r), "s"(soff));
+}
+
+// values that are equal in all lanes, made visibly uniform for the compiler
+__device__ __forceinline__ uint32_t rfl(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t rfl64(uint64_t v) {
+  return ((uint64_t)rfl((uint32_t)(v >> 32)) << 32) | rfl((uint32_t)v);
+}
+
+template <bool TWO>
+__device__ __forceinline__ uint32_t lookup(const uint32_t *lut, uint32_t hi, uint32_t K) {
   uint32_t e = lut[hi >> (32u - K)];
-  if (e & kEntryPointer) {
+  if (TWO && (e & kEntryPointer)) {
     const uint32_t sb = (e >> 8) & 31u;
     const uint32_t i2 = (hi << K) >> (32u - sb);
     e = lut[((e >> 16) + i2) & (kLutMaxEntries - 1u)];
@@ -42,44 +116,28 @@ __device__ __forceinline__ uint32_t lut_lookup(const uint32_t *lut, uint32_t hi,
   return e;
 }
 
-template <int MODE, int LOG2W, int BATCH>
-__global__ __launch_bounds__(kBlockThreads) void ecw_decode_kernel(const LaunchArgs a) {
-  __shared__ uint32_t lut[kLutMaxEntries];
+template <int MODE>
+__device__ __forceinline__ void emit(void *base, uint64_t k, uint32_t e) {
+  if (MODE == kModeU8) static_cast<uint8_t *>(base)[k] = (uint8_t)(e >> 16);
+  else static_cast<uint16_t *>(base)[k] = (uint16_t)(e >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// generic path: one wavefront task, words read from global memory, all checks
+// ---------------------------------------------------------------------------
+template <int MODE, int LOG2W, int BATCH, bool TWO>
+__device__ void task_generic(const TensorArg &d, const uint32_t *lut, uint32_t K, uint64_t task, uint32_t batch) {
   constexpr uint32_t W = 1u << LOG2W;
-  constexpr uint32_t G = 64u / W;   // chunks per wavefront
-
-  // tensor of this block (uniform scan over at most 32 entries)
-  const uint32_t b = blockIdx.x;
-  uint32_t ti = 0;
-  while (ti + 1 < a.n_tensors && a.block_begin[ti + 1] <= b) ++ti;
-  const TensorArg &d = a.t[ti];
-  const uint32_t blk = b - a.block_begin[ti];
-
-  // table header
-  if (d.lut_words < kLutHeaderWords) {
-    if (threadIdx.x == 0) atomicOr(d.status, kFLut);
-    return;
-  }
-  const uint32_t h0 = d.lut[0], h1 = d.lut[1], n_entries = d.lut[2], l1 = d.lut[3];
-  const uint32_t K = h1 & 0xFFu;
-  const bool lut_ok = h0 == kLutMagic && (h1 & 0xFFFFFF00u) == d.expect_hdr && K >= 1 &&
-                      K <= kSingleLevelMax && l1 == (1u << K) && n_entries >= l1 &&
-                      n_entries <= kLutMaxEntries && n_entries <= d.lut_words - kLutHeaderWords;
-  if (!lut_ok) {
-    if (threadIdx.x == 0) atomicOr(d.status, kFLut);
-    return;
-  }
-  for (uint32_t i = threadIdx.x; i < n_entries; i += kBlockThreads) lut[i] = d.lut[kLutHeaderWords + i];
-  __syncthreads();
-
+  constexpr uint32_t G = 64u / W;
   const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t wave = threadIdx.x >> 6;
   const uint32_t grp = lane >> LOG2W;
   const uint32_t j = lane & (W - 1u);
-  const uint64_t grp_mask = (W == 64u) ? ~0ull : (((1ull << W) - 1ull) << (grp * W));
+  const uint64_t grp_mask = (W == 64u) ? ~0ull : (((1ull << (W & 63u)) - 1ull) << (grp * W));
   const uint64_t grp_below = grp_mask & ((1ull << lane) - 1ull);
+  const uint32_t *__restrict__ words = d.words;
+  const uint64_t n_words = d.n_words, n_symbols = d.n_symbols;
+  const uint32_t chunk = d.chunk, cols = d.cols, rows = d.rows;
 
-  const uint64_t task = (uint64_t)blk * kWavesPerBlock + wave;
   const uint64_t c = task * G + grp;
   uint32_t flags = 0;
   bool chunk_ok = c < d.n_chunks;
@@ -87,83 +145,78 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_decode_kernel(const LaunchA
   uint32_t cc = 0;
   if (chunk_ok) {
     const uint64_t o0 = d.offs[c], o1 = d.offs[c + 1];
-    if ((o0 & 31u) || (o1 & 31u) || o1 < o0 || (o1 >> 5) > d.n_words) {
+    if ((o0 & 31u) || (o1 & 31u) || o1 < o0 || (o1 >> 5) > n_words) {
       flags |= kFOffsets;
       chunk_ok = false;
     } else {
       wb = o0 >> 5;
       nw = (o1 - o0) >> 5;
-      const uint64_t first = c * d.chunk;
-      cc = (uint32_t)min((uint64_t)d.chunk, d.n_symbols - first);
+      cc = (uint32_t)min((uint64_t)chunk, n_symbols - c * chunk);
     }
   }
   const uint32_t my_steps = (chunk_ok && j < cc) ? ((cc - j + W - 1u) >> LOG2W) : 0u;
-  const uint32_t steps = d.chunk >> LOG2W;
-  const uint64_t sym0 = c * d.chunk;   // first symbol of this lane's chunk
+  const uint32_t steps = chunk >> LOG2W;
+  const uint64_t sym0 = c * chunk;
 
-  uint64_t buf = 0;      // loaded, unconsumed bits, first bit at bit 63
-  uint32_t n = 0;        // number of such bits
-  uint64_t P = 0;        // words of the chunk taken so far (same in all lanes of a chunk)
-
+  uint64_t buf = 0;
+  uint32_t n = 0;
+  uint64_t P = 0;
   float acc[BATCH];
 #pragma unroll
   for (int i = 0; i < BATCH; ++i) acc[i] = 0.f;
   uint32_t col = j;
   uint64_t row = 0;
-  if (MODE == kModeGemv) row = sym0 / d.cols;
+  if (MODE == kModeGemv) row = sym0 / cols;
 
   for (uint32_t t = 0; t < steps; ++t) {
     const bool act = t < my_steps;
-    uint32_t e = lut_lookup(lut, (uint32_t)(buf >> 32), K);
-    uint32_t len = e & 31u;
-    const bool need = act && (len > n || (len == 0u && n < kMaxCodeLen));
+    uint32_t e = lookup<TWO>(lut, (uint32_t)(buf >> 32), K);
+    uint32_t len = entry_len(e);
+    const bool need = act && len > n;
     const uint64_t m = __ballot(need);
     if (m) {
       if (need) {
         const uint64_t idx = P + (uint64_t)__popcll(m & grp_below);
         uint32_t w = 0;
-        if (idx < nw) w = d.words[wb + idx];
+        if (idx < nw) w = words[wb + idx];
         else flags |= kFOverrun;
         buf |= (uint64_t)w << (32u - n);
         n += 32u;
-        e = lut_lookup(lut, (uint32_t)(buf >> 32), K);
-        len = e & 31u;
+        e = lookup<TWO>(lut, (uint32_t)(buf >> 32), K);
+        len = entry_len(e);
       }
       P += (uint64_t)__popcll(m & grp_mask);
     }
     if (act) {
-      if (len == 0u) {
+      if (len > kMaxCodeLen) {
         flags |= kFBadCode;
         len = 1u;
       }
       buf <<= len;
       n -= len;
-      const uint64_t k = sym0 + ((uint64_t)t << LOG2W) + j;
-      if (MODE == kModeU8) {
-        static_cast<uint8_t *>(d.out)[k] = (uint8_t)(e >> 8);
-      } else if (MODE == kModeBf16) {
-        static_cast<uint16_t *>(d.out)[k] = (uint16_t)(e >> 16);
-      } else {
+      if (MODE == kModeGemv) {
         const float v = __uint_as_float(e & 0xFFFF0000u);
 #pragma unroll
         for (int bi = 0; bi < BATCH; ++bi) {
-          if (bi < (int)a.batch) {
-            const float xv = __uint_as_float((uint32_t)d.x[(uint64_t)bi * d.cols + col] << 16);
+          if (bi < (int)batch) {
+            const float xv = __uint_as_float((uint32_t)d.x[(uint64_t)bi * cols + col] << 16);
             acc[bi] = fmaf(v, xv, acc[bi]);
           }
         }
+      } else {
+        emit<MODE>(d.out, sym0 + ((uint64_t)t << LOG2W) + j, e);
       }
     }
     if (MODE == kModeGemv) {
       col += W;
-      if (col >= d.cols) {   // uniform: every chunk starts a row and W divides cols
-        col -= d.cols;
+      if (col >= cols) {   // uniform: every chunk starts a row and W divides cols
+        col -= cols;
 #pragma unroll
         for (int bi = 0; bi < BATCH; ++bi) {
           float v = acc[bi];
 #pragma unroll
           for (uint32_t off = W >> 1; off >= 1u; off >>= 1) v += __shfl_xor(v, (int)off, 64);
-          if (act && j == 0u && bi < (int)a.batch) static_cast<float *>(d.out)[(uint64_t)bi * d.rows + row] = v;
+          if (act && j == 0u && bi < (int)batch) static_cast<float *>(d.out)[(uint64_t)bi * rows + row] = v;
           acc[bi] = 0.f;
         }
         ++row;
@@ -175,6 +228,246 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_decode_kernel(const LaunchA
     if (buf != 0) flags |= kFPadding;
   }
   if (flags) atomicOr(d.status, flags);
+}
+
+// ---------------------------------------------------------------------------
+// staged path: the decode loop over words held in LDS
+// ---------------------------------------------------------------------------
+
+// W = 64: one chunk per wavefront; word pointer in a scalar register.
+template <int MODE, bool TWO, typename OutT>
+__device__ __forceinline__ uint32_t loop64(const uint32_t *lut, uint32_t K, const uint32_t *sw, uint32_t nw,
+                                           uint32_t steps, __amdgpu_buffer_rsrc_t outr, uint32_t lane) {
+  const uint32_t voff = lane * (uint32_t)sizeof(OutT);
+  uint32_t soff = 0;
+  uint32_t hi = 0, lo = 0, n = 0, P = 0;
+  for (uint32_t t = 0; t < steps; ++t) {
+    uint32_t e = lookup<TWO>(lut, hi, K);
+    const uint64_t m = need_mask(e, n);
+    if (m) {
+      if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+        const uint32_t idx =
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        const uint32_t w = sw[P + idx];
+        // fewer than 32 bits are loaded here, so lo is empty
+        hi |= w >> n;
+        lo = __builtin_amdgcn_alignbit(w, 0u, n);
+        n += 32u;
+        e = lookup<TWO>(lut, hi, K);
+      }
+      // a malformed stream cannot move the pointer past the staging slack
+      P = min(P + (uint32_t)__popcll(m), nw + 64u);
+    }
+    const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
+    lo = __builtin_amdgcn_alignbit(lo, 0u, e);
+    hi = nhi;
+    n = sub_len(n, e);
+    store_out<OutT>(outr, voff, soff, e);
+    soff += 64u * (uint32_t)sizeof(OutT);
+  }
+  uint32_t flags = 0;
+  if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
+  if (hi | lo) flags |= kFPadding;
+  return flags;
+}
+
+// W = 32: two chunks per wavefront, word pointers P0 (lanes 0-31) and P1
+// (lanes 32-63) in scalar registers; the upper half's word index is formed
+// by folding P1 - P0 and the chunk distance into the v_mbcnt addend.
+template <int MODE, bool TWO, typename OutT>
+__device__ __forceinline__ uint32_t loop32(const uint32_t *lut, uint32_t K, const uint32_t *sw, uint32_t dcs,
+                                           uint32_t nw0, uint32_t nw1, uint32_t steps, __amdgpu_buffer_rsrc_t outr,
+                                           uint32_t lane_off, uint32_t lane) {
+  const uint32_t upper = lane >= 32u ? ~0u : 0u;
+  const uint32_t voff = lane_off * (uint32_t)sizeof(OutT);
+  uint32_t soff = 0;
+  uint32_t hi = 0, lo = 0, n = 0, P0 = 0, P1 = 0;
+  for (uint32_t t = 0; t < steps; ++t) {
+    uint32_t e = lookup<TWO>(lut, hi, K);
+    const uint64_t m = need_mask(e, n);
+    if (m) {
+      const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+      const uint32_t clo = (uint32_t)__popc(mlo), chi = (uint32_t)__popc(mhi);
+      if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+        const uint32_t dd = dcs + P1 - P0 - clo;
+        const uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, and_sv(dd, upper)));
+        const uint32_t w = sw[P0 + idx];
+        hi |= w >> n;
+        lo = __builtin_amdgcn_alignbit(w, 0u, n);
+        n += 32u;
+        e = lookup<TWO>(lut, hi, K);
+      }
+      P0 = min(P0 + clo, nw0 + 64u);
+      P1 = min(P1 + chi, nw1 + 64u);
+    }
+    const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
+    lo = __builtin_amdgcn_alignbit(lo, 0u, e);
+    hi = nhi;
+    n = sub_len(n, e);
+    store_out<OutT>(outr, voff, soff, e);
+    soff += 32u * (uint32_t)sizeof(OutT);
+  }
+  const uint32_t P = upper ? P1 : P0, nw = upper ? nw1 : nw0;
+  uint32_t flags = 0;
+  if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
+  if (hi | lo) flags |= kFPadding;
+  return flags;
+}
+
+// W <= 16: per-lane word pointers, group masks.
+template <int MODE, int LOG2W, bool TWO, typename OutT>
+__device__ __forceinline__ uint32_t loop_small(const uint32_t *lut, uint32_t K, const uint32_t *stage,
+                                               uint32_t cs, uint32_t nw, uint32_t steps,
+                                               __amdgpu_buffer_rsrc_t outr, uint32_t lane_off, uint32_t lane) {
+  constexpr uint32_t W = 1u << LOG2W;
+  const uint32_t voff = lane_off * (uint32_t)sizeof(OutT);
+  uint32_t soff = 0;
+  const uint32_t grp = lane >> LOG2W;
+  const uint64_t grp_mask = ((1ull << (W & 63u)) - 1ull) << (grp * W);
+  const uint64_t grp_below = grp_mask & ((1ull << lane) - 1ull);
+  uint32_t hi = 0, lo = 0, n = 0, P = 0;
+  for (uint32_t t = 0; t < steps; ++t) {
+    uint32_t e = lookup<TWO>(lut, hi, K);
+    const bool need = entry_len(e) > n;
+    const uint64_t m = __ballot(need);
+    if (m) {
+      if (need) {
+        const uint32_t w = stage[cs + P + (uint32_t)__popcll(m & grp_below)];
+        hi |= w >> n;
+        lo |= __builtin_amdgcn_alignbit(w, 0u, n);
+        n += 32u;
+        e = lookup<TWO>(lut, hi, K);
+      }
+      P = min(P + (uint32_t)__popcll(m & grp_mask), nw + 64u);
+    }
+    const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
+    lo = __builtin_amdgcn_alignbit(lo, 0u, e);
+    hi = nhi;
+    n = sub_len(n, e);
+    store_out<OutT>(outr, voff, soff, e);
+    soff += W * (uint32_t)sizeof(OutT);
+  }
+  uint32_t flags = 0;
+  if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
+  if (hi | lo) flags |= kFPadding;
+  return flags;
+}
+
+// One full wavefront task through LDS; returns false if it must take the
+// generic path (malformed offsets or more words than the staging area).
+template <int MODE, int LOG2W, bool TWO>
+__device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K, uint64_t task, uint32_t *stage,
+                            uint32_t stage_words) {
+  constexpr uint32_t W = 1u << LOG2W;
+  constexpr uint32_t G = 64u / W;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t grp = lane >> LOG2W;
+  const uint32_t j = lane & (W - 1u);
+  const uint64_t c0 = task * G;
+  const uint64_t n_words = d.n_words;
+
+  // offsets of the task's G + 1 chunk boundaries: lane l < G holds the start
+  // of chunk c0 + l, the end of the task is loaded once for all lanes
+  const uint64_t o = d.offs[c0 + min(lane, G - 1u)];
+  const uint64_t o_last = rfl64(d.offs[c0 + G]);
+  const uint64_t o_down = __shfl_down(o, 1, 64);
+  const uint64_t o_next = lane + 1u < G ? o_down : o_last;
+  const bool bad = lane < G && ((o & 31u) || (o_next & 31u) || o_next < o || (o_next >> 5) > n_words);
+  if (__ballot(bad)) return false;
+  const uint64_t o_first = rfl64(__shfl(o, 0, 64));
+  const uint64_t task_words = (o_last - o_first) >> 5;
+  if (task_words + 3u > stage_words) return false;
+
+  // stage the task's words, 16 bytes per lane per load, from a 16-byte
+  // aligned start; bytes past the tensor's words read as zero
+  const uint64_t w_first = o_first >> 5;
+  const uint32_t al = (uint32_t)(w_first & 3u);
+  const uint64_t base_al = w_first - al;
+  const uint64_t bytes_left = (n_words - base_al) * 4u;
+  const uint32_t nrec = (uint32_t)min(bytes_left, (uint64_t)0xFFFFFFF0u);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(d.words + base_al), (short)0, (int)nrec, 0x00020000);
+  const uint32_t nvec = (uint32_t)((al + task_words + 3u) >> 2);
+  u32x4 *st4 = reinterpret_cast<u32x4 *>(stage);
+  for (uint32_t v = lane; v < nvec; v += 64u) st4[v] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(v * 16u), 0, 0);
+
+  const uint64_t og = __shfl(o, (int)grp, 64), og1 = __shfl(o_next, (int)grp, 64);
+  const uint32_t cs = al + (uint32_t)((og - o_first) >> 5);
+  const uint32_t nw = (uint32_t)((og1 - og) >> 5);
+  const uint32_t steps = d.chunk >> LOG2W;
+  typedef typename std::conditional<MODE == kModeU8, uint8_t, uint16_t>::type OutT;
+  // output of the task: G full chunks from chunk c0 on
+  OutT *outp = static_cast<OutT *>(d.out) + c0 * d.chunk;
+  const uint32_t out_bytes = (uint32_t)min((uint64_t)G * d.chunk * sizeof(OutT), (uint64_t)0xFFFFFFF0u);
+  const __amdgpu_buffer_rsrc_t outr = __builtin_amdgcn_make_buffer_rsrc((void *)outp, (short)0, (int)out_bytes, 0x00020000);
+  const uint32_t lane_off = grp * d.chunk + j;
+  uint32_t flags;
+  if (LOG2W == 6) {
+    flags = loop64<MODE, TWO, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane);
+  } else if (LOG2W == 5) {
+    const uint32_t cs0 = rfl(__shfl(cs, 0, 64)), cs1 = rfl(__shfl(cs, 32, 64));
+    const uint32_t nw0 = rfl(__shfl(nw, 0, 64)), nw1 = rfl(__shfl(nw, 32, 64));
+    flags = loop32<MODE, TWO, OutT>(lut, K, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane);
+  } else {
+    flags = loop_small<MODE, LOG2W, TWO, OutT>(lut, K, stage, cs, nw, steps, outr, lane_off, lane);
+  }
+  if (flags) atomicOr(d.status, flags);
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// kernel: persistent workgroups over block tasks
+// ---------------------------------------------------------------------------
+template <int MODE, int LOG2W, int BATCH, bool TWO>
+__global__ __launch_bounds__(kBlockThreads) void ecw_kernel(const LaunchArgs a) {
+  constexpr uint32_t G = 64u >> LOG2W;
+  __shared__ uint32_t lut[kLutMaxEntries];
+  extern __shared__ u32x4 dyn_stage[];   // 16-byte aligned staging areas
+  __shared__ uint32_t lut_state;         // K | entries << 8, or 0 if the table is unusable
+
+  const uint32_t wave = rfl(threadIdx.x >> 6);
+  const uint32_t stage_words = a.stage_words;
+  uint32_t *stage = reinterpret_cast<uint32_t *>(dyn_stage) + wave * (stage_words + kStageSlack);
+  const uint32_t bt0 = blockIdx.x * a.btasks_per_block;
+  const uint32_t bt1 = min(bt0 + a.btasks_per_block, a.total_btasks);
+  uint32_t cur = 0xFFFFFFFFu;
+  uint32_t K = 0;
+  for (uint32_t bt = bt0; bt < bt1; ++bt) {
+    uint32_t ti = 0;
+    while (ti + 1 < a.n_tensors && a.btask_begin[ti + 1] <= bt) ++ti;
+    const TensorArg &d = a.t[ti];
+    if (ti != cur) {
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        uint32_t k = 0;
+        if (d.lut_words >= kLutHeaderWords) {
+          const uint32_t h0 = d.lut[0], h1 = d.lut[1], ne = d.lut[2], l1 = d.lut[3];
+          const uint32_t kk = h1 & 0xFFu;
+          if (h0 == kLutMagic && (h1 & 0xFFFFFF00u) == d.expect_hdr && kk >= 1 && kk <= kSingleLevelMax &&
+              l1 == (1u << kk) && ne >= l1 && ne <= kLutMaxEntries && ne <= d.lut_words - kLutHeaderWords &&
+              (TWO || ne == l1))
+            k = kk | (ne << 8);
+        }
+        if (!k) atomicOr(d.status, kFLut);
+        lut_state = k;
+      }
+      __syncthreads();
+      const uint32_t ne = lut_state >> 8;
+      for (uint32_t i = threadIdx.x; i < ne; i += kBlockThreads) lut[i] = kernel_entry<MODE>(d.lut[kLutHeaderWords + i]);
+      K = lut_state & 0xFFu;
+      cur = ti;
+      __syncthreads();
+    }
+    if (!K) continue;
+    const uint64_t task = (uint64_t)(bt - a.btask_begin[ti]) * kWaves + wave;
+    if (task >= d.n_tasks) continue;
+    bool done = false;
+    if (MODE != kModeGemv && stage_words) {
+      const bool full = (task + 1) * G <= d.n_chunks && (task + 1) * G * (uint64_t)d.chunk <= d.n_symbols;
+      if (full) done = task_staged<MODE, LOG2W, TWO>(d, lut, K, task, stage, stage_words);
+    }
+    if (!done) task_generic<MODE, LOG2W, BATCH, TWO>(d, lut, K, task, a.batch);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -201,13 +494,33 @@ static entro_status check_tensor(const entro_tensor &t) {
   return ENTRO_OK;
 }
 
-template <int MODE, int BATCH>
-static void launch_w(uint32_t log2w, uint32_t blocks, const LaunchArgs &a, hipStream_t s) {
+template <int MODE, int L, int BATCH, bool TWO>
+static hipError_t launch_one(uint32_t total_btasks, LaunchArgs &a, size_t dyn, hipStream_t s) {
+  auto kern = ecw_kernel<MODE, L, BATCH, TWO>;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBlockThreads, dyn) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (cus < 1) cus = 1;
+  const uint64_t slots = (uint64_t)cus * (uint64_t)per_cu;
+  const uint32_t per_block = (uint32_t)((total_btasks + slots - 1) / slots);
+  a.btasks_per_block = per_block < 1 ? 1 : per_block;
+  const uint32_t grid = (total_btasks + a.btasks_per_block - 1) / a.btasks_per_block;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlockThreads), dyn, s, a);
+  return hipGetLastError();
+}
+
+template <int MODE, int BATCH, bool TWO>
+static hipError_t launch_w(uint32_t log2w, uint32_t total_btasks, LaunchArgs &a, size_t dyn, hipStream_t s) {
   switch (log2w) {
-#define ENTRO_CASE(L) \
-  case L: hipLaunchKernelGGL((ecw_decode_kernel<MODE, L, BATCH>), dim3(blocks), dim3(kBlockThreads), 0, s, a); break;
-    ENTRO_CASE(0) ENTRO_CASE(1) ENTRO_CASE(2) ENTRO_CASE(3) ENTRO_CASE(4) ENTRO_CASE(5) ENTRO_CASE(6)
-#undef ENTRO_CASE
+    case 0: return launch_one<MODE, 0, BATCH, TWO>(total_btasks, a, dyn, s);
+    case 1: return launch_one<MODE, 1, BATCH, TWO>(total_btasks, a, dyn, s);
+    case 2: return launch_one<MODE, 2, BATCH, TWO>(total_btasks, a, dyn, s);
+    case 3: return launch_one<MODE, 3, BATCH, TWO>(total_btasks, a, dyn, s);
+    case 4: return launch_one<MODE, 4, BATCH, TWO>(total_btasks, a, dyn, s);
+    case 5: return launch_one<MODE, 5, BATCH, TWO>(total_btasks, a, dyn, s);
+    default: return launch_one<MODE, 6, BATCH, TWO>(total_btasks, a, dyn, s);
   }
 }
 
@@ -240,9 +553,9 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
     LaunchArgs a;
     std::memset(&a, 0, sizeof a);
     a.batch = batch;
-    uint32_t blocks = 0;
-    uint32_t log2w = 0;
-    uint32_t k = 0;
+    uint32_t total = 0, log2w = 0, k = 0;
+    bool two = false;
+    uint64_t max_task_words = 0;
     for (; i < n && k < (uint32_t)kMaxTensorsPerLaunch; ++i) {
       const entro_tensor &x = t[i];
       if (x.n_symbols == 0) continue;
@@ -269,21 +582,39 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
         d.out = outs[i];
       }
       const uint64_t chunks_per_wave = 64u >> lw;
-      const uint64_t wave_tasks = (d.n_chunks + chunks_per_wave - 1) / chunks_per_wave;
-      const uint64_t nb = (wave_tasks + kWavesPerBlock - 1) / kWavesPerBlock;
-      if ((uint64_t)blocks + nb > 0x7FFFFFFFull) return ENTRO_E_UNSUPPORTED;
-      a.block_begin[k] = blocks;
-      blocks += (uint32_t)nb;
+      const uint64_t tasks = (d.n_chunks + chunks_per_wave - 1) / chunks_per_wave;
+      d.n_tasks = (uint32_t)tasks;
+      const uint64_t nb = (tasks + kWaves - 1) / kWaves;
+      if ((uint64_t)total + nb > 0x7FFFFFFFull) return ENTRO_E_UNSUPPORTED;
+      a.btask_begin[k] = total;
+      total += (uint32_t)nb;
+      if (x.max_len > kSingleLevelMax) two = true;
+      max_task_words = std::max<uint64_t>(max_task_words, (x.n_words + tasks - 1) / tasks);
       ++k;
     }
     if (k == 0) continue;
     a.n_tensors = k;
-    for (uint32_t r = k; r <= (uint32_t)kMaxTensorsPerLaunch; ++r) a.block_begin[r] = blocks;
-    if (mode == kModeU8) launch_w<kModeU8, 1>(log2w, blocks, a, s);
-    else if (mode == kModeBf16) launch_w<kModeBf16, 1>(log2w, blocks, a, s);
-    else if (batch == 1) launch_w<kModeGemv, 1>(log2w, blocks, a, s);
-    else launch_w<kModeGemv, 8>(log2w, blocks, a, s);
-    if (hipGetLastError() != hipSuccess) return ENTRO_E_HIP;
+    a.total_btasks = total;
+    for (uint32_t r = k; r <= (uint32_t)kMaxTensorsPerLaunch; ++r) a.btask_begin[r] = total;
+    // staging area per wavefront: the average task with a margin, within LDS
+    size_t dyn = 0;
+    if (mode != kModeGemv) {
+      const uint64_t cap = (160u * 1024u / 4u - kLutMaxEntries - 64u) / kWaves - kStageSlack;
+      uint64_t sw = ((max_task_words * 5 / 4 + 64 + 63) / 64) * 64;
+      sw = std::max<uint64_t>(256, std::min<uint64_t>(sw, cap & ~63ull));
+      a.stage_words = (uint32_t)sw;
+      dyn = (size_t)kWaves * (sw + kStageSlack) * 4u;
+    }
+    hipError_t err;
+    if (mode == kModeU8) err = two ? launch_w<kModeU8, 1, true>(log2w, total, a, dyn, s)
+                                   : launch_w<kModeU8, 1, false>(log2w, total, a, dyn, s);
+    else if (mode == kModeBf16) err = two ? launch_w<kModeBf16, 1, true>(log2w, total, a, dyn, s)
+                                          : launch_w<kModeBf16, 1, false>(log2w, total, a, dyn, s);
+    else if (batch == 1) err = two ? launch_w<kModeGemv, 1, true>(log2w, total, a, dyn, s)
+                                   : launch_w<kModeGemv, 1, false>(log2w, total, a, dyn, s);
+    else err = two ? launch_w<kModeGemv, 8, true>(log2w, total, a, dyn, s)
+                   : launch_w<kModeGemv, 8, false>(log2w, total, a, dyn, s);
+    if (err != hipSuccess) return ENTRO_E_HIP;
   }
   return ENTRO_OK;
 }

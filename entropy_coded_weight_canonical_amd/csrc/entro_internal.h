@@ -14,6 +14,7 @@ constexpr uint32_t kSingleLevelMax = 12;      // codes up to 12 bits: one level
 constexpr uint32_t kFirstLevelBits = 11;      // longer codes: 11-bit first level
 constexpr uint32_t kEntryPointer = 0x80u;
 constexpr uint32_t kMaxChunk = 1u << 20;
+constexpr uint32_t kInvalidLen = 31u;         // length field of an entry without codeword
 
 // status bits (mirror ENTRO_F_* of entro.h)
 constexpr uint32_t kFOverrun = 0x01u, kFUnderrun = 0x02u, kFBadCode = 0x04u,
@@ -36,17 +37,25 @@ struct TensorArg {
   uint32_t rows, cols;     // GEMV shape
   uint32_t expect_hdr;     // sym_bits << 8 | max_len << 16 (header word 1 without K)
   uint32_t lut_words;      // readable uint32 words at lut
+  uint32_t n_tasks;        // wavefront tasks: ceil(n_chunks / chunks per wavefront)
+  uint32_t pad_;
 };
 
 constexpr int kMaxTensorsPerLaunch = 32;
-constexpr int kWavesPerBlock = 4;
-constexpr int kBlockThreads = 64 * kWavesPerBlock;
+constexpr int kWaves = 8;                       // wavefronts per workgroup
+constexpr int kBlockThreads = 64 * kWaves;
+constexpr uint32_t kStageSlack = 160;           // words after each wavefront's staging area
 
+// A block task is kWaves consecutive wavefront tasks of one tensor; a
+// wavefront task is 64 / lanes consecutive chunks.
 struct LaunchArgs {
   TensorArg t[kMaxTensorsPerLaunch];
-  uint32_t block_begin[kMaxTensorsPerLaunch + 1];  // first block of each tensor
+  uint32_t btask_begin[kMaxTensorsPerLaunch + 1];  // first block task of each tensor
   uint32_t n_tensors;
   uint32_t batch;                                  // GEMV rows of x / y
+  uint32_t total_btasks;
+  uint32_t btasks_per_block;
+  uint32_t stage_words;                            // staging words per wavefront (0: none)
 };
 
 }  // namespace entro
