@@ -58,7 +58,8 @@ class Tensor(ctypes.Structure):
                 ("d_chunk_bit_off", ctypes.c_void_p), ("n_words", ctypes.c_uint64),
                 ("n_symbols", ctypes.c_uint64), ("chunk_symbols", ctypes.c_uint32),
                 ("lanes", ctypes.c_uint32), ("sym_bits", ctypes.c_uint32),
-                ("max_len", ctypes.c_uint32), ("lut_bytes", ctypes.c_uint64)]
+                ("max_len", ctypes.c_uint32), ("lut_bytes", ctypes.c_uint64),
+                ("max_chunk_words", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
 
 class GemvItem(ctypes.Structure):
@@ -256,6 +257,9 @@ class DeviceTensor:
         w = np.ascontiguousarray(words, dtype=np.uint32)
         d_words = torch.from_numpy(w.view(np.int32) if w.size else np.zeros(1, np.int32)).to(device)
         d_offs = torch.from_numpy(np.ascontiguousarray(offs, dtype=np.uint64).view(np.int64)).to(device)
+        o = np.asarray(offs, dtype=np.uint64)
+        max_cw = int(np.diff(o).max() // 32) if o.size > 1 else 0
         desc = Tensor(d_lut.data_ptr(), d_words.data_ptr(), d_offs.data_ptr(), int(w.size), int(n_symbols),
-                      int(chunk), int(lanes), int(sym_bits), int(max_len), int(np.asarray(lut).nbytes))
+                      int(chunk), int(lanes), int(sym_bits), int(max_len), int(np.asarray(lut).nbytes),
+                      max_cw, 0)
         return cls(d_lut, d_words, d_offs, desc)

@@ -105,13 +105,25 @@ __device__ __forceinline__ uint64_t rfl64(uint64_t v) {
   return ((uint64_t)rfl((uint32_t)(v >> 32)) << 32) | rfl((uint32_t)v);
 }
 
-template <bool TWO>
+// Lanes whose first-level entry is a second-level pointer (byte 0 > 127).
+__device__ __forceinline__ uint64_t pointer_mask(uint32_t e) {
+  uint64_t m;
+  asm volatile("v_cmp_lt_u32_sdwa %0, %1, %2 src0_sel:DWORD src1_sel:BYTE_0" : "=s"(m) : "v"(127u), "v"(e));
+  return m;
+}
+
+// Entry for the next codeword at the top of hi: first level indexed by the
+// top K bits; a pointer entry sends the lanes that hit it (rare when K is
+// chosen as in entro_lut_build) to the subtable indexed by the next bits.
 __device__ __forceinline__ uint32_t lookup(const uint32_t *lut, uint32_t hi, uint32_t K) {
   uint32_t e = lut[hi >> (32u - K)];
-  if (TWO && (e & kEntryPointer)) {
-    const uint32_t sb = (e >> 8) & 31u;
-    const uint32_t i2 = (hi << K) >> (32u - sb);
-    e = lut[((e >> 16) + i2) & (kLutMaxEntries - 1u)];
+  const uint64_t pm = pointer_mask(e);
+  if (pm) {
+    if (__builtin_amdgcn_inverse_ballot_w64(pm)) {
+      const uint32_t sb = (e >> 8) & 31u;
+      const uint32_t i2 = (hi << K) >> (32u - sb);
+      e = lut[((e >> 16) + i2) & (kLutMaxEntries - 1u)];
+    }
   }
   return e;
 }
@@ -125,7 +137,7 @@ __device__ __forceinline__ void emit(void *base, uint64_t k, uint32_t e) {
 // ---------------------------------------------------------------------------
 // generic path: one wavefront task, words read from global memory, all checks
 // ---------------------------------------------------------------------------
-template <int MODE, int LOG2W, int BATCH, bool TWO>
+template <int MODE, int LOG2W, int BATCH>
 __device__ void task_generic(const TensorArg &d, const uint32_t *lut, uint32_t K, uint64_t task, uint32_t batch) {
   constexpr uint32_t W = 1u << LOG2W;
   constexpr uint32_t G = 64u / W;
@@ -170,7 +182,7 @@ __device__ void task_generic(const TensorArg &d, const uint32_t *lut, uint32_t K
 
   for (uint32_t t = 0; t < steps; ++t) {
     const bool act = t < my_steps;
-    uint32_t e = lookup<TWO>(lut, (uint32_t)(buf >> 32), K);
+    uint32_t e = lookup(lut, (uint32_t)(buf >> 32), K);
     uint32_t len = entry_len(e);
     const bool need = act && len > n;
     const uint64_t m = __ballot(need);
@@ -182,7 +194,7 @@ __device__ void task_generic(const TensorArg &d, const uint32_t *lut, uint32_t K
         else flags |= kFOverrun;
         buf |= (uint64_t)w << (32u - n);
         n += 32u;
-        e = lookup<TWO>(lut, (uint32_t)(buf >> 32), K);
+        e = lookup(lut, (uint32_t)(buf >> 32), K);
         len = entry_len(e);
       }
       P += (uint64_t)__popcll(m & grp_mask);
@@ -234,36 +246,41 @@ __device__ void task_generic(const TensorArg &d, const uint32_t *lut, uint32_t K
 // staged path: the decode loop over words held in LDS
 // ---------------------------------------------------------------------------
 
+// Each loop below decodes one full task from LDS.  Scalar bookkeeping is
+// kept to a minimum (the CU's single scalar unit is shared by all of its
+// wavefronts): one exec-mask branch per step for the refill, word pointers
+// advanced by the mask's popcount, the output offset doubling as the loop
+// counter.  Word pointers are not clamped: only a malformed stream moves them
+// past its chunk, its LDS reads then return data of another area (LDS
+// addressing cannot fault) and the end-of-chunk check flags the overrun,
+// because a pointer never decreases.
+
 // W = 64: one chunk per wavefront; word pointer in a scalar register.
-template <int MODE, bool TWO, typename OutT>
+template <int MODE, typename OutT>
 __device__ __forceinline__ uint32_t loop64(const uint32_t *lut, uint32_t K, const uint32_t *sw, uint32_t nw,
                                            uint32_t steps, __amdgpu_buffer_rsrc_t outr, uint32_t lane) {
   const uint32_t voff = lane * (uint32_t)sizeof(OutT);
-  uint32_t soff = 0;
+  const uint32_t send = steps * 64u * (uint32_t)sizeof(OutT);
   uint32_t hi = 0, lo = 0, n = 0, P = 0;
-  for (uint32_t t = 0; t < steps; ++t) {
-    uint32_t e = lookup<TWO>(lut, hi, K);
+  for (uint32_t soff = 0; soff != send; soff += 64u * (uint32_t)sizeof(OutT)) {
+    uint32_t e = lookup(lut, hi, K);
     const uint64_t m = need_mask(e, n);
-    if (m) {
-      if (__builtin_amdgcn_inverse_ballot_w64(m)) {
-        const uint32_t idx =
-            __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        const uint32_t w = sw[P + idx];
-        // fewer than 32 bits are loaded here, so lo is empty
-        hi |= w >> n;
-        lo = __builtin_amdgcn_alignbit(w, 0u, n);
-        n += 32u;
-        e = lookup<TWO>(lut, hi, K);
-      }
-      // a malformed stream cannot move the pointer past the staging slack
-      P = min(P + (uint32_t)__popcll(m), nw + 64u);
+    if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+      const uint32_t idx =
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const uint32_t w = sw[P + idx];
+      // fewer than 32 bits are loaded here, so lo is empty
+      hi |= w >> n;
+      lo = __builtin_amdgcn_alignbit(w, 0u, n);
+      n += 32u;
+      e = lookup(lut, hi, K);
     }
+    P += (uint32_t)__popcll(m);
     const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
     lo = __builtin_amdgcn_alignbit(lo, 0u, e);
     hi = nhi;
     n = sub_len(n, e);
     store_out<OutT>(outr, voff, soff, e);
-    soff += 64u * (uint32_t)sizeof(OutT);
   }
   uint32_t flags = 0;
   if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
@@ -271,42 +288,40 @@ __device__ __forceinline__ uint32_t loop64(const uint32_t *lut, uint32_t K, cons
   return flags;
 }
 
-// W = 32: two chunks per wavefront, word pointers P0 (lanes 0-31) and P1
-// (lanes 32-63) in scalar registers; the upper half's word index is formed
-// by folding P1 - P0 and the chunk distance into the v_mbcnt addend.
-template <int MODE, bool TWO, typename OutT>
+// W = 32: two chunks per wavefront.  Lanes 0-31 take words from chunk 0 at
+// base P0, lanes 32-63 from chunk 1; D = (chunk 1 start - chunk 0 start) +
+// P1 - P0 is kept so that one v_mbcnt pair, with addend D - popcount(lower
+// half) in the upper half, gives every lane its word index relative to P0.
+template <int MODE, typename OutT>
 __device__ __forceinline__ uint32_t loop32(const uint32_t *lut, uint32_t K, const uint32_t *sw, uint32_t dcs,
                                            uint32_t nw0, uint32_t nw1, uint32_t steps, __amdgpu_buffer_rsrc_t outr,
                                            uint32_t lane_off, uint32_t lane) {
   const uint32_t upper = lane >= 32u ? ~0u : 0u;
   const uint32_t voff = lane_off * (uint32_t)sizeof(OutT);
-  uint32_t soff = 0;
-  uint32_t hi = 0, lo = 0, n = 0, P0 = 0, P1 = 0;
-  for (uint32_t t = 0; t < steps; ++t) {
-    uint32_t e = lookup<TWO>(lut, hi, K);
+  const uint32_t send = steps * 32u * (uint32_t)sizeof(OutT);
+  uint32_t hi = 0, lo = 0, n = 0, P0 = 0, D = dcs;
+  for (uint32_t soff = 0; soff != send; soff += 32u * (uint32_t)sizeof(OutT)) {
+    uint32_t e = lookup(lut, hi, K);
     const uint64_t m = need_mask(e, n);
-    if (m) {
-      const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
-      const uint32_t clo = (uint32_t)__popc(mlo), chi = (uint32_t)__popc(mhi);
-      if (__builtin_amdgcn_inverse_ballot_w64(m)) {
-        const uint32_t dd = dcs + P1 - P0 - clo;
-        const uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, and_sv(dd, upper)));
-        const uint32_t w = sw[P0 + idx];
-        hi |= w >> n;
-        lo = __builtin_amdgcn_alignbit(w, 0u, n);
-        n += 32u;
-        e = lookup<TWO>(lut, hi, K);
-      }
-      P0 = min(P0 + clo, nw0 + 64u);
-      P1 = min(P1 + chi, nw1 + 64u);
+    const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+    const uint32_t clo = (uint32_t)__popc(mlo);
+    if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+      const uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, and_sv(D - clo, upper)));
+      const uint32_t w = sw[P0 + idx];
+      hi |= w >> n;
+      lo = __builtin_amdgcn_alignbit(w, 0u, n);
+      n += 32u;
+      e = lookup(lut, hi, K);
     }
+    P0 += clo;
+    D += (uint32_t)__popc(mhi) - clo;
     const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
     lo = __builtin_amdgcn_alignbit(lo, 0u, e);
     hi = nhi;
     n = sub_len(n, e);
     store_out<OutT>(outr, voff, soff, e);
-    soff += 32u * (uint32_t)sizeof(OutT);
   }
+  const uint32_t P1 = D - dcs + P0;
   const uint32_t P = upper ? P1 : P0, nw = upper ? nw1 : nw0;
   uint32_t flags = 0;
   if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
@@ -315,37 +330,33 @@ __device__ __forceinline__ uint32_t loop32(const uint32_t *lut, uint32_t K, cons
 }
 
 // W <= 16: per-lane word pointers, group masks.
-template <int MODE, int LOG2W, bool TWO, typename OutT>
+template <int MODE, int LOG2W, typename OutT>
 __device__ __forceinline__ uint32_t loop_small(const uint32_t *lut, uint32_t K, const uint32_t *stage,
                                                uint32_t cs, uint32_t nw, uint32_t steps,
                                                __amdgpu_buffer_rsrc_t outr, uint32_t lane_off, uint32_t lane) {
   constexpr uint32_t W = 1u << LOG2W;
   const uint32_t voff = lane_off * (uint32_t)sizeof(OutT);
-  uint32_t soff = 0;
+  const uint32_t send = steps * W * (uint32_t)sizeof(OutT);
   const uint32_t grp = lane >> LOG2W;
   const uint64_t grp_mask = ((1ull << (W & 63u)) - 1ull) << (grp * W);
   const uint64_t grp_below = grp_mask & ((1ull << lane) - 1ull);
   uint32_t hi = 0, lo = 0, n = 0, P = 0;
-  for (uint32_t t = 0; t < steps; ++t) {
-    uint32_t e = lookup<TWO>(lut, hi, K);
-    const bool need = entry_len(e) > n;
-    const uint64_t m = __ballot(need);
-    if (m) {
-      if (need) {
-        const uint32_t w = stage[cs + P + (uint32_t)__popcll(m & grp_below)];
-        hi |= w >> n;
-        lo |= __builtin_amdgcn_alignbit(w, 0u, n);
-        n += 32u;
-        e = lookup<TWO>(lut, hi, K);
-      }
-      P = min(P + (uint32_t)__popcll(m & grp_mask), nw + 64u);
+  for (uint32_t soff = 0; soff != send; soff += W * (uint32_t)sizeof(OutT)) {
+    uint32_t e = lookup(lut, hi, K);
+    const uint64_t m = need_mask(e, n);
+    if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+      const uint32_t w = stage[cs + P + (uint32_t)__popcll(m & grp_below)];
+      hi |= w >> n;
+      lo = __builtin_amdgcn_alignbit(w, 0u, n);
+      n += 32u;
+      e = lookup(lut, hi, K);
     }
+    P += (uint32_t)__popcll(m & grp_mask);
     const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
     lo = __builtin_amdgcn_alignbit(lo, 0u, e);
     hi = nhi;
     n = sub_len(n, e);
     store_out<OutT>(outr, voff, soff, e);
-    soff += W * (uint32_t)sizeof(OutT);
   }
   uint32_t flags = 0;
   if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
@@ -355,7 +366,7 @@ __device__ __forceinline__ uint32_t loop_small(const uint32_t *lut, uint32_t K, 
 
 // One full wavefront task through LDS; returns false if it must take the
 // generic path (malformed offsets or more words than the staging area).
-template <int MODE, int LOG2W, bool TWO>
+template <int MODE, int LOG2W>
 __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K, uint64_t task, uint32_t *stage,
                             uint32_t stage_words) {
   constexpr uint32_t W = 1u << LOG2W;
@@ -403,13 +414,13 @@ __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K,
   const uint32_t lane_off = grp * d.chunk + j;
   uint32_t flags;
   if (LOG2W == 6) {
-    flags = loop64<MODE, TWO, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane);
+    flags = loop64<MODE, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane);
   } else if (LOG2W == 5) {
     const uint32_t cs0 = rfl(__shfl(cs, 0, 64)), cs1 = rfl(__shfl(cs, 32, 64));
     const uint32_t nw0 = rfl(__shfl(nw, 0, 64)), nw1 = rfl(__shfl(nw, 32, 64));
-    flags = loop32<MODE, TWO, OutT>(lut, K, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane);
+    flags = loop32<MODE, OutT>(lut, K, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane);
   } else {
-    flags = loop_small<MODE, LOG2W, TWO, OutT>(lut, K, stage, cs, nw, steps, outr, lane_off, lane);
+    flags = loop_small<MODE, LOG2W, OutT>(lut, K, stage, cs, nw, steps, outr, lane_off, lane);
   }
   if (flags) atomicOr(d.status, flags);
   return true;
@@ -418,16 +429,18 @@ __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K,
 // ---------------------------------------------------------------------------
 // kernel: persistent workgroups over block tasks
 // ---------------------------------------------------------------------------
-template <int MODE, int LOG2W, int BATCH, bool TWO>
+template <int MODE, int LOG2W, int BATCH>
 __global__ __launch_bounds__(kBlockThreads) void ecw_kernel(const LaunchArgs a) {
   constexpr uint32_t G = 64u >> LOG2W;
-  __shared__ uint32_t lut[kLutMaxEntries];
-  extern __shared__ u32x4 dyn_stage[];   // 16-byte aligned staging areas
-  __shared__ uint32_t lut_state;         // K | entries << 8, or 0 if the table is unusable
+  // dynamic LDS: the table (lut_cap entries, a multiple of 4), then one
+  // 16-byte aligned staging area per wavefront
+  extern __shared__ u32x4 dyn_lds[];
+  __shared__ uint32_t lut_state;   // K | entries << 8, or 0 if the table is unusable
+  uint32_t *lut = reinterpret_cast<uint32_t *>(dyn_lds);
 
   const uint32_t wave = rfl(threadIdx.x >> 6);
   const uint32_t stage_words = a.stage_words;
-  uint32_t *stage = reinterpret_cast<uint32_t *>(dyn_stage) + wave * (stage_words + kStageSlack);
+  uint32_t *stage = lut + a.lut_cap + wave * (stage_words + kStageSlack);
   const uint32_t bt0 = blockIdx.x * a.btasks_per_block;
   const uint32_t bt1 = min(bt0 + a.btasks_per_block, a.total_btasks);
   uint32_t cur = 0xFFFFFFFFu;
@@ -444,8 +457,7 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_kernel(const LaunchArgs a) 
           const uint32_t h0 = d.lut[0], h1 = d.lut[1], ne = d.lut[2], l1 = d.lut[3];
           const uint32_t kk = h1 & 0xFFu;
           if (h0 == kLutMagic && (h1 & 0xFFFFFF00u) == d.expect_hdr && kk >= 1 && kk <= kSingleLevelMax &&
-              l1 == (1u << kk) && ne >= l1 && ne <= kLutMaxEntries && ne <= d.lut_words - kLutHeaderWords &&
-              (TWO || ne == l1))
+              l1 == (1u << kk) && ne >= l1 && ne <= a.lut_cap && ne <= d.lut_words - kLutHeaderWords)
             k = kk | (ne << 8);
         }
         if (!k) atomicOr(d.status, kFLut);
@@ -464,9 +476,9 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_kernel(const LaunchArgs a) 
     bool done = false;
     if (MODE != kModeGemv && stage_words) {
       const bool full = (task + 1) * G <= d.n_chunks && (task + 1) * G * (uint64_t)d.chunk <= d.n_symbols;
-      if (full) done = task_staged<MODE, LOG2W, TWO>(d, lut, K, task, stage, stage_words);
+      if (full) done = task_staged<MODE, LOG2W>(d, lut, K, task, stage, stage_words);
     }
-    if (!done) task_generic<MODE, LOG2W, BATCH, TWO>(d, lut, K, task, a.batch);
+    if (!done) task_generic<MODE, LOG2W, BATCH>(d, lut, K, task, a.batch);
   }
 }
 
@@ -494,9 +506,9 @@ static entro_status check_tensor(const entro_tensor &t) {
   return ENTRO_OK;
 }
 
-template <int MODE, int L, int BATCH, bool TWO>
+template <int MODE, int L, int BATCH>
 static hipError_t launch_one(uint32_t total_btasks, LaunchArgs &a, size_t dyn, hipStream_t s) {
-  auto kern = ecw_kernel<MODE, L, BATCH, TWO>;
+  auto kern = ecw_kernel<MODE, L, BATCH>;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
@@ -511,16 +523,16 @@ static hipError_t launch_one(uint32_t total_btasks, LaunchArgs &a, size_t dyn, h
   return hipGetLastError();
 }
 
-template <int MODE, int BATCH, bool TWO>
+template <int MODE, int BATCH>
 static hipError_t launch_w(uint32_t log2w, uint32_t total_btasks, LaunchArgs &a, size_t dyn, hipStream_t s) {
   switch (log2w) {
-    case 0: return launch_one<MODE, 0, BATCH, TWO>(total_btasks, a, dyn, s);
-    case 1: return launch_one<MODE, 1, BATCH, TWO>(total_btasks, a, dyn, s);
-    case 2: return launch_one<MODE, 2, BATCH, TWO>(total_btasks, a, dyn, s);
-    case 3: return launch_one<MODE, 3, BATCH, TWO>(total_btasks, a, dyn, s);
-    case 4: return launch_one<MODE, 4, BATCH, TWO>(total_btasks, a, dyn, s);
-    case 5: return launch_one<MODE, 5, BATCH, TWO>(total_btasks, a, dyn, s);
-    default: return launch_one<MODE, 6, BATCH, TWO>(total_btasks, a, dyn, s);
+    case 0: return launch_one<MODE, 0, BATCH>(total_btasks, a, dyn, s);
+    case 1: return launch_one<MODE, 1, BATCH>(total_btasks, a, dyn, s);
+    case 2: return launch_one<MODE, 2, BATCH>(total_btasks, a, dyn, s);
+    case 3: return launch_one<MODE, 3, BATCH>(total_btasks, a, dyn, s);
+    case 4: return launch_one<MODE, 4, BATCH>(total_btasks, a, dyn, s);
+    case 5: return launch_one<MODE, 5, BATCH>(total_btasks, a, dyn, s);
+    default: return launch_one<MODE, 6, BATCH>(total_btasks, a, dyn, s);
   }
 }
 
@@ -554,8 +566,8 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
     std::memset(&a, 0, sizeof a);
     a.batch = batch;
     uint32_t total = 0, log2w = 0, k = 0;
-    bool two = false;
-    uint64_t max_task_words = 0;
+    uint64_t stage_need = 0, lut_need = 0;
+    bool stage_known = true;
     for (; i < n && k < (uint32_t)kMaxTensorsPerLaunch; ++i) {
       const entro_tensor &x = t[i];
       if (x.n_symbols == 0) continue;
@@ -588,32 +600,32 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
       if ((uint64_t)total + nb > 0x7FFFFFFFull) return ENTRO_E_UNSUPPORTED;
       a.btask_begin[k] = total;
       total += (uint32_t)nb;
-      if (x.max_len > kSingleLevelMax) two = true;
-      max_task_words = std::max<uint64_t>(max_task_words, (x.n_words + tasks - 1) / tasks);
+      lut_need = std::max<uint64_t>(lut_need, d.lut_words > kLutHeaderWords ? d.lut_words - kLutHeaderWords : 0);
+      if (x.max_chunk_words) stage_need = std::max<uint64_t>(stage_need, chunks_per_wave * x.max_chunk_words);
+      else stage_known = false, stage_need = std::max<uint64_t>(stage_need, (x.n_words + tasks - 1) / tasks * 5 / 4 + 64);
       ++k;
     }
     if (k == 0) continue;
     a.n_tensors = k;
     a.total_btasks = total;
     for (uint32_t r = k; r <= (uint32_t)kMaxTensorsPerLaunch; ++r) a.btask_begin[r] = total;
-    // staging area per wavefront: the average task with a margin, within LDS
-    size_t dyn = 0;
+    (void)stage_known;
+    // LDS: the largest table of the launch, then the staging areas (room for
+    // the largest task plus 16-byte alignment), within 160 KiB
+    a.lut_cap = (uint32_t)((lut_need + 3) & ~3ull);
+    size_t dyn = (size_t)a.lut_cap * 4u;
     if (mode != kModeGemv) {
-      const uint64_t cap = (160u * 1024u / 4u - kLutMaxEntries - 64u) / kWaves - kStageSlack;
-      uint64_t sw = ((max_task_words * 5 / 4 + 64 + 63) / 64) * 64;
-      sw = std::max<uint64_t>(256, std::min<uint64_t>(sw, cap & ~63ull));
+      const uint64_t cap = ((160u * 1024u - 256u) / 4u - a.lut_cap) / kWaves - kStageSlack;
+      uint64_t sw = (stage_need + 3 + 3) & ~3ull;
+      sw = std::max<uint64_t>(64, std::min<uint64_t>(sw, cap & ~3ull));
       a.stage_words = (uint32_t)sw;
-      dyn = (size_t)kWaves * (sw + kStageSlack) * 4u;
+      dyn += (size_t)kWaves * (sw + kStageSlack) * 4u;
     }
     hipError_t err;
-    if (mode == kModeU8) err = two ? launch_w<kModeU8, 1, true>(log2w, total, a, dyn, s)
-                                   : launch_w<kModeU8, 1, false>(log2w, total, a, dyn, s);
-    else if (mode == kModeBf16) err = two ? launch_w<kModeBf16, 1, true>(log2w, total, a, dyn, s)
-                                          : launch_w<kModeBf16, 1, false>(log2w, total, a, dyn, s);
-    else if (batch == 1) err = two ? launch_w<kModeGemv, 1, true>(log2w, total, a, dyn, s)
-                                   : launch_w<kModeGemv, 1, false>(log2w, total, a, dyn, s);
-    else err = two ? launch_w<kModeGemv, 8, true>(log2w, total, a, dyn, s)
-                   : launch_w<kModeGemv, 8, false>(log2w, total, a, dyn, s);
+    if (mode == kModeU8) err = launch_w<kModeU8, 1>(log2w, total, a, dyn, s);
+    else if (mode == kModeBf16) err = launch_w<kModeBf16, 1>(log2w, total, a, dyn, s);
+    else if (batch == 1) err = launch_w<kModeGemv, 1>(log2w, total, a, dyn, s);
+    else err = launch_w<kModeGemv, 8>(log2w, total, a, dyn, s);
     if (err != hipSuccess) return ENTRO_E_HIP;
   }
   return ENTRO_OK;

@@ -11,7 +11,8 @@ constexpr uint32_t kLutHeaderWords = 4;
 constexpr uint32_t kLutMaxEntries = 4096;     // 16 KiB of LDS per workgroup
 constexpr uint32_t kMaxCodeLen = 16;
 constexpr uint32_t kSingleLevelMax = 12;      // codes up to 12 bits: one level
-constexpr uint32_t kFirstLevelBits = 11;      // longer codes: 11-bit first level
+constexpr uint32_t kFirstLevelBits = 11;      // longer codes: at most an 11-bit first level
+constexpr uint32_t kFirstLevelMin = 5;        // narrowest first level considered
 constexpr uint32_t kEntryPointer = 0x80u;
 constexpr uint32_t kMaxChunk = 1u << 20;
 constexpr uint32_t kInvalidLen = 31u;         // length field of an entry without codeword
@@ -38,13 +39,13 @@ struct TensorArg {
   uint32_t expect_hdr;     // sym_bits << 8 | max_len << 16 (header word 1 without K)
   uint32_t lut_words;      // readable uint32 words at lut
   uint32_t n_tasks;        // wavefront tasks: ceil(n_chunks / chunks per wavefront)
-  uint32_t pad_;
+  uint32_t lut_entries;    // entries the table holds according to its size
 };
 
 constexpr int kMaxTensorsPerLaunch = 32;
 constexpr int kWaves = 8;                       // wavefronts per workgroup
 constexpr int kBlockThreads = 64 * kWaves;
-constexpr uint32_t kStageSlack = 160;           // words after each wavefront's staging area
+constexpr uint32_t kStageSlack = 72;            // words after each wavefront's staging area (reads of a well-formed stream stay within 64 words past its chunk)
 
 // A block task is kWaves consecutive wavefront tasks of one tensor; a
 // wavefront task is 64 / lanes consecutive chunks.
@@ -56,6 +57,7 @@ struct LaunchArgs {
   uint32_t total_btasks;
   uint32_t btasks_per_block;
   uint32_t stage_words;                            // staging words per wavefront (0: none)
+  uint32_t lut_cap;                                // table entries reserved in LDS
 };
 
 }  // namespace entro

@@ -19,6 +19,7 @@
 //   length l <= K fills the 2^(K-l) entries that start with it.  A K-bit
 //   prefix of codes longer than K points to a subtable indexed by the next
 //   (longest length under the prefix - K) bits.
+#include <algorithm>
 #include <cstring>
 #include <vector>
 
@@ -72,24 +73,43 @@ static entro_status plan_lut(const entro_codebook *cb, Plan *p) {
   }
   for (uint32_t s = 0; s < nsym; ++s)
     if (cb->code_len[s]) p->codes[s] = next[cb->code_len[s]]++;
-  p->K = p->max_used <= kSingleLevelMax ? p->max_used : kFirstLevelBits;
-  uint32_t entries = 1u << p->K;
-  if (p->max_used > p->K) {
-    // one subtable per K-bit prefix shared by codes longer than K
-    std::vector<uint32_t> deepest(1u << p->K, 0);
-    for (uint32_t s = 0; s < nsym; ++s) {
-      uint32_t l = cb->code_len[s];
-      if (l > p->K) {
-        uint32_t pre = p->codes[s] >> (l - p->K);
-        if (l > deepest[pre]) deepest[pre] = l;
-      }
+  // First-level width: the smallest k >= kFirstLevelMin whose longer codes
+  // have an estimated probability (sum of 2^-len, in units of 2^-16) of at
+  // most 2^-10; never wider than the longest code, nor than 12 bits (11 when
+  // longer codes need second-level room).
+  const uint32_t kmax = p->max_used <= kSingleLevelMax ? p->max_used : kFirstLevelBits;
+  uint32_t K = kmax;
+  for (uint32_t k = std::min(kFirstLevelMin, kmax); k < kmax; ++k) {
+    uint64_t mass = 0;
+    for (uint32_t l = k + 1; l <= kMaxCodeLen; ++l) mass += (uint64_t)count[l] << (kMaxCodeLen - l);
+    if (mass <= (1ull << (kMaxCodeLen - 10))) {
+      K = k;
+      break;
     }
-    for (uint32_t pre = 0; pre < (1u << p->K); ++pre)
-      if (deepest[pre]) entries += 1u << (deepest[pre] - p->K);
   }
-  if (entries > kLutMaxEntries) return ENTRO_E_UNSUPPORTED;
-  p->entries = entries;
-  return ENTRO_OK;
+  // widen until the two levels fit the table size
+  for (;; ++K) {
+    uint32_t entries = 1u << K;
+    if (p->max_used > K) {
+      // one subtable per K-bit prefix shared by codes longer than K
+      std::vector<uint32_t> deepest(1u << K, 0);
+      for (uint32_t s = 0; s < nsym; ++s) {
+        uint32_t l = cb->code_len[s];
+        if (l > K) {
+          uint32_t pre = p->codes[s] >> (l - K);
+          if (l > deepest[pre]) deepest[pre] = l;
+        }
+      }
+      for (uint32_t pre = 0; pre < (1u << K); ++pre)
+        if (deepest[pre]) entries += 1u << (deepest[pre] - K);
+    }
+    if (entries <= kLutMaxEntries) {
+      p->K = K;
+      p->entries = entries;
+      return ENTRO_OK;
+    }
+    if (K >= kmax) return ENTRO_E_UNSUPPORTED;
+  }
 }
 
 }  // namespace entro

@@ -97,6 +97,10 @@ typedef struct {
   uint32_t max_len;               /* likewise                                           */
   uint64_t lut_bytes;             /* bytes readable at d_lut (entro_lut_bytes); a table
                                      whose header claims more is rejected (ENTRO_F_LUT) */
+  uint32_t max_chunk_words;       /* words of the largest chunk, or 0 if unknown; sizes
+                                     the on-chip staging (a chunk larger than stated is
+                                     still decoded correctly, only more slowly)          */
+  uint32_t reserved;              /* must be 0                                          */
 } entro_tensor;
 
 /* Operands of the fused GEMV for one tensor, read as a [rows][cols] row-major
@@ -110,8 +114,12 @@ typedef struct {
 
 /* Size in bytes of the decode table built from cb (0 if cb is invalid).
  * The table holds a 16-byte header and 4-byte entries: one level indexed by
- * the next K stream bits (K = longest code if <= 12, else 11) and, for codes
- * longer than K, second-level tables indexed by the following bits.  Each
+ * the next K stream bits and, for codes longer than K, second-level tables
+ * indexed by the following bits.  K is the smallest width from 5 up (at most
+ * 12, or 11 when longer codes exist) for which the codes longer than K have
+ * an estimated probability (sum of 2^-length) of at most 2^-10, and for which
+ * the table fits 4096 entries; a shorter first level means fewer LDS bank
+ * conflicts and less LDS per workgroup.  Each
  * entry carries the code length, the code value and its bf16 dequantized
  * value.  Defined by: canonical Huffman codes (reading of EntroLLM's Huffman
  * step, see the stream layout above) and the dequantization rule of

@@ -113,8 +113,30 @@ def test_lut_two_level_with_longest_codes():
     lengths = huffman.code_lengths(counts, 16)
     assert lengths.max() == 16
     lut = ent.lut_build(lengths, 8, 16, np.float32(0.01), 3)
-    assert (int(lut[1]) & 0xFF) == 11
+    K = int(lut[1]) & 0xFF
+    assert K == expected_first_level(lengths) and K < 16
     check_lut(lut, lengths, 8, 16, np.float32(0.01), 3)
+
+
+def expected_first_level(lengths):
+    """First-level width rule of entro_lut_build: smallest k >= 5 whose longer
+    codes carry sum 2^-len <= 2^-10, capped at the longest code (<= 12) or 11."""
+    ls = [int(l) for l in lengths if l]
+    top = max(ls)
+    kmax = top if top <= 12 else 11
+    for k in range(min(5, kmax), kmax):
+        if sum(2.0 ** -l for l in ls if l > k) <= 2.0 ** -10:
+            return k
+    return kmax
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_lut_first_level_width_rule(seed):
+    bits = 8 if seed % 2 else 4
+    q = fuzz_codes(300 + seed, 30000, bits, ["skewed", "peaked", "uniform", "sparse"][seed % 4])
+    lengths = huffman.code_lengths(quant.histogram(q, bits), 16 if bits == 8 else 12)
+    lut = ent.lut_build(lengths, bits, 16 if bits == 8 else 12, np.float32(0.02), 1)
+    assert int(lut[1]) & 0xFF == expected_first_level(lengths)
 
 
 def test_lut_single_symbol_and_incomplete_code():
