@@ -73,15 +73,16 @@ def read_traffic(name: str):
 # --------------------------------------------------------------------------
 
 class Coded:
-    def __init__(self, q, scale, zp, scheme, bits, max_len, chunk, lanes, rows, cols):
+    def __init__(self, q, scale, zp, scheme, bits, max_len, chunk, lanes, rows, cols, refill_steps):
         import entropy_coded_weight_canonical_amd as ent
 
         self.rows, self.cols = rows, cols
         self.bits, self.max_len, self.chunk, self.lanes = bits, max_len, chunk, lanes
         self.scale, self.zp, self.scheme = scale, zp, scheme
+        self.refill_steps = refill_steps
         self.n = int(q.size)
         self.lengths = ent.code_lengths(q, bits, max_len)
-        self.words, self.offs = ent.encode(q, self.lengths, bits, chunk, lanes)
+        self.words, self.offs = ent.encode(q, self.lengths, bits, chunk, lanes, refill_steps=refill_steps)
         self.lut = ent.lut_build(self.lengths, bits, max_len, scale, zp)
         self.n_chunks = int(self.offs.size - 1)
 
@@ -94,14 +95,14 @@ class Coded:
         return 8.0 * self.in_bytes / self.n
 
 
-def code_tensor(spec, bits, scheme, chunk, lanes, clip_sigma=0.0):
+def code_tensor(spec, bits, scheme, chunk, lanes, refill_steps, clip_sigma=0.0):
     import entropy_coded_weight_canonical_amd as ent
     from synth import weights
 
     w = weights(spec)
     clip = float(clip_sigma * np.std(w, dtype=np.float64)) if clip_sigma else 0.0
     q, s, zp, chosen = ent.quantize(w, bits, scheme, clip=clip)
-    return Coded(q, s, zp, chosen, bits, 16 if bits == 8 else 12, chunk, lanes, spec.rows, spec.cols)
+    return Coded(q, s, zp, chosen, bits, 16 if bits == 8 else 12, chunk, lanes, spec.rows, spec.cols, refill_steps)
 
 
 # --------------------------------------------------------------------------
@@ -118,7 +119,7 @@ def cpu_baseline(coded: Coded, budget_s: float = 12.0):
     reps = 0
     while True:
         q = ccodec.decode(coded.words, coded.offs, coded.lengths, coded.n, coded.chunk, coded.lanes,
-                          threads=threads)
+                          threads=threads, refill_steps=coded.refill_steps)
         dequant_bf16(q, coded.scale, coded.zp)
         n_done += coded.n
         reps += 1
@@ -181,10 +182,10 @@ def bench_decode(args, workload, bits, scheme, chunk, lanes, replicas, mode):
 
     spec = tensor_specs(workload)[0]
     log(f"encoding {workload} ({spec.rows}x{spec.cols}, {bits}-bit {scheme}, C={chunk}, W={lanes})")
-    coded = code_tensor(spec, bits, scheme, chunk, lanes)
+    coded = code_tensor(spec, bits, scheme, chunk, lanes, args.refill_steps)
     log(f"coded {coded.coded_bits_per_weight:.3f} bits/weight; uploading {replicas} replicas")
     dts = [ent.DeviceTensor.upload(coded.lut, coded.words, coded.offs, coded.n, chunk, lanes, bits,
-                                   coded.max_len) for _ in range(replicas)]
+                                   coded.max_len, refill_steps=args.refill_steps) for _ in range(replicas)]
     odt = torch.uint8 if mode == "u8" else torch.int16
     outs = [torch.empty(coded.n, dtype=odt, device="cuda") for _ in range(replicas)]
     status = torch.zeros(replicas, dtype=torch.int32, device="cuda")
@@ -222,7 +223,8 @@ def bench_decode(args, workload, bits, scheme, chunk, lanes, replicas, mode):
         "dtype": "bf16" if mode == "bf16" else "u8",
         "data": "synthetic",
         "config": {"workload": f"{workload}: {spec.rows}x{spec.cols} {scheme} {bits}-bit, C={chunk}, W={lanes}, "
-                               f"x{replicas} replicas, decode{'+dequant->bf16' if mode == 'bf16' else '->u8'}",
+                               f"refill every {args.refill_steps} step(s), x{replicas} replicas, "
+                               f"decode{'+dequant->bf16' if mode == 'bf16' else '->u8'}",
                    "global_batch": replicas, "symbols_per_step": n_sym,
                    "coded_bits_per_weight": round(coded.coded_bits_per_weight, 4),
                    "parallelism": "single GPU"},
@@ -256,7 +258,8 @@ def bench_gemv(args, workload, batch, clip_sigma=0.0):
         row = []
         for s in (x for x in specs if x.layer == L):
             chunk = s.cols * max(1, round(8192 / s.cols))
-            row.append((s, code_tensor(s, 4, "unsigned" if clip_sigma else "mixed", chunk, 64, clip_sigma)))
+            row.append((s, code_tensor(s, 4, "unsigned" if clip_sigma else "mixed", chunk, 64, args.refill_steps,
+                                       clip_sigma)))
         coded_layers.append(row)
     groups = []   # per layer: list of (descs, items)
     keep = []
@@ -272,7 +275,8 @@ def bench_gemv(args, workload, batch, clip_sigma=0.0):
             x = torch.from_numpy(activations_bf16(workload, len(groups), cols, batch).view(np.int16)).cuda()
             descs, items = [], []
             for s, c in members:
-                dt = ent.DeviceTensor.upload(c.lut, c.words, c.offs, c.n, c.chunk, c.lanes, c.bits, c.max_len)
+                dt = ent.DeviceTensor.upload(c.lut, c.words, c.offs, c.n, c.chunk, c.lanes, c.bits, c.max_len,
+                                             refill_steps=c.refill_steps)
                 y = torch.empty((batch, s.rows), dtype=torch.float32, device="cuda")
                 keep += [dt, y]
                 descs.append(dt.desc)
@@ -345,6 +349,8 @@ def main():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--clip-sigma", type=float, default=0.0)
     ap.add_argument("--distinct-layers", type=int, default=2)
+    ap.add_argument("--refill-steps", type=int, default=2, choices=[1, 2],
+                    help="steps per refill decision of the encoded streams")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()

@@ -78,6 +78,19 @@ __device__ __forceinline__ uint32_t sub_len(uint32_t n, uint32_t e) {
   return r;
 }
 
+// lanes whose two codewords (length bytes of a and b) are longer than n
+__device__ __forceinline__ uint32_t pair_len(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:BYTE_1"
+      : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint64_t gt_mask(uint32_t a, uint32_t n) {
+  uint64_t m;
+  asm volatile("v_cmp_gt_u32 %0, %1, %2" : "=s"(m) : "v"(a), "v"(n));
+  return m;
+}
+
 // scalar & vector, kept as one v_and (not folded into a select)
 __device__ __forceinline__ uint32_t and_sv(uint32_t s, uint32_t v) {
   uint32_t r;
@@ -149,6 +162,7 @@ __device__ void task_generic(const TensorArg &d, const uint32_t *lut, uint32_t K
   const uint32_t *__restrict__ words = d.words;
   const uint64_t n_words = d.n_words, n_symbols = d.n_symbols;
   const uint32_t chunk = d.chunk, cols = d.cols, rows = d.rows;
+  const uint32_t D = d.refill_steps;
 
   const uint64_t c = task * G + grp;
   uint32_t flags = 0;
@@ -170,9 +184,9 @@ __device__ void task_generic(const TensorArg &d, const uint32_t *lut, uint32_t K
   const uint32_t steps = chunk >> LOG2W;
   const uint64_t sym0 = c * chunk;
 
-  uint64_t buf = 0;
-  uint32_t n = 0;
-  uint64_t P = 0;
+  uint64_t buf = 0;      // loaded, unconsumed bits, first bit at bit 63
+  uint32_t n = 0;        // how many
+  uint64_t P = 0;        // words of the chunk taken so far
   float acc[BATCH];
 #pragma unroll
   for (int i = 0; i < BATCH; ++i) acc[i] = 0.f;
@@ -180,11 +194,18 @@ __device__ void task_generic(const TensorArg &d, const uint32_t *lut, uint32_t K
   uint64_t row = 0;
   if (MODE == kModeGemv) row = sym0 / cols;
 
-  for (uint32_t t = 0; t < steps; ++t) {
-    const bool act = t < my_steps;
+  for (uint32_t t0 = 0; t0 < steps; t0 += D) {
+    // bits this lane's codewords of steps t0 .. t0+D-1 need (peeked with the
+    // bits beyond n read as zeros: a code that fits is read exactly, one that
+    // does not still shows a length above n)
+    const bool act = t0 < my_steps;
     uint32_t e = lookup(lut, (uint32_t)(buf >> 32), K);
-    uint32_t len = entry_len(e);
-    const bool need = act && len > n;
+    uint32_t need_bits = entry_len(e);
+    if (D == 2 && t0 + 1 < my_steps && need_bits <= 31u) {
+      const uint32_t eb = lookup(lut, (uint32_t)((buf << need_bits) >> 32), K);
+      need_bits += entry_len(eb);
+    }
+    const bool need = act && need_bits > n;
     const uint64_t m = __ballot(need);
     if (m) {
       if (need) {
@@ -192,46 +213,52 @@ __device__ void task_generic(const TensorArg &d, const uint32_t *lut, uint32_t K
         uint32_t w = 0;
         if (idx < nw) w = words[wb + idx];
         else flags |= kFOverrun;
-        buf |= (uint64_t)w << (32u - n);
+        if (n > 32u) flags |= kFBadCode;   // only a malformed stream gets here with n > 32
+        else buf |= (uint64_t)w << (32u - n);
         n += 32u;
-        e = lookup(lut, (uint32_t)(buf >> 32), K);
-        len = entry_len(e);
       }
       P += (uint64_t)__popcll(m & grp_mask);
     }
-    if (act) {
-      if (len > kMaxCodeLen) {
-        flags |= kFBadCode;
-        len = 1u;
-      }
-      buf <<= len;
-      n -= len;
-      if (MODE == kModeGemv) {
-        const float v = __uint_as_float(e & 0xFFFF0000u);
+    for (uint32_t dt = 0; dt < D; ++dt) {
+      const uint32_t t = t0 + dt;
+      if (t >= steps) break;
+      const bool a = t < my_steps;
+      e = lookup(lut, (uint32_t)(buf >> 32), K);
+      uint32_t len = entry_len(e);
+      if (a) {
+        if (len > kMaxCodeLen || len > n) {
+          flags |= kFBadCode;
+          len = min(n, 31u);
+        }
+        buf = len >= 64u ? 0ull : buf << len;
+        n -= len;
+        if (MODE == kModeGemv) {
+          const float v = __uint_as_float(e & 0xFFFF0000u);
 #pragma unroll
-        for (int bi = 0; bi < BATCH; ++bi) {
-          if (bi < (int)batch) {
-            const float xv = __uint_as_float((uint32_t)d.x[(uint64_t)bi * cols + col] << 16);
-            acc[bi] = fmaf(v, xv, acc[bi]);
+          for (int bi = 0; bi < BATCH; ++bi) {
+            if (bi < (int)batch) {
+              const float xv = __uint_as_float((uint32_t)d.x[(uint64_t)bi * cols + col] << 16);
+              acc[bi] = fmaf(v, xv, acc[bi]);
+            }
           }
+        } else {
+          emit<MODE>(d.out, sym0 + ((uint64_t)t << LOG2W) + j, e);
         }
-      } else {
-        emit<MODE>(d.out, sym0 + ((uint64_t)t << LOG2W) + j, e);
       }
-    }
-    if (MODE == kModeGemv) {
-      col += W;
-      if (col >= cols) {   // uniform: every chunk starts a row and W divides cols
-        col -= cols;
+      if (MODE == kModeGemv) {
+        col += W;
+        if (col >= cols) {   // uniform: every chunk starts a row and W divides cols
+          col -= cols;
 #pragma unroll
-        for (int bi = 0; bi < BATCH; ++bi) {
-          float v = acc[bi];
+          for (int bi = 0; bi < BATCH; ++bi) {
+            float v = acc[bi];
 #pragma unroll
-          for (uint32_t off = W >> 1; off >= 1u; off >>= 1) v += __shfl_xor(v, (int)off, 64);
-          if (act && j == 0u && bi < (int)batch) static_cast<float *>(d.out)[(uint64_t)bi * rows + row] = v;
-          acc[bi] = 0.f;
+            for (uint32_t off = W >> 1; off >= 1u; off >>= 1) v += __shfl_xor(v, (int)off, 64);
+            if (a && j == 0u && bi < (int)batch) static_cast<float *>(d.out)[(uint64_t)bi * rows + row] = v;
+            acc[bi] = 0.f;
+          }
+          ++row;
         }
-        ++row;
       }
     }
   }
@@ -364,6 +391,179 @@ __device__ __forceinline__ uint32_t loop_small(const uint32_t *lut, uint32_t K, 
   return flags;
 }
 
+// Pair loops (refill decision every two steps).  Per pair: look up the
+// codeword A at the top of the buffer and B right after it; the lanes whose
+// A+B is longer than their loaded bits take one word (32 bits always cover
+// two codes of at most 16 bits) and look both up again; then A and B are
+// consumed with one shift by their summed length (the alignbit shift fields
+// of the two entries add up to (32 - lenA - lenB) mod 32).  An odd last step
+// is a group of one.
+template <typename OutT>
+__device__ __forceinline__ void consume_pair(uint32_t &hi, uint32_t &lo, uint32_t &n, uint32_t eA, uint32_t eB,
+                                             uint32_t lab, __amdgpu_buffer_rsrc_t outr, uint32_t voff,
+                                             uint32_t soff, uint32_t boff) {
+  const uint32_t sab = eA + eB;
+  const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, sab);
+  lo = __builtin_amdgcn_alignbit(lo, 0u, sab);
+  hi = nhi;
+  n -= lab;
+  store_out<OutT>(outr, voff, soff, eA);
+  store_out<OutT>(outr, voff, soff + boff, eB);
+}
+
+template <int MODE, typename OutT>
+__device__ __forceinline__ uint32_t pairs64(const uint32_t *lut, uint32_t K, const uint32_t *sw, uint32_t nw,
+                                            uint32_t steps, __amdgpu_buffer_rsrc_t outr, uint32_t lane) {
+  constexpr uint32_t B = 64u * (uint32_t)sizeof(OutT);   // bytes per step
+  const uint32_t voff = lane * (uint32_t)sizeof(OutT);
+  const uint32_t send = (steps & ~1u) * B;
+  uint32_t hi = 0, lo = 0, n = 0, P = 0;
+  for (uint32_t soff = 0; soff != send; soff += 2u * B) {
+    uint32_t eA = lookup(lut, hi, K);
+    uint32_t eB = lookup(lut, __builtin_amdgcn_alignbit(hi, lo, eA), K);
+    uint32_t lab = pair_len(eA, eB);
+    const uint64_t m = gt_mask(lab, n);
+    if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+      const uint32_t idx =
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const uint32_t w = sw[P + idx];
+      hi |= w >> n;
+      lo = __builtin_amdgcn_alignbit(w, 0u, n);
+      n += 32u;
+      eA = lookup(lut, hi, K);
+      eB = lookup(lut, __builtin_amdgcn_alignbit(hi, lo, eA), K);
+      lab = pair_len(eA, eB);
+    }
+    P += (uint32_t)__popcll(m);
+    consume_pair<OutT>(hi, lo, n, eA, eB, lab, outr, voff, soff, B);
+  }
+  if (steps & 1u) {   // last step alone
+    uint32_t e = lookup(lut, hi, K);
+    const uint64_t m = need_mask(e, n);
+    if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+      const uint32_t idx =
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const uint32_t w = sw[P + idx];
+      hi |= w >> n;
+      lo = __builtin_amdgcn_alignbit(w, 0u, n);
+      n += 32u;
+      e = lookup(lut, hi, K);
+    }
+    P += (uint32_t)__popcll(m);
+    const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
+    lo = __builtin_amdgcn_alignbit(lo, 0u, e);
+    hi = nhi;
+    n = sub_len(n, e);
+    store_out<OutT>(outr, voff, send, e);
+  }
+  uint32_t flags = 0;
+  if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
+  if (hi | lo) flags |= kFPadding;
+  return flags;
+}
+
+template <int MODE, typename OutT>
+__device__ __forceinline__ uint32_t pairs32(const uint32_t *lut, uint32_t K, const uint32_t *sw, uint32_t dcs,
+                                            uint32_t nw0, uint32_t nw1, uint32_t steps, __amdgpu_buffer_rsrc_t outr,
+                                            uint32_t lane_off, uint32_t lane) {
+  constexpr uint32_t B = 32u * (uint32_t)sizeof(OutT);
+  const uint32_t upper = lane >= 32u ? ~0u : 0u;
+  const uint32_t voff = lane_off * (uint32_t)sizeof(OutT);
+  const uint32_t send = (steps & ~1u) * B;
+  uint32_t hi = 0, lo = 0, n = 0, P0 = 0, D = dcs;
+  for (uint32_t soff = 0; soff != send; soff += 2u * B) {
+    uint32_t eA = lookup(lut, hi, K);
+    uint32_t eB = lookup(lut, __builtin_amdgcn_alignbit(hi, lo, eA), K);
+    uint32_t lab = pair_len(eA, eB);
+    const uint64_t m = gt_mask(lab, n);
+    const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+    const uint32_t clo = (uint32_t)__popc(mlo);
+    if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+      const uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, and_sv(D - clo, upper)));
+      const uint32_t w = sw[P0 + idx];
+      hi |= w >> n;
+      lo = __builtin_amdgcn_alignbit(w, 0u, n);
+      n += 32u;
+      eA = lookup(lut, hi, K);
+      eB = lookup(lut, __builtin_amdgcn_alignbit(hi, lo, eA), K);
+      lab = pair_len(eA, eB);
+    }
+    P0 += clo;
+    D += (uint32_t)__popc(mhi) - clo;
+    consume_pair<OutT>(hi, lo, n, eA, eB, lab, outr, voff, soff, B);
+  }
+  if (steps & 1u) {
+    uint32_t e = lookup(lut, hi, K);
+    const uint64_t m = need_mask(e, n);
+    const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+    const uint32_t clo = (uint32_t)__popc(mlo);
+    if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+      const uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, and_sv(D - clo, upper)));
+      const uint32_t w = sw[P0 + idx];
+      hi |= w >> n;
+      lo = __builtin_amdgcn_alignbit(w, 0u, n);
+      n += 32u;
+      e = lookup(lut, hi, K);
+    }
+    P0 += clo;
+    D += (uint32_t)__popc(mhi) - clo;
+    const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
+    lo = __builtin_amdgcn_alignbit(lo, 0u, e);
+    hi = nhi;
+    n = sub_len(n, e);
+    store_out<OutT>(outr, voff, send, e);
+  }
+  const uint32_t P1 = D - dcs + P0;
+  const uint32_t P = upper ? P1 : P0, nw = upper ? nw1 : nw0;
+  uint32_t flags = 0;
+  if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
+  if (hi | lo) flags |= kFPadding;
+  return flags;
+}
+
+template <int MODE, int LOG2W, typename OutT>
+__device__ __forceinline__ uint32_t pairs_small(const uint32_t *lut, uint32_t K, const uint32_t *stage,
+                                                uint32_t cs, uint32_t nw, uint32_t steps,
+                                                __amdgpu_buffer_rsrc_t outr, uint32_t lane_off, uint32_t lane) {
+  constexpr uint32_t W = 1u << LOG2W;
+  constexpr uint32_t B = W * (uint32_t)sizeof(OutT);
+  const uint32_t voff = lane_off * (uint32_t)sizeof(OutT);
+  const uint32_t grp = lane >> LOG2W;
+  const uint64_t grp_mask = ((1ull << (W & 63u)) - 1ull) << (grp * W);
+  const uint64_t grp_below = grp_mask & ((1ull << lane) - 1ull);
+  uint32_t hi = 0, lo = 0, n = 0, P = 0;
+  for (uint32_t t = 0; t < steps; t += 2u) {
+    const bool two = t + 1u < steps;
+    uint32_t eA = lookup(lut, hi, K);
+    uint32_t eB = two ? lookup(lut, __builtin_amdgcn_alignbit(hi, lo, eA), K) : 0u;
+    uint32_t lab = pair_len(eA, eB);
+    const uint64_t m = gt_mask(lab, n);
+    if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+      const uint32_t w = stage[cs + P + (uint32_t)__popcll(m & grp_below)];
+      hi |= w >> n;
+      lo = __builtin_amdgcn_alignbit(w, 0u, n);
+      n += 32u;
+      eA = lookup(lut, hi, K);
+      eB = two ? lookup(lut, __builtin_amdgcn_alignbit(hi, lo, eA), K) : 0u;
+      lab = pair_len(eA, eB);
+    }
+    P += (uint32_t)__popcll(m & grp_mask);
+    if (two) {
+      consume_pair<OutT>(hi, lo, n, eA, eB, lab, outr, voff, t * B, B);
+    } else {
+      const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, eA);
+      lo = __builtin_amdgcn_alignbit(lo, 0u, eA);
+      hi = nhi;
+      n = sub_len(n, eA);
+      store_out<OutT>(outr, voff, t * B, eA);
+    }
+  }
+  uint32_t flags = 0;
+  if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
+  if (hi | lo) flags |= kFPadding;
+  return flags;
+}
+
 // One full wavefront task through LDS; returns false if it must take the
 // generic path (malformed offsets or more words than the staging area).
 template <int MODE, int LOG2W>
@@ -413,14 +613,18 @@ __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K,
   const __amdgpu_buffer_rsrc_t outr = __builtin_amdgcn_make_buffer_rsrc((void *)outp, (short)0, (int)out_bytes, 0x00020000);
   const uint32_t lane_off = grp * d.chunk + j;
   uint32_t flags;
+  const bool pairs = d.refill_steps == 2u;
   if (LOG2W == 6) {
-    flags = loop64<MODE, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane);
+    flags = pairs ? pairs64<MODE, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane)
+                  : loop64<MODE, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane);
   } else if (LOG2W == 5) {
     const uint32_t cs0 = rfl(__shfl(cs, 0, 64)), cs1 = rfl(__shfl(cs, 32, 64));
     const uint32_t nw0 = rfl(__shfl(nw, 0, 64)), nw1 = rfl(__shfl(nw, 32, 64));
-    flags = loop32<MODE, OutT>(lut, K, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane);
+    flags = pairs ? pairs32<MODE, OutT>(lut, K, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane)
+                  : loop32<MODE, OutT>(lut, K, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane);
   } else {
-    flags = loop_small<MODE, LOG2W, OutT>(lut, K, stage, cs, nw, steps, outr, lane_off, lane);
+    flags = pairs ? pairs_small<MODE, LOG2W, OutT>(lut, K, stage, cs, nw, steps, outr, lane_off, lane)
+                  : loop_small<MODE, LOG2W, OutT>(lut, K, stage, cs, nw, steps, outr, lane_off, lane);
   }
   if (flags) atomicOr(d.status, flags);
   return true;
@@ -499,6 +703,7 @@ static entro_status check_tensor(const entro_tensor &t) {
   if (t.chunk_symbols == 0 || t.chunk_symbols % t.lanes || t.chunk_symbols > kMaxChunk) return ENTRO_E_FORMAT;
   if (t.sym_bits != 4 && t.sym_bits != 8) return ENTRO_E_FORMAT;
   if (t.max_len < 1 || t.max_len > kMaxCodeLen) return ENTRO_E_FORMAT;
+  if (t.refill_steps > 2) return ENTRO_E_FORMAT;
   if (t.n_symbols == 0) return ENTRO_OK;
   if (!t.d_lut || !t.d_words || !t.d_chunk_bit_off) return ENTRO_E_INVAL;
   const uint64_t nc = (t.n_symbols + t.chunk_symbols - 1) / t.chunk_symbols;
@@ -585,6 +790,7 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
       d.n_chunks = (uint32_t)((x.n_symbols + x.chunk_symbols - 1) / x.chunk_symbols);
       d.expect_hdr = (x.sym_bits << 8) | (x.max_len << 16);
       d.lut_words = (uint32_t)std::min<uint64_t>(x.lut_bytes / 4, kLutHeaderWords + kLutMaxEntries);
+      d.refill_steps = x.refill_steps == 2u ? 2u : 1u;
       if (mode == kModeGemv) {
         d.out = g[i].d_y;
         d.x = g[i].d_x;

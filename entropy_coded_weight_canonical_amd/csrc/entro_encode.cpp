@@ -258,10 +258,12 @@ extern "C" entro_status entro_encode_layout(const uint8_t *q, uint64_t n, const 
 }
 
 extern "C" entro_status entro_encode(const uint8_t *q, uint64_t n, const uint8_t *code_len, uint32_t bits,
-                                     uint32_t chunk, uint32_t lanes, const uint64_t *chunk_bit_off, uint32_t *words,
-                                     uint32_t threads) {
+                                     uint32_t chunk, uint32_t lanes, uint32_t refill_steps,
+                                     const uint64_t *chunk_bit_off, uint32_t *words, uint32_t threads) {
   entro_status st = check_layout(q, n, code_len, bits, chunk, lanes);
   if (st != ENTRO_OK) return st;
+  if (refill_steps == 0) refill_steps = 1;
+  if (refill_steps > 2) return ENTRO_E_FORMAT;
   if (!chunk_bit_off || (!words && n)) return ENTRO_E_INVAL;
   const uint32_t nsym = 1u << bits;
   // canonical codewords
@@ -296,15 +298,27 @@ extern "C" entro_status entro_encode(const uint8_t *q, uint64_t n, const uint8_t
         avail[j] = 0;
         has_cur[j] = has_next[j] = false;
       }
+      const uint64_t steps = (cc + lanes - 1) / lanes;
       for (uint64_t k = 0; k < cc; ++k) {
         const uint32_t j = (uint32_t)(k & (lanes - 1));
+        const uint64_t t = k / lanes;
         const uint8_t s = q[beg + k];
         const uint32_t l = s < nsym ? code_len[s] : 0;
         if (!l || out > end) {
           bad = true;
           return;
         }
-        if (l > avail[j]) {          // the decoder takes the next word here
+        // bits the lane needs at this decision point (its codewords of the
+        // next refill_steps steps), only at the first step of the group
+        uint32_t need = 0;
+        if (t % refill_steps == 0) {
+          need = l;
+          for (uint32_t d = 1; d < refill_steps && t + d < steps; ++d) {
+            const uint64_t k2 = k + (uint64_t)d * lanes;
+            if (k2 < cc) need += q[beg + k2] < nsym ? code_len[q[beg + k2]] : 0;
+          }
+        }
+        if (need > avail[j]) {       // the decoder takes the next word here
           if (!has_cur[j]) {
             slot_cur[j] = out++;
             has_cur[j] = true;
@@ -314,7 +328,7 @@ extern "C" entro_status entro_encode(const uint8_t *q, uint64_t n, const uint8_t
           }
           avail[j] += 32;
         }
-        avail[j] -= l;
+        avail[j] -= l;   // (the group's later codewords find avail already covering them)
         acc[j] = (acc[j] << l) | code[s];
         nacc[j] += l;
         if (nacc[j] >= 32) {

@@ -39,7 +39,7 @@ struct TensorArg {
   uint32_t expect_hdr;     // sym_bits << 8 | max_len << 16 (header word 1 without K)
   uint32_t lut_words;      // readable uint32 words at lut
   uint32_t n_tasks;        // wavefront tasks: ceil(n_chunks / chunks per wavefront)
-  uint32_t lut_entries;    // entries the table holds according to its size
+  uint32_t refill_steps;   // steps per refill decision (1 or 2)
 };
 
 constexpr int kMaxTensorsPerLaunch = 32;

@@ -16,9 +16,12 @@
  *   - each lane's codewords (canonical: codes of one length are consecutive in
  *     symbol order, shorter codes first, first code zero; MSB-first) are packed
  *     into 32-bit words, first bit in bit 31, the last word zero-padded;
- *   - a lane takes its next word at the step whose codeword is longer than the
- *     number of loaded, unconsumed bits it holds; words are stored in the order
- *     they are taken, lanes of one step in increasing lane order;
+ *   - refill decisions are taken every D steps (D = refill_steps, 1 or 2): at a
+ *     step t with t mod D == 0 a lane takes its next word when its codewords of
+ *     steps t .. t+D-1 are together longer than the number of loaded,
+ *     unconsumed bits it holds (one word always suffices: codes are at most 16
+ *     bits); words are stored in the order they are taken, lanes of one
+ *     decision point in increasing lane order;
  *   - chunk_bit_off[c] = 32 * (words before chunk c); chunk_bit_off[n_chunks]
  *     = 32 * n_words.  Words are little-endian uint32.
  *
@@ -100,7 +103,8 @@ typedef struct {
   uint32_t max_chunk_words;       /* words of the largest chunk, or 0 if unknown; sizes
                                      the on-chip staging (a chunk larger than stated is
                                      still decoded correctly, only more slowly)          */
-  uint32_t reserved;              /* must be 0                                          */
+  uint32_t refill_steps;          /* steps per refill decision the stream was encoded
+                                     with: 1 or 2 (0 is read as 1)                       */
 } entro_tensor;
 
 /* Operands of the fused GEMV for one tensor, read as a [rows][cols] row-major

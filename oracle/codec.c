@@ -15,14 +15,17 @@
  *     order, shorter codes first, first code zero; MSB-first);
  *   - lane j of a chunk holds symbols k = j (mod W); its codewords are cut
  *     into 32-bit words, first bit in bit 31, last word zero-padded;
- *   - a lane takes its next word at the step whose codeword is longer than
- *     its count of loaded, unconsumed bits; words are stored in the order they
- *     are taken, lanes of one step in increasing lane index;
+ *   - refill decisions every D = refill_steps steps (1 or 2): at a step t with
+ *     t mod D == 0 a lane takes its next word when its codewords of steps
+ *     t .. t+D-1 are together longer than its count of loaded, unconsumed
+ *     bits; words are stored in the order they are taken, lanes of one
+ *     decision point in increasing lane index;
  *   - chunk_bit_off[c] = 32 * (words before chunk c), plus a final entry.
  *
  * The decoder reads one bit at a time and compares against the canonical
- * first code of each length; a lane that runs out of bits takes the chunk's
- * next word.  It never builds a lookup table.
+ * first code of each length; at a decision point a lane tries to read its
+ * next D codewords from the bits it holds and, if it runs dry, takes the
+ * chunk's next word and reads them again.  It never builds a lookup table.
  *
  * Plain C99, no intrinsics, no threads (callers run chunk ranges in parallel).
  */
@@ -37,9 +40,10 @@
 #define OC_E_NOMEM 4
 #define OC_MAXLEN 32
 
-static int check_params(uint32_t chunk, uint32_t lanes) {
+static int check_params(uint32_t chunk, uint32_t lanes, uint32_t refill_steps) {
   if (lanes < 1 || lanes > 64 || (lanes & (lanes - 1))) return OC_E_PARAM;
   if (chunk < 1 || chunk % lanes) return OC_E_PARAM;
+  if (refill_steps != 1 && refill_steps != 2) return OC_E_PARAM;
   return OC_OK;
 }
 
@@ -83,7 +87,7 @@ static uint64_t chunk_words(const uint8_t *q, uint64_t cc, const uint8_t *len, u
 int oc_layout(const uint8_t *q, uint64_t n, const uint8_t *len, uint32_t nsym,
               uint32_t chunk, uint32_t lanes, uint64_t *chunk_bit_off, uint64_t *n_words) {
   uint64_t nc, c, acc = 0, i;
-  if (check_params(chunk, lanes)) return OC_E_PARAM;
+  if (check_params(chunk, lanes, 1)) return OC_E_PARAM;
   for (i = 0; i < n; i++)
     if (q[i] >= nsym || len[q[i]] == 0) return OC_E_CODEBOOK;
   nc = (n + chunk - 1) / chunk;
@@ -99,7 +103,7 @@ int oc_layout(const uint8_t *q, uint64_t n, const uint8_t *len, uint32_t nsym,
 
 /* Encode chunks [c0, c1) into words; chunk_bit_off must come from oc_layout. */
 int oc_encode(const uint8_t *q, uint64_t n, const uint8_t *len, uint32_t nsym,
-              uint32_t chunk, uint32_t lanes, const uint64_t *chunk_bit_off,
+              uint32_t chunk, uint32_t lanes, uint32_t refill_steps, const uint64_t *chunk_bit_off,
               uint32_t *words, uint64_t c0, uint64_t c1) {
   uint32_t code[256];
   uint64_t c, k;
@@ -108,7 +112,7 @@ int oc_encode(const uint8_t *q, uint64_t n, const uint8_t *len, uint32_t nsym,
   uint32_t *lane_buf;
   uint64_t lane_n[64], taken[64];
   int32_t avail[64];
-  if (check_params(chunk, lanes) || nsym > 256) return OC_E_PARAM;
+  if (check_params(chunk, lanes, refill_steps) || nsym > 256) return OC_E_PARAM;
   if (canonical(len, nsym, code) < 0) return OC_E_CODEBOOK;
   /* per-lane word buffer: at most ceil(chunk/lanes) codewords of <= 32 bits */
   lane_cap = ((uint64_t)chunk / lanes) + 2;
@@ -138,12 +142,14 @@ int oc_encode(const uint8_t *q, uint64_t n, const uint8_t *len, uint32_t nsym,
     }
     /* 2. store the words in the order the lanes take them */
     steps = (cc + lanes - 1) / lanes;
-    for (t = 0; t < steps; t++) {
+    for (t = 0; t < steps; t += refill_steps) {
       for (j = 0; j < lanes; j++) {
         uint64_t kk = (uint64_t)t * lanes + j;
-        int32_t l;
+        int32_t l = 0;
+        uint32_t d;
         if (kk >= cc) continue;
-        l = len[q[beg + kk]];
+        for (d = 0; d < refill_steps; d++)
+          if (kk + (uint64_t)d * lanes < cc) l += len[q[beg + kk + (uint64_t)d * lanes]];
         if (l > avail[j]) {
           if (taken[j] >= lane_n[j]) { free(lane_buf); return OC_E_STREAM; }
           words[out++] = lane_buf[(uint64_t)j * lane_cap + taken[j]++];
@@ -160,18 +166,44 @@ int oc_encode(const uint8_t *q, uint64_t n, const uint8_t *len, uint32_t nsym,
   return OC_OK;
 }
 
+/* Read the next `count` codewords from the `nbits` bits at the top of `buf`
+ * (first bit = bit 63) one bit at a time.  Returns the bits used, 0 if the
+ * bits end first, -1 if no codeword matches. */
+static int read_codewords(uint64_t buf, int nbits, uint32_t count_, int max_len, const uint32_t *count,
+                          const uint32_t *first, const uint32_t *offset, const uint8_t *sorted_syms,
+                          uint8_t *syms) {
+  int p = 0;
+  uint32_t i, l, code;
+  for (i = 0; i < count_; i++) {
+    int found = 0;
+    code = 0;
+    for (l = 1; l <= (uint32_t)max_len; l++) {
+      if (p >= nbits) return 0;
+      code = (code << 1) | (uint32_t)((buf >> (63 - p)) & 1u);
+      p++;
+      if (code >= first[l] && code - first[l] < count[l]) {
+        syms[i] = sorted_syms[offset[l] + code - first[l]];
+        found = 1;
+        break;
+      }
+    }
+    if (!found) return -1;
+  }
+  return p;
+}
+
 /* Decode chunks [c0, c1) bit by bit into out[c*chunk ...]. */
 int oc_decode(const uint32_t *words, uint64_t n_words, const uint64_t *chunk_bit_off,
               uint64_t n, const uint8_t *len, uint32_t nsym, uint32_t chunk, uint32_t lanes,
-              uint8_t *out, uint64_t c0, uint64_t c1) {
+              uint32_t refill_steps, uint8_t *out, uint64_t c0, uint64_t c1) {
   uint32_t count[OC_MAXLEN + 1], first[OC_MAXLEN + 1], offset[OC_MAXLEN + 1];
   uint8_t sorted_syms[256];
-  uint32_t cur[64];      /* current word of each lane */
-  int32_t left[64];      /* unread bits of cur */
+  uint64_t buf[64];      /* unconsumed bits of each lane, first bit at bit 63 */
+  int32_t nb[64];        /* how many */
   int max_len = 0;
   uint32_t s, l, code, acc, j;
   uint64_t c;
-  if (check_params(chunk, lanes) || nsym > 256) return OC_E_PARAM;
+  if (check_params(chunk, lanes, refill_steps) || nsym > 256) return OC_E_PARAM;
   memset(count, 0, sizeof count);
   for (s = 0; s < nsym; s++) {
     if (len[s] > OC_MAXLEN) return OC_E_CODEBOOK;
@@ -190,41 +222,39 @@ int oc_decode(const uint32_t *words, uint64_t n_words, const uint64_t *chunk_bit
   for (l = 1; l <= (uint32_t)max_len; l++)
     for (s = 0; s < nsym; s++)
       if (len[s] == l) sorted_syms[acc++] = (uint8_t)s;
+  /* one word must cover the codewords of a decision point */
+  if ((int)refill_steps * max_len > 32) return OC_E_CODEBOOK;
   for (c = c0; c < c1; c++) {
     uint64_t beg = c * chunk, cc = n - beg < chunk ? n - beg : chunk;
     uint64_t pos = chunk_bit_off[c] / 32, end = chunk_bit_off[c + 1] / 32, t, steps;
     if (chunk_bit_off[c] % 32 || end < pos || end > n_words) return OC_E_STREAM;
-    for (j = 0; j < lanes; j++) { left[j] = 0; cur[j] = 0; }
+    for (j = 0; j < lanes; j++) { buf[j] = 0; nb[j] = 0; }
     steps = (cc + lanes - 1) / lanes;
-    for (t = 0; t < steps; t++) {
+    for (t = 0; t < steps; t += refill_steps) {
       for (j = 0; j < lanes; j++) {
         uint64_t k = t * lanes + j;
-        int found = 0;
+        uint8_t syms[2];
+        uint32_t cnt = 0, d;
+        int used;
         if (k >= cc) continue;
-        code = 0;
-        for (l = 1; l <= (uint32_t)max_len; l++) {
-          uint32_t bit;
-          if (left[j] == 0) {
-            if (pos >= end) return OC_E_STREAM;
-            cur[j] = words[pos++];
-            left[j] = 32;
-          }
-          bit = (cur[j] >> (left[j] - 1)) & 1u;
-          left[j]--;
-          code = (code << 1) | bit;
-          if (code >= first[l] && code - first[l] < count[l]) {
-            out[beg + k] = sorted_syms[offset[l] + code - first[l]];
-            found = 1;
-            break;
-          }
+        for (d = 0; d < refill_steps; d++)
+          if (k + (uint64_t)d * lanes < cc) cnt++;
+        used = read_codewords(buf[j], nb[j], cnt, max_len, count, first, offset, sorted_syms, syms);
+        if (used == 0) {
+          if (pos >= end || nb[j] > 32) return OC_E_STREAM;
+          buf[j] |= (uint64_t)words[pos++] << (32 - nb[j]);
+          nb[j] += 32;
+          used = read_codewords(buf[j], nb[j], cnt, max_len, count, first, offset, sorted_syms, syms);
         }
-        if (!found) return OC_E_STREAM;
+        if (used <= 0) return OC_E_STREAM;
+        for (d = 0; d < cnt; d++) out[beg + k + (uint64_t)d * lanes] = syms[d];
+        buf[j] = used == 64 ? 0 : buf[j] << used;
+        nb[j] -= used;
       }
     }
     if (pos != end) return OC_E_STREAM;
     for (j = 0; j < lanes; j++)
-      if (left[j] && (cur[j] & ((left[j] == 32) ? 0xFFFFFFFFu : ((1u << left[j]) - 1u))))
-        return OC_E_STREAM;
+      if (buf[j]) return OC_E_STREAM;
   }
   return OC_OK;
 }

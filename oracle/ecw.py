@@ -18,11 +18,15 @@ Layout
    cut into 32-bit words whose first bit is bit 31; the last word is padded
    with zero bits.
 5. Word order inside a chunk: each lane keeps a count ``n`` of loaded but
-   unconsumed bits (0 at the start).  At step ``t`` a lane takes its next word
-   exactly when its codeword for this step is longer than ``n`` (then
-   ``n += 32``), and then consumes the codeword (``n -= l``).  The chunk's
-   words are stored in the order they are taken, lanes of one step in
-   increasing lane index.
+   unconsumed bits (0 at the start).  Refill decisions are taken every
+   ``refill_steps`` (D, 1 or 2) steps: at a step ``t`` with ``t mod D == 0`` a
+   lane takes its next word exactly when its codewords of steps
+   ``t .. t+D-1`` (those it has) are together longer than ``n`` (then
+   ``n += 32``), and then consumes them.  Since codes are at most 16 bits
+   long, one word always suffices.  The chunk's words are stored in the order
+   they are taken, lanes of one decision point in increasing lane index.
+   D = 1 decides per step; D = 2 decides per pair of steps, which halves the
+   decision points a decoder has to synchronize on.
 6. Chunks are concatenated; ``chunk_bit_off[c]`` = 32 x (words before chunk c),
    with a final entry for the end.  Words are little-endian uint32 in memory.
 """
@@ -37,16 +41,18 @@ def n_chunks(n_symbols: int, chunk: int) -> int:
     return -(-n_symbols // chunk)
 
 
-def _check_params(chunk: int, lanes: int) -> None:
+def _check_params(chunk: int, lanes: int, refill_steps: int = 1) -> None:
     if lanes < 1 or lanes > 64 or (lanes & (lanes - 1)):
         raise ValueError("lanes must be a power of two in [1, 64]")
     if chunk < 1 or chunk % lanes:
         raise ValueError("chunk must be a positive multiple of lanes")
+    if refill_steps not in (1, 2):
+        raise ValueError("refill_steps must be 1 or 2")
 
 
-def encode(q: np.ndarray, lengths: np.ndarray, chunk: int, lanes: int):
+def encode(q: np.ndarray, lengths: np.ndarray, chunk: int, lanes: int, refill_steps: int = 1):
     """Encode codes ``q`` (any shape, row-major) -> ``(words uint32, chunk_bit_off uint64)``."""
-    _check_params(chunk, lanes)
+    _check_params(chunk, lanes, refill_steps)
     q = np.asarray(q, dtype=np.uint8).ravel()
     lengths = np.asarray(lengths, dtype=np.int64)
     codes = canonical_codes(lengths)
@@ -63,12 +69,12 @@ def encode(q: np.ndarray, lengths: np.ndarray, chunk: int, lanes: int):
             lane_words.append([int(bits[i:i + 32].ljust(32, "0"), 2) for i in range(0, len(bits), 32)])
         n = [0] * lanes
         taken = [0] * lanes
-        for t in range(-(-cc // lanes)):
+        for t0 in range(0, -(-cc // lanes), refill_steps):
             for j in range(lanes):
-                k = t * lanes + j
-                if k >= cc:
+                ks = [t * lanes + j for t in range(t0, t0 + refill_steps) if t * lanes + j < cc]
+                if not ks:
                     continue
-                l = int(lengths[sl[k]])
+                l = sum(int(lengths[sl[k]]) for k in ks)
                 if l > n[j]:
                     words.append(lane_words[j][taken[j]])
                     taken[j] += 1
@@ -105,16 +111,18 @@ def _canonical_tables(lengths: np.ndarray):
 
 
 def decode(words: np.ndarray, chunk_bit_off: np.ndarray, lengths: np.ndarray,
-           n_symbols: int, chunk: int, lanes: int) -> np.ndarray:
+           n_symbols: int, chunk: int, lanes: int, refill_steps: int = 1) -> np.ndarray:
     """Bit-serial canonical decoder: reads one bit at a time, never a table.
 
-    A lane that needs a bit and has none left takes the chunk's next word.
-    Because a lane only runs dry inside a codeword it could not finish, this
-    reproduces the encoder's word order without computing it.  Raises
-    ``StreamError`` on an undecodable prefix, on running past the chunk's
-    words, on unused words, or on nonzero padding bits.
+    At each decision point a lane first tries to read its next codewords
+    (one, or two for ``refill_steps`` 2) bit by bit from the bits it holds;
+    if it runs dry it takes the chunk's next word and reads them again.  This
+    finds the encoder's word order by decoding, without computing it from
+    code lengths.  Raises ``StreamError`` on an undecodable prefix, on
+    running past the chunk's words, on unused words, or on nonzero padding
+    bits.
     """
-    _check_params(chunk, lanes)
+    _check_params(chunk, lanes, refill_steps)
     lengths = np.asarray(lengths, dtype=np.int64)
     max_len, count, first, offset, sorted_syms = _canonical_tables(lengths)
     words = [int(w) for w in np.asarray(words, dtype=np.uint32)]
@@ -131,30 +139,44 @@ def decode(words: np.ndarray, chunk_bit_off: np.ndarray, lengths: np.ndarray,
         cc = min(chunk, n_symbols - c * chunk)
         pending = [[] for _ in range(lanes)]   # unconsumed bits of each lane, first bit first
 
-        def next_bit(j):
-            nonlocal pos
-            if not pending[j]:
-                if pos >= end:
-                    raise StreamError(f"chunk {c}: lane {j} runs past the chunk's words")
-                w = words[pos]
-                pos += 1
-                pending[j].extend((w >> (31 - i)) & 1 for i in range(32))
-            return pending[j].pop(0)
-
-        for t in range(-(-cc // lanes)):
-            for j in range(lanes):
-                k = t * lanes + j
-                if k >= cc:
-                    continue
+        def read_codewords(bits, count_):
+            """Symbols of the next ``count_`` codewords of ``bits`` and the bits they
+            use, or None if ``bits`` end first."""
+            syms, p = [], 0
+            for _ in range(count_):
                 code = 0
                 for l in range(1, max_len + 1):
-                    code = (code << 1) | next_bit(j)
+                    if p >= len(bits):
+                        return None
+                    code = (code << 1) | bits[p]
+                    p += 1
                     d = code - first[l]
                     if 0 <= d < count[l]:
-                        out[c * chunk + k] = sorted_syms[offset[l] + d]
+                        syms.append(sorted_syms[offset[l] + d])
                         break
                 else:
-                    raise StreamError(f"chunk {c}: lane {j} step {t}: no codeword matches")
+                    raise StreamError(f"chunk {c}: no codeword matches")
+            return syms, p
+
+        for t0 in range(0, -(-cc // lanes), refill_steps):
+            for j in range(lanes):
+                ks = [t * lanes + j for t in range(t0, t0 + refill_steps) if t * lanes + j < cc]
+                if not ks:
+                    continue
+                got = read_codewords(pending[j], len(ks))
+                if got is None:
+                    if pos >= end:
+                        raise StreamError(f"chunk {c}: lane {j} runs past the chunk's words")
+                    w = words[pos]
+                    pos += 1
+                    pending[j].extend((w >> (31 - i)) & 1 for i in range(32))
+                    got = read_codewords(pending[j], len(ks))
+                    if got is None:
+                        raise StreamError(f"chunk {c}: lane {j}: codewords longer than a word")
+                syms, used = got
+                for k, sym in zip(ks, syms):
+                    out[c * chunk + k] = sym
+                del pending[j][:used]
         if pos != end:
             raise StreamError(f"chunk {c}: {end - pos} words left unused")
         for j in range(lanes):

@@ -27,6 +27,7 @@ class Case:
     lut: np.ndarray
     rows: int = 0
     cols: int = 0
+    refill_steps: int = 1
 
     @property
     def n(self) -> int:
@@ -37,7 +38,7 @@ class Case:
 
 
 def make_case(q, bits, chunk, lanes, scale=0.0123, zp=None, max_len=None, lengths=None,
-              rows=0, cols=0) -> Case:
+              rows=0, cols=0, refill_steps=1) -> Case:
     q = np.ascontiguousarray(np.asarray(q, dtype=np.uint8).ravel())
     max_len = max_len or (16 if bits == 8 else 12)
     if lengths is None:
@@ -46,15 +47,15 @@ def make_case(q, bits, chunk, lanes, scale=0.0123, zp=None, max_len=None, length
         lengths = np.zeros(1 << bits, dtype=np.int64)
         lengths[0] = 1
     zp = (1 << (bits - 1)) if zp is None else zp
-    words, offs = ccodec.encode(q, lengths, chunk, lanes, threads=8)
+    words, offs = ccodec.encode(q, lengths, chunk, lanes, threads=8, refill_steps=refill_steps)
     lut = ent.lut_build(lengths, bits, max_len, np.float32(scale), zp)
     return Case(q, bits, max_len, np.asarray(lengths, dtype=np.uint8), np.float32(scale), int(zp), chunk,
-                lanes, words, offs, lut, rows, cols)
+                lanes, words, offs, lut, rows, cols, refill_steps)
 
 
 def upload(case: Case, device="cuda"):
     return ent.DeviceTensor.upload(case.lut, case.words, case.offs, case.n, case.chunk, case.lanes, case.bits,
-                                   case.max_len, device=device)
+                                   case.max_len, device=device, refill_steps=case.refill_steps)
 
 
 def run_decode(cases, mode="u8", device="cuda"):

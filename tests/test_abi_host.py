@@ -195,6 +195,7 @@ def test_device_entry_points_validate_before_launch(lib):
     assert dec(chunk_symbols=0) == 3
     assert dec(sym_bits=6) == 3
     assert dec(max_len=17) == 3
+    assert dec(refill_steps=3) == 3
     assert dec(d_words=None) == 1
     assert lib.entro_decode(arr, 1, None, st, None) == 1
     assert lib.entro_decode(arr, 1, outs, None, None) == 1
@@ -267,18 +268,19 @@ def test_code_lengths_binding_cap_is_optimal():
     assert int((counts * mine).sum()) == int((counts * ref).sum())
 
 
+@pytest.mark.parametrize("refill_steps", [1, 2])
 @pytest.mark.parametrize("lanes,chunk,n", [(1, 64, 1000), (2, 10, 333), (8, 64, 4097), (32, 4096, 70000),
-                                           (64, 64, 129), (64, 8192, 100000), (16, 48, 7)])
+                                           (64, 64, 129), (64, 8192, 100000), (16, 48, 7), (4, 12, 999)])
 @pytest.mark.parametrize("bits", [4, 8])
-def test_encoder_byte_identical_to_oracle(lanes, chunk, n, bits):
+def test_encoder_byte_identical_to_oracle(lanes, chunk, n, bits, refill_steps):
     q = fuzz_codes(lanes + n, n, bits, "skewed")
     lengths = huffman.code_lengths(quant.histogram(q, bits), 16 if bits == 8 else 12)
-    words, offs = ent.encode(q, lengths, bits, chunk, lanes, threads=3)
-    ow, oo = ccodec.encode(q, lengths, chunk, lanes)
+    words, offs = ent.encode(q, lengths, bits, chunk, lanes, threads=3, refill_steps=refill_steps)
+    ow, oo = ccodec.encode(q, lengths, chunk, lanes, refill_steps=refill_steps)
     assert np.array_equal(offs, oo) and np.array_equal(words, ow)
-    assert np.array_equal(ccodec.decode(words, offs, lengths, n, chunk, lanes), q)
+    assert np.array_equal(ccodec.decode(words, offs, lengths, n, chunk, lanes, refill_steps=refill_steps), q)
     if n <= 1000:
-        pw, po = ecw.encode(q, lengths, chunk, lanes)
+        pw, po = ecw.encode(q, lengths, chunk, lanes, refill_steps)
         assert np.array_equal(words, pw)
 
 

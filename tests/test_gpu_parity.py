@@ -36,16 +36,18 @@ def say(msg):
 LANE_GRID = [(1, 16), (2, 8), (4, 4), (8, 2), (16, 3), (32, 1), (32, 4), (64, 1), (64, 3)]
 
 
+@pytest.mark.parametrize("refill_steps", [1, 2])
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("lanes,mult", LANE_GRID)
-def test_fuzz_grid_u8_and_bf16(bits, lanes, mult):
+def test_fuzz_grid_u8_and_bf16(bits, lanes, mult, refill_steps):
     cases = []
     for i, kind in enumerate(CODE_KINDS):
-        chunk = lanes * mult * 8
+        chunk = lanes * (mult * 8 + (i % 2))       # even and odd steps per chunk
         n = chunk * (3 + i) + (17 * i + 5) % chunk   # several chunks and a ragged tail
         q = fuzz_codes(1000 * lanes + 10 * mult + i, n, bits, kind)
-        cases.append(make_case(q, bits, chunk, lanes, scale=0.0031 * (i + 1), zp=(7 * i) % (1 << bits)))
-    say(f"fuzz bits={bits} lanes={lanes} mult={mult}")
+        cases.append(make_case(q, bits, chunk, lanes, scale=0.0031 * (i + 1), zp=(7 * i) % (1 << bits),
+                               refill_steps=refill_steps))
+    say(f"fuzz bits={bits} lanes={lanes} mult={mult} refill_steps={refill_steps}")
     outs, st = run_decode(cases, "u8")
     assert (st == 0).all(), st
     for c, o in zip(cases, outs):
@@ -56,16 +58,17 @@ def test_fuzz_grid_u8_and_bf16(bits, lanes, mult):
         assert np.array_equal(o, c.expected_bf16())
 
 
-def test_longest_codes_use_second_level():
+@pytest.mark.parametrize("refill_steps", [1, 2])
+def test_longest_codes_use_second_level(refill_steps):
     counts = np.zeros(256, dtype=np.int64)
     counts[:40] = (2.0 ** np.arange(40, 0, -1)).astype(np.int64) // 2 + 1
     rng = np.random.default_rng(3)
     q = rng.choice(256, size=200_000, p=counts / counts.sum()).astype(np.uint8)
     # force the rarest symbols in so that 16-bit codes occur in the stream
     q[rng.choice(q.size, 40, replace=False)] = np.arange(40, dtype=np.uint8)
-    c = make_case(q, 8, 4096, 32)
+    c = make_case(q, 8, 4096, 32, refill_steps=refill_steps)
     assert c.lengths.max() >= 15
-    say("two-level table")
+    say(f"two-level table refill_steps={refill_steps}")
     outs, st = run_decode([c], "u8")
     assert st[0] == 0 and np.array_equal(outs[0], c.q)
     outs, st = run_decode([c], "bf16")
@@ -96,7 +99,8 @@ def test_more_tensors_than_one_launch_and_mixed_lanes():
         lanes = [64, 32, 64, 8][i % 4]
         bits = 8 if i % 3 else 4
         q = fuzz_codes(50 + i, 5000 + 37 * i, bits, CODE_KINDS[i % len(CODE_KINDS)])
-        cases.append(make_case(q, bits, lanes * 32, lanes, scale=0.001 * (i + 1), zp=i % 16))
+        cases.append(make_case(q, bits, lanes * 32, lanes, scale=0.001 * (i + 1), zp=i % 16,
+                               refill_steps=1 + (i % 5 == 2)))
     say("45 tensors")
     outs, st = run_decode(cases, "bf16")
     assert (st == 0).all(), st
@@ -161,7 +165,8 @@ def test_tensor_2048_asymmetric_8bit_full_size():
     qz = quant.quantize_asymmetric(weights(_spec("tensor_2048")), 8)
     cases = [make_case(qz.q, 8, 4096, 32, scale=qz.scale, zp=qz.zero_point),
              make_case(qz.q, 8, 4096, 64, scale=qz.scale, zp=qz.zero_point),
-             make_case(qz.q, 8, 4096, 1, scale=qz.scale, zp=qz.zero_point)]
+             make_case(qz.q, 8, 4096, 1, scale=qz.scale, zp=qz.zero_point),
+             make_case(qz.q, 8, 4096, 32, scale=qz.scale, zp=qz.zero_point, refill_steps=2)]
     say("tensor_2048 W=32/64/1")
     outs, st = run_decode(cases, "u8")
     assert (st == 0).all()
@@ -173,10 +178,11 @@ def test_tensor_2048_asymmetric_8bit_full_size():
         assert np.array_equal(o, c.expected_bf16())
 
 
-def test_tensor_4096_unsigned_4bit_full_size_replicated():
+@pytest.mark.parametrize("refill_steps", [1, 2])
+def test_tensor_4096_unsigned_4bit_full_size_replicated(refill_steps):
     qz = quant.quantize_unsigned(weights(_spec("tensor_4096")), 4)
-    c = make_case(qz.q, 4, 8192, 32, scale=qz.scale, zp=qz.zero_point)
-    say("tensor_4096 x16 replicas")
+    c = make_case(qz.q, 4, 8192, 32, scale=qz.scale, zp=qz.zero_point, refill_steps=refill_steps)
+    say(f"tensor_4096 x16 replicas refill_steps={refill_steps}")
     outs, st = run_decode([c] * 16, "bf16")
     assert (st == 0).all()
     exp = c.expected_bf16()
@@ -188,20 +194,21 @@ def test_tensor_4096_unsigned_4bit_full_size_replicated():
 # fused GEMV
 # --------------------------------------------------------------------------
 
-def _gemv_case(rows, cols, bits, seed, rows_per_chunk=1, lanes=64, scheme="mixed"):
+def _gemv_case(rows, cols, bits, seed, rows_per_chunk=1, lanes=64, scheme="mixed", refill_steps=1):
     rng = np.random.default_rng(seed)
     w = (rng.standard_t(4, size=(rows, cols)) * 0.02).astype(np.float32)
     qz = {"mixed": quant.quantize_mixed, "asymmetric": quant.quantize_asymmetric,
           "unsigned": quant.quantize_unsigned}[scheme](w, bits)
     return make_case(qz.q, bits, cols * rows_per_chunk, lanes, scale=qz.scale, zp=qz.zero_point,
-                     rows=rows, cols=cols)
+                     rows=rows, cols=cols, refill_steps=refill_steps)
 
 
 @pytest.mark.parametrize("batch", [1, 3, 8])
 def test_gemv_small_shapes(batch):
     cases = [_gemv_case(37, 128, 4, 1), _gemv_case(64, 192, 8, 2, rows_per_chunk=3),
              _gemv_case(100, 64, 4, 3, rows_per_chunk=7), _gemv_case(9, 320, 8, 4, lanes=32),
-             _gemv_case(33, 48, 4, 5, lanes=16, rows_per_chunk=2), _gemv_case(5, 8, 8, 6, lanes=1)]
+             _gemv_case(33, 48, 4, 5, lanes=16, rows_per_chunk=2), _gemv_case(5, 8, 8, 6, lanes=1),
+             _gemv_case(40, 192, 4, 7, refill_steps=2), _gemv_case(21, 96, 8, 8, lanes=32, refill_steps=2)]
     xs = [activations_bf16("phi3_stack", i, c.cols, batch) for i, c in enumerate(cases)]
     say(f"gemv small batch={batch}")
     ys, st = run_gemv(cases, xs, batch)

@@ -29,6 +29,26 @@ def golden():
     return lengths, q, int(g["chunk"][0][0]), int(g["lanes"][0][0]), words, offs
 
 
+def test_golden_pairs_encode_decode():
+    g, _ = load("ecw_pairs_tiny.txt")
+    lengths = np.array([int(x) for x in g["lengths"][0]])
+    q = np.array([int(x) for x in g["q"][0]], dtype=np.uint8)
+    chunk, lanes = int(g["chunk"][0][0]), int(g["lanes"][0][0])
+    offs = np.array([int(x) for x in g["chunk_bit_off"][0]], dtype=np.uint64)
+    for rs in (1, 2):
+        words = np.array([int(x, 16) for x in g[f"words_steps{rs}"][0]], dtype=np.uint32)
+        w, o = ecw.encode(q, lengths, chunk, lanes, rs)
+        assert w.tolist() == words.tolist() and o.tolist() == offs.tolist()
+        assert ecw.decode(words, offs, lengths, len(q), chunk, lanes, rs).tolist() == q.tolist()
+        w2, o2 = ccodec.encode(q, lengths, chunk, lanes, refill_steps=rs)
+        assert w2.tolist() == words.tolist() and o2.tolist() == offs.tolist()
+        assert ccodec.decode(words, offs, lengths, len(q), chunk, lanes, refill_steps=rs).tolist() == q.tolist()
+    # the two orders differ here, so each rule rejects the other's stream
+    w1 = np.array([int(x, 16) for x in g["words_steps1"][0]], dtype=np.uint32)
+    with pytest.raises(ecw.StreamError):
+        ecw.decode(w1, offs, lengths, len(q), chunk, lanes, 2)
+
+
 def test_golden_encode_decode():
     lengths, q, chunk, lanes, words, offs = golden()
     w, o = ecw.encode(q, lengths, chunk, lanes)
@@ -55,15 +75,26 @@ GRID = [
 ]
 
 
+@pytest.mark.parametrize("refill_steps", [1, 2])
 @pytest.mark.parametrize("bits,kind,lanes,chunk_mult,n", GRID)
-def test_round_trip_python_and_c(bits, kind, lanes, chunk_mult, n):
+def test_round_trip_python_and_c(bits, kind, lanes, chunk_mult, n, refill_steps):
     q, lengths = make_case(lanes * 100 + n, bits, kind, n)
     chunk = lanes * chunk_mult
-    w, o = ecw.encode(q, lengths, chunk, lanes)
-    assert ecw.decode(w, o, lengths, n, chunk, lanes).tolist() == q.tolist()
-    wc, oc = ccodec.encode(q, lengths, chunk, lanes)
+    w, o = ecw.encode(q, lengths, chunk, lanes, refill_steps)
+    assert ecw.decode(w, o, lengths, n, chunk, lanes, refill_steps).tolist() == q.tolist()
+    wc, oc = ccodec.encode(q, lengths, chunk, lanes, refill_steps=refill_steps)
     assert wc.tolist() == w.tolist() and oc.tolist() == o.tolist()
-    assert ccodec.decode(w, o, lengths, n, chunk, lanes).tolist() == q.tolist()
+    assert ccodec.decode(w, o, lengths, n, chunk, lanes, refill_steps=refill_steps).tolist() == q.tolist()
+    # a stream decoded under the other decision period either fails or (when
+    # the word orders happen to agree) still gives the codes back
+    other = 3 - refill_steps
+    try:
+        back = ccodec.decode(w, o, lengths, n, chunk, lanes, refill_steps=other)
+    except ccodec.CodecError:
+        back = None
+    if back is not None:
+        w2, _ = ccodec.encode(q, lengths, chunk, lanes, refill_steps=other)
+        assert np.array_equal(w2, w) and np.array_equal(back, q)
     # word count identity, chunk by chunk
     for c in range(len(o) - 1):
         sl = q[c * chunk:(c + 1) * chunk]
