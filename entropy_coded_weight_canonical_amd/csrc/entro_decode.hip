@@ -564,11 +564,172 @@ __device__ __forceinline__ uint32_t pairs_small(const uint32_t *lut, uint32_t K,
   return flags;
 }
 
+// Two-code table, built in LDS from the code table when a 4-bit tensor is
+// decoded in pairs: entry i (the next kPairBits stream bits) holds the
+// entry of codeword A (first word) and, in the second word, B's value with
+// the pair's summed length in byte 1 and its alignbit shift in bits [4:0],
+// so that one 8-byte read gives a whole pair.  Indices whose A and B do not
+// both fit in kPairBits bits carry kPairFallback; lanes that hit one look the
+// two codes up in the code table instead.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pair_word(uint32_t eB, uint32_t lab) {
+  return (eB & 0xFFFF0000u) | (lab << 8) | ((32u - lab) & 31u);
+}
+
+__device__ u32x2 build_pair_entry(const uint32_t *lut, uint32_t K, uint32_t i) {
+  const uint32_t hi = i << (32u - kPairBits);
+  const uint32_t eA = lookup(lut, hi, K);
+  const uint32_t lA = entry_len(eA);
+  u32x2 r;
+  r.x = 0u;
+  r.y = kPairFallback;
+  if (lA <= kPairBits) {
+    const uint32_t eB = lookup(lut, hi << lA, K);
+    const uint32_t lB = entry_len(eB);
+    if (lA + lB <= kPairBits) {
+      r.x = eA;
+      r.y = pair_word(eB, lA + lB);
+    }
+  }
+  return r;
+}
+
+__device__ __forceinline__ u32x2 pair_lookup(const uint32_t *lut, uint32_t K, const u32x2 *ptab, uint32_t hi,
+                                             uint32_t lo) {
+  u32x2 e2 = ptab[hi >> (32u - kPairBits)];
+  const uint64_t fb = pointer_mask(e2.y);
+  if (fb) {
+    if (__builtin_amdgcn_inverse_ballot_w64(fb)) {
+      const uint32_t eA = lookup(lut, hi, K);
+      const uint32_t eB = lookup(lut, __builtin_amdgcn_alignbit(hi, lo, eA), K);
+      e2.x = eA;
+      e2.y = pair_word(eB, pair_len(eA, eB));
+    }
+  }
+  return e2;
+}
+
+// W = 64 / W = 32 pair loops reading the two-code table.
+template <int MODE, typename OutT>
+__device__ __forceinline__ uint32_t tab_pairs64(const uint32_t *lut, uint32_t K, const u32x2 *ptab,
+                                                const uint32_t *sw, uint32_t nw, uint32_t steps,
+                                                __amdgpu_buffer_rsrc_t outr, uint32_t lane) {
+  constexpr uint32_t B = 64u * (uint32_t)sizeof(OutT);
+  const uint32_t voff = lane * (uint32_t)sizeof(OutT);
+  const uint32_t send = (steps & ~1u) * B;
+  uint32_t hi = 0, lo = 0, n = 0, P = 0;
+  for (uint32_t soff = 0; soff != send; soff += 2u * B) {
+    u32x2 e2 = pair_lookup(lut, K, ptab, hi, lo);
+    const uint64_t m = need_mask(e2.y, n);
+    if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+      const uint32_t idx =
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const uint32_t w = sw[P + idx];
+      hi |= w >> n;
+      lo = __builtin_amdgcn_alignbit(w, 0u, n);
+      n += 32u;
+      e2 = pair_lookup(lut, K, ptab, hi, lo);
+    }
+    P += (uint32_t)__popcll(m);
+    const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e2.y);
+    lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
+    hi = nhi;
+    n = sub_len(n, e2.y);
+    store_out<OutT>(outr, voff, soff, e2.x);
+    store_out<OutT>(outr, voff, soff + B, e2.y);
+  }
+  if (steps & 1u) {   // last step alone
+    uint32_t e = lookup(lut, hi, K);
+    const uint64_t m = need_mask(e, n);
+    if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+      const uint32_t idx =
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const uint32_t w = sw[P + idx];
+      hi |= w >> n;
+      lo = __builtin_amdgcn_alignbit(w, 0u, n);
+      n += 32u;
+      e = lookup(lut, hi, K);
+    }
+    P += (uint32_t)__popcll(m);
+    const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
+    lo = __builtin_amdgcn_alignbit(lo, 0u, e);
+    hi = nhi;
+    n = sub_len(n, e);
+    store_out<OutT>(outr, voff, send, e);
+  }
+  uint32_t flags = 0;
+  if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
+  if (hi | lo) flags |= kFPadding;
+  return flags;
+}
+
+template <int MODE, typename OutT>
+__device__ __forceinline__ uint32_t tab_pairs32(const uint32_t *lut, uint32_t K, const u32x2 *ptab,
+                                                const uint32_t *sw, uint32_t dcs, uint32_t nw0, uint32_t nw1,
+                                                uint32_t steps, __amdgpu_buffer_rsrc_t outr, uint32_t lane_off,
+                                                uint32_t lane) {
+  constexpr uint32_t B = 32u * (uint32_t)sizeof(OutT);
+  const uint32_t upper = lane >= 32u ? ~0u : 0u;
+  const uint32_t voff = lane_off * (uint32_t)sizeof(OutT);
+  const uint32_t send = (steps & ~1u) * B;
+  uint32_t hi = 0, lo = 0, n = 0, P0 = 0, D = dcs;
+  for (uint32_t soff = 0; soff != send; soff += 2u * B) {
+    u32x2 e2 = pair_lookup(lut, K, ptab, hi, lo);
+    const uint64_t m = need_mask(e2.y, n);
+    const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+    const uint32_t clo = (uint32_t)__popc(mlo);
+    if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+      const uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, and_sv(D - clo, upper)));
+      const uint32_t w = sw[P0 + idx];
+      hi |= w >> n;
+      lo = __builtin_amdgcn_alignbit(w, 0u, n);
+      n += 32u;
+      e2 = pair_lookup(lut, K, ptab, hi, lo);
+    }
+    P0 += clo;
+    D += (uint32_t)__popc(mhi) - clo;
+    const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e2.y);
+    lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
+    hi = nhi;
+    n = sub_len(n, e2.y);
+    store_out<OutT>(outr, voff, soff, e2.x);
+    store_out<OutT>(outr, voff, soff + B, e2.y);
+  }
+  if (steps & 1u) {
+    uint32_t e = lookup(lut, hi, K);
+    const uint64_t m = need_mask(e, n);
+    const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+    const uint32_t clo = (uint32_t)__popc(mlo);
+    if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+      const uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, and_sv(D - clo, upper)));
+      const uint32_t w = sw[P0 + idx];
+      hi |= w >> n;
+      lo = __builtin_amdgcn_alignbit(w, 0u, n);
+      n += 32u;
+      e = lookup(lut, hi, K);
+    }
+    P0 += clo;
+    D += (uint32_t)__popc(mhi) - clo;
+    const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
+    lo = __builtin_amdgcn_alignbit(lo, 0u, e);
+    hi = nhi;
+    n = sub_len(n, e);
+    store_out<OutT>(outr, voff, send, e);
+  }
+  const uint32_t P1 = D - dcs + P0;
+  const uint32_t P = upper ? P1 : P0, nw = upper ? nw1 : nw0;
+  uint32_t flags = 0;
+  if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
+  if (hi | lo) flags |= kFPadding;
+  return flags;
+}
+
 // One full wavefront task through LDS; returns false if it must take the
 // generic path (malformed offsets or more words than the staging area).
 template <int MODE, int LOG2W>
-__device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K, uint64_t task, uint32_t *stage,
-                            uint32_t stage_words) {
+__device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K, const u32x2 *ptab,
+                            uint64_t task, uint32_t *stage, uint32_t stage_words) {
   constexpr uint32_t W = 1u << LOG2W;
   constexpr uint32_t G = 64u / W;
   const uint32_t lane = threadIdx.x & 63u;
@@ -615,13 +776,18 @@ __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K,
   uint32_t flags;
   const bool pairs = d.refill_steps == 2u;
   if (LOG2W == 6) {
-    flags = pairs ? pairs64<MODE, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane)
-                  : loop64<MODE, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane);
+    if (pairs && ptab) flags = tab_pairs64<MODE, OutT>(lut, K, ptab, stage + al, rfl(nw), steps, outr, lane);
+    else if (pairs) flags = pairs64<MODE, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane);
+    else flags = loop64<MODE, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane);
   } else if (LOG2W == 5) {
     const uint32_t cs0 = rfl(__shfl(cs, 0, 64)), cs1 = rfl(__shfl(cs, 32, 64));
     const uint32_t nw0 = rfl(__shfl(nw, 0, 64)), nw1 = rfl(__shfl(nw, 32, 64));
-    flags = pairs ? pairs32<MODE, OutT>(lut, K, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane)
-                  : loop32<MODE, OutT>(lut, K, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane);
+    if (pairs && ptab)
+      flags = tab_pairs32<MODE, OutT>(lut, K, ptab, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane);
+    else if (pairs)
+      flags = pairs32<MODE, OutT>(lut, K, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane);
+    else
+      flags = loop32<MODE, OutT>(lut, K, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane);
   } else {
     flags = pairs ? pairs_small<MODE, LOG2W, OutT>(lut, K, stage, cs, nw, steps, outr, lane_off, lane)
                   : loop_small<MODE, LOG2W, OutT>(lut, K, stage, cs, nw, steps, outr, lane_off, lane);
@@ -642,9 +808,11 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_kernel(const LaunchArgs a) 
   __shared__ uint32_t lut_state;   // K | entries << 8, or 0 if the table is unusable
   uint32_t *lut = reinterpret_cast<uint32_t *>(dyn_lds);
 
+  u32x2 *ptab_area = reinterpret_cast<u32x2 *>(lut + a.lut_cap);   // two-code table, if any
   const uint32_t wave = rfl(threadIdx.x >> 6);
   const uint32_t stage_words = a.stage_words;
-  uint32_t *stage = lut + a.lut_cap + wave * (stage_words + kStageSlack);
+  uint32_t *stage = lut + a.lut_cap + (a.pair_bits ? 2u << a.pair_bits : 0u) + wave * (stage_words + kStageSlack);
+  const u32x2 *ptab = nullptr;
   const uint32_t bt0 = blockIdx.x * a.btasks_per_block;
   const uint32_t bt1 = min(bt0 + a.btasks_per_block, a.total_btasks);
   uint32_t cur = 0xFFFFFFFFu;
@@ -673,6 +841,14 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_kernel(const LaunchArgs a) 
       K = lut_state & 0xFFu;
       cur = ti;
       __syncthreads();
+      // two-code table for 4-bit tensors decoded in pairs
+      ptab = nullptr;
+      if (MODE != kModeGemv && a.pair_bits && K && d.refill_steps == 2u && ((d.expect_hdr >> 8) & 0xFFu) == 4u) {
+        for (uint32_t i = threadIdx.x; i < (1u << kPairBits); i += kBlockThreads)
+          ptab_area[i] = build_pair_entry(lut, K, i);
+        ptab = ptab_area;
+        __syncthreads();
+      }
     }
     if (!K) continue;
     const uint64_t task = (uint64_t)(bt - a.btask_begin[ti]) * kWaves + wave;
@@ -680,7 +856,7 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_kernel(const LaunchArgs a) 
     bool done = false;
     if (MODE != kModeGemv && stage_words) {
       const bool full = (task + 1) * G <= d.n_chunks && (task + 1) * G * (uint64_t)d.chunk <= d.n_symbols;
-      if (full) done = task_staged<MODE, LOG2W>(d, lut, K, task, stage, stage_words);
+      if (full) done = task_staged<MODE, LOG2W>(d, lut, K, ptab, task, stage, stage_words);
     }
     if (!done) task_generic<MODE, LOG2W, BATCH>(d, lut, K, task, a.batch);
   }
@@ -772,7 +948,7 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
     a.batch = batch;
     uint32_t total = 0, log2w = 0, k = 0;
     uint64_t stage_need = 0, lut_need = 0;
-    bool stage_known = true;
+    bool stage_known = true, want_pairs = false;
     for (; i < n && k < (uint32_t)kMaxTensorsPerLaunch; ++i) {
       const entro_tensor &x = t[i];
       if (x.n_symbols == 0) continue;
@@ -791,6 +967,7 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
       d.expect_hdr = (x.sym_bits << 8) | (x.max_len << 16);
       d.lut_words = (uint32_t)std::min<uint64_t>(x.lut_bytes / 4, kLutHeaderWords + kLutMaxEntries);
       d.refill_steps = x.refill_steps == 2u ? 2u : 1u;
+      if (d.refill_steps == 2u && x.sym_bits == 4u) want_pairs = true;
       if (mode == kModeGemv) {
         d.out = g[i].d_y;
         d.x = g[i].d_x;
@@ -819,9 +996,10 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
     // LDS: the largest table of the launch, then the staging areas (room for
     // the largest task plus 16-byte alignment), within 160 KiB
     a.lut_cap = (uint32_t)((lut_need + 3) & ~3ull);
-    size_t dyn = (size_t)a.lut_cap * 4u;
+    a.pair_bits = (mode != kModeGemv && want_pairs) ? kPairBits : 0u;
+    size_t dyn = (size_t)a.lut_cap * 4u + (a.pair_bits ? (size_t)8u << a.pair_bits : 0u);
     if (mode != kModeGemv) {
-      const uint64_t cap = ((160u * 1024u - 256u) / 4u - a.lut_cap) / kWaves - kStageSlack;
+      const uint64_t cap = ((160u * 1024u - 256u) / 4u - dyn / 4u) / kWaves - kStageSlack;
       uint64_t sw = (stage_need + 3 + 3) & ~3ull;
       sw = std::max<uint64_t>(64, std::min<uint64_t>(sw, cap & ~3ull));
       a.stage_words = (uint32_t)sw;

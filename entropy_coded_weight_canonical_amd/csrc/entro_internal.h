@@ -58,6 +58,10 @@ struct LaunchArgs {
   uint32_t btasks_per_block;
   uint32_t stage_words;                            // staging words per wavefront (0: none)
   uint32_t lut_cap;                                // table entries reserved in LDS
+  uint32_t pair_bits;                              // index bits of the two-code table (0: none)
 };
+
+constexpr uint32_t kPairBits = 10;                 // two-code table: 1024 entries of 8 bytes
+constexpr uint32_t kPairFallback = 0x80u;          // flag (byte 0 of the second word): no pair
 
 }  // namespace entro
