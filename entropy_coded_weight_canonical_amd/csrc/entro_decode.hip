@@ -50,6 +50,29 @@
 namespace entro {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// The workgroup's dynamic LDS.  The kernel declares no static LDS, so it
+// starts at LDS address 0 (checked once per workgroup, see lds_at_zero) and
+// the two-code table placed there is read at plain byte addresses.
+extern __shared__ u32x4 dyn_lds[];
+
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+
+__device__ __forceinline__ bool lds_at_zero() { return lds_addr(dyn_lds) == 0u; }
+
+// Word pointer into LDS advanced by c words with one s_lshl2_add_u32 (which
+// also writes SCC, so SCC is declared clobbered).
+__device__ __forceinline__ const uint32_t *lds_advance(const uint32_t *p, uint32_t c) {
+  uint32_t r;
+  asm("s_lshl2_add_u32 %0, %1, %2" : "=s"(r) : "s"(c), "s"(lds_addr(p)) : "scc");
+  return (const uint32_t *)(lds_u32 *)(uintptr_t)r;
+}
 
 template <int MODE>
 __device__ __forceinline__ uint32_t kernel_entry(uint32_t h) {
@@ -110,6 +133,36 @@ __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, uint32_t vof
     asm volatile("buffer_store_byte_d16_hi %0, %1, %2, %3 offen" : : "v"(e), "v"(voff), "s"(r), "s"(soff));
   else
     asm volatile("buffer_store_short_d16_hi %0, %1, %2, %3 offen" : : "v"(e), "v"(voff), "s"(r), "s"(soff));
+}
+
+// Both outputs of a pair step with one store per lane.  ab holds the lane's
+// two values packed (bf16: step t in bits [15:0], step t+1 in [31:16]; codes:
+// bytes 0 and 1).  Adjacent lanes swap ab (DPP quad_perm 1,0,3,2); an even
+// lane then stores its own and its odd neighbour's step-t value, an odd lane
+// both step-(t+1) values, at voffp = (even lane's offset) + (lane & 1) * W
+// elements.  All 64 lanes must be active; W >= 2.
+template <int MODE>
+__device__ __forceinline__ uint32_t pack_ab(uint32_t eA, uint32_t eB) {
+  return MODE == kModeU8 ? __builtin_amdgcn_perm(eB, eA, 0x0C0C0602u) : __builtin_amdgcn_perm(eB, eA, 0x07060302u);
+}
+
+template <int MODE>
+__device__ __forceinline__ uint32_t pair_sel(uint32_t lane) {
+  if (MODE == kModeU8) return (lane & 1u) ? 0x0C0C0105u : 0x0C0C0400u;
+  return (lane & 1u) ? 0x03020706u : 0x05040100u;
+}
+
+template <int MODE>
+__device__ __forceinline__ void store_pair(__amdgpu_buffer_rsrc_t r, uint32_t voffp, uint32_t soff, uint32_t ab,
+                                           uint32_t sel) {
+  const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)ab, 0xB1, 0xF, 0xF, false);
+  const uint32_t v = __builtin_amdgcn_perm(nb, ab, sel);
+  if (MODE == kModeU8) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, r, (int)voffp, (int)soff, 0);
+  else __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)voffp, (int)soff, 0);
+}
+
+__device__ __forceinline__ uint32_t pair_voff(uint32_t lane_off, uint32_t lane, uint32_t W, uint32_t elem) {
+  return ((lane_off & ~1u) + (lane & 1u) * W) * elem;
 }
 
 // values that are equal in all lanes, made visibly uniform for the compiler
@@ -396,19 +449,24 @@ __device__ __forceinline__ uint32_t loop_small(const uint32_t *lut, uint32_t K, 
 // A+B is longer than their loaded bits take one word (32 bits always cover
 // two codes of at most 16 bits) and look both up again; then A and B are
 // consumed with one shift by their summed length (the alignbit shift fields
-// of the two entries add up to (32 - lenA - lenB) mod 32).  An odd last step
-// is a group of one.
-template <typename OutT>
+// of the two entries add up to (32 - lenA - lenB) mod 32) and written with
+// one store per lane (store_pair; two stores for W = 1, where neighbouring
+// lanes belong to different chunks).  An odd last step is a group of one.
+template <int MODE, bool PACK, typename OutT>
 __device__ __forceinline__ void consume_pair(uint32_t &hi, uint32_t &lo, uint32_t &n, uint32_t eA, uint32_t eB,
                                              uint32_t lab, __amdgpu_buffer_rsrc_t outr, uint32_t voff,
-                                             uint32_t soff, uint32_t boff) {
+                                             uint32_t soff, uint32_t boff, uint32_t sel) {
   const uint32_t sab = eA + eB;
   const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, sab);
   lo = __builtin_amdgcn_alignbit(lo, 0u, sab);
   hi = nhi;
   n -= lab;
-  store_out<OutT>(outr, voff, soff, eA);
-  store_out<OutT>(outr, voff, soff + boff, eB);
+  if (PACK) {
+    store_pair<MODE>(outr, voff, soff, pack_ab<MODE>(eA, eB), sel);
+  } else {
+    store_out<OutT>(outr, voff, soff, eA);
+    store_out<OutT>(outr, voff, soff + boff, eB);
+  }
 }
 
 template <int MODE, typename OutT>
@@ -416,8 +474,11 @@ __device__ __forceinline__ uint32_t pairs64(const uint32_t *lut, uint32_t K, con
                                             uint32_t steps, __amdgpu_buffer_rsrc_t outr, uint32_t lane) {
   constexpr uint32_t B = 64u * (uint32_t)sizeof(OutT);   // bytes per step
   const uint32_t voff = lane * (uint32_t)sizeof(OutT);
+  const uint32_t voffp = pair_voff(lane, lane, 64u, (uint32_t)sizeof(OutT));
+  const uint32_t sel = pair_sel<MODE>(lane);
   const uint32_t send = (steps & ~1u) * B;
-  uint32_t hi = 0, lo = 0, n = 0, P = 0;
+  uint32_t hi = 0, lo = 0, n = 0;
+  const uint32_t *p = sw;
   for (uint32_t soff = 0; soff != send; soff += 2u * B) {
     uint32_t eA = lookup(lut, hi, K);
     uint32_t eB = lookup(lut, __builtin_amdgcn_alignbit(hi, lo, eA), K);
@@ -426,7 +487,7 @@ __device__ __forceinline__ uint32_t pairs64(const uint32_t *lut, uint32_t K, con
     if (__builtin_amdgcn_inverse_ballot_w64(m)) {
       const uint32_t idx =
           __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      const uint32_t w = sw[P + idx];
+      const uint32_t w = p[idx];
       hi |= w >> n;
       lo = __builtin_amdgcn_alignbit(w, 0u, n);
       n += 32u;
@@ -434,8 +495,8 @@ __device__ __forceinline__ uint32_t pairs64(const uint32_t *lut, uint32_t K, con
       eB = lookup(lut, __builtin_amdgcn_alignbit(hi, lo, eA), K);
       lab = pair_len(eA, eB);
     }
-    P += (uint32_t)__popcll(m);
-    consume_pair<OutT>(hi, lo, n, eA, eB, lab, outr, voff, soff, B);
+    p = lds_advance(p, (uint32_t)__popcll(m));
+    consume_pair<MODE, true, OutT>(hi, lo, n, eA, eB, lab, outr, voffp, soff, B, sel);
   }
   if (steps & 1u) {   // last step alone
     uint32_t e = lookup(lut, hi, K);
@@ -443,19 +504,20 @@ __device__ __forceinline__ uint32_t pairs64(const uint32_t *lut, uint32_t K, con
     if (__builtin_amdgcn_inverse_ballot_w64(m)) {
       const uint32_t idx =
           __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      const uint32_t w = sw[P + idx];
+      const uint32_t w = p[idx];
       hi |= w >> n;
       lo = __builtin_amdgcn_alignbit(w, 0u, n);
       n += 32u;
       e = lookup(lut, hi, K);
     }
-    P += (uint32_t)__popcll(m);
+    p = lds_advance(p, (uint32_t)__popcll(m));
     const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
     lo = __builtin_amdgcn_alignbit(lo, 0u, e);
     hi = nhi;
     n = sub_len(n, e);
     store_out<OutT>(outr, voff, send, e);
   }
+  const uint32_t P = (uint32_t)(p - sw);
   uint32_t flags = 0;
   if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
   if (hi | lo) flags |= kFPadding;
@@ -469,8 +531,11 @@ __device__ __forceinline__ uint32_t pairs32(const uint32_t *lut, uint32_t K, con
   constexpr uint32_t B = 32u * (uint32_t)sizeof(OutT);
   const uint32_t upper = lane >= 32u ? ~0u : 0u;
   const uint32_t voff = lane_off * (uint32_t)sizeof(OutT);
+  const uint32_t voffp = pair_voff(lane_off, lane, 32u, (uint32_t)sizeof(OutT));
+  const uint32_t sel = pair_sel<MODE>(lane);
   const uint32_t send = (steps & ~1u) * B;
-  uint32_t hi = 0, lo = 0, n = 0, P0 = 0, D = dcs;
+  uint32_t hi = 0, lo = 0, n = 0, D = dcs;
+  const uint32_t *p0 = sw;
   for (uint32_t soff = 0; soff != send; soff += 2u * B) {
     uint32_t eA = lookup(lut, hi, K);
     uint32_t eB = lookup(lut, __builtin_amdgcn_alignbit(hi, lo, eA), K);
@@ -480,7 +545,7 @@ __device__ __forceinline__ uint32_t pairs32(const uint32_t *lut, uint32_t K, con
     const uint32_t clo = (uint32_t)__popc(mlo);
     if (__builtin_amdgcn_inverse_ballot_w64(m)) {
       const uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, and_sv(D - clo, upper)));
-      const uint32_t w = sw[P0 + idx];
+      const uint32_t w = p0[idx];
       hi |= w >> n;
       lo = __builtin_amdgcn_alignbit(w, 0u, n);
       n += 32u;
@@ -488,9 +553,9 @@ __device__ __forceinline__ uint32_t pairs32(const uint32_t *lut, uint32_t K, con
       eB = lookup(lut, __builtin_amdgcn_alignbit(hi, lo, eA), K);
       lab = pair_len(eA, eB);
     }
-    P0 += clo;
+    p0 = lds_advance(p0, clo);
     D += (uint32_t)__popc(mhi) - clo;
-    consume_pair<OutT>(hi, lo, n, eA, eB, lab, outr, voff, soff, B);
+    consume_pair<MODE, true, OutT>(hi, lo, n, eA, eB, lab, outr, voffp, soff, B, sel);
   }
   if (steps & 1u) {
     uint32_t e = lookup(lut, hi, K);
@@ -499,13 +564,13 @@ __device__ __forceinline__ uint32_t pairs32(const uint32_t *lut, uint32_t K, con
     const uint32_t clo = (uint32_t)__popc(mlo);
     if (__builtin_amdgcn_inverse_ballot_w64(m)) {
       const uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, and_sv(D - clo, upper)));
-      const uint32_t w = sw[P0 + idx];
+      const uint32_t w = p0[idx];
       hi |= w >> n;
       lo = __builtin_amdgcn_alignbit(w, 0u, n);
       n += 32u;
       e = lookup(lut, hi, K);
     }
-    P0 += clo;
+    p0 = lds_advance(p0, clo);
     D += (uint32_t)__popc(mhi) - clo;
     const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
     lo = __builtin_amdgcn_alignbit(lo, 0u, e);
@@ -513,6 +578,7 @@ __device__ __forceinline__ uint32_t pairs32(const uint32_t *lut, uint32_t K, con
     n = sub_len(n, e);
     store_out<OutT>(outr, voff, send, e);
   }
+  const uint32_t P0 = (uint32_t)(p0 - sw);
   const uint32_t P1 = D - dcs + P0;
   const uint32_t P = upper ? P1 : P0, nw = upper ? nw1 : nw0;
   uint32_t flags = 0;
@@ -526,8 +592,11 @@ __device__ __forceinline__ uint32_t pairs_small(const uint32_t *lut, uint32_t K,
                                                 uint32_t cs, uint32_t nw, uint32_t steps,
                                                 __amdgpu_buffer_rsrc_t outr, uint32_t lane_off, uint32_t lane) {
   constexpr uint32_t W = 1u << LOG2W;
+  constexpr bool PACK = LOG2W > 0;
   constexpr uint32_t B = W * (uint32_t)sizeof(OutT);
   const uint32_t voff = lane_off * (uint32_t)sizeof(OutT);
+  const uint32_t voffp = PACK ? pair_voff(lane_off, lane, W, (uint32_t)sizeof(OutT)) : voff;
+  const uint32_t sel = pair_sel<MODE>(lane);
   const uint32_t grp = lane >> LOG2W;
   const uint64_t grp_mask = ((1ull << (W & 63u)) - 1ull) << (grp * W);
   const uint64_t grp_below = grp_mask & ((1ull << lane) - 1ull);
@@ -549,7 +618,7 @@ __device__ __forceinline__ uint32_t pairs_small(const uint32_t *lut, uint32_t K,
     }
     P += (uint32_t)__popcll(m & grp_mask);
     if (two) {
-      consume_pair<OutT>(hi, lo, n, eA, eB, lab, outr, voff, t * B, B);
+      consume_pair<MODE, PACK, OutT>(hi, lo, n, eA, eB, lab, outr, PACK ? voffp : voff, t * B, B, sel);
     } else {
       const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, eA);
       lo = __builtin_amdgcn_alignbit(lo, 0u, eA);
@@ -565,18 +634,15 @@ __device__ __forceinline__ uint32_t pairs_small(const uint32_t *lut, uint32_t K,
 }
 
 // Two-code table, built in LDS from the code table when a 4-bit tensor is
-// decoded in pairs: entry i (the next kPairBits stream bits) holds the
-// entry of codeword A (first word) and, in the second word, B's value with
-// the pair's summed length in byte 1 and its alignbit shift in bits [4:0],
-// so that one 8-byte read gives a whole pair.  Indices whose A and B do not
-// both fit in kPairBits bits carry kPairFallback; lanes that hit one look the
-// two codes up in the code table instead.
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// decoded in pairs: entry i (the next kPairBits stream bits) holds, in its
+// first word, the pair's two output values packed as by pack_ab and, in the
+// second, the pair's summed length in byte 1 and its alignbit shift in bits
+// [4:0], so that one 8-byte read gives a whole pair.  Indices whose A and B
+// do not both fit in kPairBits bits carry kPairFallback in byte 0 (length 0);
+// lanes that hit one look the two codes up in the code table instead.
+__device__ __forceinline__ uint32_t pair_word(uint32_t lab) { return (lab << 8) | ((32u - lab) & 31u); }
 
-__device__ __forceinline__ uint32_t pair_word(uint32_t eB, uint32_t lab) {
-  return (eB & 0xFFFF0000u) | (lab << 8) | ((32u - lab) & 31u);
-}
-
+template <int MODE>
 __device__ u32x2 build_pair_entry(const uint32_t *lut, uint32_t K, uint32_t i) {
   const uint32_t hi = i << (32u - kPairBits);
   const uint32_t eA = lookup(lut, hi, K);
@@ -588,23 +654,23 @@ __device__ u32x2 build_pair_entry(const uint32_t *lut, uint32_t K, uint32_t i) {
     const uint32_t eB = lookup(lut, hi << lA, K);
     const uint32_t lB = entry_len(eB);
     if (lA + lB <= kPairBits) {
-      r.x = eA;
-      r.y = pair_word(eB, lA + lB);
+      r.x = pack_ab<MODE>(eA, eB);
+      r.y = pair_word(lA + lB);
     }
   }
   return r;
 }
 
-__device__ __forceinline__ u32x2 pair_lookup(const uint32_t *lut, uint32_t K, const u32x2 *ptab, uint32_t hi,
-                                             uint32_t lo) {
-  u32x2 e2 = ptab[hi >> (32u - kPairBits)];
+template <int MODE>
+__device__ __forceinline__ u32x2 pair_lookup(const uint32_t *lut, uint32_t K, uint32_t hi, uint32_t lo) {
+  u32x2 e2 = *(lds_u32x2 *)(uintptr_t)((hi >> (32u - kPairBits)) << 3);   // table at LDS address 0
   const uint64_t fb = pointer_mask(e2.y);
   if (fb) {
     if (__builtin_amdgcn_inverse_ballot_w64(fb)) {
       const uint32_t eA = lookup(lut, hi, K);
       const uint32_t eB = lookup(lut, __builtin_amdgcn_alignbit(hi, lo, eA), K);
-      e2.x = eA;
-      e2.y = pair_word(eB, pair_len(eA, eB));
+      e2.x = pack_ab<MODE>(eA, eB);
+      e2.y = pair_word(pair_len(eA, eB));
     }
   }
   return e2;
@@ -612,32 +678,33 @@ __device__ __forceinline__ u32x2 pair_lookup(const uint32_t *lut, uint32_t K, co
 
 // W = 64 / W = 32 pair loops reading the two-code table.
 template <int MODE, typename OutT>
-__device__ __forceinline__ uint32_t tab_pairs64(const uint32_t *lut, uint32_t K, const u32x2 *ptab,
-                                                const uint32_t *sw, uint32_t nw, uint32_t steps,
+__device__ __forceinline__ uint32_t tab_pairs64(const uint32_t *lut, uint32_t K, const uint32_t *sw, uint32_t nw, uint32_t steps,
                                                 __amdgpu_buffer_rsrc_t outr, uint32_t lane) {
   constexpr uint32_t B = 64u * (uint32_t)sizeof(OutT);
   const uint32_t voff = lane * (uint32_t)sizeof(OutT);
+  const uint32_t voffp = pair_voff(lane, lane, 64u, (uint32_t)sizeof(OutT));
+  const uint32_t sel = pair_sel<MODE>(lane);
   const uint32_t send = (steps & ~1u) * B;
-  uint32_t hi = 0, lo = 0, n = 0, P = 0;
+  uint32_t hi = 0, lo = 0, n = 0;
+  const uint32_t *p = sw;
   for (uint32_t soff = 0; soff != send; soff += 2u * B) {
-    u32x2 e2 = pair_lookup(lut, K, ptab, hi, lo);
+    u32x2 e2 = pair_lookup<MODE>(lut, K, hi, lo);
     const uint64_t m = need_mask(e2.y, n);
     if (__builtin_amdgcn_inverse_ballot_w64(m)) {
       const uint32_t idx =
           __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      const uint32_t w = sw[P + idx];
+      const uint32_t w = p[idx];
       hi |= w >> n;
       lo = __builtin_amdgcn_alignbit(w, 0u, n);
       n += 32u;
-      e2 = pair_lookup(lut, K, ptab, hi, lo);
+      e2 = pair_lookup<MODE>(lut, K, hi, lo);
     }
-    P += (uint32_t)__popcll(m);
+    p = lds_advance(p, (uint32_t)__popcll(m));
     const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e2.y);
     lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
     hi = nhi;
     n = sub_len(n, e2.y);
-    store_out<OutT>(outr, voff, soff, e2.x);
-    store_out<OutT>(outr, voff, soff + B, e2.y);
+    store_pair<MODE>(outr, voffp, soff, e2.x, sel);
   }
   if (steps & 1u) {   // last step alone
     uint32_t e = lookup(lut, hi, K);
@@ -645,19 +712,20 @@ __device__ __forceinline__ uint32_t tab_pairs64(const uint32_t *lut, uint32_t K,
     if (__builtin_amdgcn_inverse_ballot_w64(m)) {
       const uint32_t idx =
           __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      const uint32_t w = sw[P + idx];
+      const uint32_t w = p[idx];
       hi |= w >> n;
       lo = __builtin_amdgcn_alignbit(w, 0u, n);
       n += 32u;
       e = lookup(lut, hi, K);
     }
-    P += (uint32_t)__popcll(m);
+    p = lds_advance(p, (uint32_t)__popcll(m));
     const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
     lo = __builtin_amdgcn_alignbit(lo, 0u, e);
     hi = nhi;
     n = sub_len(n, e);
     store_out<OutT>(outr, voff, send, e);
   }
+  const uint32_t P = (uint32_t)(p - sw);
   uint32_t flags = 0;
   if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
   if (hi | lo) flags |= kFPadding;
@@ -665,36 +733,37 @@ __device__ __forceinline__ uint32_t tab_pairs64(const uint32_t *lut, uint32_t K,
 }
 
 template <int MODE, typename OutT>
-__device__ __forceinline__ uint32_t tab_pairs32(const uint32_t *lut, uint32_t K, const u32x2 *ptab,
-                                                const uint32_t *sw, uint32_t dcs, uint32_t nw0, uint32_t nw1,
+__device__ __forceinline__ uint32_t tab_pairs32(const uint32_t *lut, uint32_t K, const uint32_t *sw, uint32_t dcs, uint32_t nw0, uint32_t nw1,
                                                 uint32_t steps, __amdgpu_buffer_rsrc_t outr, uint32_t lane_off,
                                                 uint32_t lane) {
   constexpr uint32_t B = 32u * (uint32_t)sizeof(OutT);
   const uint32_t upper = lane >= 32u ? ~0u : 0u;
   const uint32_t voff = lane_off * (uint32_t)sizeof(OutT);
+  const uint32_t voffp = pair_voff(lane_off, lane, 32u, (uint32_t)sizeof(OutT));
+  const uint32_t sel = pair_sel<MODE>(lane);
   const uint32_t send = (steps & ~1u) * B;
-  uint32_t hi = 0, lo = 0, n = 0, P0 = 0, D = dcs;
+  uint32_t hi = 0, lo = 0, n = 0, D = dcs;
+  const uint32_t *p0 = sw;
   for (uint32_t soff = 0; soff != send; soff += 2u * B) {
-    u32x2 e2 = pair_lookup(lut, K, ptab, hi, lo);
+    u32x2 e2 = pair_lookup<MODE>(lut, K, hi, lo);
     const uint64_t m = need_mask(e2.y, n);
     const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
     const uint32_t clo = (uint32_t)__popc(mlo);
     if (__builtin_amdgcn_inverse_ballot_w64(m)) {
       const uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, and_sv(D - clo, upper)));
-      const uint32_t w = sw[P0 + idx];
+      const uint32_t w = p0[idx];
       hi |= w >> n;
       lo = __builtin_amdgcn_alignbit(w, 0u, n);
       n += 32u;
-      e2 = pair_lookup(lut, K, ptab, hi, lo);
+      e2 = pair_lookup<MODE>(lut, K, hi, lo);
     }
-    P0 += clo;
+    p0 = lds_advance(p0, clo);
     D += (uint32_t)__popc(mhi) - clo;
     const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e2.y);
     lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
     hi = nhi;
     n = sub_len(n, e2.y);
-    store_out<OutT>(outr, voff, soff, e2.x);
-    store_out<OutT>(outr, voff, soff + B, e2.y);
+    store_pair<MODE>(outr, voffp, soff, e2.x, sel);
   }
   if (steps & 1u) {
     uint32_t e = lookup(lut, hi, K);
@@ -703,13 +772,13 @@ __device__ __forceinline__ uint32_t tab_pairs32(const uint32_t *lut, uint32_t K,
     const uint32_t clo = (uint32_t)__popc(mlo);
     if (__builtin_amdgcn_inverse_ballot_w64(m)) {
       const uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, and_sv(D - clo, upper)));
-      const uint32_t w = sw[P0 + idx];
+      const uint32_t w = p0[idx];
       hi |= w >> n;
       lo = __builtin_amdgcn_alignbit(w, 0u, n);
       n += 32u;
       e = lookup(lut, hi, K);
     }
-    P0 += clo;
+    p0 = lds_advance(p0, clo);
     D += (uint32_t)__popc(mhi) - clo;
     const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
     lo = __builtin_amdgcn_alignbit(lo, 0u, e);
@@ -717,6 +786,7 @@ __device__ __forceinline__ uint32_t tab_pairs32(const uint32_t *lut, uint32_t K,
     n = sub_len(n, e);
     store_out<OutT>(outr, voff, send, e);
   }
+  const uint32_t P0 = (uint32_t)(p0 - sw);
   const uint32_t P1 = D - dcs + P0;
   const uint32_t P = upper ? P1 : P0, nw = upper ? nw1 : nw0;
   uint32_t flags = 0;
@@ -776,14 +846,14 @@ __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K,
   uint32_t flags;
   const bool pairs = d.refill_steps == 2u;
   if (LOG2W == 6) {
-    if (pairs && ptab) flags = tab_pairs64<MODE, OutT>(lut, K, ptab, stage + al, rfl(nw), steps, outr, lane);
+    if (pairs && ptab) flags = tab_pairs64<MODE, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane);
     else if (pairs) flags = pairs64<MODE, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane);
     else flags = loop64<MODE, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane);
   } else if (LOG2W == 5) {
     const uint32_t cs0 = rfl(__shfl(cs, 0, 64)), cs1 = rfl(__shfl(cs, 32, 64));
     const uint32_t nw0 = rfl(__shfl(nw, 0, 64)), nw1 = rfl(__shfl(nw, 32, 64));
     if (pairs && ptab)
-      flags = tab_pairs32<MODE, OutT>(lut, K, ptab, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane);
+      flags = tab_pairs32<MODE, OutT>(lut, K, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane);
     else if (pairs)
       flags = pairs32<MODE, OutT>(lut, K, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane);
     else
@@ -802,16 +872,17 @@ __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K,
 template <int MODE, int LOG2W, int BATCH>
 __global__ __launch_bounds__(kBlockThreads) void ecw_kernel(const LaunchArgs a) {
   constexpr uint32_t G = 64u >> LOG2W;
-  // dynamic LDS: the table (lut_cap entries, a multiple of 4), then one
+  // dynamic LDS: the two-code table if any (first, so that its address is a
+  // constant), the code table (lut_cap entries, a multiple of 4), then one
   // 16-byte aligned staging area per wavefront
-  extern __shared__ u32x4 dyn_lds[];
-  __shared__ uint32_t lut_state;   // K | entries << 8, or 0 if the table is unusable
-  uint32_t *lut = reinterpret_cast<uint32_t *>(dyn_lds);
-
-  u32x2 *ptab_area = reinterpret_cast<u32x2 *>(lut + a.lut_cap);   // two-code table, if any
+  // K | entries << 8 of the current table, or 0 if it is unusable (kept in
+  // dynamic LDS so that the workgroup has no static LDS and dyn_lds is at 0)
+  uint32_t &lut_state = reinterpret_cast<uint32_t *>(dyn_lds)[a.state_word];
+  u32x2 *ptab_area = reinterpret_cast<u32x2 *>(dyn_lds);
+  uint32_t *lut = reinterpret_cast<uint32_t *>(dyn_lds) + (a.pair_bits ? 2u << a.pair_bits : 0u);
   const uint32_t wave = rfl(threadIdx.x >> 6);
   const uint32_t stage_words = a.stage_words;
-  uint32_t *stage = lut + a.lut_cap + (a.pair_bits ? 2u << a.pair_bits : 0u) + wave * (stage_words + kStageSlack);
+  uint32_t *stage = lut + a.lut_cap + wave * (stage_words + kStageSlack);
   const u32x2 *ptab = nullptr;
   const uint32_t bt0 = blockIdx.x * a.btasks_per_block;
   const uint32_t bt1 = min(bt0 + a.btasks_per_block, a.total_btasks);
@@ -843,9 +914,10 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_kernel(const LaunchArgs a) 
       __syncthreads();
       // two-code table for 4-bit tensors decoded in pairs
       ptab = nullptr;
-      if (MODE != kModeGemv && a.pair_bits && K && d.refill_steps == 2u && ((d.expect_hdr >> 8) & 0xFFu) == 4u) {
+      if (MODE != kModeGemv && a.pair_bits && K && d.refill_steps == 2u && ((d.expect_hdr >> 8) & 0xFFu) == 4u &&
+          lds_at_zero()) {
         for (uint32_t i = threadIdx.x; i < (1u << kPairBits); i += kBlockThreads)
-          ptab_area[i] = build_pair_entry(lut, K, i);
+          ptab_area[i] = build_pair_entry<MODE>(lut, K, i);
         ptab = ptab_area;
         __syncthreads();
       }
@@ -895,6 +967,11 @@ static hipError_t launch_one(uint32_t total_btasks, LaunchArgs &a, size_t dyn, h
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBlockThreads, dyn) != hipSuccess || per_cu < 1)
     per_cu = 1;
+  // Plan with less LDS than the CU has: workgroups that fill it to the last
+  // KiB are not all resident at once, and the persistent grid then runs in
+  // two rounds.
+  const int lds_fit = (int)((kLdsPerCu - kLdsPlanReserve) / (dyn + kStaticLds));
+  if (lds_fit >= 1 && per_cu > lds_fit) per_cu = lds_fit;
   if (cus < 1) cus = 1;
   const uint64_t slots = (uint64_t)cus * (uint64_t)per_cu;
   const uint32_t per_block = (uint32_t)((total_btasks + slots - 1) / slots);
@@ -937,8 +1014,10 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
       if (t[i].n_symbols == 0) continue;
       if (!it.d_x || !it.d_y) return ENTRO_E_INVAL;
       if (it.cols % t[i].lanes || t[i].chunk_symbols % it.cols) return ENTRO_E_FORMAT;
-    } else if (t[i].n_symbols && !outs[i]) {
-      return ENTRO_E_INVAL;
+    } else if (t[i].n_symbols) {
+      // neighbouring lanes' outputs are stored together (2 or 4 bytes)
+      const uintptr_t align = mode == kModeU8 ? 2u : 4u;
+      if (!outs[i] || (reinterpret_cast<uintptr_t>(outs[i]) & (align - 1u))) return ENTRO_E_INVAL;
     }
   }
   size_t i = 0;
@@ -999,12 +1078,14 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
     a.pair_bits = (mode != kModeGemv && want_pairs) ? kPairBits : 0u;
     size_t dyn = (size_t)a.lut_cap * 4u + (a.pair_bits ? (size_t)8u << a.pair_bits : 0u);
     if (mode != kModeGemv) {
-      const uint64_t cap = ((160u * 1024u - 256u) / 4u - dyn / 4u) / kWaves - kStageSlack;
+      const uint64_t cap = ((kLdsPerCu - kStaticLds) / 4u - dyn / 4u) / kWaves - kStageSlack;
       uint64_t sw = (stage_need + 3 + 3) & ~3ull;
       sw = std::max<uint64_t>(64, std::min<uint64_t>(sw, cap & ~3ull));
       a.stage_words = (uint32_t)sw;
       dyn += (size_t)kWaves * (sw + kStageSlack) * 4u;
     }
+    a.state_word = (uint32_t)(dyn / 4u);
+    dyn += 16u;
     hipError_t err;
     if (mode == kModeU8) err = launch_w<kModeU8, 1>(log2w, total, a, dyn, s);
     else if (mode == kModeBf16) err = launch_w<kModeBf16, 1>(log2w, total, a, dyn, s);

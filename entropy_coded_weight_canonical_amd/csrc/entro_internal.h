@@ -43,8 +43,11 @@ struct TensorArg {
 };
 
 constexpr int kMaxTensorsPerLaunch = 32;
-constexpr int kWaves = 8;                       // wavefronts per workgroup
+constexpr int kWaves = 16;                      // wavefronts per workgroup
 constexpr int kBlockThreads = 64 * kWaves;
+constexpr uint32_t kLdsPerCu = 160u * 1024u;     // gfx950
+constexpr uint32_t kLdsPlanReserve = 4u * 1024u; // kept free when sizing the persistent grid
+constexpr uint32_t kStaticLds = 256u;            // margin for static LDS (the kernel declares none)
 constexpr uint32_t kStageSlack = 72;            // words after each wavefront's staging area (reads of a well-formed stream stay within 64 words past its chunk)
 
 // A block task is kWaves consecutive wavefront tasks of one tensor; a
@@ -59,6 +62,7 @@ struct LaunchArgs {
   uint32_t stage_words;                            // staging words per wavefront (0: none)
   uint32_t lut_cap;                                // table entries reserved in LDS
   uint32_t pair_bits;                              // index bits of the two-code table (0: none)
+  uint32_t state_word;                             // LDS word (from the dynamic base) of the table state
 };
 
 constexpr uint32_t kPairBits = 10;                 // two-code table: 1024 entries of 8 bytes

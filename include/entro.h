@@ -142,7 +142,9 @@ entro_status entro_lut_build(const entro_codebook *cb, void *host_lut, size_t ca
  * (gist.science technical summary, Methodology item 3) and LazyWeights'
  * interleaved-lane Huffman decoding (abstract).  One wavefront decodes
  * 64 / lanes chunks in lockstep.  t and d_out are host arrays of n entries;
- * d_status is a device array of n uint32 that the caller zeroes first. */
+ * d_status is a device array of n uint32 that the caller zeroes first.
+ * Each d_out[i] must be 2-byte aligned (outputs of neighbouring lanes are
+ * written together); ENTRO_E_INVAL otherwise. */
 entro_status entro_decode(const entro_tensor *t, size_t n, uint8_t *const *d_out,
                           uint32_t *d_status, hipStream_t stream);
 
@@ -150,7 +152,8 @@ entro_status entro_decode(const entro_tensor *t, size_t n, uint8_t *const *d_out
  * values, RNE(f32(scale) * f32(q - zero_point)), the scale and zero point
  * being those the LUT was built with.  Defined by: EntroLLM's tensor-level
  * unsigned/asymmetric quantization (abstract; gist.science technical summary,
- * Methodology item 1) undone after decoding. */
+ * Methodology item 1) undone after decoding.  Each d_out_bf16[i] must be
+ * 4-byte aligned; ENTRO_E_INVAL otherwise. */
 entro_status entro_decode_dequant(const entro_tensor *t, size_t n, uint16_t *const *d_out_bf16,
                                   uint32_t *d_status, hipStream_t stream);
 

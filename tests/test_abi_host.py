@@ -200,6 +200,11 @@ def test_device_entry_points_validate_before_launch(lib):
     assert lib.entro_decode(arr, 1, None, st, None) == 1
     assert lib.entro_decode(arr, 1, outs, None, None) == 1
     assert lib.entro_decode(arr, 0, outs, st, None) == 0
+    # outputs of neighbouring lanes are stored together: 2-byte aligned codes,
+    # 4-byte aligned bf16 (rejected before anything is enqueued)
+    assert lib.entro_decode(arr, 1, (ctypes.c_void_p * 1)(0x1001), st, None) == 1
+    assert lib.entro_decode_dequant(arr, 1, (ctypes.c_void_p * 1)(0x1002), st, None) == 1
+    assert lib.entro_decode_dequant(arr, 1, (ctypes.c_void_p * 1)(0x1001), st, None) == 1
     # GEMV shape checks
     g = (ent.GemvItem * 1)(ent.GemvItem(10, 10, 1, 1))
     assert lib.entro_decode_gemv(arr, 1, g, 1, st, None) == 3      # W=64 does not divide cols=10
