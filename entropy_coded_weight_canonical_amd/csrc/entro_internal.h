@@ -46,6 +46,7 @@ constexpr int kMaxTensorsPerLaunch = 32;
 constexpr int kWaves = 16;                      // wavefronts per workgroup
 constexpr int kBlockThreads = 64 * kWaves;
 constexpr uint32_t kLdsPerCu = 160u * 1024u;     // gfx950
+constexpr int kKernelSgprs = 64;                 // scalar registers per wavefront (residency)
 constexpr uint32_t kLdsPlanReserve = 4u * 1024u; // kept free when sizing the persistent grid
 constexpr uint32_t kStaticLds = 256u;            // margin for static LDS (the kernel declares none)
 constexpr uint32_t kStageSlack = 72;            // words after each wavefront's staging area (reads of a well-formed stream stay within 64 words past its chunk)
