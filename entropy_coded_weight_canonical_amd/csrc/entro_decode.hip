@@ -824,11 +824,133 @@ __device__ __forceinline__ uint32_t tab_pairs32(const uint32_t *lut, uint32_t K,
   return flags;
 }
 
+// Fused GEMV from LDS (W = 64: a wavefront decodes one chunk of whole rows;
+// 4-bit codes decoded in pairs through the two-code table).  Lane j meets
+// columns j, j+64, ... of every row, so for pair q of a row it needs
+// x[b][128q + j] and x[b][128q + 64 + j]: the workgroup stages x with those
+// two values packed in one dword per batch slot (layout in stage_x), and one
+// v_dot2_f32_bf16 multiplies them with the pair's two packed bf16 weights and
+// accumulates in fp32.  At a row end the 64 partial sums are added with DPP
+// and lane 63 writes y.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t w2, uint32_t x2, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), __builtin_bit_cast(bf16x2, x2), acc, false);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_amdgcn_update_dpp(0.f, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Sum over the 64 lanes, left in lane 63 (quad swaps, half-row and row
+// mirrors, then the row broadcasts of lanes 15 and 31).
+__device__ __forceinline__ float wave_sum63(float v) {
+  v = dpp_add<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+  v = dpp_add<0x141, 0xF>(v);   // row_half_mirror
+  v = dpp_add<0x140, 0xF>(v);   // row_mirror
+  v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1, 3
+  v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+// Activation slots staged per workgroup: one (BATCH = 1) or eight (batches
+// 2..8, unused slots zero).
+template <int BATCH>
+struct XSlots { static constexpr uint32_t n = BATCH == 1 ? 1u : 8u; };
+
+// x[b][cols] (bf16, global) -> LDS.  One slot: dword q*64 + j holds
+// x[128q + j] | x[128q + 64 + j] << 16.  Eight slots: 16-byte unit
+// (2q + h)*64 + j holds that dword for b = 4h .. 4h+3, so a lane reads its
+// four slots with one conflict-free 16-byte read.
+template <int BATCH>
+__device__ void stage_x(uint32_t *xl, const uint16_t *x, uint32_t cols, uint32_t batch) {
+  const uint32_t units = (cols >> 7) * 64u;
+  for (uint32_t s = threadIdx.x; s < units; s += kBlockThreads) {
+    const uint32_t q = s >> 6, j = s & 63u, c = q * 128u + j;
+    if (BATCH == 1) {
+      xl[s] = (uint32_t)x[c] | ((uint32_t)x[c + 64u] << 16);
+    } else {
+#pragma unroll
+      for (uint32_t h = 0; h < 2u; ++h) {
+        u32x4 v;
+#pragma unroll
+        for (uint32_t i = 0; i < 4u; ++i) {
+          const uint32_t b = 4u * h + i;
+          v[i] = b < batch ? ((uint32_t)x[(uint64_t)b * cols + c] | ((uint32_t)x[(uint64_t)b * cols + c + 64u] << 16)) : 0u;
+        }
+        reinterpret_cast<u32x4 *>(xl)[(2u * q + h) * 64u + j] = v;
+      }
+    }
+  }
+}
+
+template <int BATCH>
+__device__ __forceinline__ uint32_t gemv_rows64(const uint32_t *lut, uint32_t K, const uint32_t *sw, uint32_t nw,
+                                                const uint32_t *xl, uint32_t cols, uint32_t nrows,
+                                                float *y, uint64_t row0, uint32_t rows, uint32_t batch,
+                                                uint32_t lane) {
+  constexpr uint32_t SB = XSlots<BATCH>::n;
+  const uint32_t pairs_per_row = cols >> 7;
+  uint32_t hi = 0, lo = 0, n = 0;
+  const uint32_t *p = sw;
+  for (uint32_t r = 0; r < nrows; ++r) {
+    float acc[SB];
+#pragma unroll
+    for (uint32_t b = 0; b < SB; ++b) acc[b] = 0.f;
+    const uint32_t *xp = xl + lane * (SB == 1 ? 1u : 4u);
+    for (uint32_t q = 0; q < pairs_per_row; ++q) {
+      u32x2 e2 = pair_lookup<kModeGemv>(lut, K, hi, lo);
+      const uint64_t m = need_mask(e2.y, n);
+      if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+        const uint32_t idx =
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        const uint32_t w = p[idx];
+        hi |= w >> n;
+        lo = __builtin_amdgcn_alignbit(w, 0u, n);
+        n += 32u;
+        e2 = pair_lookup<kModeGemv>(lut, K, hi, lo);
+      }
+      p = lds_advance(p, (uint32_t)__popcll(m));
+      const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e2.y);
+      lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
+      hi = nhi;
+      n = sub_len(n, e2.y);
+      if (SB == 1) {
+        acc[0] = dot2(e2.x, xp[0], acc[0]);
+      } else {
+        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(xp);
+        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(xp + 256);
+#pragma unroll
+        for (uint32_t i = 0; i < 4u; ++i) {
+          acc[i] = dot2(e2.x, x0[i], acc[i]);
+          acc[4u + i] = dot2(e2.x, x1[i], acc[4u + i]);
+        }
+      }
+      xp += 64u * SB;
+    }
+#pragma unroll
+    for (uint32_t b = 0; b < SB; ++b) acc[b] = wave_sum63(acc[b]);
+    if (lane == 63u) {
+#pragma unroll
+      for (uint32_t b = 0; b < SB; ++b)
+        if (b < batch) y[(uint64_t)b * rows + row0 + r] = acc[b];
+    }
+  }
+  const uint32_t P = (uint32_t)(p - sw);
+  uint32_t flags = 0;
+  if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
+  if (hi | lo) flags |= kFPadding;
+  return flags;
+}
+
 // One full wavefront task through LDS; returns false if it must take the
 // generic path (malformed offsets or more words than the staging area).
-template <int MODE, int LOG2W>
+template <int MODE, int LOG2W, int BATCH>
 __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K, const u32x2 *ptab,
-                            uint64_t task, uint32_t *stage, uint32_t stage_words, uint32_t prio) {
+                            uint64_t task, uint32_t *stage, uint32_t stage_words, uint32_t prio,
+                            const uint32_t *xl, uint32_t batch) {
   constexpr uint32_t W = 1u << LOG2W;
   constexpr uint32_t G = 64u / W;
   const uint32_t lane = threadIdx.x & 63u;
@@ -865,6 +987,14 @@ __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K,
   const uint64_t og = __shfl(o, (int)grp, 64), og1 = __shfl(o_next, (int)grp, 64);
   const uint32_t cs = al + (uint32_t)((og - o_first) >> 5);
   const uint32_t nw = (uint32_t)((og1 - og) >> 5);
+  if constexpr (MODE == kModeGemv) {
+    // one chunk (LOG2W == 6) of d.chunk / cols whole rows
+    const uint32_t nrows = d.chunk / d.cols;
+    const uint32_t flags = gemv_rows64<BATCH>(lut, K, stage + al, rfl(nw), xl, d.cols, nrows,
+                                              static_cast<float *>(d.out), c0 * nrows, d.rows, batch, lane);
+    if (flags) atomicOr(d.status, flags);
+    return true;
+  } else {
   const uint32_t steps = d.chunk >> LOG2W;
   typedef typename std::conditional<MODE == kModeU8, uint8_t, uint16_t>::type OutT;
   // output of the task: G full chunks from chunk c0 on
@@ -893,6 +1023,7 @@ __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K,
   }
   if (flags) atomicOr(d.status, flags);
   return true;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -909,17 +1040,20 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
     const LaunchArgs a) {
   constexpr uint32_t G = 64u >> LOG2W;
   // dynamic LDS: the two-code table if any (first, so that its address is a
-  // constant), the code table (lut_cap entries, a multiple of 4), then one
-  // 16-byte aligned staging area per wavefront
+  // constant), the code table (lut_cap entries, a multiple of 4), the staged
+  // activations of the GEMV (x_words), then one 16-byte aligned staging area
+  // per wavefront
   // K | entries << 8 of the current table, or 0 if it is unusable (kept in
   // dynamic LDS so that the workgroup has no static LDS and dyn_lds is at 0)
   uint32_t &lut_state = reinterpret_cast<uint32_t *>(dyn_lds)[a.state_word];
   u32x2 *ptab_area = reinterpret_cast<u32x2 *>(dyn_lds);
   uint32_t *lut = reinterpret_cast<uint32_t *>(dyn_lds) + (a.pair_bits ? 2u << a.pair_bits : 0u);
+  uint32_t *xl = lut + a.lut_cap;
   const uint32_t wave = rfl(threadIdx.x >> 6);
   const uint32_t stage_words = a.stage_words;
-  uint32_t *stage = lut + a.lut_cap + wave * (stage_words + kStageSlack);
+  uint32_t *stage = xl + a.x_words + wave * (stage_words + kStageSlack);
   const u32x2 *ptab = nullptr;
+  bool x_staged = false;
   const uint32_t bt0 = blockIdx.x * a.btasks_per_block;
   const uint32_t bt1 = min(bt0 + a.btasks_per_block, a.total_btasks);
   uint32_t cur = 0xFFFFFFFFu;
@@ -950,23 +1084,30 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
       __syncthreads();
       // two-code table for 4-bit tensors decoded in pairs
       ptab = nullptr;
-      if (MODE != kModeGemv && a.pair_bits && K && d.refill_steps == 2u && ((d.expect_hdr >> 8) & 0xFFu) == 4u &&
-          lds_at_zero()) {
+      if (a.pair_bits && K && d.refill_steps == 2u && ((d.expect_hdr >> 8) & 0xFFu) == 4u && lds_at_zero()) {
         for (uint32_t i = threadIdx.x; i < (1u << kPairBits); i += kBlockThreads)
           ptab_area[i] = build_pair_entry<MODE>(lut, K, i);
         ptab = ptab_area;
-        __syncthreads();
       }
+      // activations of a GEMV tensor that the LDS path takes: W = 64, pairs,
+      // two-code table, an even number of steps per row, x fits its area
+      x_staged = false;
+      if (MODE == kModeGemv && LOG2W == 6 && ptab && stage_words && (d.cols & 127u) == 0u &&
+          (uint64_t)(d.cols >> 1) * XSlots<BATCH>::n <= a.x_words) {
+        stage_x<BATCH>(xl, d.x, d.cols, a.batch);
+        x_staged = true;
+      }
+      __syncthreads();
     }
     if (!K) continue;
     const uint64_t task = (uint64_t)(bt - a.btask_begin[ti]) * kWaves + wave;
     if (task >= d.n_tasks) continue;
     bool done = false;
-    if (MODE != kModeGemv && stage_words) {
+    if (stage_words && (MODE != kModeGemv || x_staged)) {
       const bool full = (task + 1) * G <= d.n_chunks && (task + 1) * G * (uint64_t)d.chunk <= d.n_symbols;
       // priority 3, 2 over the wavefront's first task, 1, 0 over the second
       const uint32_t k = bt - bt0, prio = k == 0u ? 3u : (k == 1u ? 1u : 0u);
-      if (full) done = task_staged<MODE, LOG2W>(d, lut, K, ptab, task, stage, stage_words, prio);
+      if (full) done = task_staged<MODE, LOG2W, BATCH>(d, lut, K, ptab, task, stage, stage_words, prio, xl, a.batch);
     }
     if (!done) task_generic<MODE, LOG2W, BATCH>(d, lut, K, task, a.batch);
   }
@@ -1064,7 +1205,7 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
     std::memset(&a, 0, sizeof a);
     a.batch = batch;
     uint32_t total = 0, log2w = 0, k = 0;
-    uint64_t stage_need = 0, lut_need = 0;
+    uint64_t stage_need = 0, lut_need = 0, x_cols_max = 0;
     bool stage_known = true, want_pairs = false;
     for (; i < n && k < (uint32_t)kMaxTensorsPerLaunch; ++i) {
       const entro_tensor &x = t[i];
@@ -1090,6 +1231,7 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
         d.x = g[i].d_x;
         d.rows = g[i].rows;
         d.cols = g[i].cols;
+        if ((d.cols & 127u) == 0u) x_cols_max = std::max<uint64_t>(x_cols_max, d.cols);
       } else {
         d.out = outs[i];
       }
@@ -1113,9 +1255,22 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
     // LDS: the largest table of the launch, then the staging areas (room for
     // the largest task plus 16-byte alignment), within 160 KiB
     a.lut_cap = (uint32_t)((lut_need + 3) & ~3ull);
-    a.pair_bits = (mode != kModeGemv && want_pairs) ? kPairBits : 0u;
+    a.pair_bits = want_pairs ? kPairBits : 0u;
     size_t dyn = (size_t)a.lut_cap * 4u + (a.pair_bits ? (size_t)8u << a.pair_bits : 0u);
-    if (mode != kModeGemv) {
+    // GEMV from LDS: W = 64 with pairs, and the launch's largest activation
+    // block within kGemvXMaxBytes; otherwise every GEMV task takes the
+    // generic path
+    bool stage = mode != kModeGemv;
+    if (mode == kModeGemv && log2w == 6 && want_pairs) {
+      const uint64_t slots = batch == 1 ? 1u : 8u;
+      const uint64_t x_words = (x_cols_max >> 1) * slots;
+      if (x_words * 4u <= kGemvXMaxBytes) {
+        a.x_words = (uint32_t)((x_words + 3u) & ~3ull);
+        dyn += (size_t)a.x_words * 4u;
+        stage = true;
+      }
+    }
+    if (stage) {
       const uint64_t cap = ((kLdsPerCu - kStaticLds) / 4u - dyn / 4u) / kWaves - kStageSlack;
       uint64_t sw = (stage_need + 3 + 3) & ~3ull;
       sw = std::max<uint64_t>(64, std::min<uint64_t>(sw, cap & ~3ull));

@@ -219,18 +219,44 @@ def test_gemv_small_shapes(batch):
         assert ogemv.rel_err(y, ref) <= 1e-4   # fp32 accumulation
 
 
+@pytest.mark.parametrize("batch", [1, 3, 8])
+def test_gemv_lds_path_shapes(batch):
+    """Tensors the LDS GEMV path takes (W = 64, 4-bit, refill every two steps,
+    128 | cols): one or several rows per chunk, a ragged last chunk (generic
+    path for that task), and a tensor with 128 not dividing cols in the same
+    launch (generic path throughout)."""
+    cases = [_gemv_case(37, 128, 4, 11, refill_steps=2),
+             _gemv_case(50, 256, 4, 12, rows_per_chunk=3, refill_steps=2),
+             _gemv_case(64, 1024, 4, 13, rows_per_chunk=2, refill_steps=2),
+             _gemv_case(9, 4096, 4, 14, refill_steps=2, scheme="unsigned"),
+             _gemv_case(33, 192, 4, 15, refill_steps=2),
+             _gemv_case(129, 384, 4, 16, rows_per_chunk=4, refill_steps=2, scheme="asymmetric")]
+    xs = [activations_bf16("mistral_stack", 20 + i, c.cols, batch) for i, c in enumerate(cases)]
+    say(f"gemv lds path batch={batch}")
+    ys, st = run_gemv(cases, xs, batch)
+    assert (st == 0).all(), st
+    for c, x, y in zip(cases, xs, ys):
+        ref = ogemv.gemv_f64(c.expected_bf16().reshape(c.rows, c.cols), x)
+        assert ogemv.rel_err(y, ref) <= 1e-4
+
+
+@pytest.mark.parametrize("refill_steps", [1, 2])
 @pytest.mark.parametrize("batch", [1, 8])
-def test_gemv_mistral_shapes_sampled_layer(batch):
+def test_gemv_mistral_shapes_sampled_layer(batch, refill_steps):
     """One layer of the 4-bit Mistral-shaped stack at full size (row-aligned
-    chunks, 64 lanes), every output checked against the float64 oracle."""
+    chunks, 64 lanes), every output checked against the float64 oracle; with
+    refill every two steps the LDS path takes every full chunk (at batch 8 the
+    14336-column down projection, whose activations exceed the LDS block,
+    takes the generic path)."""
     specs = [s for s in __import__("synth").tensor_specs("mistral_stack") if s.layer == 0]
     cases, xs = [], []
     for gi, s in enumerate(specs):
         qz = quant.quantize_mixed(weights(s), 4)
         chunk = s.cols * max(1, round(8192 / s.cols))
-        cases.append(make_case(qz.q, 4, chunk, 64, scale=qz.scale, zp=qz.zero_point, rows=s.rows, cols=s.cols))
+        cases.append(make_case(qz.q, 4, chunk, 64, scale=qz.scale, zp=qz.zero_point, rows=s.rows, cols=s.cols,
+                               refill_steps=refill_steps))
         xs.append(activations_bf16("mistral_stack", gi, s.cols, batch))
-    say(f"gemv mistral layer0 batch={batch}")
+    say(f"gemv mistral layer0 batch={batch} refill_steps={refill_steps}")
     ys, st = run_gemv(cases, xs, batch)
     assert (st == 0).all(), st
     for c, x, y in zip(cases, xs, ys):
