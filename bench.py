@@ -8,8 +8,9 @@ Default workload (one "step" = one call of entro_decode_dequant):
   well above the 256 MB last-level cache, so the timed data comes from HBM.
 
 Other workloads (``--workload``): tensor_2048 (8-bit asymmetric, 4096-code
-chunks, decode to codes and to bf16), smollm_stack (decode all 169 tensors),
-phi3_stack / mistral_stack (fused decode + GEMV per token).
+chunks, decode to codes and to bf16), smollm_stack / smollm_stack_u8 (decode
+all 169 tensors in one call), phi3_stack / mistral_stack (fused decode + GEMV
+per token).
 
 The encoder used to produce the inputs is the library's own (host C++), not
 the oracle; the oracle is only timed in the CPU-baseline leg.
@@ -323,6 +324,81 @@ def bench_gemv(args, workload, batch, clip_sigma=0.0):
     return res
 
 
+def bench_stack_decode(args, workload, mode):
+    """Decode a whole stack in one call (all tensors, batched by the library
+    into launches of up to 32 tensors): 8-bit mixed codes, C 4096, W 32."""
+    import torch
+
+    import entropy_coded_weight_canonical_amd as ent
+    from synth import tensor_specs
+
+    specs = tensor_specs(workload)
+    layers = max(s.layer for s in specs) + 1
+    n_distinct = min(args.distinct_layers, layers)
+    lanes = args.lanes or 32
+    log(f"{workload}: encoding {n_distinct} distinct layer(s) of {layers} and the unlayered tensors")
+    coded = {}
+    for s in specs:
+        key = (s.layer % n_distinct, s.name.split(".", 1)[-1]) if s.layer >= 0 else ("x", s.name)
+        if key not in coded:
+            coded[key] = code_tensor(s, 8, "mixed", 4096, lanes, args.refill_steps)
+    dts, outs, keep = [], [], []
+    n_sym = 0
+    bytes_step = 0
+    odt = torch.uint8 if mode == "u8" else torch.int16
+    for s in specs:
+        key = (s.layer % n_distinct, s.name.split(".", 1)[-1]) if s.layer >= 0 else ("x", s.name)
+        c = coded[key]
+        dts.append(ent.DeviceTensor.upload(c.lut, c.words, c.offs, c.n, c.chunk, c.lanes, c.bits, c.max_len,
+                                           refill_steps=c.refill_steps))
+        outs.append(torch.empty(c.n, dtype=odt, device="cuda"))
+        n_sym += c.n
+        bytes_step += c.in_bytes + c.n * (1 if mode == "u8" else 2)
+    status = torch.zeros(len(specs), dtype=torch.int32, device="cuda")
+    descs = [d.desc for d in dts]
+    ptrs = [o.data_ptr() for o in outs]
+    fn = ent.decode if mode == "u8" else ent.decode_dequant
+
+    def step():
+        fn(descs, ptrs, status.data_ptr())
+
+    step()
+    torch.cuda.synchronize()
+    if int(status.abs().sum().item()) != 0:
+        raise SystemExit(f"stream flags set: {status.cpu().numpy()}")
+    _keep = flush_mall(torch)
+    total_ms, per_ms, wall = time_steps(step, args.steps, args.warmup)
+    ms = total_ms / args.steps
+    call_ms = float(np.mean(per_ms))
+    launches = -(-len(specs) // 32)   # one lane count: up to 32 tensors per launch
+    bits = 8.0 * sum(c.in_bytes for c in coded.values()) / sum(c.n for c in coded.values())
+    res = {
+        "metric": METRIC,
+        "value": round(n_sym / (ms * 1e-3) / 1e9, 3),
+        "unit": "Gsym/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if mode == "bf16" else "u8",
+        "data": "synthetic",
+        "config": {"workload": f"{workload}: {len(specs)} tensors, 8-bit mixed, C=4096, W={lanes}, "
+                               f"refill every {args.refill_steps} step(s), decode all "
+                               f"{'+dequant->bf16' if mode == 'bf16' else '->u8'} in one call",
+                   "global_batch": 1, "symbols_per_step": n_sym, "distinct_layers": n_distinct,
+                   "coded_bits_per_weight": round(bits, 4), "parallelism": "single GPU"},
+        "eff_GBps": round(bytes_step / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(bytes_step / (call_ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(bytes_step / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None},
+        "kernel": {"name": "ecw_decode_kernel", "launches_per_step": launches, "avg_call_ms": round(call_ms, 5),
+                   "algorithmic_bytes_per_step": bytes_step, "src_sha": kernel_src_sha()},
+    }
+    return res
+
+
 def calibrate_copy(nbytes=256 << 20):
     """A plain device copy of known size, for scaling HBM byte counters."""
     import torch
@@ -342,8 +418,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="tensor_4096",
-                    choices=["tensor_4096", "tensor_2048", "tensor_2048_u8", "smollm_stack", "phi3_stack",
-                             "mistral_stack"])
+                    choices=["tensor_4096", "tensor_2048", "tensor_2048_u8", "smollm_stack", "smollm_stack_u8",
+                             "phi3_stack", "mistral_stack"])
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--lanes", type=int, default=0)
     ap.add_argument("--batch", type=int, default=1)
@@ -375,8 +451,10 @@ def main():
                                   args.replicas or 64, "u8" if args.workload.endswith("u8") else "bf16")
     elif args.workload in ("phi3_stack", "mistral_stack"):
         res = bench_gemv(args, args.workload, args.batch, args.clip_sigma)
+    elif args.workload in ("smollm_stack", "smollm_stack_u8"):
+        res = bench_stack_decode(args, "smollm_stack", "u8" if args.workload.endswith("u8") else "bf16")
     else:
-        raise SystemExit(f"workload {args.workload} not wired yet")
+        raise SystemExit(f"unknown workload {args.workload}")
     res["gpu"] = torch.cuda.get_device_name(0)
     if coded is not None and not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
