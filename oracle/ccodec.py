@@ -49,8 +49,8 @@ def _load():
             U64 = ctypes.c_uint64
             U32 = ctypes.c_uint32
             lib.oc_layout.argtypes = [P, U64, P, U32, U32, U32, P, P]
-            lib.oc_encode.argtypes = [P, U64, P, U32, U32, U32, U32, P, P, U64, U64]
-            lib.oc_decode.argtypes = [P, U64, P, U64, P, U32, U32, U32, U32, P, U64, U64]
+            lib.oc_encode.argtypes = [P, U64, P, U32, U32, U32, U32, U32, P, P, U64, U64]
+            lib.oc_decode.argtypes = [P, U64, P, U64, P, U32, U32, U32, U32, U32, P, U64, U64]
             for f in (lib.oc_layout, lib.oc_encode, lib.oc_decode):
                 f.restype = ctypes.c_int
             _lib = lib
@@ -72,7 +72,8 @@ def _split(nc: int, threads: int):
     return [(bounds[i], bounds[i + 1]) for i in range(threads)]
 
 
-def encode(q: np.ndarray, lengths: np.ndarray, chunk: int, lanes: int, threads: int = 1, refill_steps: int = 1):
+def encode(q: np.ndarray, lengths: np.ndarray, chunk: int, lanes: int, threads: int = 1, refill_steps: int = 1,
+           ahead: bool = False):
     """Encode -> ``(words uint32, chunk_bit_off uint64)``; same result as ``oracle.ecw.encode``."""
     lib = _load()
     q = np.ascontiguousarray(np.asarray(q, dtype=np.uint8).ravel())
@@ -86,8 +87,8 @@ def encode(q: np.ndarray, lengths: np.ndarray, chunk: int, lanes: int, threads: 
     ranges = _split(nc, threads)
 
     def run(r):
-        return lib.oc_encode(_ptr(q), n, _ptr(ln), ln.size, chunk, lanes, refill_steps, _ptr(offs), _ptr(words),
-                             r[0], r[1])
+        return lib.oc_encode(_ptr(q), n, _ptr(ln), ln.size, chunk, lanes, refill_steps, int(ahead), _ptr(offs),
+                             _ptr(words), r[0], r[1])
 
     if len(ranges) == 1:
         _check(run(ranges[0]) if nc else 0, "encode")
@@ -100,7 +101,7 @@ def encode(q: np.ndarray, lengths: np.ndarray, chunk: int, lanes: int, threads: 
 
 def decode(words: np.ndarray, chunk_bit_off: np.ndarray, lengths: np.ndarray,
            n_symbols: int, chunk: int, lanes: int, threads: int = 1,
-           chunk_range: tuple[int, int] | None = None, refill_steps: int = 1) -> np.ndarray:
+           chunk_range: tuple[int, int] | None = None, refill_steps: int = 1, ahead: bool = False) -> np.ndarray:
     """Bit-serial decode of all chunks (or ``chunk_range``) -> uint8 codes."""
     lib = _load()
     words = np.ascontiguousarray(words, dtype=np.uint32)
@@ -115,7 +116,7 @@ def decode(words: np.ndarray, chunk_bit_off: np.ndarray, lengths: np.ndarray,
 
     def run(r):
         return lib.oc_decode(_ptr(words), words.size, _ptr(offs), n_symbols, _ptr(ln), ln.size,
-                             chunk, lanes, refill_steps, _ptr(out), r[0], r[1])
+                             chunk, lanes, refill_steps, int(ahead), _ptr(out), r[0], r[1])
 
     if len(ranges) == 1:
         _check(run(ranges[0]), "decode")

@@ -17,9 +17,11 @@
  *     into 32-bit words, first bit in bit 31, last word zero-padded;
  *   - refill decisions every D = refill_steps steps (1 or 2): at a step t with
  *     t mod D == 0 a lane takes its next word when its codewords of steps
- *     t .. t+D-1 are together longer than its count of loaded, unconsumed
- *     bits; words are stored in the order they are taken, lanes of one
- *     decision point in increasing lane index;
+ *     t .. t+D-1 are together longer than its count n of loaded, unconsumed
+ *     bits; with `ahead`, a lane that still has R codes to go with
+ *     R * l_min >= 32 (l_min: shortest code length) takes its next word
+ *     exactly when n < 32 instead; words are stored in the order they are
+ *     taken, lanes of one decision point in increasing lane index;
  *   - chunk_bit_off[c] = 32 * (words before chunk c), plus a final entry.
  *
  * The decoder reads one bit at a time and compares against the canonical
@@ -71,6 +73,19 @@ static int canonical(const uint8_t *len, uint32_t nsym, uint32_t *code) {
   return max_len;
 }
 
+/* Shortest nonzero code length (1 if none). */
+static uint32_t min_len(const uint8_t *len, uint32_t nsym) {
+  uint32_t s, m = 0;
+  for (s = 0; s < nsym; s++)
+    if (len[s] && (m == 0 || len[s] < m)) m = len[s];
+  return m ? m : 1;
+}
+
+/* Steps lane j of a chunk of cc codes has. */
+static uint64_t lane_steps(uint64_t cc, uint32_t j, uint32_t lanes) {
+  return cc > j ? (cc - j + lanes - 1) / lanes : 0;
+}
+
 /* Words of one chunk = sum over lanes of ceil(bits / 32). */
 static uint64_t chunk_words(const uint8_t *q, uint64_t cc, const uint8_t *len, uint32_t lanes) {
   uint64_t total = 0, k;
@@ -103,8 +118,8 @@ int oc_layout(const uint8_t *q, uint64_t n, const uint8_t *len, uint32_t nsym,
 
 /* Encode chunks [c0, c1) into words; chunk_bit_off must come from oc_layout. */
 int oc_encode(const uint8_t *q, uint64_t n, const uint8_t *len, uint32_t nsym,
-              uint32_t chunk, uint32_t lanes, uint32_t refill_steps, const uint64_t *chunk_bit_off,
-              uint32_t *words, uint64_t c0, uint64_t c1) {
+              uint32_t chunk, uint32_t lanes, uint32_t refill_steps, uint32_t ahead,
+              const uint64_t *chunk_bit_off, uint32_t *words, uint64_t c0, uint64_t c1) {
   uint32_t code[256];
   uint64_t c, k;
   uint32_t j;
@@ -112,8 +127,10 @@ int oc_encode(const uint8_t *q, uint64_t n, const uint8_t *len, uint32_t nsym,
   uint32_t *lane_buf;
   uint64_t lane_n[64], taken[64];
   int32_t avail[64];
+  uint32_t lmin;
   if (check_params(chunk, lanes, refill_steps) || nsym > 256) return OC_E_PARAM;
   if (canonical(len, nsym, code) < 0) return OC_E_CODEBOOK;
+  lmin = min_len(len, nsym);
   /* per-lane word buffer: at most ceil(chunk/lanes) codewords of <= 32 bits */
   lane_cap = ((uint64_t)chunk / lanes) + 2;
   lane_buf = (uint32_t *)calloc((size_t)(lane_cap * lanes), sizeof(uint32_t));
@@ -148,9 +165,12 @@ int oc_encode(const uint8_t *q, uint64_t n, const uint8_t *len, uint32_t nsym,
         int32_t l = 0;
         uint32_t d;
         if (kk >= cc) continue;
+        int take;
         for (d = 0; d < refill_steps; d++)
           if (kk + (uint64_t)d * lanes < cc) l += len[q[beg + kk + (uint64_t)d * lanes]];
-        if (l > avail[j]) {
+        if (ahead && (lane_steps(cc, j, lanes) - t) * lmin >= 32) take = avail[j] < 32;
+        else take = l > avail[j];
+        if (take) {
           if (taken[j] >= lane_n[j]) { free(lane_buf); return OC_E_STREAM; }
           words[out++] = lane_buf[(uint64_t)j * lane_cap + taken[j]++];
           avail[j] += 32;
@@ -195,15 +215,16 @@ static int read_codewords(uint64_t buf, int nbits, uint32_t count_, int max_len,
 /* Decode chunks [c0, c1) bit by bit into out[c*chunk ...]. */
 int oc_decode(const uint32_t *words, uint64_t n_words, const uint64_t *chunk_bit_off,
               uint64_t n, const uint8_t *len, uint32_t nsym, uint32_t chunk, uint32_t lanes,
-              uint32_t refill_steps, uint8_t *out, uint64_t c0, uint64_t c1) {
+              uint32_t refill_steps, uint32_t ahead, uint8_t *out, uint64_t c0, uint64_t c1) {
   uint32_t count[OC_MAXLEN + 1], first[OC_MAXLEN + 1], offset[OC_MAXLEN + 1];
   uint8_t sorted_syms[256];
   uint64_t buf[64];      /* unconsumed bits of each lane, first bit at bit 63 */
   int32_t nb[64];        /* how many */
   int max_len = 0;
-  uint32_t s, l, code, acc, j;
+  uint32_t s, l, code, acc, j, lmin;
   uint64_t c;
   if (check_params(chunk, lanes, refill_steps) || nsym > 256) return OC_E_PARAM;
+  lmin = min_len(len, nsym);
   memset(count, 0, sizeof count);
   for (s = 0; s < nsym; s++) {
     if (len[s] > OC_MAXLEN) return OC_E_CODEBOOK;
@@ -239,7 +260,18 @@ int oc_decode(const uint32_t *words, uint64_t n_words, const uint64_t *chunk_bit
         if (k >= cc) continue;
         for (d = 0; d < refill_steps; d++)
           if (k + (uint64_t)d * lanes < cc) cnt++;
-        used = read_codewords(buf[j], nb[j], cnt, max_len, count, first, offset, sorted_syms, syms);
+        if (ahead && (lane_steps(cc, j, lanes) - t) * lmin >= 32) {
+          /* take a word whenever fewer than 32 bits are loaded, then read */
+          if (nb[j] < 32) {
+            if (pos >= end) return OC_E_STREAM;
+            buf[j] |= (uint64_t)words[pos++] << (32 - nb[j]);
+            nb[j] += 32;
+          }
+          used = read_codewords(buf[j], nb[j], cnt, max_len, count, first, offset, sorted_syms, syms);
+          if (used <= 0) return OC_E_STREAM;
+        } else {
+          used = read_codewords(buf[j], nb[j], cnt, max_len, count, first, offset, sorted_syms, syms);
+        }
         if (used == 0) {
           if (pos >= end || nb[j] > 32) return OC_E_STREAM;
           buf[j] |= (uint64_t)words[pos++] << (32 - nb[j]);

@@ -27,6 +27,14 @@ Layout
    they are taken, lanes of one decision point in increasing lane index.
    D = 1 decides per step; D = 2 decides per pair of steps, which halves the
    decision points a decoder has to synchronize on.
+   With ``ahead`` the decision changes while a lane still has many codes to
+   go: if R codes of the lane remain from step t on and R * l_min >= 32
+   (l_min = the shortest code length of the codebook), the lane takes its
+   next word exactly when n < 32, whatever its next codewords are; once
+   R * l_min < 32 it decides as above.  Such a word always exists (the R
+   codes hold at least 32 > n bits), so no padding words arise and the word
+   count is the same; a decoder can issue the fetch before looking at the
+   codewords.
 6. Chunks are concatenated; ``chunk_bit_off[c]`` = 32 x (words before chunk c),
    with a final entry for the end.  Words are little-endian uint32 in memory.
 """
@@ -41,6 +49,12 @@ def n_chunks(n_symbols: int, chunk: int) -> int:
     return -(-n_symbols // chunk)
 
 
+def min_length(lengths) -> int:
+    """Shortest code length of a codebook (lengths of absent values are 0)."""
+    ls = [int(x) for x in lengths if int(x) > 0]
+    return min(ls) if ls else 1
+
+
 def _check_params(chunk: int, lanes: int, refill_steps: int = 1) -> None:
     if lanes < 1 or lanes > 64 or (lanes & (lanes - 1)):
         raise ValueError("lanes must be a power of two in [1, 64]")
@@ -50,12 +64,14 @@ def _check_params(chunk: int, lanes: int, refill_steps: int = 1) -> None:
         raise ValueError("refill_steps must be 1 or 2")
 
 
-def encode(q: np.ndarray, lengths: np.ndarray, chunk: int, lanes: int, refill_steps: int = 1):
+def encode(q: np.ndarray, lengths: np.ndarray, chunk: int, lanes: int, refill_steps: int = 1,
+           ahead: bool = False):
     """Encode codes ``q`` (any shape, row-major) -> ``(words uint32, chunk_bit_off uint64)``."""
     _check_params(chunk, lanes, refill_steps)
     q = np.asarray(q, dtype=np.uint8).ravel()
     lengths = np.asarray(lengths, dtype=np.int64)
     codes = canonical_codes(lengths)
+    l_min = min_length(lengths)
     if len(q) and (lengths[q] == 0).any():
         raise ValueError("a code value present in the tensor has no codeword")
     words: list[int] = []
@@ -75,7 +91,12 @@ def encode(q: np.ndarray, lengths: np.ndarray, chunk: int, lanes: int, refill_st
                 if not ks:
                     continue
                 l = sum(int(lengths[sl[k]]) for k in ks)
-                if l > n[j]:
+                codes_left = -(-(cc - j) // lanes) - t0
+                if ahead and codes_left * l_min >= 32:
+                    take = n[j] < 32
+                else:
+                    take = l > n[j]
+                if take:
                     words.append(lane_words[j][taken[j]])
                     taken[j] += 1
                     n[j] += 32
@@ -111,20 +132,22 @@ def _canonical_tables(lengths: np.ndarray):
 
 
 def decode(words: np.ndarray, chunk_bit_off: np.ndarray, lengths: np.ndarray,
-           n_symbols: int, chunk: int, lanes: int, refill_steps: int = 1) -> np.ndarray:
+           n_symbols: int, chunk: int, lanes: int, refill_steps: int = 1, ahead: bool = False) -> np.ndarray:
     """Bit-serial canonical decoder: reads one bit at a time, never a table.
 
     At each decision point a lane first tries to read its next codewords
     (one, or two for ``refill_steps`` 2) bit by bit from the bits it holds;
     if it runs dry it takes the chunk's next word and reads them again.  This
     finds the encoder's word order by decoding, without computing it from
-    code lengths.  Raises ``StreamError`` on an undecodable prefix, on
-    running past the chunk's words, on unused words, or on nonzero padding
-    bits.
+    code lengths.  With ``ahead``, a lane with R codes left and R * l_min >= 32
+    instead takes a word whenever it holds fewer than 32 bits, then reads.
+    Raises ``StreamError`` on an undecodable prefix, on running past the
+    chunk's words, on unused words, or on nonzero padding bits.
     """
     _check_params(chunk, lanes, refill_steps)
     lengths = np.asarray(lengths, dtype=np.int64)
     max_len, count, first, offset, sorted_syms = _canonical_tables(lengths)
+    l_min = min_length(lengths)
     words = [int(w) for w in np.asarray(words, dtype=np.uint32)]
     offs = [int(o) for o in np.asarray(chunk_bit_off, dtype=np.uint64)]
     out = np.zeros(n_symbols, dtype=np.uint8)
@@ -163,7 +186,19 @@ def decode(words: np.ndarray, chunk_bit_off: np.ndarray, lengths: np.ndarray,
                 ks = [t * lanes + j for t in range(t0, t0 + refill_steps) if t * lanes + j < cc]
                 if not ks:
                     continue
-                got = read_codewords(pending[j], len(ks))
+                codes_left = -(-(cc - j) // lanes) - t0
+                if ahead and codes_left * l_min >= 32:
+                    if len(pending[j]) < 32:
+                        if pos >= end:
+                            raise StreamError(f"chunk {c}: lane {j} runs past the chunk's words")
+                        w = words[pos]
+                        pos += 1
+                        pending[j].extend((w >> (31 - i)) & 1 for i in range(32))
+                    got = read_codewords(pending[j], len(ks))
+                    if got is None:
+                        raise StreamError(f"chunk {c}: lane {j}: codewords longer than the loaded bits")
+                else:
+                    got = read_codewords(pending[j], len(ks))
                 if got is None:
                     if pos >= end:
                         raise StreamError(f"chunk {c}: lane {j} runs past the chunk's words")

@@ -1,6 +1,7 @@
 """Pins for the oracle stream codec (oracle.ecw, oracle.ccodec).
 
-* hand-derived fixture (tests/golden/ecw_tiny.txt), both directions;
+* hand-derived fixtures (tests/golden/ecw_tiny.txt, ecw_pairs_tiny.txt,
+  ecw_ahead_tiny.txt), both directions;
 * lossless round trip over a grid of lanes, chunk sizes, ragged tails and
   histogram shapes (the pages call the coding lossless);
 * word count per chunk = sum over lanes of ceil(bits / 32), computed here
@@ -47,6 +48,78 @@ def test_golden_pairs_encode_decode():
     w1 = np.array([int(x, 16) for x in g["words_steps1"][0]], dtype=np.uint32)
     with pytest.raises(ecw.StreamError):
         ecw.decode(w1, offs, lengths, len(q), chunk, lanes, 2)
+
+
+def test_golden_ahead_encode_decode():
+    g, _ = load("ecw_ahead_tiny.txt")
+    lengths = np.array([int(x) for x in g["lengths"][0]])
+    q = np.array([int(x) for x in g["q"][0]], dtype=np.uint8)
+    chunk, lanes = int(g["chunk"][0][0]), int(g["lanes"][0][0])
+    offs = np.array([int(x) for x in g["chunk_bit_off"][0]], dtype=np.uint64)
+    streams = {}
+    for key, ahead in (("words_demand", False), ("words_ahead", True)):
+        words = np.array([int(x, 16) for x in g[key][0]], dtype=np.uint32)
+        streams[ahead] = words
+        w, o = ecw.encode(q, lengths, chunk, lanes, 2, ahead=ahead)
+        assert w.tolist() == words.tolist() and o.tolist() == offs.tolist()
+        assert ecw.decode(words, offs, lengths, len(q), chunk, lanes, 2, ahead=ahead).tolist() == q.tolist()
+        w2, o2 = ccodec.encode(q, lengths, chunk, lanes, refill_steps=2, ahead=ahead)
+        assert w2.tolist() == words.tolist() and o2.tolist() == offs.tolist()
+        assert ccodec.decode(words, offs, lengths, len(q), chunk, lanes, refill_steps=2,
+                             ahead=ahead).tolist() == q.tolist()
+    # the orders differ: read under the other rule, a stream fails or decodes wrongly
+    for ahead in (False, True):
+        try:
+            back = ecw.decode(streams[ahead], offs, lengths, len(q), chunk, lanes, 2, ahead=not ahead)
+        except ecw.StreamError:
+            back = None
+        assert back is None or back.tolist() != q.tolist()
+
+
+AHEAD_GRID = [
+    (bits, kind, lanes, steps, n_chunks_, refill_steps)
+    for bits in (4, 8)
+    for kind in ("uniform", "skewed", "peaked", "two", "sparse")
+    for lanes, steps, n_chunks_ in ((1, 200, 2), (2, 81, 3), (8, 40, 2), (32, 64, 2), (64, 33, 3))
+    for refill_steps in (1, 2)
+]
+
+
+@pytest.mark.parametrize("bits,kind,lanes,steps,n_chunks_,refill_steps", AHEAD_GRID)
+def test_ahead_round_trip_python_and_c(bits, kind, lanes, steps, n_chunks_, refill_steps):
+    """Refilling ahead: lossless, Python and C byte-identical, and the same
+    word count per chunk as the demand rule (no padding words)."""
+    chunk = lanes * steps
+    n = chunk * (n_chunks_ - 1) + (7 * lanes + 3) % chunk + 1          # ragged last chunk
+    q, lengths = make_case(1000 * lanes + steps + bits, bits, kind, n)
+    w, o = ecw.encode(q, lengths, chunk, lanes, refill_steps, ahead=True)
+    assert ecw.decode(w, o, lengths, n, chunk, lanes, refill_steps, ahead=True).tolist() == q.tolist()
+    wc, oc = ccodec.encode(q, lengths, chunk, lanes, refill_steps=refill_steps, ahead=True)
+    assert wc.tolist() == w.tolist() and oc.tolist() == o.tolist()
+    assert np.array_equal(ccodec.decode(w, o, lengths, n, chunk, lanes, refill_steps=refill_steps, ahead=True), q)
+    for c in range(len(o) - 1):
+        sl = q[c * chunk:(c + 1) * chunk]
+        expect = sum(-(-int(lengths[sl[j::lanes]].sum()) // 32) for j in range(lanes))
+        assert (int(o[c + 1]) - int(o[c])) // 32 == expect
+
+
+@pytest.mark.parametrize("refill_steps", [1, 2])
+def test_ahead_equals_demand_when_no_lane_is_early(refill_steps):
+    """With fewer than 32 / l_min steps per lane no decision is an early one,
+    so refilling ahead stores exactly the demand rule's words."""
+    q, lengths = make_case(5, 4, "skewed", 5000)
+    l_min = ecw.min_length(lengths)
+    steps = max(1, 32 // l_min - 1)
+    while steps * l_min >= 32:
+        steps -= 1
+    chunk = 16 * steps
+    w1, o1 = ccodec.encode(q, lengths, chunk, 16, refill_steps=refill_steps)
+    w2, o2 = ccodec.encode(q, lengths, chunk, 16, refill_steps=refill_steps, ahead=True)
+    assert np.array_equal(w1, w2) and np.array_equal(o1, o2)
+    # and with long chunks the two rules do store the words differently
+    w3, _ = ccodec.encode(q, lengths, 16 * 200, 16, refill_steps=refill_steps)
+    w4, _ = ccodec.encode(q, lengths, 16 * 200, 16, refill_steps=refill_steps, ahead=True)
+    assert w3.size == w4.size and not np.array_equal(w3, w4)
 
 
 def test_golden_encode_decode():
