@@ -74,16 +74,17 @@ def read_traffic(name: str):
 # --------------------------------------------------------------------------
 
 class Coded:
-    def __init__(self, q, scale, zp, scheme, bits, max_len, chunk, lanes, rows, cols, refill_steps):
+    def __init__(self, q, scale, zp, scheme, bits, max_len, chunk, lanes, rows, cols, refill_steps, ahead=False):
         import entropy_coded_weight_canonical_amd as ent
 
         self.rows, self.cols = rows, cols
         self.bits, self.max_len, self.chunk, self.lanes = bits, max_len, chunk, lanes
         self.scale, self.zp, self.scheme = scale, zp, scheme
-        self.refill_steps = refill_steps
+        self.refill_steps, self.ahead = refill_steps, bool(ahead)
         self.n = int(q.size)
         self.lengths = ent.code_lengths(q, bits, max_len)
-        self.words, self.offs = ent.encode(q, self.lengths, bits, chunk, lanes, refill_steps=refill_steps)
+        self.words, self.offs = ent.encode(q, self.lengths, bits, chunk, lanes, refill_steps=refill_steps,
+                                           ahead=self.ahead)
         self.lut = ent.lut_build(self.lengths, bits, max_len, scale, zp)
         self.n_chunks = int(self.offs.size - 1)
 
@@ -96,14 +97,15 @@ class Coded:
         return 8.0 * self.in_bytes / self.n
 
 
-def code_tensor(spec, bits, scheme, chunk, lanes, refill_steps, clip_sigma=0.0):
+def code_tensor(spec, bits, scheme, chunk, lanes, refill_steps, clip_sigma=0.0, ahead=False):
     import entropy_coded_weight_canonical_amd as ent
     from synth import weights
 
     w = weights(spec)
     clip = float(clip_sigma * np.std(w, dtype=np.float64)) if clip_sigma else 0.0
     q, s, zp, chosen = ent.quantize(w, bits, scheme, clip=clip)
-    return Coded(q, s, zp, chosen, bits, 16 if bits == 8 else 12, chunk, lanes, spec.rows, spec.cols, refill_steps)
+    return Coded(q, s, zp, chosen, bits, 16 if bits == 8 else 12, chunk, lanes, spec.rows, spec.cols, refill_steps,
+                 ahead)
 
 
 # --------------------------------------------------------------------------
@@ -120,7 +122,7 @@ def cpu_baseline(coded: Coded, budget_s: float = 12.0):
     reps = 0
     while True:
         q = ccodec.decode(coded.words, coded.offs, coded.lengths, coded.n, coded.chunk, coded.lanes,
-                          threads=threads, refill_steps=coded.refill_steps)
+                          threads=threads, refill_steps=coded.refill_steps, ahead=coded.ahead)
         dequant_bf16(q, coded.scale, coded.zp)
         n_done += coded.n
         reps += 1
@@ -183,10 +185,11 @@ def bench_decode(args, workload, bits, scheme, chunk, lanes, replicas, mode):
 
     spec = tensor_specs(workload)[0]
     log(f"encoding {workload} ({spec.rows}x{spec.cols}, {bits}-bit {scheme}, C={chunk}, W={lanes})")
-    coded = code_tensor(spec, bits, scheme, chunk, lanes, args.refill_steps)
+    coded = code_tensor(spec, bits, scheme, chunk, lanes, args.refill_steps, ahead=args.refill_ahead)
     log(f"coded {coded.coded_bits_per_weight:.3f} bits/weight; uploading {replicas} replicas")
     dts = [ent.DeviceTensor.upload(coded.lut, coded.words, coded.offs, coded.n, chunk, lanes, bits,
-                                   coded.max_len, refill_steps=args.refill_steps) for _ in range(replicas)]
+                                   coded.max_len, refill_steps=args.refill_steps, ahead=coded.ahead)
+           for _ in range(replicas)]
     odt = torch.uint8 if mode == "u8" else torch.int16
     outs = [torch.empty(coded.n, dtype=odt, device="cuda") for _ in range(replicas)]
     status = torch.zeros(replicas, dtype=torch.int32, device="cuda")
@@ -224,7 +227,8 @@ def bench_decode(args, workload, bits, scheme, chunk, lanes, replicas, mode):
         "dtype": "bf16" if mode == "bf16" else "u8",
         "data": "synthetic",
         "config": {"workload": f"{workload}: {spec.rows}x{spec.cols} {scheme} {bits}-bit, C={chunk}, W={lanes}, "
-                               f"refill every {args.refill_steps} step(s), x{replicas} replicas, "
+                               f"refill every {args.refill_steps} step(s){', ahead' if coded.ahead else ''}, "
+                               f"x{replicas} replicas, "
                                f"decode{'+dequant->bf16' if mode == 'bf16' else '->u8'}",
                    "global_batch": replicas, "symbols_per_step": n_sym,
                    "coded_bits_per_weight": round(coded.coded_bits_per_weight, 4),
@@ -260,7 +264,7 @@ def bench_gemv(args, workload, batch, clip_sigma=0.0):
         for s in (x for x in specs if x.layer == L):
             chunk = s.cols * max(1, round(8192 / s.cols))
             row.append((s, code_tensor(s, 4, "unsigned" if clip_sigma else "mixed", chunk, 64, args.refill_steps,
-                                       clip_sigma)))
+                                       clip_sigma, ahead=args.refill_ahead)))
         coded_layers.append(row)
     groups = []   # per layer: list of (descs, items)
     keep = []
@@ -277,7 +281,7 @@ def bench_gemv(args, workload, batch, clip_sigma=0.0):
             descs, items = [], []
             for s, c in members:
                 dt = ent.DeviceTensor.upload(c.lut, c.words, c.offs, c.n, c.chunk, c.lanes, c.bits, c.max_len,
-                                             refill_steps=c.refill_steps)
+                                             refill_steps=c.refill_steps, ahead=c.ahead)
                 y = torch.empty((batch, s.rows), dtype=torch.float32, device="cuda")
                 keep += [dt, y]
                 descs.append(dt.desc)
@@ -341,7 +345,7 @@ def bench_stack_decode(args, workload, mode):
     for s in specs:
         key = (s.layer % n_distinct, s.name.split(".", 1)[-1]) if s.layer >= 0 else ("x", s.name)
         if key not in coded:
-            coded[key] = code_tensor(s, 8, "mixed", 4096, lanes, args.refill_steps)
+            coded[key] = code_tensor(s, 8, "mixed", 4096, lanes, args.refill_steps, ahead=args.refill_ahead)
     dts, outs, keep = [], [], []
     n_sym = 0
     bytes_step = 0
@@ -350,7 +354,7 @@ def bench_stack_decode(args, workload, mode):
         key = (s.layer % n_distinct, s.name.split(".", 1)[-1]) if s.layer >= 0 else ("x", s.name)
         c = coded[key]
         dts.append(ent.DeviceTensor.upload(c.lut, c.words, c.offs, c.n, c.chunk, c.lanes, c.bits, c.max_len,
-                                           refill_steps=c.refill_steps))
+                                           refill_steps=c.refill_steps, ahead=c.ahead))
         outs.append(torch.empty(c.n, dtype=odt, device="cuda"))
         n_sym += c.n
         bytes_step += c.in_bytes + c.n * (1 if mode == "u8" else 2)
@@ -384,7 +388,8 @@ def bench_stack_decode(args, workload, mode):
         "dtype": "bf16" if mode == "bf16" else "u8",
         "data": "synthetic",
         "config": {"workload": f"{workload}: {len(specs)} tensors, 8-bit mixed, C=4096, W={lanes}, "
-                               f"refill every {args.refill_steps} step(s), decode all "
+                               f"refill every {args.refill_steps} step(s){', ahead' if args.refill_ahead else ''}, "
+                               f"decode all "
                                f"{'+dequant->bf16' if mode == 'bf16' else '->u8'} in one call",
                    "global_batch": 1, "symbols_per_step": n_sym, "distinct_layers": n_distinct,
                    "coded_bits_per_weight": round(bits, 4), "parallelism": "single GPU"},
@@ -427,12 +432,17 @@ def main():
     ap.add_argument("--distinct-layers", type=int, default=2)
     ap.add_argument("--refill-steps", type=int, default=2, choices=[1, 2],
                     help="steps per refill decision of the encoded streams")
+    ap.add_argument("--refill-ahead", type=int, default=-1, choices=[-1, 0, 1],
+                    help="encode the streams refilling ahead (same words, fetch order for early decoding); "
+                         "-1: on for the decode workloads, off for the GEMV stacks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         raise SystemExit(2)
+    if args.refill_ahead < 0:
+        args.refill_ahead = 0 if args.workload in ("phi3_stack", "mistral_stack") else 1
     import torch
 
     if not torch.cuda.is_available():

@@ -59,7 +59,8 @@ class Tensor(ctypes.Structure):
                 ("n_symbols", ctypes.c_uint64), ("chunk_symbols", ctypes.c_uint32),
                 ("lanes", ctypes.c_uint32), ("sym_bits", ctypes.c_uint32),
                 ("max_len", ctypes.c_uint32), ("lut_bytes", ctypes.c_uint64),
-                ("max_chunk_words", ctypes.c_uint32), ("refill_steps", ctypes.c_uint32)]
+                ("max_chunk_words", ctypes.c_uint32), ("refill_steps", ctypes.c_uint32),
+                ("refill_ahead", ctypes.c_uint32)]
 
 
 class GemvItem(ctypes.Structure):
@@ -92,7 +93,7 @@ def load():
     lib.entro_quantize.argtypes = [P, U64, U32, ctypes.c_int, ctypes.c_float, P, P, P, P]
     lib.entro_code_lengths.argtypes = [P, U64, U32, U32, P]
     lib.entro_encode_layout.argtypes = [P, U64, P, U32, U32, U32, P, P]
-    lib.entro_encode.argtypes = [P, U64, P, U32, U32, U32, U32, P, P, U32]
+    lib.entro_encode.argtypes = [P, U64, P, U32, U32, U32, U32, U32, P, P, U32]
     for name in ("entro_lut_build", "entro_decode", "entro_decode_dequant", "entro_decode_gemv",
                  "entro_quantize", "entro_code_lengths", "entro_encode_layout", "entro_encode"):
         getattr(lib, name).restype = ctypes.c_int
@@ -223,14 +224,14 @@ def encode_layout(q: np.ndarray, code_len: np.ndarray, bits: int, chunk: int, la
 
 
 def encode(q: np.ndarray, code_len: np.ndarray, bits: int, chunk: int, lanes: int, threads: int = 0,
-           refill_steps: int = 1):
+           refill_steps: int = 1, ahead: bool = False):
     """-> ``(words uint32, chunk_bit_off uint64)``."""
     q = np.ascontiguousarray(q, dtype=np.uint8).ravel()
     cl = np.ascontiguousarray(code_len, dtype=np.uint8)
     offs, nw = encode_layout(q, cl, bits, chunk, lanes)
     words = np.zeros(nw, dtype=np.uint32)
-    _check(load().entro_encode(_np_ptr(q), q.size, _np_ptr(cl), bits, chunk, lanes, refill_steps, _np_ptr(offs),
-                               _np_ptr(words), threads), "entro_encode")
+    _check(load().entro_encode(_np_ptr(q), q.size, _np_ptr(cl), bits, chunk, lanes, refill_steps, int(ahead),
+                               _np_ptr(offs), _np_ptr(words), threads), "entro_encode")
     return words, offs
 
 
@@ -251,7 +252,8 @@ class DeviceTensor:
 
     @classmethod
     def upload(cls, lut: np.ndarray, words: np.ndarray, offs: np.ndarray, n_symbols: int,
-               chunk: int, lanes: int, sym_bits: int, max_len: int, device="cuda", refill_steps: int = 1):
+               chunk: int, lanes: int, sym_bits: int, max_len: int, device="cuda", refill_steps: int = 1,
+               ahead: bool = False):
         import torch
 
         d_lut = torch.from_numpy(np.ascontiguousarray(lut).view(np.int32)).to(device)
@@ -262,5 +264,5 @@ class DeviceTensor:
         max_cw = int(np.diff(o).max() // 32) if o.size > 1 else 0
         desc = Tensor(d_lut.data_ptr(), d_words.data_ptr(), d_offs.data_ptr(), int(w.size), int(n_symbols),
                       int(chunk), int(lanes), int(sym_bits), int(max_len), int(np.asarray(lut).nbytes),
-                      max_cw, int(refill_steps))
+                      max_cw, int(refill_steps), int(ahead))
         return cls(d_lut, d_words, d_offs, desc)

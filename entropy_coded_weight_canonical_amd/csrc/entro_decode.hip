@@ -66,12 +66,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 
 __device__ __forceinline__ bool lds_at_zero() { return lds_addr(dyn_lds) == 0u; }
 
-// Word pointer into LDS advanced by c words with one s_lshl2_add_u32 (which
-// also writes SCC, so SCC is declared clobbered).
-__device__ __forceinline__ const uint32_t *lds_advance(const uint32_t *p, uint32_t c) {
+// Word pointers into LDS are kept as 32-bit LDS byte addresses (scalar
+// registers): lds_word reads word idx after address a, lds_adv advances a by
+// c words with one s_lshl2_add_u32 (which also writes SCC, so SCC is
+// declared clobbered).
+__device__ __forceinline__ uint32_t lds_word(uint32_t a, uint32_t idx) {
+  return *(lds_u32 *)(uintptr_t)(a + (idx << 2));
+}
+
+__device__ __forceinline__ uint32_t lds_adv(uint32_t a, uint32_t c) {
   uint32_t r;
-  asm("s_lshl2_add_u32 %0, %1, %2" : "=s"(r) : "s"(c), "s"(lds_addr(p)) : "scc");
-  return (const uint32_t *)(lds_u32 *)(uintptr_t)r;
+  asm("s_lshl2_add_u32 %0, %1, %2" : "=s"(r) : "s"(__builtin_amdgcn_readfirstlane(c)),
+      "s"(__builtin_amdgcn_readfirstlane(a)) : "scc");
+  return r;
 }
 
 template <int MODE>
@@ -126,13 +133,18 @@ __device__ __forceinline__ uint32_t and_sv(uint32_t s, uint32_t v) {
 // The value sits in bits [31:16] ([23:16] for codes) of the table entry and
 // goes out with the d16_hi store forms, so no shift is spent on it.  (The
 // outputs are never read back by the kernel, so the compiler needs no
-// knowledge of these writes.)
+// knowledge of these writes.)  The compiler does not insert hazard wait
+// states around inline assembly, and a vector-memory instruction must not
+// read an SGPR in the 5 cycles after a VALU wrote it (as v_readlane does when
+// the resource comes back from a spill), hence the s_nop 4.
 template <typename OutT>
 __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t e) {
   if (sizeof(OutT) == 1)
-    asm volatile("buffer_store_byte_d16_hi %0, %1, %2, %3 offen" : : "v"(e), "v"(voff), "s"(r), "s"(soff));
+    asm volatile("s_nop 4\n\tbuffer_store_byte_d16_hi %0, %1, %2, %3 offen"
+                 : : "v"(e), "v"(voff), "s"(r), "s"(soff));
   else
-    asm volatile("buffer_store_short_d16_hi %0, %1, %2, %3 offen" : : "v"(e), "v"(voff), "s"(r), "s"(soff));
+    asm volatile("s_nop 4\n\tbuffer_store_short_d16_hi %0, %1, %2, %3 offen"
+                 : : "v"(e), "v"(voff), "s"(r), "s"(soff));
 }
 
 // Both outputs of a pair step with one store per lane.  ab holds the lane's
@@ -219,7 +231,8 @@ __device__ __forceinline__ void emit(void *base, uint64_t k, uint32_t e) {
 // generic path: one wavefront task, words read from global memory, all checks
 // ---------------------------------------------------------------------------
 template <int MODE, int LOG2W, int BATCH>
-__device__ void task_generic(const TensorArg &d, const uint32_t *lut, uint32_t K, uint64_t task, uint32_t batch) {
+__device__ void task_generic(const TensorArg &d, const uint32_t *lut, uint32_t K, uint64_t task, uint32_t batch,
+                             uint32_t l_min) {
   constexpr uint32_t W = 1u << LOG2W;
   constexpr uint32_t G = 64u / W;
   const uint32_t lane = threadIdx.x & 63u;
@@ -273,7 +286,10 @@ __device__ void task_generic(const TensorArg &d, const uint32_t *lut, uint32_t K
       const uint32_t eb = lookup(lut, (uint32_t)((buf << need_bits) >> 32), K);
       need_bits += entry_len(eb);
     }
-    const bool need = act && need_bits > n;
+    // refilling ahead: while the lane has codes_left * l_min >= 32, a word
+    // whenever fewer than 32 bits are loaded
+    const bool early = d.ahead && act && (uint64_t)(my_steps - t0) * l_min >= 32u;
+    const bool need = early ? n < 32u : (act && need_bits > n);
     const uint64_t m = __ballot(need);
     if (m) {
       if (need) {
@@ -484,17 +500,78 @@ __device__ __forceinline__ void consume_pair(uint32_t &hi, uint32_t &lo, uint32_
   }
 }
 
+// Early phase with code-table lookups (codes up to 16 bits): A is looked up
+// in the bits loaded before the fetch, in flight together with the word;
+// lanes whose A reaches past those bits look it up again, and B is looked
+// up in the merged buffer (at least 32 bits hold both codes).
+template <int MODE>
+__device__ __forceinline__ void early_cpair64(const uint32_t *lut, uint32_t K, uint32_t &hi, uint32_t &lo,
+                                              uint32_t &n, uint32_t &pa, uint32_t &eA, uint32_t &eB) {
+  const uint64_t m = gt_mask(32u, n);
+  uint32_t a = lookup(lut, hi, K);
+  const uint32_t n0 = n;
+  if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+    const uint32_t idx =
+        __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    const uint32_t w = lds_word(pa, idx);
+    hi |= w >> n;
+    lo = __builtin_amdgcn_alignbit(w, 0u, n);
+    n += 32u;
+  }
+  pa = lds_adv(pa, (uint32_t)__popcll(m));
+  const uint64_t bad = need_mask(a, n0);
+  if (bad) {
+    if (__builtin_amdgcn_inverse_ballot_w64(bad)) a = lookup(lut, hi, K);
+  }
+  eA = a;
+  eB = lookup(lut, __builtin_amdgcn_alignbit(hi, lo, a), K);
+}
+
+template <int MODE>
+__device__ __forceinline__ void early_cpair32(const uint32_t *lut, uint32_t K, uint32_t &hi, uint32_t &lo,
+                                              uint32_t &n, uint32_t &pa, uint32_t &D, uint32_t upper,
+                                              uint32_t &eA, uint32_t &eB) {
+  const uint64_t m = gt_mask(32u, n);
+  const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+  const uint32_t clo = (uint32_t)__popc(mlo);
+  uint32_t a = lookup(lut, hi, K);
+  const uint32_t n0 = n;
+  if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+    const uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, and_sv(D - clo, upper)));
+    const uint32_t w = lds_word(pa, idx);
+    hi |= w >> n;
+    lo = __builtin_amdgcn_alignbit(w, 0u, n);
+    n += 32u;
+  }
+  pa = lds_adv(pa, clo);
+  D += (uint32_t)__popc(mhi) - clo;
+  const uint64_t bad = need_mask(a, n0);
+  if (bad) {
+    if (__builtin_amdgcn_inverse_ballot_w64(bad)) a = lookup(lut, hi, K);
+  }
+  eA = a;
+  eB = lookup(lut, __builtin_amdgcn_alignbit(hi, lo, a), K);
+}
+
 template <int MODE, typename OutT>
 __device__ __forceinline__ uint32_t pairs64(const uint32_t *lut, uint32_t K, const uint32_t *sw, uint32_t nw,
-                                            uint32_t steps, __amdgpu_buffer_rsrc_t outr, uint32_t lane) {
+                                            uint32_t steps, __amdgpu_buffer_rsrc_t outr, uint32_t lane,
+                                            uint32_t early) {
   constexpr uint32_t B = 64u * (uint32_t)sizeof(OutT);   // bytes per step
   const uint32_t voff = lane * (uint32_t)sizeof(OutT);
   const uint32_t voffp = pair_voff(lane, lane, 64u, (uint32_t)sizeof(OutT));
   const uint32_t sel = pair_sel<MODE>(lane);
   const uint32_t send = (steps & ~1u) * B;
   uint32_t hi = 0, lo = 0, n = 0;
-  const uint32_t *p = sw;
-  for (uint32_t soff = 0; soff != send; soff += 2u * B) {
+  uint32_t pa = lds_addr(sw);
+  // pairs [0, early) in the early phase of a stream encoded refilling ahead
+  uint32_t soff = 0;
+  for (const uint32_t eoff = early * 2u * B; soff < eoff; soff += 2u * B) {
+    uint32_t eA, eB;
+    early_cpair64<MODE>(lut, K, hi, lo, n, pa, eA, eB);
+    consume_pair<MODE, true, OutT>(hi, lo, n, eA, eB, pair_len(eA, eB), outr, voffp, soff, B, sel);
+  }
+  for (; soff != send; soff += 2u * B) {
     uint32_t eA = lookup(lut, hi, K);
     uint32_t eB = lookup(lut, __builtin_amdgcn_alignbit(hi, lo, eA), K);
     uint32_t lab = pair_len(eA, eB);
@@ -502,7 +579,7 @@ __device__ __forceinline__ uint32_t pairs64(const uint32_t *lut, uint32_t K, con
     if (__builtin_amdgcn_inverse_ballot_w64(m)) {
       const uint32_t idx =
           __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      const uint32_t w = p[idx];
+      const uint32_t w = lds_word(pa, idx);
       hi |= w >> n;
       lo = __builtin_amdgcn_alignbit(w, 0u, n);
       n += 32u;
@@ -510,7 +587,7 @@ __device__ __forceinline__ uint32_t pairs64(const uint32_t *lut, uint32_t K, con
       eB = lookup(lut, __builtin_amdgcn_alignbit(hi, lo, eA), K);
       lab = pair_len(eA, eB);
     }
-    p = lds_advance(p, (uint32_t)__popcll(m));
+    pa = lds_adv(pa, (uint32_t)__popcll(m));
     consume_pair<MODE, true, OutT>(hi, lo, n, eA, eB, lab, outr, voffp, soff, B, sel);
   }
   if (steps & 1u) {   // last step alone
@@ -519,20 +596,20 @@ __device__ __forceinline__ uint32_t pairs64(const uint32_t *lut, uint32_t K, con
     if (__builtin_amdgcn_inverse_ballot_w64(m)) {
       const uint32_t idx =
           __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      const uint32_t w = p[idx];
+      const uint32_t w = lds_word(pa, idx);
       hi |= w >> n;
       lo = __builtin_amdgcn_alignbit(w, 0u, n);
       n += 32u;
       e = lookup(lut, hi, K);
     }
-    p = lds_advance(p, (uint32_t)__popcll(m));
+    pa = lds_adv(pa, (uint32_t)__popcll(m));
     const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
     lo = __builtin_amdgcn_alignbit(lo, 0u, e);
     hi = nhi;
     n = sub_len(n, e);
     store_out<OutT>(outr, voff, send, e);
   }
-  const uint32_t P = (uint32_t)(p - sw);
+  const uint32_t P = ((pa - lds_addr(sw)) >> 2);
   uint32_t flags = 0;
   if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
   if (hi | lo) flags |= kFPadding;
@@ -542,7 +619,7 @@ __device__ __forceinline__ uint32_t pairs64(const uint32_t *lut, uint32_t K, con
 template <int MODE, typename OutT>
 __device__ __forceinline__ uint32_t pairs32(const uint32_t *lut, uint32_t K, const uint32_t *sw, uint32_t dcs,
                                             uint32_t nw0, uint32_t nw1, uint32_t steps, __amdgpu_buffer_rsrc_t outr,
-                                            uint32_t lane_off, uint32_t lane) {
+                                            uint32_t lane_off, uint32_t lane, uint32_t early) {
   constexpr uint32_t B = 32u * (uint32_t)sizeof(OutT);
   const uint32_t upper = lane >= 32u ? ~0u : 0u;
   const uint32_t voff = lane_off * (uint32_t)sizeof(OutT);
@@ -550,8 +627,15 @@ __device__ __forceinline__ uint32_t pairs32(const uint32_t *lut, uint32_t K, con
   const uint32_t sel = pair_sel<MODE>(lane);
   const uint32_t send = (steps & ~1u) * B;
   uint32_t hi = 0, lo = 0, n = 0, D = dcs;
-  const uint32_t *p0 = sw;
-  for (uint32_t soff = 0; soff != send; soff += 2u * B) {
+  uint32_t pa = lds_addr(sw);
+  // pairs [0, early) in the early phase of a stream encoded refilling ahead
+  uint32_t soff = 0;
+  for (const uint32_t eoff = early * 2u * B; soff < eoff; soff += 2u * B) {
+    uint32_t eA, eB;
+    early_cpair32<MODE>(lut, K, hi, lo, n, pa, D, upper, eA, eB);
+    consume_pair<MODE, true, OutT>(hi, lo, n, eA, eB, pair_len(eA, eB), outr, voffp, soff, B, sel);
+  }
+  for (; soff != send; soff += 2u * B) {
     uint32_t eA = lookup(lut, hi, K);
     uint32_t eB = lookup(lut, __builtin_amdgcn_alignbit(hi, lo, eA), K);
     uint32_t lab = pair_len(eA, eB);
@@ -560,7 +644,7 @@ __device__ __forceinline__ uint32_t pairs32(const uint32_t *lut, uint32_t K, con
     const uint32_t clo = (uint32_t)__popc(mlo);
     if (__builtin_amdgcn_inverse_ballot_w64(m)) {
       const uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, and_sv(D - clo, upper)));
-      const uint32_t w = p0[idx];
+      const uint32_t w = lds_word(pa, idx);
       hi |= w >> n;
       lo = __builtin_amdgcn_alignbit(w, 0u, n);
       n += 32u;
@@ -568,7 +652,7 @@ __device__ __forceinline__ uint32_t pairs32(const uint32_t *lut, uint32_t K, con
       eB = lookup(lut, __builtin_amdgcn_alignbit(hi, lo, eA), K);
       lab = pair_len(eA, eB);
     }
-    p0 = lds_advance(p0, clo);
+    pa = lds_adv(pa, clo);
     D += (uint32_t)__popc(mhi) - clo;
     consume_pair<MODE, true, OutT>(hi, lo, n, eA, eB, lab, outr, voffp, soff, B, sel);
   }
@@ -579,13 +663,13 @@ __device__ __forceinline__ uint32_t pairs32(const uint32_t *lut, uint32_t K, con
     const uint32_t clo = (uint32_t)__popc(mlo);
     if (__builtin_amdgcn_inverse_ballot_w64(m)) {
       const uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, and_sv(D - clo, upper)));
-      const uint32_t w = p0[idx];
+      const uint32_t w = lds_word(pa, idx);
       hi |= w >> n;
       lo = __builtin_amdgcn_alignbit(w, 0u, n);
       n += 32u;
       e = lookup(lut, hi, K);
     }
-    p0 = lds_advance(p0, clo);
+    pa = lds_adv(pa, clo);
     D += (uint32_t)__popc(mhi) - clo;
     const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
     lo = __builtin_amdgcn_alignbit(lo, 0u, e);
@@ -593,7 +677,7 @@ __device__ __forceinline__ uint32_t pairs32(const uint32_t *lut, uint32_t K, con
     n = sub_len(n, e);
     store_out<OutT>(outr, voff, send, e);
   }
-  const uint32_t P0 = (uint32_t)(p0 - sw);
+  const uint32_t P0 = ((pa - lds_addr(sw)) >> 2);
   const uint32_t P1 = D - dcs + P0;
   const uint32_t P = upper ? P1 : P0, nw = upper ? nw1 : nw0;
   uint32_t flags = 0;
@@ -664,7 +748,7 @@ __device__ u32x2 build_pair_entry(const uint32_t *lut, uint32_t K, uint32_t i) {
   const uint32_t lA = entry_len(eA);
   u32x2 r;
   r.x = 0u;
-  r.y = kPairFallback;
+  r.y = kPairFallback | 0xFF00u;   // length byte above any loaded count
   if (lA <= kPairBits) {
     const uint32_t eB = lookup(lut, hi << lA, K);
     const uint32_t lB = entry_len(eB);
@@ -691,36 +775,105 @@ __device__ __forceinline__ u32x2 pair_lookup(const uint32_t *lut, uint32_t K, ui
   return e2;
 }
 
+// Pairs of the early phase of a stream encoded refilling ahead (see entro.h):
+// a lane takes a word exactly when it holds fewer than 32 bits, so the fetch
+// is decided before the lookup and both LDS reads are in flight together.
+// The pair is looked up in the bits loaded before the fetch; the lanes whose
+// pair reaches past them (or that hit a table miss, length byte 0xFF) look it
+// up again in the merged buffer.
+__device__ __forceinline__ uint32_t early_pairs(uint32_t ahead, uint32_t steps, uint32_t l_min) {
+  if (!ahead) return 0u;
+  const uint32_t need = (32u + l_min - 1u) / l_min;   // early while codes_left >= need
+  return steps >= need ? (steps - need) / 2u + 1u : 0u;
+}
+
+template <int MODE>
+__device__ __forceinline__ u32x2 early_pair64(const uint32_t *lut, uint32_t K, uint32_t &hi, uint32_t &lo,
+                                              uint32_t &n, uint32_t &pa) {
+  const uint64_t m = gt_mask(32u, n);
+  u32x2 e2 = *(lds_u32x2 *)(uintptr_t)((hi >> (32u - kPairBits)) << 3);
+  const uint32_t n0 = n;
+  if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+    const uint32_t idx =
+        __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    const uint32_t w = lds_word(pa, idx);
+    hi |= w >> n;
+    lo = __builtin_amdgcn_alignbit(w, 0u, n);
+    n += 32u;
+  }
+  pa = lds_adv(pa, (uint32_t)__popcll(m));
+  const uint64_t bad = need_mask(e2.y, n0);
+  if (bad) {
+    if (__builtin_amdgcn_inverse_ballot_w64(bad)) e2 = pair_lookup<MODE>(lut, K, hi, lo);
+  }
+  return e2;
+}
+
+template <int MODE>
+__device__ __forceinline__ u32x2 early_pair32(const uint32_t *lut, uint32_t K, uint32_t &hi, uint32_t &lo,
+                                              uint32_t &n, uint32_t &pa, uint32_t &D, uint32_t upper) {
+  const uint64_t m = gt_mask(32u, n);
+  const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+  const uint32_t clo = (uint32_t)__popc(mlo);
+  u32x2 e2 = *(lds_u32x2 *)(uintptr_t)((hi >> (32u - kPairBits)) << 3);
+  const uint32_t n0 = n;
+  if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+    const uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, and_sv(D - clo, upper)));
+    const uint32_t w = lds_word(pa, idx);
+    hi |= w >> n;
+    lo = __builtin_amdgcn_alignbit(w, 0u, n);
+    n += 32u;
+  }
+  pa = lds_adv(pa, clo);
+  D += (uint32_t)__popc(mhi) - clo;
+  const uint64_t bad = need_mask(e2.y, n0);
+  if (bad) {
+    if (__builtin_amdgcn_inverse_ballot_w64(bad)) e2 = pair_lookup<MODE>(lut, K, hi, lo);
+  }
+  return e2;
+}
+
 // W = 64 / W = 32 pair loops reading the two-code table.
 template <int MODE, typename OutT>
 __device__ __forceinline__ uint32_t tab_pairs64(const uint32_t *lut, uint32_t K, const uint32_t *sw, uint32_t nw, uint32_t steps,
-                                                __amdgpu_buffer_rsrc_t outr, uint32_t lane, uint32_t prio) {
+                                                __amdgpu_buffer_rsrc_t outr, uint32_t lane, uint32_t prio,
+                                                uint32_t early) {
   constexpr uint32_t B = 64u * (uint32_t)sizeof(OutT);
   const uint32_t voff = lane * (uint32_t)sizeof(OutT);
   const uint32_t voffp = pair_voff(lane, lane, 64u, (uint32_t)sizeof(OutT));
   const uint32_t sel = pair_sel<MODE>(lane);
   const uint32_t send = (steps & ~1u) * B;
   uint32_t hi = 0, lo = 0, n = 0;
-  const uint32_t *p = sw;
+  uint32_t pa = lds_addr(sw);
   // first half of the pairs at priority prio, second half one lower
   const uint32_t mid = send / (4u * B) * (2u * B);
+  // pairs [0, early) in the early phase of a stream encoded refilling ahead
+  const uint32_t eoff = early * 2u * B;
   uint32_t soff = 0;
   for (uint32_t h = 0; h < 2u; ++h) {
     set_prio(h ? (prio ? prio - 1u : 0u) : prio);
     const uint32_t stop = h ? send : mid;
+    for (const uint32_t estop = min(stop, eoff); soff < estop; soff += 2u * B) {
+      const u32x2 e2 = early_pair64<MODE>(lut, K, hi, lo, n, pa);
+      const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e2.y);
+      lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
+      hi = nhi;
+      n = sub_len(n, e2.y);
+      store_pair<MODE>(outr, voffp, soff, e2.x, sel);
+    }
     for (; soff != stop; soff += 2u * B) {
       u32x2 e2 = pair_lookup<MODE>(lut, K, hi, lo);
       const uint64_t m = need_mask(e2.y, n);
       if (__builtin_amdgcn_inverse_ballot_w64(m)) {
         const uint32_t idx =
             __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        const uint32_t w = p[idx];
+        const uint32_t w = lds_word(pa, idx);
         hi |= w >> n;
         lo = __builtin_amdgcn_alignbit(w, 0u, n);
         n += 32u;
         e2 = pair_lookup<MODE>(lut, K, hi, lo);
       }
-      p = lds_advance(p, (uint32_t)__popcll(m));
+      pa = lds_adv(pa, (uint32_t)__popcll(m));
       const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e2.y);
       lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
       hi = nhi;
@@ -734,20 +887,20 @@ __device__ __forceinline__ uint32_t tab_pairs64(const uint32_t *lut, uint32_t K,
     if (__builtin_amdgcn_inverse_ballot_w64(m)) {
       const uint32_t idx =
           __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      const uint32_t w = p[idx];
+      const uint32_t w = lds_word(pa, idx);
       hi |= w >> n;
       lo = __builtin_amdgcn_alignbit(w, 0u, n);
       n += 32u;
       e = lookup(lut, hi, K);
     }
-    p = lds_advance(p, (uint32_t)__popcll(m));
+    pa = lds_adv(pa, (uint32_t)__popcll(m));
     const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
     lo = __builtin_amdgcn_alignbit(lo, 0u, e);
     hi = nhi;
     n = sub_len(n, e);
     store_out<OutT>(outr, voff, send, e);
   }
-  const uint32_t P = (uint32_t)(p - sw);
+  const uint32_t P = ((pa - lds_addr(sw)) >> 2);
   uint32_t flags = 0;
   if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
   if (hi | lo) flags |= kFPadding;
@@ -757,7 +910,7 @@ __device__ __forceinline__ uint32_t tab_pairs64(const uint32_t *lut, uint32_t K,
 template <int MODE, typename OutT>
 __device__ __forceinline__ uint32_t tab_pairs32(const uint32_t *lut, uint32_t K, const uint32_t *sw, uint32_t dcs, uint32_t nw0, uint32_t nw1,
                                                 uint32_t steps, __amdgpu_buffer_rsrc_t outr, uint32_t lane_off,
-                                                uint32_t lane, uint32_t prio) {
+                                                uint32_t lane, uint32_t prio, uint32_t early) {
   constexpr uint32_t B = 32u * (uint32_t)sizeof(OutT);
   const uint32_t upper = lane >= 32u ? ~0u : 0u;
   const uint32_t voff = lane_off * (uint32_t)sizeof(OutT);
@@ -765,13 +918,23 @@ __device__ __forceinline__ uint32_t tab_pairs32(const uint32_t *lut, uint32_t K,
   const uint32_t sel = pair_sel<MODE>(lane);
   const uint32_t send = (steps & ~1u) * B;
   uint32_t hi = 0, lo = 0, n = 0, D = dcs;
-  const uint32_t *p0 = sw;
+  uint32_t pa = lds_addr(sw);
   // first half of the pairs at priority prio, second half one lower
   const uint32_t mid = send / (4u * B) * (2u * B);
+  // pairs [0, early) in the early phase of a stream encoded refilling ahead
+  const uint32_t eoff = early * 2u * B;
   uint32_t soff = 0;
   for (uint32_t h = 0; h < 2u; ++h) {
     set_prio(h ? (prio ? prio - 1u : 0u) : prio);
     const uint32_t stop = h ? send : mid;
+    for (const uint32_t estop = min(stop, eoff); soff < estop; soff += 2u * B) {
+      const u32x2 e2 = early_pair32<MODE>(lut, K, hi, lo, n, pa, D, upper);
+      const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e2.y);
+      lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
+      hi = nhi;
+      n = sub_len(n, e2.y);
+      store_pair<MODE>(outr, voffp, soff, e2.x, sel);
+    }
     for (; soff != stop; soff += 2u * B) {
       u32x2 e2 = pair_lookup<MODE>(lut, K, hi, lo);
       const uint64_t m = need_mask(e2.y, n);
@@ -779,13 +942,13 @@ __device__ __forceinline__ uint32_t tab_pairs32(const uint32_t *lut, uint32_t K,
       const uint32_t clo = (uint32_t)__popc(mlo);
       if (__builtin_amdgcn_inverse_ballot_w64(m)) {
         const uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, and_sv(D - clo, upper)));
-        const uint32_t w = p0[idx];
+        const uint32_t w = lds_word(pa, idx);
         hi |= w >> n;
         lo = __builtin_amdgcn_alignbit(w, 0u, n);
         n += 32u;
         e2 = pair_lookup<MODE>(lut, K, hi, lo);
       }
-      p0 = lds_advance(p0, clo);
+      pa = lds_adv(pa, clo);
       D += (uint32_t)__popc(mhi) - clo;
       const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e2.y);
       lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
@@ -801,13 +964,13 @@ __device__ __forceinline__ uint32_t tab_pairs32(const uint32_t *lut, uint32_t K,
     const uint32_t clo = (uint32_t)__popc(mlo);
     if (__builtin_amdgcn_inverse_ballot_w64(m)) {
       const uint32_t idx = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, and_sv(D - clo, upper)));
-      const uint32_t w = p0[idx];
+      const uint32_t w = lds_word(pa, idx);
       hi |= w >> n;
       lo = __builtin_amdgcn_alignbit(w, 0u, n);
       n += 32u;
       e = lookup(lut, hi, K);
     }
-    p0 = lds_advance(p0, clo);
+    pa = lds_adv(pa, clo);
     D += (uint32_t)__popc(mhi) - clo;
     const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e);
     lo = __builtin_amdgcn_alignbit(lo, 0u, e);
@@ -815,7 +978,7 @@ __device__ __forceinline__ uint32_t tab_pairs32(const uint32_t *lut, uint32_t K,
     n = sub_len(n, e);
     store_out<OutT>(outr, voff, send, e);
   }
-  const uint32_t P0 = (uint32_t)(p0 - sw);
+  const uint32_t P0 = ((pa - lds_addr(sw)) >> 2);
   const uint32_t P1 = D - dcs + P0;
   const uint32_t P = upper ? P1 : P0, nw = upper ? nw1 : nw0;
   uint32_t flags = 0;
@@ -894,7 +1057,7 @@ __device__ __forceinline__ uint32_t gemv_rows64(const uint32_t *lut, uint32_t K,
   constexpr uint32_t SB = XSlots<BATCH>::n;
   const uint32_t pairs_per_row = cols >> 7;
   uint32_t hi = 0, lo = 0, n = 0;
-  const uint32_t *p = sw;
+  uint32_t pa = lds_addr(sw);
   for (uint32_t r = 0; r < nrows; ++r) {
     float acc[SB];
 #pragma unroll
@@ -906,13 +1069,13 @@ __device__ __forceinline__ uint32_t gemv_rows64(const uint32_t *lut, uint32_t K,
       if (__builtin_amdgcn_inverse_ballot_w64(m)) {
         const uint32_t idx =
             __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        const uint32_t w = p[idx];
+        const uint32_t w = lds_word(pa, idx);
         hi |= w >> n;
         lo = __builtin_amdgcn_alignbit(w, 0u, n);
         n += 32u;
         e2 = pair_lookup<kModeGemv>(lut, K, hi, lo);
       }
-      p = lds_advance(p, (uint32_t)__popcll(m));
+      pa = lds_adv(pa, (uint32_t)__popcll(m));
       const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e2.y);
       lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
       hi = nhi;
@@ -938,7 +1101,7 @@ __device__ __forceinline__ uint32_t gemv_rows64(const uint32_t *lut, uint32_t K,
         if (b < batch) y[(uint64_t)b * rows + row0 + r] = acc[b];
     }
   }
-  const uint32_t P = (uint32_t)(p - sw);
+  const uint32_t P = ((pa - lds_addr(sw)) >> 2);
   uint32_t flags = 0;
   if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
   if (hi | lo) flags |= kFPadding;
@@ -950,7 +1113,7 @@ __device__ __forceinline__ uint32_t gemv_rows64(const uint32_t *lut, uint32_t K,
 template <int MODE, int LOG2W, int BATCH>
 __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K, const u32x2 *ptab,
                             uint64_t task, uint32_t *stage, uint32_t stage_words, uint32_t prio,
-                            const uint32_t *xl, uint32_t batch) {
+                            const uint32_t *xl, uint32_t batch, uint32_t l_min) {
   constexpr uint32_t W = 1u << LOG2W;
   constexpr uint32_t G = 64u / W;
   const uint32_t lane = threadIdx.x & 63u;
@@ -1005,16 +1168,22 @@ __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K,
   uint32_t flags;
   const bool pairs = d.refill_steps == 2u;
   if (LOG2W == 6) {
-    if (pairs && ptab) flags = tab_pairs64<MODE, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane, prio);
-    else if (pairs) flags = pairs64<MODE, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane);
+    if (pairs && ptab)
+      flags = tab_pairs64<MODE, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane, prio,
+                                      rfl(early_pairs(d.ahead, steps, l_min)));
+    else if (pairs)
+      flags = pairs64<MODE, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane,
+                                  rfl(early_pairs(d.ahead, steps, l_min)));
     else flags = loop64<MODE, OutT>(lut, K, stage + al, rfl(nw), steps, outr, lane);
   } else if (LOG2W == 5) {
     const uint32_t cs0 = rfl(__shfl(cs, 0, 64)), cs1 = rfl(__shfl(cs, 32, 64));
     const uint32_t nw0 = rfl(__shfl(nw, 0, 64)), nw1 = rfl(__shfl(nw, 32, 64));
     if (pairs && ptab)
-      flags = tab_pairs32<MODE, OutT>(lut, K, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane, prio);
+      flags = tab_pairs32<MODE, OutT>(lut, K, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane, prio,
+                                      rfl(early_pairs(d.ahead, steps, l_min)));
     else if (pairs)
-      flags = pairs32<MODE, OutT>(lut, K, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane);
+      flags = pairs32<MODE, OutT>(lut, K, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane,
+                                  rfl(early_pairs(d.ahead, steps, l_min)));
     else
       flags = loop32<MODE, OutT>(lut, K, stage + cs0, cs1 - cs0, nw0, nw1, steps, outr, lane_off, lane);
   } else {
@@ -1057,7 +1226,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
   const uint32_t bt0 = blockIdx.x * a.btasks_per_block;
   const uint32_t bt1 = min(bt0 + a.btasks_per_block, a.total_btasks);
   uint32_t cur = 0xFFFFFFFFu;
-  uint32_t K = 0;
+  uint32_t K = 0, l_min = 1;
   for (uint32_t bt = bt0; bt < bt1; ++bt) {
     uint32_t ti = 0;
     while (ti + 1 < a.n_tensors && a.btask_begin[ti + 1] <= bt) ++ti;
@@ -1069,17 +1238,20 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
         if (d.lut_words >= kLutHeaderWords) {
           const uint32_t h0 = d.lut[0], h1 = d.lut[1], ne = d.lut[2], l1 = d.lut[3];
           const uint32_t kk = h1 & 0xFFu;
-          if (h0 == kLutMagic && (h1 & 0xFFFFFF00u) == d.expect_hdr && kk >= 1 && kk <= kSingleLevelMax &&
-              l1 == (1u << kk) && ne >= l1 && ne <= a.lut_cap && ne <= d.lut_words - kLutHeaderWords)
-            k = kk | (ne << 8);
+          const uint32_t lmin = h1 >> 24;
+          if (h0 == kLutMagic && (h1 & 0x00FFFF00u) == d.expect_hdr && kk >= 1 && kk <= kSingleLevelMax &&
+              l1 == (1u << kk) && ne >= l1 && ne <= a.lut_cap && ne <= d.lut_words - kLutHeaderWords &&
+              lmin >= 1u && lmin <= kMaxCodeLen)
+            k = kk | (ne << 8) | (lmin << 24);
         }
         if (!k) atomicOr(d.status, kFLut);
         lut_state = k;
       }
       __syncthreads();
-      const uint32_t ne = lut_state >> 8;
+      const uint32_t ne = (lut_state >> 8) & 0xFFFFu;
       for (uint32_t i = threadIdx.x; i < ne; i += kBlockThreads) lut[i] = kernel_entry<MODE>(d.lut[kLutHeaderWords + i]);
-      K = lut_state & 0xFFu;
+      K = rfl(lut_state & 0xFFu);
+      l_min = rfl(lut_state >> 24);
       cur = ti;
       __syncthreads();
       // two-code table for 4-bit tensors decoded in pairs
@@ -1103,13 +1275,16 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
     const uint64_t task = (uint64_t)(bt - a.btask_begin[ti]) * kWaves + wave;
     if (task >= d.n_tasks) continue;
     bool done = false;
-    if (stage_words && (MODE != kModeGemv || x_staged)) {
+    // streams encoded refilling ahead: the pair loops for W = 32, 64
+    const bool ahead_ok = !d.ahead || (MODE != kModeGemv && d.refill_steps == 2u && LOG2W >= 5);
+    if (stage_words && (MODE != kModeGemv || x_staged) && ahead_ok) {
       const bool full = (task + 1) * G <= d.n_chunks && (task + 1) * G * (uint64_t)d.chunk <= d.n_symbols;
       // priority 3, 2 over the wavefront's first task, 1, 0 over the second
       const uint32_t k = bt - bt0, prio = k == 0u ? 3u : (k == 1u ? 1u : 0u);
-      if (full) done = task_staged<MODE, LOG2W, BATCH>(d, lut, K, ptab, task, stage, stage_words, prio, xl, a.batch);
+      if (full)
+        done = task_staged<MODE, LOG2W, BATCH>(d, lut, K, ptab, task, stage, stage_words, prio, xl, a.batch, l_min);
     }
-    if (!done) task_generic<MODE, LOG2W, BATCH>(d, lut, K, task, a.batch);
+    if (!done) task_generic<MODE, LOG2W, BATCH>(d, lut, K, task, a.batch, l_min);
   }
 }
 
@@ -1130,7 +1305,7 @@ static entro_status check_tensor(const entro_tensor &t) {
   if (t.chunk_symbols == 0 || t.chunk_symbols % t.lanes || t.chunk_symbols > kMaxChunk) return ENTRO_E_FORMAT;
   if (t.sym_bits != 4 && t.sym_bits != 8) return ENTRO_E_FORMAT;
   if (t.max_len < 1 || t.max_len > kMaxCodeLen) return ENTRO_E_FORMAT;
-  if (t.refill_steps > 2) return ENTRO_E_FORMAT;
+  if (t.refill_steps > 2 || t.refill_ahead > 1) return ENTRO_E_FORMAT;
   if (t.n_symbols == 0) return ENTRO_OK;
   if (!t.d_lut || !t.d_words || !t.d_chunk_bit_off) return ENTRO_E_INVAL;
   const uint64_t nc = (t.n_symbols + t.chunk_symbols - 1) / t.chunk_symbols;
@@ -1225,6 +1400,7 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
       d.expect_hdr = (x.sym_bits << 8) | (x.max_len << 16);
       d.lut_words = (uint32_t)std::min<uint64_t>(x.lut_bytes / 4, kLutHeaderWords + kLutMaxEntries);
       d.refill_steps = x.refill_steps == 2u ? 2u : 1u;
+      d.ahead = x.refill_ahead;
       if (d.refill_steps == 2u && x.sym_bits == 4u) want_pairs = true;
       if (mode == kModeGemv) {
         d.out = g[i].d_y;

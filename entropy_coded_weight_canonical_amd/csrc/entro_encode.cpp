@@ -258,12 +258,12 @@ extern "C" entro_status entro_encode_layout(const uint8_t *q, uint64_t n, const 
 }
 
 extern "C" entro_status entro_encode(const uint8_t *q, uint64_t n, const uint8_t *code_len, uint32_t bits,
-                                     uint32_t chunk, uint32_t lanes, uint32_t refill_steps,
+                                     uint32_t chunk, uint32_t lanes, uint32_t refill_steps, uint32_t refill_ahead,
                                      const uint64_t *chunk_bit_off, uint32_t *words, uint32_t threads) {
   entro_status st = check_layout(q, n, code_len, bits, chunk, lanes);
   if (st != ENTRO_OK) return st;
   if (refill_steps == 0) refill_steps = 1;
-  if (refill_steps > 2) return ENTRO_E_FORMAT;
+  if (refill_steps > 2 || refill_ahead > 1) return ENTRO_E_FORMAT;
   if (!chunk_bit_off || (!words && n)) return ENTRO_E_INVAL;
   const uint32_t nsym = 1u << bits;
   // canonical codewords
@@ -277,6 +277,11 @@ extern "C" entro_status entro_encode(const uint8_t *q, uint64_t n, const uint8_t
   }
   for (uint32_t s = 0; s < nsym; ++s)
     if (code_len[s]) code[s] = next[code_len[s]]++;
+  // refilling ahead: a lane is "early" while codes_left * l_min >= 32
+  uint32_t l_min = 0;
+  for (uint32_t s = 0; s < nsym; ++s)
+    if (code_len[s] && (l_min == 0 || code_len[s] < l_min)) l_min = code_len[s];
+  if (l_min == 0) l_min = 1;
 
   const uint64_t nc = (n + chunk - 1) / chunk;
   std::atomic<bool> bad{false};
@@ -318,7 +323,16 @@ extern "C" entro_status entro_encode(const uint8_t *q, uint64_t n, const uint8_t
             if (k2 < cc) need += q[beg + k2] < nsym ? code_len[q[beg + k2]] : 0;
           }
         }
-        if (need > avail[j]) {       // the decoder takes the next word here
+        bool take = false;
+        if (t % refill_steps == 0) {
+          const uint64_t codes_left = (cc - j + lanes - 1) / lanes - t;
+          take = (refill_ahead && codes_left * l_min >= 32) ? avail[j] < 32u : need > avail[j];
+        }
+        if (take) {                  // the decoder takes the next word here
+          if (has_next[j]) {         // (never: a lane holds under 64 loaded bits)
+            bad = true;
+            return;
+          }
           if (!has_cur[j]) {
             slot_cur[j] = out++;
             has_cur[j] = true;

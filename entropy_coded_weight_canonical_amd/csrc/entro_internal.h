@@ -40,6 +40,7 @@ struct TensorArg {
   uint32_t lut_words;      // readable uint32 words at lut
   uint32_t n_tasks;        // wavefront tasks: ceil(n_chunks / chunks per wavefront)
   uint32_t refill_steps;   // steps per refill decision (1 or 2)
+  uint32_t ahead;          // 1: refill ahead while codes_left * l_min >= 32
 };
 
 constexpr int kMaxTensorsPerLaunch = 32;

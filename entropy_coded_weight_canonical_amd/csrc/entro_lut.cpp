@@ -10,7 +10,7 @@
 // shorter codes first, first code zero, MSB-first; bf16 = RNE(f32 product).
 //
 // Table layout (uint32 words):
-//   [0] magic "ECW1"            [1] K | sym_bits << 8 | max_len << 16
+//   [0] magic "ECW1"            [1] K | sym_bits << 8 | max_len << 16 | shortest length << 24
 //   [2] number of entries E     [3] 2^K (first-level entries)
 //   [4 .. 4+E) entries.  Entry bits: [4:0] code length (0 = no codeword),
 //   [7] second-level pointer, [15:8] code value (pointer: index bits of the
@@ -132,7 +132,10 @@ extern "C" entro_status entro_lut_build(const entro_codebook *cb, void *host_lut
   uint32_t *out = (uint32_t *)host_lut;
   std::memset(out, 0, bytes);
   out[0] = kLutMagic;
-  out[1] = p.K | (cb->sym_bits << 8) | (cb->max_len << 16);
+  uint32_t l_min = 0;
+  for (uint32_t s = 0; s < (1u << cb->sym_bits); ++s)
+    if (cb->code_len[s] && (l_min == 0 || cb->code_len[s] < l_min)) l_min = cb->code_len[s];
+  out[1] = p.K | (cb->sym_bits << 8) | (cb->max_len << 16) | (l_min << 24);
   out[2] = p.entries;
   out[3] = 1u << p.K;
   uint32_t *e = out + kLutHeaderWords;

@@ -22,6 +22,11 @@
  *     unconsumed bits it holds (one word always suffices: codes are at most 16
  *     bits); words are stored in the order they are taken, lanes of one
  *     decision point in increasing lane order;
+ *   - with refill_ahead, a lane that still has R codes to decode from step t
+ *     on, with R * l_min >= 32 (l_min: the codebook's shortest code length),
+ *     instead takes its next word at a decision point exactly when it holds
+ *     fewer than 32 loaded bits; such a word always exists, so the word count
+ *     is unchanged, and a decoder can fetch it before looking up codewords;
  *   - chunk_bit_off[c] = 32 * (words before chunk c); chunk_bit_off[n_chunks]
  *     = 32 * n_words.  Words are little-endian uint32.
  *
@@ -105,6 +110,7 @@ typedef struct {
                                      still decoded correctly, only more slowly)          */
   uint32_t refill_steps;          /* steps per refill decision the stream was encoded
                                      with: 1 or 2 (0 is read as 1)                       */
+  uint32_t refill_ahead;          /* 1 if the stream was encoded refilling ahead, else 0 */
 } entro_tensor;
 
 /* Operands of the fused GEMV for one tensor, read as a [rows][cols] row-major
@@ -123,7 +129,8 @@ typedef struct {
  * 12, or 11 when longer codes exist) for which the codes longer than K have
  * an estimated probability (sum of 2^-length) of at most 2^-10, and for which
  * the table fits 4096 entries; a shorter first level means fewer LDS bank
- * conflicts and less LDS per workgroup.  Each
+ * conflicts and less LDS per workgroup.  The header also records the
+ * shortest code length (which the refill-ahead layout depends on).  Each
  * entry carries the code length, the code value and its bf16 dequantized
  * value.  Defined by: canonical Huffman codes (reading of EntroLLM's Huffman
  * step, see the stream layout above) and the dequantization rule of

@@ -65,11 +65,13 @@ entro_status entro_encode_layout(const uint8_t *q, uint64_t n, const uint8_t *co
 
 /* Write the ECW v1 words of q (offsets from entro_encode_layout) using up to
  * `threads` host threads (0 = hardware concurrency).  refill_steps (1 or 2;
- * 0 means 1) is the number of steps per refill decision, see entro.h; the
- * same value must be given to the decoder.  With 2, every code length must
- * be at most 16 (always true for the codebooks of entro_code_lengths). */
+ * 0 means 1) is the number of steps per refill decision and refill_ahead
+ * (0 or 1) selects refilling ahead, see entro.h; the decoder must be given
+ * the same values.  With 2 steps, every code length must be at most 16
+ * (always true for the codebooks of entro_code_lengths).  Refilling ahead
+ * stores the same words in another order (offsets are unchanged). */
 entro_status entro_encode(const uint8_t *q, uint64_t n, const uint8_t *code_len, uint32_t bits,
-                          uint32_t chunk, uint32_t lanes, uint32_t refill_steps,
+                          uint32_t chunk, uint32_t lanes, uint32_t refill_steps, uint32_t refill_ahead,
                           const uint64_t *chunk_bit_off, uint32_t *words, uint32_t threads);
 
 #ifdef __cplusplus

@@ -28,6 +28,7 @@ class Case:
     rows: int = 0
     cols: int = 0
     refill_steps: int = 1
+    ahead: bool = False
 
     @property
     def n(self) -> int:
@@ -38,7 +39,7 @@ class Case:
 
 
 def make_case(q, bits, chunk, lanes, scale=0.0123, zp=None, max_len=None, lengths=None,
-              rows=0, cols=0, refill_steps=1) -> Case:
+              rows=0, cols=0, refill_steps=1, ahead=False) -> Case:
     q = np.ascontiguousarray(np.asarray(q, dtype=np.uint8).ravel())
     max_len = max_len or (16 if bits == 8 else 12)
     if lengths is None:
@@ -47,15 +48,15 @@ def make_case(q, bits, chunk, lanes, scale=0.0123, zp=None, max_len=None, length
         lengths = np.zeros(1 << bits, dtype=np.int64)
         lengths[0] = 1
     zp = (1 << (bits - 1)) if zp is None else zp
-    words, offs = ccodec.encode(q, lengths, chunk, lanes, threads=8, refill_steps=refill_steps)
+    words, offs = ccodec.encode(q, lengths, chunk, lanes, threads=8, refill_steps=refill_steps, ahead=ahead)
     lut = ent.lut_build(lengths, bits, max_len, np.float32(scale), zp)
     return Case(q, bits, max_len, np.asarray(lengths, dtype=np.uint8), np.float32(scale), int(zp), chunk,
-                lanes, words, offs, lut, rows, cols, refill_steps)
+                lanes, words, offs, lut, rows, cols, refill_steps, bool(ahead))
 
 
 def upload(case: Case, device="cuda"):
     return ent.DeviceTensor.upload(case.lut, case.words, case.offs, case.n, case.chunk, case.lanes, case.bits,
-                                   case.max_len, device=device, refill_steps=case.refill_steps)
+                                   case.max_len, device=device, refill_steps=case.refill_steps, ahead=case.ahead)
 
 
 def run_decode(cases, mode="u8", device="cuda"):

@@ -65,7 +65,8 @@ def check_lut(lut, lengths, sym_bits, max_len, scale, zp):
     vals = dequant_bf16(np.arange(1 << sym_bits), scale, zp)
     assert lut[0] == 0x31574345
     K = int(lut[1]) & 0xFF
-    assert (int(lut[1]) >> 8) & 0xFF == sym_bits and int(lut[1]) >> 16 == max_len
+    assert (int(lut[1]) >> 8) & 0xFF == sym_bits and (int(lut[1]) >> 16) & 0xFF == max_len
+    assert int(lut[1]) >> 24 == min(int(x) for x in lengths if x)
     n_entries, l1 = int(lut[2]), int(lut[3])
     assert l1 == 1 << K and lut.size == 4 + n_entries
     e = lut[4:]
@@ -196,6 +197,7 @@ def test_device_entry_points_validate_before_launch(lib):
     assert dec(sym_bits=6) == 3
     assert dec(max_len=17) == 3
     assert dec(refill_steps=3) == 3
+    assert dec(refill_ahead=2) == 3
     assert dec(d_words=None) == 1
     assert lib.entro_decode(arr, 1, None, st, None) == 1
     assert lib.entro_decode(arr, 1, outs, None, None) == 1
@@ -273,19 +275,22 @@ def test_code_lengths_binding_cap_is_optimal():
     assert int((counts * mine).sum()) == int((counts * ref).sum())
 
 
+@pytest.mark.parametrize("ahead", [False, True])
 @pytest.mark.parametrize("refill_steps", [1, 2])
 @pytest.mark.parametrize("lanes,chunk,n", [(1, 64, 1000), (2, 10, 333), (8, 64, 4097), (32, 4096, 70000),
-                                           (64, 64, 129), (64, 8192, 100000), (16, 48, 7), (4, 12, 999)])
+                                           (64, 64, 129), (64, 8192, 100000), (16, 48, 7), (4, 12, 999),
+                                           (2, 400, 1000)])
 @pytest.mark.parametrize("bits", [4, 8])
-def test_encoder_byte_identical_to_oracle(lanes, chunk, n, bits, refill_steps):
+def test_encoder_byte_identical_to_oracle(lanes, chunk, n, bits, refill_steps, ahead):
     q = fuzz_codes(lanes + n, n, bits, "skewed")
     lengths = huffman.code_lengths(quant.histogram(q, bits), 16 if bits == 8 else 12)
-    words, offs = ent.encode(q, lengths, bits, chunk, lanes, threads=3, refill_steps=refill_steps)
-    ow, oo = ccodec.encode(q, lengths, chunk, lanes, refill_steps=refill_steps)
+    words, offs = ent.encode(q, lengths, bits, chunk, lanes, threads=3, refill_steps=refill_steps, ahead=ahead)
+    ow, oo = ccodec.encode(q, lengths, chunk, lanes, refill_steps=refill_steps, ahead=ahead)
     assert np.array_equal(offs, oo) and np.array_equal(words, ow)
-    assert np.array_equal(ccodec.decode(words, offs, lengths, n, chunk, lanes, refill_steps=refill_steps), q)
+    assert np.array_equal(ccodec.decode(words, offs, lengths, n, chunk, lanes, refill_steps=refill_steps,
+                                        ahead=ahead), q)
     if n <= 1000:
-        pw, po = ecw.encode(q, lengths, chunk, lanes, refill_steps)
+        pw, po = ecw.encode(q, lengths, chunk, lanes, refill_steps, ahead=ahead)
         assert np.array_equal(words, pw)
 
 

@@ -59,6 +59,29 @@ def test_fuzz_grid_u8_and_bf16(bits, lanes, mult, refill_steps):
 
 
 @pytest.mark.parametrize("refill_steps", [1, 2])
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("lanes", [1, 2, 8, 32, 64])
+def test_refill_ahead_streams(lanes, bits, refill_steps):
+    """Streams encoded refilling ahead: long chunks (the early phase covers most
+    steps), odd and even step counts, ragged last chunks; the 4-bit
+    two-step W = 32 / 64 cases run the LDS loops, the rest the generic path."""
+    cases = []
+    for i, kind in enumerate(CODE_KINDS):
+        steps = [40, 81, 256, 64, 129, 33][i]
+        chunk = lanes * steps
+        n = chunk * (2 + i % 2) + (29 * i + 7) % chunk
+        q = fuzz_codes(7000 + 100 * lanes + 10 * bits + i, n, bits, kind)
+        cases.append(make_case(q, bits, chunk, lanes, scale=0.002 * (i + 1), zp=(5 * i) % (1 << bits),
+                               refill_steps=refill_steps, ahead=True))
+    say(f"refill ahead bits={bits} lanes={lanes} refill_steps={refill_steps}")
+    for mode in ("u8", "bf16"):
+        outs, st = run_decode(cases, mode)
+        assert (st == 0).all(), st
+        for c, o in zip(cases, outs):
+            assert np.array_equal(o, c.q if mode == "u8" else c.expected_bf16())
+
+
+@pytest.mark.parametrize("refill_steps", [1, 2])
 def test_longest_codes_use_second_level(refill_steps):
     counts = np.zeros(256, dtype=np.int64)
     counts[:40] = (2.0 ** np.arange(40, 0, -1)).astype(np.int64) // 2 + 1
@@ -178,11 +201,11 @@ def test_tensor_2048_asymmetric_8bit_full_size():
         assert np.array_equal(o, c.expected_bf16())
 
 
-@pytest.mark.parametrize("refill_steps", [1, 2])
-def test_tensor_4096_unsigned_4bit_full_size_replicated(refill_steps):
+@pytest.mark.parametrize("refill_steps,ahead", [(1, False), (2, False), (2, True)])
+def test_tensor_4096_unsigned_4bit_full_size_replicated(refill_steps, ahead):
     qz = quant.quantize_unsigned(weights(_spec("tensor_4096")), 4)
-    c = make_case(qz.q, 4, 8192, 32, scale=qz.scale, zp=qz.zero_point, refill_steps=refill_steps)
-    say(f"tensor_4096 x16 replicas refill_steps={refill_steps}")
+    c = make_case(qz.q, 4, 8192, 32, scale=qz.scale, zp=qz.zero_point, refill_steps=refill_steps, ahead=ahead)
+    say(f"tensor_4096 x16 replicas refill_steps={refill_steps} ahead={ahead}")
     outs, st = run_decode([c] * 16, "bf16")
     assert (st == 0).all()
     exp = c.expected_bf16()
@@ -194,13 +217,13 @@ def test_tensor_4096_unsigned_4bit_full_size_replicated(refill_steps):
 # fused GEMV
 # --------------------------------------------------------------------------
 
-def _gemv_case(rows, cols, bits, seed, rows_per_chunk=1, lanes=64, scheme="mixed", refill_steps=1):
+def _gemv_case(rows, cols, bits, seed, rows_per_chunk=1, lanes=64, scheme="mixed", refill_steps=1, ahead=False):
     rng = np.random.default_rng(seed)
     w = (rng.standard_t(4, size=(rows, cols)) * 0.02).astype(np.float32)
     qz = {"mixed": quant.quantize_mixed, "asymmetric": quant.quantize_asymmetric,
           "unsigned": quant.quantize_unsigned}[scheme](w, bits)
     return make_case(qz.q, bits, cols * rows_per_chunk, lanes, scale=qz.scale, zp=qz.zero_point,
-                     rows=rows, cols=cols, refill_steps=refill_steps)
+                     rows=rows, cols=cols, refill_steps=refill_steps, ahead=ahead)
 
 
 @pytest.mark.parametrize("batch", [1, 3, 8])
@@ -217,6 +240,21 @@ def test_gemv_small_shapes(batch):
         ref = ogemv.gemv_f64(c.expected_bf16().reshape(c.rows, c.cols), x)
         assert ogemv.rel_err(y, ref) <= 1e-2
         assert ogemv.rel_err(y, ref) <= 1e-4   # fp32 accumulation
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_gemv_refill_ahead(batch):
+    cases = [_gemv_case(37, 1024, 4, 31, refill_steps=2, ahead=True),
+             _gemv_case(50, 256, 4, 32, rows_per_chunk=3, refill_steps=2, ahead=True),
+             _gemv_case(20, 512, 8, 33, refill_steps=2, ahead=True),
+             _gemv_case(9, 4096, 4, 34, refill_steps=1, ahead=True, lanes=32)]
+    xs = [activations_bf16("phi3_stack", 40 + i, c.cols, batch) for i, c in enumerate(cases)]
+    say(f"gemv refill ahead batch={batch}")
+    ys, st = run_gemv(cases, xs, batch)
+    assert (st == 0).all(), st
+    for c, x, y in zip(cases, xs, ys):
+        ref = ogemv.gemv_f64(c.expected_bf16().reshape(c.rows, c.cols), x)
+        assert ogemv.rel_err(y, ref) <= 1e-4
 
 
 @pytest.mark.parametrize("batch", [1, 3, 8])
