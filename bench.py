@@ -318,6 +318,7 @@ def bench_gemv(args, workload, batch, clip_sigma=0.0):
         "config": {"workload": f"{workload}: {len(specs)} matrices, 4-bit "
                                f"{'unsigned clip %.2f sigma' % clip_sigma if clip_sigma else 'mixed'}, "
                                f"row-aligned chunks, W=64, fused decode+dequant+GEMV batch {batch}",
+                   "refill_ahead": bool(args.refill_ahead),
                    "global_batch": batch, "symbols_per_token": n_sym, "launch_groups": len(groups),
                    "distinct_layers": n_distinct, "coded_bits_per_weight": round(float(bits), 4),
                    "parallelism": "single GPU"},
@@ -432,17 +433,14 @@ def main():
     ap.add_argument("--distinct-layers", type=int, default=2)
     ap.add_argument("--refill-steps", type=int, default=2, choices=[1, 2],
                     help="steps per refill decision of the encoded streams")
-    ap.add_argument("--refill-ahead", type=int, default=-1, choices=[-1, 0, 1],
-                    help="encode the streams refilling ahead (same words, fetch order for early decoding); "
-                         "-1: on for the decode workloads, off for the GEMV stacks")
+    ap.add_argument("--refill-ahead", type=int, default=1, choices=[0, 1],
+                    help="encode the streams refilling ahead (same words, fetch order for early decoding)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         raise SystemExit(2)
-    if args.refill_ahead < 0:
-        args.refill_ahead = 0 if args.workload in ("phi3_stack", "mistral_stack") else 1
     import torch
 
     if not torch.cuda.is_available():

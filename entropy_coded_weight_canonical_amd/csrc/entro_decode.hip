@@ -1053,29 +1053,35 @@ template <int BATCH>
 __device__ __forceinline__ uint32_t gemv_rows64(const uint32_t *lut, uint32_t K, const uint32_t *sw, uint32_t nw,
                                                 const uint32_t *xl, uint32_t cols, uint32_t nrows,
                                                 float *y, uint64_t row0, uint32_t rows, uint32_t batch,
-                                                uint32_t lane) {
+                                                uint32_t lane, uint32_t early) {
   constexpr uint32_t SB = XSlots<BATCH>::n;
   const uint32_t pairs_per_row = cols >> 7;
   uint32_t hi = 0, lo = 0, n = 0;
   uint32_t pa = lds_addr(sw);
+  uint32_t kk = 0;   // pair index in the chunk: [0, early) is the early phase of refilling ahead
   for (uint32_t r = 0; r < nrows; ++r) {
     float acc[SB];
 #pragma unroll
     for (uint32_t b = 0; b < SB; ++b) acc[b] = 0.f;
     const uint32_t *xp = xl + lane * (SB == 1 ? 1u : 4u);
-    for (uint32_t q = 0; q < pairs_per_row; ++q) {
-      u32x2 e2 = pair_lookup<kModeGemv>(lut, K, hi, lo);
-      const uint64_t m = need_mask(e2.y, n);
-      if (__builtin_amdgcn_inverse_ballot_w64(m)) {
-        const uint32_t idx =
-            __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        const uint32_t w = lds_word(pa, idx);
-        hi |= w >> n;
-        lo = __builtin_amdgcn_alignbit(w, 0u, n);
-        n += 32u;
+    for (uint32_t q = 0; q < pairs_per_row; ++q, ++kk) {
+      u32x2 e2;
+      if (kk < early) {
+        e2 = early_pair64<kModeGemv>(lut, K, hi, lo, n, pa);
+      } else {
         e2 = pair_lookup<kModeGemv>(lut, K, hi, lo);
+        const uint64_t m = need_mask(e2.y, n);
+        if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+          const uint32_t idx =
+              __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          const uint32_t w = lds_word(pa, idx);
+          hi |= w >> n;
+          lo = __builtin_amdgcn_alignbit(w, 0u, n);
+          n += 32u;
+          e2 = pair_lookup<kModeGemv>(lut, K, hi, lo);
+        }
+        pa = lds_adv(pa, (uint32_t)__popcll(m));
       }
-      pa = lds_adv(pa, (uint32_t)__popcll(m));
       const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e2.y);
       lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
       hi = nhi;
@@ -1154,7 +1160,8 @@ __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K,
     // one chunk (LOG2W == 6) of d.chunk / cols whole rows
     const uint32_t nrows = d.chunk / d.cols;
     const uint32_t flags = gemv_rows64<BATCH>(lut, K, stage + al, rfl(nw), xl, d.cols, nrows,
-                                              static_cast<float *>(d.out), c0 * nrows, d.rows, batch, lane);
+                                              static_cast<float *>(d.out), c0 * nrows, d.rows, batch, lane,
+                                              rfl(early_pairs(d.ahead, d.chunk >> 6, l_min)));
     if (flags) atomicOr(d.status, flags);
     return true;
   } else {
@@ -1276,7 +1283,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
     if (task >= d.n_tasks) continue;
     bool done = false;
     // streams encoded refilling ahead: the pair loops for W = 32, 64
-    const bool ahead_ok = !d.ahead || (MODE != kModeGemv && d.refill_steps == 2u && LOG2W >= 5);
+    const bool ahead_ok = !d.ahead || (d.refill_steps == 2u && LOG2W >= 5);
     if (stage_words && (MODE != kModeGemv || x_staged) && ahead_ok) {
       const bool full = (task + 1) * G <= d.n_chunks && (task + 1) * G * (uint64_t)d.chunk <= d.n_symbols;
       // priority 3, 2 over the wavefront's first task, 1, 0 over the second
