@@ -1027,11 +1027,16 @@ struct XSlots { static constexpr uint32_t n = BATCH == 1 ? 1u : 8u; };
 // x[128q + j] | x[128q + 64 + j] << 16.  Eight slots: 16-byte unit
 // (2q + h)*64 + j holds that dword for b = 4h .. 4h+3, so a lane reads its
 // four slots with one conflict-free 16-byte read.
+// x[b][cols] (bf16, global) -> LDS for the pairs [q0, q0 + np) of a row.
+// One slot: dword (q - q0)*64 + j holds x[128q + j] | x[128q + 64 + j] << 16.
+// Eight slots: 16-byte unit (2(q - q0) + h)*64 + j holds that dword for
+// b = 4h .. 4h+3, so a lane reads its four slots with one conflict-free
+// 16-byte read.
 template <int BATCH>
-__device__ void stage_x(uint32_t *xl, const uint16_t *x, uint32_t cols, uint32_t batch) {
-  const uint32_t units = (cols >> 7) * 64u;
+__device__ void stage_x(uint32_t *xl, const uint16_t *x, uint32_t cols, uint32_t batch, uint32_t q0, uint32_t np) {
+  const uint32_t units = np * 64u;
   for (uint32_t s = threadIdx.x; s < units; s += kBlockThreads) {
-    const uint32_t q = s >> 6, j = s & 63u, c = q * 128u + j;
+    const uint32_t q = s >> 6, j = s & 63u, c = (q0 + q) * 128u + j;
     if (BATCH == 1) {
       xl[s] = (uint32_t)x[c] | ((uint32_t)x[c + 64u] << 16);
     } else {
@@ -1049,6 +1054,81 @@ __device__ void stage_x(uint32_t *xl, const uint16_t *x, uint32_t cols, uint32_t
   }
 }
 
+// Decode state of one GEMV wavefront (W = 64, one chunk of whole rows).
+template <int BATCH>
+struct GemvLane {
+  uint32_t hi, lo, n, pa, kk;   // bit buffer, loaded bits, word address, pair index in the chunk
+  float acc[XSlots<BATCH>::n];
+};
+
+// One pair of the row: decode (early phase of refilling ahead for kk < early,
+// else on demand), then one v_dot2_f32_bf16 per batch slot with the x pair at
+// xp (staged as in stage_x).
+template <int BATCH>
+__device__ __forceinline__ void gemv_pair(GemvLane<BATCH> &g, const uint32_t *lut, uint32_t K, uint32_t early,
+                                          const uint32_t *xp) {
+  constexpr uint32_t SB = XSlots<BATCH>::n;
+  u32x2 e2;
+  if (g.kk < early) {
+    e2 = early_pair64<kModeGemv>(lut, K, g.hi, g.lo, g.n, g.pa);
+  } else {
+    e2 = pair_lookup<kModeGemv>(lut, K, g.hi, g.lo);
+    const uint64_t m = need_mask(e2.y, g.n);
+    if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+      const uint32_t idx =
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const uint32_t w = lds_word(g.pa, idx);
+      g.hi |= w >> g.n;
+      g.lo = __builtin_amdgcn_alignbit(w, 0u, g.n);
+      g.n += 32u;
+      e2 = pair_lookup<kModeGemv>(lut, K, g.hi, g.lo);
+    }
+    g.pa = lds_adv(g.pa, (uint32_t)__popcll(m));
+  }
+  ++g.kk;
+  const uint32_t nhi = __builtin_amdgcn_alignbit(g.hi, g.lo, e2.y);
+  g.lo = __builtin_amdgcn_alignbit(g.lo, 0u, e2.y);
+  g.hi = nhi;
+  g.n = sub_len(g.n, e2.y);
+  if (SB == 1) {
+    g.acc[0] = dot2(e2.x, xp[0], g.acc[0]);
+  } else {
+    const u32x4 x0 = *reinterpret_cast<const u32x4 *>(xp);
+    const u32x4 x1 = *reinterpret_cast<const u32x4 *>(xp + 256);
+#pragma unroll
+    for (uint32_t i = 0; i < 4u; ++i) {
+      g.acc[i] = dot2(e2.x, x0[i], g.acc[i]);
+      g.acc[4u + i] = dot2(e2.x, x1[i], g.acc[4u + i]);
+    }
+  }
+}
+
+// Row end: the 64 partial sums of every slot added, y written by lane 63.
+template <int BATCH>
+__device__ __forceinline__ void gemv_row_end(GemvLane<BATCH> &g, float *y, uint64_t row, uint32_t rows,
+                                             uint32_t batch, uint32_t lane) {
+  constexpr uint32_t SB = XSlots<BATCH>::n;
+#pragma unroll
+  for (uint32_t b = 0; b < SB; ++b) g.acc[b] = wave_sum63(g.acc[b]);
+  if (lane == 63u) {
+#pragma unroll
+    for (uint32_t b = 0; b < SB; ++b)
+      if (b < batch) y[(uint64_t)b * rows + row] = g.acc[b];
+  }
+#pragma unroll
+  for (uint32_t b = 0; b < SB; ++b) g.acc[b] = 0.f;
+}
+
+template <int BATCH>
+__device__ __forceinline__ uint32_t gemv_end_flags(const GemvLane<BATCH> &g, uint32_t pa0, uint32_t nw) {
+  const uint32_t P = (g.pa - pa0) >> 2;
+  uint32_t flags = 0;
+  if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
+  if (g.hi | g.lo) flags |= kFPadding;
+  return flags;
+}
+
+// A chunk of nrows whole rows with the whole of x staged in LDS.
 template <int BATCH>
 __device__ __forceinline__ uint32_t gemv_rows64(const uint32_t *lut, uint32_t K, const uint32_t *sw, uint32_t nw,
                                                 const uint32_t *xl, uint32_t cols, uint32_t nrows,
@@ -1056,77 +1136,87 @@ __device__ __forceinline__ uint32_t gemv_rows64(const uint32_t *lut, uint32_t K,
                                                 uint32_t lane, uint32_t early) {
   constexpr uint32_t SB = XSlots<BATCH>::n;
   const uint32_t pairs_per_row = cols >> 7;
-  uint32_t hi = 0, lo = 0, n = 0;
-  uint32_t pa = lds_addr(sw);
-  uint32_t kk = 0;   // pair index in the chunk: [0, early) is the early phase of refilling ahead
+  GemvLane<BATCH> g;
+  g.hi = g.lo = g.n = g.kk = 0u;
+  g.pa = lds_addr(sw);
+#pragma unroll
+  for (uint32_t b = 0; b < SB; ++b) g.acc[b] = 0.f;
   for (uint32_t r = 0; r < nrows; ++r) {
-    float acc[SB];
-#pragma unroll
-    for (uint32_t b = 0; b < SB; ++b) acc[b] = 0.f;
     const uint32_t *xp = xl + lane * (SB == 1 ? 1u : 4u);
-    for (uint32_t q = 0; q < pairs_per_row; ++q, ++kk) {
-      u32x2 e2;
-      if (kk < early) {
-        e2 = early_pair64<kModeGemv>(lut, K, hi, lo, n, pa);
-      } else {
-        e2 = pair_lookup<kModeGemv>(lut, K, hi, lo);
-        const uint64_t m = need_mask(e2.y, n);
-        if (__builtin_amdgcn_inverse_ballot_w64(m)) {
-          const uint32_t idx =
-              __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-          const uint32_t w = lds_word(pa, idx);
-          hi |= w >> n;
-          lo = __builtin_amdgcn_alignbit(w, 0u, n);
-          n += 32u;
-          e2 = pair_lookup<kModeGemv>(lut, K, hi, lo);
-        }
-        pa = lds_adv(pa, (uint32_t)__popcll(m));
-      }
-      const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e2.y);
-      lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
-      hi = nhi;
-      n = sub_len(n, e2.y);
-      if (SB == 1) {
-        acc[0] = dot2(e2.x, xp[0], acc[0]);
-      } else {
-        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(xp);
-        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(xp + 256);
-#pragma unroll
-        for (uint32_t i = 0; i < 4u; ++i) {
-          acc[i] = dot2(e2.x, x0[i], acc[i]);
-          acc[4u + i] = dot2(e2.x, x1[i], acc[4u + i]);
-        }
-      }
-      xp += 64u * SB;
-    }
-#pragma unroll
-    for (uint32_t b = 0; b < SB; ++b) acc[b] = wave_sum63(acc[b]);
-    if (lane == 63u) {
-#pragma unroll
-      for (uint32_t b = 0; b < SB; ++b)
-        if (b < batch) y[(uint64_t)b * rows + row0 + r] = acc[b];
-    }
+    for (uint32_t q = 0; q < pairs_per_row; ++q, xp += 64u * SB) gemv_pair<BATCH>(g, lut, K, early, xp);
+    gemv_row_end<BATCH>(g, y, row0 + r, rows, batch, lane);
   }
-  const uint32_t P = ((pa - lds_addr(sw)) >> 2);
-  uint32_t flags = 0;
-  if (P != nw) flags |= P < nw ? kFUnderrun : kFOverrun;
-  if (hi | lo) flags |= kFPadding;
-  return flags;
+  return gemv_end_flags<BATCH>(g, lds_addr(sw), nw);
 }
 
-// One full wavefront task through LDS; returns false if it must take the
-// generic path (malformed offsets or more words than the staging area).
-template <int MODE, int LOG2W, int BATCH>
-__device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K, const u32x2 *ptab,
-                            uint64_t task, uint32_t *stage, uint32_t stage_words, uint32_t prio,
-                            const uint32_t *xl, uint32_t batch, uint32_t l_min) {
+// Eight batch slots whose x does not fit in LDS: the workgroup's wavefronts
+// walk their rows in lockstep over slices of kGemvSlicePairs pairs (128
+// columns each); between workgroup barriers all threads stage the next
+// slice of x into one of two buffers while the other is read.  Called by
+// every wavefront of the workgroup for one block task; those without a
+// staged full chunk (have == false) only take part in the barriers and
+// loads.
+template <int BATCH>
+__device__ uint32_t gemv_sliced64(const TensorArg &d, const uint32_t *lut, uint32_t K, bool have,
+                                  const uint32_t *sw, uint32_t nw, uint32_t *xb, uint64_t row0, uint32_t batch,
+                                  uint32_t lane, uint32_t early) {
+  constexpr uint32_t SB = XSlots<BATCH>::n;
+  constexpr uint32_t S = kGemvSlicePairs;
+  constexpr uint32_t BUF = S * 64u * SB;   // words per slice buffer
+  const uint32_t cols = d.cols, nrows = d.chunk / d.cols;
+  const uint32_t ppr = cols >> 7;
+  const uint32_t nsl = (ppr + S - 1u) / S;
+  const uint32_t total = nrows * nsl;
+  const uint16_t *x = d.x;
+  float *y = static_cast<float *>(d.out);
+  GemvLane<BATCH> g;
+  g.hi = g.lo = g.n = g.kk = 0u;
+  g.pa = lds_addr(sw);
+#pragma unroll
+  for (uint32_t b = 0; b < SB; ++b) g.acc[b] = 0.f;
+  stage_x<BATCH>(xb, x, cols, batch, 0u, min(S, ppr));
+  if (total > 1u) {
+    const uint32_t s1 = 1u % nsl;
+    stage_x<BATCH>(xb + BUF, x, cols, batch, s1 * S, min(S, ppr - s1 * S));
+  }
+  __syncthreads();
+  for (uint32_t gi = 0; gi < total; ++gi) {
+    const uint32_t r = gi / nsl, sl = gi - r * nsl;
+    const uint32_t q0 = sl * S, q1 = min(q0 + S, ppr);
+    const uint32_t *buf = xb + (gi & 1u) * BUF;
+    if (have) {
+      const uint32_t *xp = buf + lane * (SB == 1 ? 1u : 4u);
+      for (uint32_t q = q0; q < q1; ++q, xp += 64u * SB) gemv_pair<BATCH>(g, lut, K, early, xp);
+      if (q1 == ppr) gemv_row_end<BATCH>(g, y, row0 + r, d.rows, batch, lane);
+    }
+    __syncthreads();
+    if (gi + 2u < total) {
+      const uint32_t s2 = (gi + 2u) % nsl;
+      stage_x<BATCH>(xb + (gi & 1u) * BUF, x, cols, batch, s2 * S, min(S, ppr - s2 * S));
+    }
+  }
+  return have ? gemv_end_flags<BATCH>(g, lds_addr(sw), nw) : 0u;
+}
+
+// Where a staged task's words sit in its LDS area: chunk of lane group g
+// starts at word cs (al = 16-byte alignment shift of the first chunk) and
+// has nw words.
+struct Staged {
+  uint32_t al, cs, nw;
+};
+
+// Copy the words of wavefront task `task` (64 / W consecutive chunks) into
+// the wavefront's LDS area; false (nothing usable staged) if the offsets are
+// malformed or the words do not fit.
+template <int LOG2W>
+__device__ bool stage_task(const TensorArg &d, uint64_t task, uint32_t *stage, uint32_t stage_words, Staged &st) {
   constexpr uint32_t W = 1u << LOG2W;
   constexpr uint32_t G = 64u / W;
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t grp = lane >> LOG2W;
-  const uint32_t j = lane & (W - 1u);
   const uint64_t c0 = task * G;
   const uint64_t n_words = d.n_words;
+  (void)W;
 
   // offsets of the task's G + 1 chunk boundaries: lane l < G holds the start
   // of chunk c0 + l, the end of the task is loaded once for all lanes
@@ -1156,6 +1246,27 @@ __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K,
   const uint64_t og = __shfl(o, (int)grp, 64), og1 = __shfl(o_next, (int)grp, 64);
   const uint32_t cs = al + (uint32_t)((og - o_first) >> 5);
   const uint32_t nw = (uint32_t)((og1 - og) >> 5);
+  st.al = al;
+  st.cs = cs;
+  st.nw = nw;
+  return true;
+}
+
+template <int MODE, int LOG2W, int BATCH>
+__device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K, const u32x2 *ptab,
+                            uint64_t task, uint32_t *stage, uint32_t stage_words, uint32_t prio,
+                            const uint32_t *xl, uint32_t batch, uint32_t l_min) {
+  constexpr uint32_t W = 1u << LOG2W;
+  constexpr uint32_t G = 64u / W;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t grp = lane >> LOG2W;
+  const uint32_t j = lane & (W - 1u);
+  const uint64_t c0 = task * G;
+  const uint64_t n_words = d.n_words;
+
+  Staged st;
+  if (!stage_task<LOG2W>(d, task, stage, stage_words, st)) return false;
+  const uint32_t al = st.al, cs = st.cs, nw = st.nw;
   if constexpr (MODE == kModeGemv) {
     // one chunk (LOG2W == 6) of d.chunk / cols whole rows
     const uint32_t nrows = d.chunk / d.cols;
@@ -1229,7 +1340,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
   const uint32_t stage_words = a.stage_words;
   uint32_t *stage = xl + a.x_words + wave * (stage_words + kStageSlack);
   const u32x2 *ptab = nullptr;
-  bool x_staged = false;
+  bool x_staged = false, x_sliced = false;
   const uint32_t bt0 = blockIdx.x * a.btasks_per_block;
   const uint32_t bt1 = min(bt0 + a.btasks_per_block, a.total_btasks);
   uint32_t cur = 0xFFFFFFFFu;
@@ -1268,18 +1379,35 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
           ptab_area[i] = build_pair_entry<MODE>(lut, K, i);
         ptab = ptab_area;
       }
-      // activations of a GEMV tensor that the LDS path takes: W = 64, pairs,
-      // two-code table, an even number of steps per row, x fits its area
-      x_staged = false;
-      if (MODE == kModeGemv && LOG2W == 6 && ptab && stage_words && (d.cols & 127u) == 0u &&
-          (uint64_t)(d.cols >> 1) * XSlots<BATCH>::n <= a.x_words) {
-        stage_x<BATCH>(xl, d.x, d.cols, a.batch);
-        x_staged = true;
+      // activations of a GEMV tensor that the LDS path takes (W = 64, pairs,
+      // two-code table, an even number of steps per row): all of x if it
+      // fits its area, else slices of it (eight batch slots)
+      x_staged = x_sliced = false;
+      if (MODE == kModeGemv && LOG2W == 6 && ptab && stage_words && (d.cols & 127u) == 0u) {
+        if ((uint64_t)(d.cols >> 1) * XSlots<BATCH>::n <= a.x_words) {
+          stage_x<BATCH>(xl, d.x, d.cols, a.batch, 0u, d.cols >> 7);
+          x_staged = true;
+        } else if (BATCH != 1 && a.x_slice) {
+          x_sliced = true;
+        }
       }
       __syncthreads();
     }
     if (!K) continue;
     const uint64_t task = (uint64_t)(bt - a.btask_begin[ti]) * kWaves + wave;
+    if (MODE == kModeGemv && x_sliced) {
+      // every wavefront of the workgroup takes part in the sliced walk
+      const bool mine = task < d.n_tasks;
+      const bool full = mine && (task + 1) * G <= d.n_chunks && (task + 1) * G * (uint64_t)d.chunk <= d.n_symbols;
+      Staged st{0u, 0u, 0u};
+      const bool have = full && stage_task<LOG2W>(d, task, stage, stage_words, st);
+      const uint32_t flags =
+          gemv_sliced64<BATCH>(d, lut, K, have, stage + st.al, rfl(st.nw), xl, task * (d.chunk / d.cols), a.batch,
+                               threadIdx.x & 63u, rfl(early_pairs(d.ahead, d.chunk >> 6, l_min)));
+      if (flags) atomicOr(d.status, flags);
+      if (mine && !have) task_generic<MODE, LOG2W, BATCH>(d, lut, K, task, a.batch, l_min);
+      continue;
+    }
     if (task >= d.n_tasks) continue;
     bool done = false;
     // streams encoded refilling ahead: the pair loops for W = 32, 64
@@ -1387,7 +1515,8 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
     std::memset(&a, 0, sizeof a);
     a.batch = batch;
     uint32_t total = 0, log2w = 0, k = 0;
-    uint64_t stage_need = 0, lut_need = 0, x_cols_max = 0;
+    uint64_t stage_need = 0, lut_need = 0, x_fit_words = 0;
+    bool x_slices = false;
     bool stage_known = true, want_pairs = false;
     for (; i < n && k < (uint32_t)kMaxTensorsPerLaunch; ++i) {
       const entro_tensor &x = t[i];
@@ -1414,7 +1543,11 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
         d.x = g[i].d_x;
         d.rows = g[i].rows;
         d.cols = g[i].cols;
-        if ((d.cols & 127u) == 0u) x_cols_max = std::max<uint64_t>(x_cols_max, d.cols);
+        if ((d.cols & 127u) == 0u) {
+          const uint64_t xw = (uint64_t)(d.cols >> 1) * (batch == 1 ? 1u : 8u);
+          if (xw * 4u <= kGemvXMaxBytes) x_fit_words = std::max<uint64_t>(x_fit_words, xw);
+          else if (batch != 1) x_slices = true;
+        }
       } else {
         d.out = outs[i];
       }
@@ -1445,10 +1578,13 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
     // generic path
     bool stage = mode != kModeGemv;
     if (mode == kModeGemv && log2w == 6 && want_pairs) {
-      const uint64_t slots = batch == 1 ? 1u : 8u;
-      const uint64_t x_words = (x_cols_max >> 1) * slots;
-      if (x_words * 4u <= kGemvXMaxBytes) {
+      // x of every tensor that fits kGemvXMaxBytes, or two slice buffers
+      // for those that do not (eight batch slots)
+      const uint64_t slice_words = x_slices ? 2u * kGemvSlicePairs * 64u * 8u : 0u;
+      const uint64_t x_words = std::max<uint64_t>(x_fit_words, slice_words);
+      if (x_words) {
         a.x_words = (uint32_t)((x_words + 3u) & ~3ull);
+        a.x_slice = x_slices ? 1u : 0u;
         dyn += (size_t)a.x_words * 4u;
         stage = true;
       }

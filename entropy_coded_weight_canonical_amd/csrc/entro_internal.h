@@ -48,6 +48,7 @@ constexpr int kWaves = 16;                      // wavefronts per workgroup
 constexpr int kBlockThreads = 64 * kWaves;
 constexpr uint32_t kLdsPerCu = 160u * 1024u;     // gfx950
 constexpr uint32_t kGemvXMaxBytes = 64u * 1024u; // largest activation block staged in LDS
+constexpr uint32_t kGemvSlicePairs = 8;          // pairs of steps (1024 columns) per activation slice
 constexpr int kKernelSgprs = 64;                 // scalar registers per wavefront (residency)
 constexpr uint32_t kLdsPlanReserve = 4u * 1024u; // kept free when sizing the persistent grid
 constexpr uint32_t kStaticLds = 256u;            // margin for static LDS (the kernel declares none)
@@ -67,6 +68,7 @@ struct LaunchArgs {
   uint32_t pair_bits;                              // index bits of the two-code table (0: none)
   uint32_t state_word;                             // LDS word (from the dynamic base) of the table state
   uint32_t x_words;                                // LDS words of staged GEMV activations (0: none)
+  uint32_t x_slice;                                // 1: activations too large for x_words go in slices
 };
 
 constexpr uint32_t kPairBits = 10;                 // two-code table: 1024 entries of 8 bytes

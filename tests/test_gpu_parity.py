@@ -257,6 +257,26 @@ def test_gemv_refill_ahead(batch):
         assert ogemv.rel_err(y, ref) <= 1e-4
 
 
+@pytest.mark.parametrize("ahead", [False, True])
+@pytest.mark.parametrize("batch", [2, 8])
+def test_gemv_sliced_activations(batch, ahead):
+    """Batches of 2..8 whose activations exceed the LDS block (cols * 16 bytes
+    > 64 KiB) are walked in column slices by the whole workgroup: one and two
+    rows per chunk, a last slice of one pair (4224 = 33 * 128 columns), ragged
+    last chunks, and a tensor whose x fits in the same launch."""
+    cases = [_gemv_case(70, 5120, 4, 51, refill_steps=2, ahead=ahead),
+             _gemv_case(33, 6144, 4, 52, rows_per_chunk=2, refill_steps=2, ahead=ahead, scheme="unsigned"),
+             _gemv_case(41, 4224, 4, 53, refill_steps=2, ahead=ahead),
+             _gemv_case(50, 1024, 4, 54, rows_per_chunk=3, refill_steps=2, ahead=ahead)]
+    xs = [activations_bf16("mistral_stack", 60 + i, c.cols, batch) for i, c in enumerate(cases)]
+    say(f"gemv sliced x batch={batch} ahead={ahead}")
+    ys, st = run_gemv(cases, xs, batch)
+    assert (st == 0).all(), st
+    for c, x, y in zip(cases, xs, ys):
+        ref = ogemv.gemv_f64(c.expected_bf16().reshape(c.rows, c.cols), x)
+        assert ogemv.rel_err(y, ref) <= 1e-4
+
+
 @pytest.mark.parametrize("batch", [1, 3, 8])
 def test_gemv_lds_path_shapes(batch):
     """Tensors the LDS GEMV path takes (W = 64, 4-bit, refill every two steps,
@@ -284,8 +304,8 @@ def test_gemv_mistral_shapes_sampled_layer(batch, refill_steps):
     """One layer of the 4-bit Mistral-shaped stack at full size (row-aligned
     chunks, 64 lanes), every output checked against the float64 oracle; with
     refill every two steps the LDS path takes every full chunk (at batch 8 the
-    14336-column down projection, whose activations exceed the LDS block,
-    takes the generic path)."""
+    14336-column down projection, whose activations exceed the LDS block, is
+    walked in column slices)."""
     specs = [s for s in __import__("synth").tensor_specs("mistral_stack") if s.layer == 0]
     cases, xs = [], []
     for gi, s in enumerate(specs):
