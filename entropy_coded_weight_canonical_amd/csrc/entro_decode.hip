@@ -133,17 +133,18 @@ __device__ __forceinline__ uint32_t and_sv(uint32_t s, uint32_t v) {
 // The value sits in bits [31:16] ([23:16] for codes) of the table entry and
 // goes out with the d16_hi store forms, so no shift is spent on it.  (The
 // outputs are never read back by the kernel, so the compiler needs no
-// knowledge of these writes.)  The compiler does not insert hazard wait
+// knowledge of these writes; they are streamed (nt) like every output
+// store, see kStoreNT.)  The compiler does not insert hazard wait
 // states around inline assembly, and a vector-memory instruction must not
 // read an SGPR in the 5 cycles after a VALU wrote it (as v_readlane does when
 // the resource comes back from a spill), hence the s_nop 4.
 template <typename OutT>
 __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t e) {
   if (sizeof(OutT) == 1)
-    asm volatile("s_nop 4\n\tbuffer_store_byte_d16_hi %0, %1, %2, %3 offen"
+    asm volatile("s_nop 4\n\tbuffer_store_byte_d16_hi %0, %1, %2, %3 offen nt"
                  : : "v"(e), "v"(voff), "s"(r), "s"(soff));
   else
-    asm volatile("s_nop 4\n\tbuffer_store_short_d16_hi %0, %1, %2, %3 offen"
+    asm volatile("s_nop 4\n\tbuffer_store_short_d16_hi %0, %1, %2, %3 offen nt"
                  : : "v"(e), "v"(voff), "s"(r), "s"(soff));
 }
 
@@ -169,8 +170,8 @@ __device__ __forceinline__ void store_pair(__amdgpu_buffer_rsrc_t r, uint32_t vo
                                            uint32_t sel) {
   const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)ab, 0xB1, 0xF, 0xF, false);
   const uint32_t v = __builtin_amdgcn_perm(nb, ab, sel);
-  if (MODE == kModeU8) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, r, (int)voffp, (int)soff, 0);
-  else __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)voffp, (int)soff, 0);
+  if (MODE == kModeU8) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, r, (int)voffp, (int)soff, kStoreNT);
+  else __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)voffp, (int)soff, kStoreNT);
 }
 
 __device__ __forceinline__ uint32_t pair_voff(uint32_t lane_off, uint32_t lane, uint32_t W, uint32_t elem) {
@@ -223,8 +224,8 @@ __device__ __forceinline__ uint32_t lookup(const uint32_t *lut, uint32_t hi, uin
 
 template <int MODE>
 __device__ __forceinline__ void emit(void *base, uint64_t k, uint32_t e) {
-  if (MODE == kModeU8) static_cast<uint8_t *>(base)[k] = (uint8_t)(e >> 16);
-  else static_cast<uint16_t *>(base)[k] = (uint16_t)(e >> 16);
+  if (MODE == kModeU8) __builtin_nontemporal_store((uint8_t)(e >> 16), static_cast<uint8_t *>(base) + k);
+  else __builtin_nontemporal_store((uint16_t)(e >> 16), static_cast<uint16_t *>(base) + k);
 }
 
 // ---------------------------------------------------------------------------
