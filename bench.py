@@ -9,8 +9,11 @@ Default workload (one "step" = one call of entro_decode_dequant):
 
 Other workloads (``--workload``): tensor_2048 (8-bit asymmetric, 4096-code
 chunks, decode to codes and to bf16), smollm_stack / smollm_stack_u8 (decode
-all 169 tensors in one call), phi3_stack / mistral_stack (fused decode + GEMV
-per token).
+all 169 tensors in one call), phi3_stack / mistral_stack (per token: fused
+decode + GEMV, or with ``--path ahead`` each matrix decoded to bf16 on a side
+stream just ahead of the stock linear kernel, or with ``--path dense`` the
+stock kernel on resident bf16 weights; ``--graph`` replays the token as one
+HIP graph).
 
 The encoder used to produce the inputs is the library's own (host C++), not
 the oracle; the oracle is only timed in the CPU-baseline leg.
@@ -268,6 +271,7 @@ def bench_gemv(args, workload, batch, clip_sigma=0.0):
         coded_layers.append(row)
     groups = []   # per layer: list of (descs, items)
     keep = []
+    mats = []     # (DeviceTensor, rows, cols, x) in token order, for the unfused paths
     n_sym = 0
     in_bytes = 0
     for L in range(layers):
@@ -286,20 +290,77 @@ def bench_gemv(args, workload, batch, clip_sigma=0.0):
                 keep += [dt, y]
                 descs.append(dt.desc)
                 items.append(ent.GemvItem(s.rows, s.cols, x.data_ptr(), y.data_ptr()))
+                mats.append((dt, s.rows, s.cols, x))
                 n_sym += c.n
                 in_bytes += c.in_bytes + 2 * batch * s.cols + 4 * batch * s.rows
             keep.append(x)
             groups.append((descs, items))
     status = torch.zeros(64, dtype=torch.int32, device="cuda")
+    path = args.path
+    hbm_bytes = in_bytes   # algorithmic HBM bytes per token of the chosen path
 
-    def step():
-        for descs, items in groups:
-            ent.decode_gemv(descs, items, batch, status.data_ptr())
+    if path == "fused":
+        def step():
+            for descs, items in groups:
+                ent.decode_gemv(descs, items, batch, status.data_ptr())
+
+        def flags():
+            return status
+    elif path == "ahead":
+        # decode-ahead streaming: each matrix decoded to bf16 on a side stream
+        # just before the stock linear kernel reads it
+        from entropy_coded_weight_canonical_amd.ahead import DecodeAhead
+
+        da = DecodeAhead([m[0] for m in mats], [(m[1], m[2]) for m in mats], depth=args.ahead_depth,
+                         block_elems=args.ahead_block or None)
+        xs_bf = [m[3].view(torch.bfloat16) for m in mats]
+        hbm_bytes = sum(m[0].desc.n_words * 4 + 2 * m[1] * m[2] * 2 + 2 * batch * m[2] + 2 * batch * m[1]
+                        for m in mats)
+
+        def step():
+            da.run(xs_bf)
+
+        def flags():
+            return da.status
+    else:
+        # dense bf16 baseline: every matrix decoded once to its own resident bf16
+        # copy, then only the stock linear kernel per token
+        import torch.nn.functional as F
+
+        dense = []
+        for dt, r, c, x in mats:
+            wbuf = torch.empty((r, c), dtype=torch.bfloat16, device="cuda")
+            ent.decode_dequant([dt.desc], [wbuf.data_ptr()], status.data_ptr())
+            dense.append((wbuf, x.view(torch.bfloat16)))
+        hbm_bytes = sum(2 * w.numel() + 2 * batch * w.shape[1] + 2 * batch * w.shape[0] for w, _ in dense)
+
+        def step():
+            for w, x in dense:
+                F.linear(x, w)
+
+        def flags():
+            return status
 
     step()
     torch.cuda.synchronize()
-    if int(status.abs().sum().item()) != 0:
-        raise SystemExit(f"stream flags set: {status.cpu().numpy()}")
+    if int(flags().abs().sum().item()) != 0:
+        raise SystemExit(f"stream flags set: {flags().cpu().numpy()}")
+    if args.graph:
+        # the whole token as one HIP graph (warm-up on a side stream first)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        step = graph.replay
+        step()
+        torch.cuda.synchronize()
+        if int(flags().abs().sum().item()) != 0:
+            raise SystemExit(f"stream flags set in graph replay: {flags().cpu().numpy()}")
     _keep = flush_mall(torch)
     total_ms, per_ms, wall = time_steps(step, args.steps, args.warmup)
     ms = total_ms / args.steps
@@ -317,14 +378,22 @@ def bench_gemv(args, workload, batch, clip_sigma=0.0):
         "data": "synthetic",
         "config": {"workload": f"{workload}: {len(specs)} matrices, 4-bit "
                                f"{'unsigned clip %.2f sigma' % clip_sigma if clip_sigma else 'mixed'}, "
-                               f"row-aligned chunks, W=64, fused decode+dequant+GEMV batch {batch}",
+                               f"row-aligned chunks, W=64, " + {
+                                   "fused": f"fused decode+dequant+GEMV batch {batch}",
+                                   "ahead": f"decode-ahead to bf16 (depth {args.ahead_depth}, blocks of "
+                                            f"{args.ahead_block or 'whole'} weights) + stock matmul, "
+                                            f"batch {batch}",
+                                   "dense": f"dense bf16 weights (decoded once) + stock linear kernel, "
+                                            f"batch {batch}"}[path],
+                   "path": path, "hip_graph": bool(args.graph),
                    "refill_ahead": bool(args.refill_ahead),
                    "global_batch": batch, "symbols_per_token": n_sym, "launch_groups": len(groups),
                    "distinct_layers": n_distinct, "coded_bits_per_weight": round(float(bits), 4),
                    "parallelism": "single GPU"},
         "decoded_Gsym_per_s": round(n_sym / (ms * 1e-3) / 1e9, 3),
-        "eff_GBps": round(in_bytes / (ms * 1e-3) / 1e9, 1),
-        "hbm_frac": round(in_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "hbm_bytes_per_token": int(hbm_bytes),
+        "eff_GBps": round(hbm_bytes / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(hbm_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
     }
     return res
 
@@ -435,6 +504,12 @@ def main():
                     help="steps per refill decision of the encoded streams")
     ap.add_argument("--refill-ahead", type=int, default=1, choices=[0, 1],
                     help="encode the streams refilling ahead (same words, fetch order for early decoding)")
+    ap.add_argument("--path", default="fused", choices=["fused", "ahead", "dense"],
+                    help="GEMV workloads: fused decode+GEMV, decode-ahead + stock linear, or dense bf16")
+    ap.add_argument("--ahead-depth", type=int, default=2, help="staging buffers of the decode-ahead path")
+    ap.add_argument("--ahead-block", type=int, default=0,
+                    help="weights per decode-ahead block (whole chunks; 0 = whole matrices)")
+    ap.add_argument("--graph", action="store_true", help="GEMV workloads: replay each token as one HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()

@@ -29,6 +29,11 @@
  *     is unchanged, and a decoder can fetch it before looking up codewords;
  *   - chunk_bit_off[c] = 32 * (words before chunk c); chunk_bit_off[n_chunks]
  *     = 32 * n_words.  Words are little-endian uint32.
+ *   - A descriptor may also cover only the whole chunks c0 .. c1 - 1 of a
+ *     stream: d_chunk_bit_off then points at entry c0 of the stream's offsets,
+ *     n_symbols counts those chunks' codes, and d_words / n_words stay the
+ *     whole stream's (the offsets remain bit positions in it).  This decodes
+ *     a block of rows of a matrix whose chunks hold whole rows.
  *
  * Conventions
  *   - Pointers named d_* are DEVICE pointers (hipMalloc'd or torch CUDA/HIP
