@@ -265,7 +265,7 @@ def bench_gemv(args, workload, batch, clip_sigma=0.0):
     for L in range(n_distinct):
         row = []
         for s in (x for x in specs if x.layer == L):
-            chunk = s.cols * max(1, round(8192 / s.cols))
+            chunk = s.cols * max(1, round(args.gemv_chunk / s.cols))
             row.append((s, code_tensor(s, 4, "unsigned" if clip_sigma else "mixed", chunk, 64, args.refill_steps,
                                        clip_sigma, ahead=args.refill_ahead)))
         coded_layers.append(row)
@@ -385,7 +385,7 @@ def bench_gemv(args, workload, batch, clip_sigma=0.0):
                                             f"batch {batch}",
                                    "dense": f"dense bf16 weights (decoded once) + stock linear kernel, "
                                             f"batch {batch}"}[path],
-                   "path": path, "hip_graph": bool(args.graph),
+                   "path": path, "hip_graph": bool(args.graph), "chunk_target": args.gemv_chunk,
                    "refill_ahead": bool(args.refill_ahead),
                    "global_batch": batch, "symbols_per_token": n_sym, "launch_groups": len(groups),
                    "distinct_layers": n_distinct, "coded_bits_per_weight": round(float(bits), 4),
@@ -510,6 +510,8 @@ def main():
     ap.add_argument("--ahead-block", type=int, default=0,
                     help="weights per decode-ahead block (whole chunks; 0 = whole matrices)")
     ap.add_argument("--graph", action="store_true", help="GEMV workloads: replay each token as one HIP graph")
+    ap.add_argument("--gemv-chunk", type=int, default=4096,
+                    help="GEMV workloads: target chunk size in weights (rounded to whole rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
