@@ -18,7 +18,7 @@ import numpy as np
 __all__ = [
     "LibraryNotBuilt", "EntroError", "library_path", "load",
     "Codebook", "Tensor", "GemvItem", "FLAGS",
-    "lut_bytes", "lut_build", "decode", "decode_dequant", "decode_gemv", "status_str",
+    "lut_bytes", "lut_build", "decode", "decode_dequant", "decode_gemv", "decode_gemm", "status_str",
     "quantize", "code_lengths", "encode_layout", "encode",
     "SCHEME_ASYMMETRIC", "SCHEME_UNSIGNED", "SCHEME_MIXED",
 ]
@@ -88,6 +88,7 @@ def load():
     for name in ("entro_decode", "entro_decode_dequant"):
         getattr(lib, name).argtypes = [P, SZ, P, P, P]
     lib.entro_decode_gemv.argtypes = [P, SZ, P, U32, P, P]
+    lib.entro_decode_gemm.argtypes = [P, SZ, P, U32, P, P]
     lib.entro_status_str.argtypes = [ctypes.c_int]
     lib.entro_status_str.restype = ctypes.c_char_p
     lib.entro_quantize.argtypes = [P, U64, U32, ctypes.c_int, ctypes.c_float, P, P, P, P]
@@ -95,7 +96,7 @@ def load():
     lib.entro_encode_layout.argtypes = [P, U64, P, U32, U32, U32, P, P]
     lib.entro_encode.argtypes = [P, U64, P, U32, U32, U32, U32, U32, P, P, U32]
     for name in ("entro_lut_build", "entro_decode", "entro_decode_dequant", "entro_decode_gemv",
-                 "entro_quantize", "entro_code_lengths", "entro_encode_layout", "entro_encode"):
+                 "entro_decode_gemm", "entro_quantize", "entro_code_lengths", "entro_encode_layout", "entro_encode"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -187,6 +188,17 @@ def decode_gemv(tensors, items, batch: int, d_status: int, stream=None) -> None:
         ia[i] = it
     _check(load().entro_decode_gemv(ta, len(tensors), ia, int(batch), ctypes.c_void_p(d_status),
                                     ctypes.c_void_p(_stream_handle(stream))), "entro_decode_gemv")
+
+
+def decode_gemm(tensors, items, n_tokens: int, d_status: int, stream=None) -> None:
+    """``entro_decode_gemm``: like ``decode_gemv`` for ``n_tokens`` (1..512)
+    activation rows at once, products on the matrix cores."""
+    ta = _tensor_array(tensors)
+    ia = (GemvItem * len(items))()
+    for i, it in enumerate(items):
+        ia[i] = it
+    _check(load().entro_decode_gemm(ta, len(tensors), ia, int(n_tokens), ctypes.c_void_p(d_status),
+                                    ctypes.c_void_p(_stream_handle(stream))), "entro_decode_gemm")
 
 
 # --------------------------------------------------------------------------

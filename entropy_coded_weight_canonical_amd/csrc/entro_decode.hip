@@ -1425,6 +1425,232 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
 }
 
 // ---------------------------------------------------------------------------
+// decode + GEMM (prefill, n_tokens up to kGemmMaxTokens):
+//   y[t][o] = sum_k deq(W[o][k]) * x[t][k]
+// A workgroup owns kWaves consecutive rows of one matrix; wavefront w
+// decodes row w of the tile (its chunk: one row, W = 64, 4-bit codes in
+// pairs through the two-code table).  Each pair of steps gives a lane the
+// weights of columns 128q + j and 128q + 64 + j; the wavefronts write them
+// (packed like the decode outputs) into one of two LDS slices of
+// kWaves x 128 bf16, and after a workgroup barrier every wavefront that owns
+// 16-token groups multiplies the slice with them on the matrix cores
+// (v_mfma_f32_16x16x32_bf16: A = 16 rows x 32 columns of the slice,
+// B = 32 columns x 16 tokens of x, fp32 accumulation), while the next pair
+// is decoded into the other slice.  Every weight is decoded once.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Decode the next pair of steps of a GEMM row (no arithmetic on it).
+__device__ __forceinline__ u32x2 gemm_pair(GemvLane<1> &g, const uint32_t *lut, uint32_t K, uint32_t early) {
+  u32x2 e2;
+  if (g.kk < early) {
+    e2 = early_pair64<kModeGemv>(lut, K, g.hi, g.lo, g.n, g.pa);
+  } else {
+    e2 = pair_lookup<kModeGemv>(lut, K, g.hi, g.lo);
+    const uint64_t m = need_mask(e2.y, g.n);
+    if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+      const uint32_t idx =
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const uint32_t w = lds_word(g.pa, idx);
+      g.hi |= w >> g.n;
+      g.lo = __builtin_amdgcn_alignbit(w, 0u, g.n);
+      g.n += 32u;
+      e2 = pair_lookup<kModeGemv>(lut, K, g.hi, g.lo);
+    }
+    g.pa = lds_adv(g.pa, (uint32_t)__popcll(m));
+  }
+  ++g.kk;
+  const uint32_t nhi = __builtin_amdgcn_alignbit(g.hi, g.lo, e2.y);
+  g.lo = __builtin_amdgcn_alignbit(g.lo, 0u, e2.y);
+  g.hi = nhi;
+  g.n = sub_len(g.n, e2.y);
+  return e2;
+}
+
+// The pair's two bf16 weights of every lane into slice row `row` (byte
+// address): neighbouring lanes swap values (as for the packed decode
+// outputs), so an even lane writes columns j, j+1 and an odd lane columns
+// 64 + j - 1, 64 + j, one dword each.
+__device__ __forceinline__ void gemm_put(uint32_t row_addr, uint32_t lane, uint32_t ab) {
+  const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)ab, 0xB1, 0xF, 0xF, false);
+  const uint32_t v = __builtin_amdgcn_perm(nb, ab, pair_sel<kModeGemv>(lane));
+  const uint32_t col = (lane & ~1u) + (lane & 1u) * 64u;
+  *(__attribute__((address_space(3))) uint32_t *)(uintptr_t)(row_addr + col * 2u) = v;
+}
+
+// 16 consecutive bytes of x (8 bf16) as an MFMA operand; zero past the tokens.
+__device__ __forceinline__ bf16x8 gemm_x8(const uint16_t *x, uint32_t cols, uint32_t tok, uint32_t n_tokens,
+                                          uint32_t col) {
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (tok < n_tokens) v = *reinterpret_cast<const u32x4 *>(x + (uint64_t)tok * cols + col);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Activations of one slice (the tile's 128 columns of every token) staged in
+// LDS for prompts of at most kGemmXlTokens tokens: 16-byte units, unit u =
+// token u / 16, columns 8 (u % 16) .. +7; two units per thread at most.
+struct XSliceRegs { u32x4 v[2]; };
+
+__device__ __forceinline__ void gemm_x_load(XSliceRegs &r, const uint16_t *x, uint32_t cols, uint32_t n_tokens,
+                                            uint32_t units, uint32_t col0) {
+#pragma unroll
+  for (uint32_t h = 0; h < 2u; ++h) {
+    const uint32_t u = threadIdx.x + h * kBlockThreads;
+    const uint32_t tok = u >> 4;
+    r.v[h] = u32x4{0u, 0u, 0u, 0u};
+    if (u < units && tok < n_tokens)
+      r.v[h] = *reinterpret_cast<const u32x4 *>(x + (uint64_t)tok * cols + col0 + 8u * (u & 15u));
+  }
+}
+
+__device__ __forceinline__ void gemm_x_store(const XSliceRegs &r, uint32_t xs_addr, uint32_t units) {
+#pragma unroll
+  for (uint32_t h = 0; h < 2u; ++h) {
+    const uint32_t u = threadIdx.x + h * kBlockThreads;
+    if (u < units)
+      *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)(xs_addr + ((u >> 4) * kGemmRowStride + 8u * (u & 15u)) * 2u) =
+          r.v[h];
+  }
+}
+
+template <int NT, bool XL>
+__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKernelSgprs))) void ecw_gemm_kernel(
+    const GemmArgs a) {
+  // dynamic LDS: two-code table (at 0), code table, the two weight slices,
+  // the table state word, one staging area per wavefront
+  u32x2 *ptab_area = reinterpret_cast<u32x2 *>(dyn_lds);
+  uint32_t *lut = reinterpret_cast<uint32_t *>(dyn_lds) + (2u << kPairBits);
+  const uint32_t slices = lds_addr(dyn_lds) + a.slice_byte;
+  const uint32_t xslices = slices + 2u * kGemmSliceBytes;   // two activation slices (XL)
+  if (!lds_at_zero()) {   // the two-code table is addressed from LDS address 0
+    if (threadIdx.x == 0)
+      for (uint32_t i = 0; i < a.n_tensors; ++i) atomicOr(a.t[i].status, kFLut);
+    return;
+  }
+  uint32_t &lut_state = reinterpret_cast<uint32_t *>(dyn_lds)[a.state_word];
+  const uint32_t wave = rfl(threadIdx.x >> 6);
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t stage_words = a.stage_words;
+  uint32_t *stage = reinterpret_cast<uint32_t *>(dyn_lds) + a.state_word + 4u + wave * (stage_words + kStageSlack);
+  const uint32_t tok_groups = (a.n_tokens + 15u) >> 4;
+  const uint32_t t0 = blockIdx.x * a.tiles_per_block;
+  const uint32_t t1 = min(t0 + a.tiles_per_block, a.total_tiles);
+  uint32_t cur = 0xFFFFFFFFu;
+  uint32_t K = 0, l_min = 1;
+  for (uint32_t tile = t0; tile < t1; ++tile) {
+    uint32_t ti = 0;
+    while (ti + 1 < a.n_tensors && a.tile_begin[ti + 1] <= tile) ++ti;
+    const TensorArg &d = a.t[ti];
+    if (ti != cur) {
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        uint32_t k = 0;
+        if (d.lut_words >= kLutHeaderWords) {
+          const uint32_t h0 = d.lut[0], h1 = d.lut[1], ne = d.lut[2], l1 = d.lut[3];
+          const uint32_t kk = h1 & 0xFFu;
+          const uint32_t lmin = h1 >> 24;
+          if (h0 == kLutMagic && (h1 & 0x00FFFF00u) == d.expect_hdr && kk >= 1 && kk <= kSingleLevelMax &&
+              l1 == (1u << kk) && ne >= l1 && ne <= a.lut_cap && ne <= d.lut_words - kLutHeaderWords &&
+              lmin >= 1u && lmin <= kMaxCodeLen)
+            k = kk | (ne << 8) | (lmin << 24);
+        }
+        if (!k) atomicOr(d.status, kFLut);
+        lut_state = k;
+      }
+      __syncthreads();
+      const uint32_t ne = (lut_state >> 8) & 0xFFFFu;
+      for (uint32_t i = threadIdx.x; i < ne; i += kBlockThreads) lut[i] = kernel_entry<kModeGemv>(d.lut[kLutHeaderWords + i]);
+      K = rfl(lut_state & 0xFFu);
+      l_min = rfl(lut_state >> 24);
+      cur = ti;
+      __syncthreads();
+      if (K)
+        for (uint32_t i = threadIdx.x; i < (1u << kPairBits); i += kBlockThreads)
+          ptab_area[i] = build_pair_entry<kModeGemv>(lut, K, i);
+      __syncthreads();
+    }
+    if (!K) continue;
+    const uint32_t r0 = (tile - a.tile_begin[ti]) * (uint32_t)kWaves;
+    const uint32_t row = r0 + wave;
+    const uint32_t cols = d.cols, rows = d.rows;
+    // this wavefront's row: chunk `row` (the host requires one row per chunk)
+    Staged st{0u, 0u, 0u};
+    const bool mine = row < rows;
+    const bool have = mine && stage_task<6>(d, row, stage, stage_words, st);
+    if (mine && !have && lane == 0u) atomicOr(d.status, kFOffsets);
+    GemvLane<1> g;
+    g.hi = g.lo = g.n = g.kk = 0u;
+    g.pa = lds_addr(stage + st.al);
+    const uint32_t early = rfl(early_pairs(d.ahead, cols >> 6, l_min));
+    const uint32_t q_n = cols / kGemmSliceCols;
+    const uint32_t my_row_addr = slices + wave * kGemmRowStride * 2u;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // A operand: row lane % 16 of the slice, columns 8 * (lane / 16) + 32 ks
+    const uint32_t a_addr = slices + ((lane & 15u) * kGemmRowStride + 8u * (lane >> 4)) * 2u;
+    // staged activations (XL): B operand of group grp from token row
+    // grp * 16 + lane % 16 of the x slice, same column pattern as A
+    const uint32_t xunits = tok_groups * 256u;
+    const uint32_t b_addr = xslices + ((lane & 15u) * kGemmRowStride + 8u * (lane >> 4)) * 2u;
+    XSliceRegs xr;
+    if (XL) {
+      gemm_x_load(xr, d.x, cols, a.n_tokens, xunits, 0u);
+      gemm_x_store(xr, xslices, xunits);
+    }
+    if (have) gemm_put(my_row_addr, lane, gemm_pair(g, lut, K, early).x);
+    __syncthreads();
+    for (uint32_t q = 0; q < q_n; ++q) {
+      const uint32_t buf = (q & 1u) * kGemmSliceBytes;
+      const bool next = q + 1u < q_n;
+      if (XL && next) gemm_x_load(xr, d.x, cols, a.n_tokens, xunits, (q + 1u) * kGemmSliceCols);
+      if (have && next) gemm_put(my_row_addr + (kGemmSliceBytes - buf), lane, gemm_pair(g, lut, K, early).x);
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        const uint32_t grp = wave + (uint32_t)tt * (uint32_t)kWaves;
+        if (grp < tok_groups) {
+          const uint32_t tok = grp * 16u + (lane & 15u);
+#pragma unroll
+          for (uint32_t ks = 0; ks < 4u; ++ks) {
+            const bf16x8 av = __builtin_bit_cast(
+                bf16x8, *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(a_addr + buf + ks * 64u));
+            bf16x8 bv;
+            if (XL)
+              bv = __builtin_bit_cast(bf16x8, *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(
+                                                  b_addr + (q & 1u) * a.xslice_bytes + grp * 16u * kGemmRowStride * 2u +
+                                                  ks * 64u));
+            else
+              bv = gemm_x8(d.x, cols, tok, a.n_tokens, q * kGemmSliceCols + ks * 32u + 8u * (lane >> 4));
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[tt], 0, 0, 0);
+          }
+        }
+      }
+      if (XL && next) gemm_x_store(xr, xslices + ((q + 1u) & 1u) * a.xslice_bytes, xunits);
+      __syncthreads();
+    }
+    if (have) {
+      const uint32_t flags = gemv_end_flags<1>(g, lds_addr(stage + st.al), rfl(st.nw));
+      if (flags && lane == 0u) atomicOr(d.status, flags);
+    }
+    // D of group grp: lane holds rows r0 + 4 (lane / 16) + v for token grp * 16 + lane % 16
+    float *y = static_cast<float *>(d.out);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const uint32_t grp = wave + (uint32_t)tt * (uint32_t)kWaves;
+      const uint32_t tok = grp * 16u + (lane & 15u);
+      if (grp < tok_groups && tok < a.n_tokens) {
+#pragma unroll
+        for (uint32_t v = 0; v < 4u; ++v) {
+          const uint32_t o = r0 + 4u * (lane >> 4) + v;
+          if (o < rows) y[(uint64_t)tok * rows + o] = acc[tt][v];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 
@@ -1609,6 +1835,105 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
   return ENTRO_OK;
 }
 
+static hipError_t launch_gemm(GemmArgs &a, size_t dyn, hipStream_t s) {
+  auto kern = a.xslice_bytes ? ecw_gemm_kernel<1, true>
+                             : (a.n_tokens <= 16u * (uint32_t)kWaves ? ecw_gemm_kernel<1, false> : ecw_gemm_kernel<2, false>);
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBlockThreads, dyn) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int lds_fit = (int)((kLdsPerCu - kLdsPlanReserve) / (dyn + kStaticLds));
+  if (lds_fit >= 1 && per_cu > lds_fit) per_cu = lds_fit;
+  if (cus < 1) cus = 1;
+  const uint64_t slots = (uint64_t)cus * (uint64_t)per_cu;
+  const uint32_t per_block = (uint32_t)((a.total_tiles + slots - 1) / slots);
+  a.tiles_per_block = per_block < 1 ? 1 : per_block;
+  const uint32_t grid = (a.total_tiles + a.tiles_per_block - 1) / a.tiles_per_block;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlockThreads), dyn, s, a);
+  return hipGetLastError();
+}
+
+static entro_status run_gemm(const entro_tensor *t, size_t n, const entro_gemv_item *g, uint32_t n_tokens,
+                             uint32_t *d_status, hipStream_t s) {
+  if (n == 0) return ENTRO_OK;
+  if (!t || !g || !d_status || n_tokens < 1 || n_tokens > kGemmMaxTokens) return ENTRO_E_INVAL;
+  for (size_t i = 0; i < n; ++i) {
+    const entro_status st = check_tensor(t[i]);
+    if (st != ENTRO_OK) return st;
+    const entro_gemv_item &it = g[i];
+    if ((uint64_t)it.rows * it.cols != t[i].n_symbols) return ENTRO_E_INVAL;
+    if (t[i].n_symbols == 0) continue;
+    if (!it.d_x || !it.d_y || (reinterpret_cast<uintptr_t>(it.d_x) & 15u)) return ENTRO_E_INVAL;
+    if (it.cols % kGemmSliceCols || t[i].chunk_symbols != it.cols) return ENTRO_E_FORMAT;
+    if (t[i].lanes != 64u || t[i].sym_bits != 4u || t[i].refill_steps != 2u || t[i].max_chunk_words == 0u)
+      return ENTRO_E_UNSUPPORTED;
+  }
+  size_t i = 0;
+  while (i < n) {
+    GemmArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.n_tokens = n_tokens;
+    uint32_t total = 0, k = 0;
+    uint64_t stage_need = 0, lut_need = 0;
+    for (; i < n && k < (uint32_t)kMaxTensorsPerLaunch; ++i) {
+      const entro_tensor &x = t[i];
+      if (x.n_symbols == 0) continue;
+      TensorArg &d = a.t[k];
+      d.lut = static_cast<const uint32_t *>(x.d_lut);
+      d.words = x.d_words;
+      d.offs = x.d_chunk_bit_off;
+      d.status = d_status + i;
+      d.n_words = x.n_words;
+      d.n_symbols = x.n_symbols;
+      d.chunk = x.chunk_symbols;
+      d.n_chunks = (uint32_t)((x.n_symbols + x.chunk_symbols - 1) / x.chunk_symbols);
+      d.expect_hdr = (x.sym_bits << 8) | (x.max_len << 16);
+      d.lut_words = (uint32_t)std::min<uint64_t>(x.lut_bytes / 4, kLutHeaderWords + kLutMaxEntries);
+      d.refill_steps = 2u;
+      d.ahead = x.refill_ahead;
+      d.out = g[i].d_y;
+      d.x = g[i].d_x;
+      d.rows = g[i].rows;
+      d.cols = g[i].cols;
+      d.n_tasks = d.n_chunks;
+      const uint64_t tiles = (d.rows + kWaves - 1) / kWaves;
+      if ((uint64_t)total + tiles > 0x7FFFFFFFull) return ENTRO_E_UNSUPPORTED;
+      a.tile_begin[k] = total;
+      total += (uint32_t)tiles;
+      lut_need = std::max<uint64_t>(lut_need, d.lut_words > kLutHeaderWords ? d.lut_words - kLutHeaderWords : 0);
+      stage_need = std::max<uint64_t>(stage_need, x.max_chunk_words);
+      ++k;
+    }
+    if (k == 0) continue;
+    a.n_tensors = k;
+    a.total_tiles = total;
+    for (uint32_t r = k; r <= (uint32_t)kMaxTensorsPerLaunch; ++r) a.tile_begin[r] = total;
+    // LDS: two-code table, code table, two weight slices, state word, then
+    // one staging area per wavefront (the largest row plus alignment)
+    a.lut_cap = (uint32_t)((lut_need + 3) & ~3ull);
+    size_t dyn = ((size_t)8u << kPairBits) + (size_t)a.lut_cap * 4u;
+    dyn = (dyn + 15u) & ~(size_t)15u;
+    a.slice_byte = (uint32_t)dyn;
+    dyn += 2u * kGemmSliceBytes;
+    // short prompts: the activations of each slice staged in LDS as well
+    const uint32_t tok_pad = (n_tokens + 15u) & ~15u;
+    if (n_tokens <= kGemmXlTokens) {
+      a.xslice_bytes = tok_pad * kGemmRowStride * 2u;
+      dyn += 2u * (size_t)a.xslice_bytes;
+    }
+    a.state_word = (uint32_t)(dyn / 4u);
+    dyn += 16u;
+    const uint64_t sw = (stage_need + 3 + 3) & ~3ull;
+    const uint64_t cap = ((kLdsPerCu - kStaticLds) / 4u - dyn / 4u) / kWaves - kStageSlack;
+    if (sw > cap) return ENTRO_E_UNSUPPORTED;
+    a.stage_words = (uint32_t)sw;
+    dyn += (size_t)kWaves * (sw + kStageSlack) * 4u;
+    if (launch_gemm(a, dyn, s) != hipSuccess) return ENTRO_E_HIP;
+  }
+  return ENTRO_OK;
+}
+
 }  // namespace entro
 
 using namespace entro;
@@ -1626,4 +1951,9 @@ extern "C" entro_status entro_decode_dequant(const entro_tensor *t, size_t n, ui
 extern "C" entro_status entro_decode_gemv(const entro_tensor *t, size_t n, const entro_gemv_item *g,
                                           uint32_t batch, uint32_t *d_status, hipStream_t stream) {
   return run(kModeGemv, t, n, nullptr, g, batch, d_status, stream);
+}
+
+extern "C" entro_status entro_decode_gemm(const entro_tensor *t, size_t n, const entro_gemv_item *g,
+                                          uint32_t n_tokens, uint32_t *d_status, hipStream_t stream) {
+  return run_gemm(t, n, g, n_tokens, d_status, stream);
 }

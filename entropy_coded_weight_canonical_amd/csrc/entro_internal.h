@@ -77,6 +77,30 @@ struct LaunchArgs {
   uint32_t x_slice;                                // 1: activations too large for x_words go in slices
 };
 
+// Decode + GEMM (prefill): a workgroup owns a tile of kWaves weight rows, one
+// row (one chunk) per wavefront, and all tokens; the rows are decoded two
+// steps (128 columns) at a time into one of two LDS slices, which the
+// matrix cores multiply with the activations.
+constexpr uint32_t kGemmMaxTokens = 512;
+constexpr uint32_t kGemmSliceCols = 128;                       // columns per slice (one pair of steps)
+constexpr uint32_t kGemmRowStride = kGemmSliceCols + 8;        // bf16 per slice row (padding: no bank conflicts)
+constexpr uint32_t kGemmSliceBytes = kWaves * kGemmRowStride * 2u;
+constexpr uint32_t kGemmXlTokens = 128;                         // prompts staged through LDS slices
+
+struct GemmArgs {
+  TensorArg t[kMaxTensorsPerLaunch];
+  uint32_t tile_begin[kMaxTensorsPerLaunch + 1];   // first row tile of each tensor
+  uint32_t n_tensors;
+  uint32_t n_tokens;
+  uint32_t total_tiles;
+  uint32_t tiles_per_block;
+  uint32_t stage_words;                            // staging words per wavefront
+  uint32_t lut_cap;                                // table entries reserved in LDS
+  uint32_t slice_byte;                             // LDS byte offset of the two weight slices
+  uint32_t xslice_bytes;                           // bytes of one activation slice in LDS (0: none)
+  uint32_t state_word;                             // LDS word of the table state
+};
+
 constexpr uint32_t kPairBits = 10;                 // two-code table: 1024 entries of 8 bytes
 constexpr uint32_t kPairFallback = 0x80u;          // flag (byte 0 of the second word): no pair
 

@@ -180,6 +180,26 @@ entro_status entro_decode_dequant(const entro_tensor *t, size_t n, uint16_t *con
 entro_status entro_decode_gemv(const entro_tensor *t, size_t n, const entro_gemv_item *g,
                                uint32_t batch, uint32_t *d_status, hipStream_t stream);
 
+/* Fused decode + dequant + GEMM for prompt processing (n_tokens activations
+ * at once): for each tensor i,
+ *   g[i].d_y[t][o] = sum_k deq(W_i[o][k]) * x_i[t][k]   for t < n_tokens,
+ * with every weight decoded once and the products on the matrix cores
+ * (bf16 inputs, fp32 accumulation).  Defined by: EntroLLM's separate
+ * pre-fill measurement of the coded uint4 model (gist.science technical
+ * summary, Experimental results, inference-latency item) with LazyWeights'
+ * decode on demand (abstract); the dense product is where matrix cores
+ * belong.  n_tokens in
+ * 1..512; d_x[i] is bf16 [n_tokens][cols], 16-byte aligned; d_y[i] is fp32
+ * [n_tokens][rows], overwritten.  Layouts decoded here: 4-bit codes, 64
+ * lanes, refill every two steps, one row per chunk (chunk_symbols == cols,
+ * cols a multiple of 128) and max_chunk_words stated; ENTRO_E_FORMAT or
+ * ENTRO_E_UNSUPPORTED otherwise, ENTRO_E_UNSUPPORTED also when the largest
+ * row does not fit the on-chip staging.  Data faults set d_status bits as
+ * for the other entry points (ENTRO_F_OFFSETS also when a row's words cannot
+ * be staged). */
+entro_status entro_decode_gemm(const entro_tensor *t, size_t n, const entro_gemv_item *g,
+                               uint32_t n_tokens, uint32_t *d_status, hipStream_t stream);
+
 /* Static English text for a status code. */
 const char *entro_status_str(entro_status s);
 

@@ -217,6 +217,31 @@ def test_device_entry_points_validate_before_launch(lib):
     assert lib.entro_decode_gemv(arr, 1, g, 0, st, None) == 1
 
 
+def test_gemm_entry_point_validates_before_launch(lib):
+    st = ctypes.c_void_p(1)
+
+    def gemm(n_tokens=16, rows=2, cols=128, x=0x1000, y=0x2000, **kw):
+        t = ent.Tensor(1, 1, 1, 10, rows * cols, cols, 64, 4, 12, 64, 8, 2, 1)
+        for k, v in kw.items():
+            setattr(t, k, v)
+        g = (ent.GemvItem * 1)(ent.GemvItem(rows, cols, x, y))
+        return lib.entro_decode_gemm((ent.Tensor * 1)(t), 1, g, n_tokens, st, None)
+
+    assert gemm(n_tokens=0) == 1
+    assert gemm(n_tokens=513) == 1
+    assert gemm(x=0x1008) == 1                       # activations not 16-byte aligned
+    assert gemm(x=0) == 1
+    assert gemm(rows=3, n_symbols=256) == 1           # rows * cols != n_symbols
+    assert gemm(cols=192, chunk_symbols=192) == 3     # cols not a multiple of 128
+    assert gemm(chunk_symbols=256) == 3               # two rows per chunk
+    assert gemm(lanes=32) == 4                        # only 64 lanes
+    assert gemm(sym_bits=8, max_len=16) == 4          # only 4-bit codes
+    assert gemm(refill_steps=1) == 4                  # only pairs of steps
+    assert gemm(max_chunk_words=0) == 4               # staging size must be stated
+    assert gemm(max_chunk_words=1 << 20) == 4         # a row larger than the on-chip staging
+    assert lib.entro_decode_gemm((ent.Tensor * 1)(), 0, None, 16, st, None) == 0
+
+
 # --------------------------------------------------------------------------
 # the library's offline encoder against the oracle
 # --------------------------------------------------------------------------
