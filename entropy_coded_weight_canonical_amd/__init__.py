@@ -17,9 +17,10 @@ import numpy as np
 
 __all__ = [
     "LibraryNotBuilt", "EntroError", "library_path", "load",
-    "Codebook", "Tensor", "GemvItem", "FLAGS",
+    "Codebook", "Tensor", "GemvItem", "RansTensor", "FLAGS",
     "lut_bytes", "lut_build", "decode", "decode_dequant", "decode_gemv", "decode_gemm", "status_str",
     "quantize", "code_lengths", "encode_layout", "encode",
+    "rans_freqs", "rans_table_build", "rans_encode", "rans_decode", "rans_decode_dequant",
     "SCHEME_ASYMMETRIC", "SCHEME_UNSIGNED", "SCHEME_MIXED",
 ]
 
@@ -63,6 +64,14 @@ class Tensor(ctypes.Structure):
                 ("refill_ahead", ctypes.c_uint32)]
 
 
+class RansTensor(ctypes.Structure):
+    _fields_ = [("d_table", ctypes.c_void_p), ("d_units", ctypes.c_void_p),
+                ("d_chunk_unit_off", ctypes.c_void_p), ("n_units", ctypes.c_uint64),
+                ("n_symbols", ctypes.c_uint64), ("chunk_symbols", ctypes.c_uint32),
+                ("lanes", ctypes.c_uint32), ("sym_bits", ctypes.c_uint32),
+                ("max_chunk_units", ctypes.c_uint32)]
+
+
 class GemvItem(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_uint32), ("cols", ctypes.c_uint32),
                 ("d_x", ctypes.c_void_p), ("d_y", ctypes.c_void_p)]
@@ -89,6 +98,13 @@ def load():
         getattr(lib, name).argtypes = [P, SZ, P, P, P]
     lib.entro_decode_gemv.argtypes = [P, SZ, P, U32, P, P]
     lib.entro_decode_gemm.argtypes = [P, SZ, P, U32, P, P]
+    lib.entro_rans_freqs.argtypes = [P, U32, P]
+    lib.entro_rans_table_bytes.argtypes = []
+    lib.entro_rans_table_bytes.restype = SZ
+    lib.entro_rans_table_build.argtypes = [U32, P, ctypes.c_float, ctypes.c_int32, P, SZ]
+    lib.entro_rans_encode.argtypes = [P, U64, P, U32, U32, U32, P, P, U64, P, U32]
+    for name in ("entro_rans_decode", "entro_rans_decode_dequant"):
+        getattr(lib, name).argtypes = [P, SZ, P, P, P]
     lib.entro_status_str.argtypes = [ctypes.c_int]
     lib.entro_status_str.restype = ctypes.c_char_p
     lib.entro_quantize.argtypes = [P, U64, U32, ctypes.c_int, ctypes.c_float, P, P, P, P]
@@ -96,7 +112,9 @@ def load():
     lib.entro_encode_layout.argtypes = [P, U64, P, U32, U32, U32, P, P]
     lib.entro_encode.argtypes = [P, U64, P, U32, U32, U32, U32, U32, P, P, U32]
     for name in ("entro_lut_build", "entro_decode", "entro_decode_dequant", "entro_decode_gemv",
-                 "entro_decode_gemm", "entro_quantize", "entro_code_lengths", "entro_encode_layout", "entro_encode"):
+                 "entro_decode_gemm", "entro_quantize", "entro_code_lengths", "entro_encode_layout", "entro_encode",
+                 "entro_rans_freqs", "entro_rans_table_build", "entro_rans_encode", "entro_rans_decode",
+                 "entro_rans_decode_dequant"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -199,6 +217,85 @@ def decode_gemm(tensors, items, n_tokens: int, d_status: int, stream=None) -> No
         ia[i] = it
     _check(load().entro_decode_gemm(ta, len(tensors), ia, int(n_tokens), ctypes.c_void_p(d_status),
                                     ctypes.c_void_p(_stream_handle(stream))), "entro_decode_gemm")
+
+
+def _rans_array(tensors):
+    arr = (RansTensor * len(tensors))()
+    for i, t in enumerate(tensors):
+        arr[i] = t
+    return arr
+
+
+def rans_decode(tensors, outs, d_status: int, stream=None) -> None:
+    """``entro_rans_decode``: ``tensors`` are ``RansTensor`` descriptors."""
+    _check(load().entro_rans_decode(_rans_array(tensors), len(tensors), _ptr_array(outs), ctypes.c_void_p(d_status),
+                                    ctypes.c_void_p(_stream_handle(stream))), "entro_rans_decode")
+
+
+def rans_decode_dequant(tensors, outs, d_status: int, stream=None) -> None:
+    """``entro_rans_decode_dequant``: like ``rans_decode`` with bf16 outputs."""
+    _check(load().entro_rans_decode_dequant(_rans_array(tensors), len(tensors), _ptr_array(outs),
+                                            ctypes.c_void_p(d_status), ctypes.c_void_p(_stream_handle(stream))),
+           "entro_rans_decode_dequant")
+
+
+def rans_freqs(counts: np.ndarray) -> np.ndarray:
+    """Histogram -> frequencies summing to 4096 (``entro_rans_freqs``)."""
+    c = np.ascontiguousarray(counts, dtype=np.uint64)
+    f = np.zeros(c.size, dtype=np.uint32)
+    _check(load().entro_rans_freqs(_np_ptr(c), c.size, _np_ptr(f)), "entro_rans_freqs")
+    return f
+
+
+def rans_table_build(freqs: np.ndarray, sym_bits: int, scale: float, zero_point: int) -> np.ndarray:
+    f = np.ascontiguousarray(freqs, dtype=np.uint32)
+    lib = load()
+    nb = int(lib.entro_rans_table_bytes())
+    out = np.zeros(nb // 4, dtype=np.uint32)
+    _check(lib.entro_rans_table_build(int(sym_bits), _np_ptr(f), ctypes.c_float(scale), int(zero_point),
+                                      _np_ptr(out), nb), "entro_rans_table_build")
+    return out
+
+
+def rans_encode(q: np.ndarray, freqs: np.ndarray, sym_bits: int, chunk: int, lanes: int, threads: int = 0):
+    """-> ``(units uint16, chunk_unit_off uint64)`` (``entro_rans_encode``)."""
+    q = np.ascontiguousarray(q, dtype=np.uint8).ravel()
+    f = np.ascontiguousarray(freqs, dtype=np.uint32)
+    nc = -(-q.size // chunk) if q.size else 0
+    offs = np.zeros(nc + 1, dtype=np.uint64)
+    nu = ctypes.c_uint64()
+    lib = load()
+    _check(lib.entro_rans_encode(_np_ptr(q), q.size, _np_ptr(f), int(sym_bits), int(chunk), int(lanes),
+                                 _np_ptr(offs), None, 0, ctypes.byref(nu), int(threads)), "entro_rans_encode")
+    units = np.zeros(max(int(nu.value), 1), dtype=np.uint16)
+    _check(lib.entro_rans_encode(_np_ptr(q), q.size, _np_ptr(f), int(sym_bits), int(chunk), int(lanes),
+                                 _np_ptr(offs), _np_ptr(units), units.size, ctypes.byref(nu), int(threads)),
+           "entro_rans_encode")
+    return units[: int(nu.value)], offs
+
+
+@dataclass
+class DeviceRansTensor:
+    """Device copies of one rANS-coded tensor plus its ``RansTensor`` descriptor."""
+    table: object
+    units: object
+    offs: object
+    desc: RansTensor
+
+    @classmethod
+    def upload(cls, table: np.ndarray, units: np.ndarray, offs: np.ndarray, n_symbols: int, chunk: int,
+               lanes: int, sym_bits: int, device="cuda"):
+        import torch
+
+        d_table = torch.from_numpy(np.ascontiguousarray(table).view(np.int32)).to(device)
+        u = np.ascontiguousarray(units, dtype=np.uint16)
+        d_units = torch.from_numpy(u.view(np.int16) if u.size else np.zeros(8, np.int16)).to(device)
+        d_offs = torch.from_numpy(np.ascontiguousarray(offs, dtype=np.uint64).view(np.int64)).to(device)
+        o = np.asarray(offs, dtype=np.uint64)
+        mcu = int(np.diff(o).max()) if o.size > 1 else 0
+        desc = RansTensor(d_table.data_ptr(), d_units.data_ptr(), d_offs.data_ptr(), int(u.size), int(n_symbols),
+                          int(chunk), int(lanes), int(sym_bits), mcu)
+        return cls(d_table, d_units, d_offs, desc)
 
 
 # --------------------------------------------------------------------------

@@ -338,3 +338,79 @@ def test_full_workload_tensor_encodes_like_oracle():
     words, offs = ent.encode(q, lengths, 8, 4096, 32)
     ow, oo = ccodec.encode(ref.q, lengths, 4096, 32, threads=4)
     assert np.array_equal(words, ow) and np.array_equal(offs, oo)
+
+
+# --------------------------------------------------------------------------
+# rANS variant: host side against the oracle
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("kind", ["uniform", "skewed", "peaked", "degenerate", "two", "sparse"])
+def test_rans_frequencies_and_encoder_match_oracle(bits, kind):
+    from oracle import rans
+    from synth import fuzz_codes
+
+    q = fuzz_codes(bits * 3 + len(kind), 7000, bits, kind)
+    counts = quant.histogram(q, bits)
+    f = ent.rans_freqs(counts)
+    assert f.tolist() == rans.quantize_freqs(counts).tolist()
+    for lanes, chunk in ((32, 256), (64, 640), (1, 64), (8, 1000)):
+        units, offs = ent.rans_encode(q, f, bits, chunk, lanes, threads=4)
+        ou, oo = rans.encode(q, f, chunk, lanes)
+        assert np.array_equal(units, ou) and np.array_equal(offs, oo)
+
+
+def test_rans_table_layout():
+    from oracle import rans
+    from oracle.dequant import dequant_bf16
+
+    counts = np.array([0, 5, 1, 90, 0, 3, 1, 0, 0, 0, 0, 0, 0, 0, 0, 900], dtype=np.int64)
+    f = ent.rans_freqs(counts)
+    t = ent.rans_table_build(f, 4, np.float32(0.0123), 7)
+    assert t[0] == 0x31524345 and t[1] == (4 | (12 << 8)) and t[2] == 4096
+    cum = rans.cumulative(f)
+    vals = dequant_bf16(np.arange(16, dtype=np.uint8), np.float32(0.0123), 7)
+    slots = t[4:].reshape(4096, 2)
+    for s in range(16):
+        for k in range(int(f[s])):
+            x, y = int(slots[cum[s] + k, 0]), int(slots[cum[s] + k, 1])
+            assert x == (int(vals[s]) << 16) | s
+            assert y == int(f[s]) | (k << 16)
+
+
+def test_rans_host_validation(lib):
+    f = np.zeros(16, dtype=np.uint32)
+    f[3] = 4096
+    q = np.full(10, 3, dtype=np.uint8)
+    offs = np.zeros(2, dtype=np.uint64)
+    nu = ctypes.c_uint64()
+    enc = lambda qq, ff, bits=4, chunk=10, lanes=2: lib.entro_rans_encode(
+        qq.ctypes.data, qq.size, ff.ctypes.data, bits, chunk, lanes, offs.ctypes.data, None, 0, ctypes.byref(nu), 1)
+    assert enc(q, f) == 0 and nu.value == 4
+    assert enc(q, f, lanes=3) == 3
+    assert enc(q, f, chunk=9) == 3
+    assert enc(q, f, bits=5) == 3
+    g = f.copy()
+    g[3] = 4095
+    assert enc(q, g) == 2                               # frequencies do not sum to 4096
+    assert enc(np.full(10, 4, dtype=np.uint8), f) == 2   # a code with frequency 0
+    t = np.zeros(4, dtype=np.uint32)
+    assert lib.entro_rans_table_build(4, f.ctypes.data, ctypes.c_float(1.0), 0, t.ctypes.data, t.nbytes) == 1
+    assert lib.entro_rans_freqs(np.zeros(4, dtype=np.uint64).ctypes.data, 4, f.ctypes.data) == 1
+    # device entry points: descriptor checks before launch
+    st = ctypes.c_void_p(1)
+    outs = (ctypes.c_void_p * 1)(0x1000)
+
+    def dec(**kw):
+        x = ent.RansTensor(1, 1, 1, 100, 1000, 256, 32, 4, 100)
+        for k, v in kw.items():
+            setattr(x, k, v)
+        return lib.entro_rans_decode((ent.RansTensor * 1)(x), 1, outs, st, None)
+
+    assert dec(lanes=16) == 3
+    assert dec(chunk_symbols=100) == 3
+    assert dec(sym_bits=6) == 3
+    assert dec(d_units=None) == 1
+    assert dec(max_chunk_units=1 << 20) == 4      # larger than the on-chip staging
+    assert lib.entro_rans_decode_dequant((ent.RansTensor * 1)(ent.RansTensor(1, 1, 1, 100, 1000, 256, 32, 4, 100)), 1,
+                                         (ctypes.c_void_p * 1)(0x1002), st, None) == 1
