@@ -13,7 +13,8 @@ all 169 tensors in one call), phi3_stack / mistral_stack (per token: fused
 decode + GEMV, or with ``--path ahead`` each matrix decoded to bf16 on a side
 stream just ahead of the stock linear kernel, or with ``--path dense`` the
 stock kernel on resident bf16 weights; ``--graph`` replays the token as one
-HIP graph).
+HIP graph).  ``--coder rans`` runs the tensor workloads on interleaved-rANS
+streams of the same codes instead (entro_rans_decode[_dequant]).
 
 The encoder used to produce the inputs is the library's own (host C++), not
 the oracle; the oracle is only timed in the CPU-baseline leg.
@@ -37,6 +38,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 METRIC = "decoded Gsym/s + effective HBM GB/s (% of peak); fused decode+GEMV ms/token"
 KERNEL_SOURCES = ["entropy_coded_weight_canonical_amd/csrc/entro_decode.hip",
+                  "entropy_coded_weight_canonical_amd/csrc/entro_device.h",
                   "entropy_coded_weight_canonical_amd/csrc/entro_internal.h"]
 
 
@@ -245,6 +247,122 @@ def bench_decode(args, workload, bits, scheme, chunk, lanes, replicas, mode):
                    "algorithmic_bytes_per_launch": bytes_step, "src_sha": kernel_src_sha()},
     }
     return res, coded
+
+
+
+class RansCoded:
+    """One tensor coded with the library's rANS encoder (ECR v1)."""
+
+    def __init__(self, q, scale, zp, bits, chunk, lanes, rows, cols):
+        import entropy_coded_weight_canonical_amd as ent
+
+        self.q = np.ascontiguousarray(q, dtype=np.uint8).ravel()
+        self.rows, self.cols, self.bits, self.chunk, self.lanes = rows, cols, bits, chunk, lanes
+        self.scale, self.zp, self.n = scale, zp, int(self.q.size)
+        self.freqs = ent.rans_freqs(np.bincount(self.q, minlength=1 << bits).astype(np.uint64))
+        self.units, self.offs = ent.rans_encode(self.q, self.freqs, bits, chunk, lanes)
+        self.table = ent.rans_table_build(self.freqs, bits, scale, zp)
+        self.n_chunks = int(self.offs.size - 1)
+
+    @property
+    def in_bytes(self) -> int:
+        return 2 * int(self.units.size) + 8 * (self.n_chunks + 1)
+
+    @property
+    def coded_bits_per_weight(self) -> float:
+        return 8.0 * self.in_bytes / self.n
+
+
+def cpu_baseline_rans(rc: RansCoded, budget_s: float = 12.0):
+    """The rANS oracle (pure Python, one thread) on the tensor's first chunks."""
+    from oracle import rans
+    from oracle.dequant import dequant_bf16
+
+    k = min(rc.n_chunks, 2)
+    n = min(rc.n, k * rc.chunk)
+    offs = rc.offs[: k + 1]
+    units = rc.units[: int(offs[-1])]
+    freqs = rc.freqs.astype(np.int64)
+    n_done, reps = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        q = rans.decode(units, offs, freqs, n, rc.chunk, rc.lanes)
+        dequant_bf16(q, rc.scale, rc.zp)
+        n_done += n
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(n_done / dt / 1e9, 6), "unit": "Gsym/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} x the first {k} chunks ({n} codes) of one {rc.rows}x{rc.cols} tensor: "
+                      f"pure-Python rANS decode + numpy bf16 dequant, {dt:.1f} s wall"}
+
+
+def bench_decode_rans(args, workload, bits, scheme, chunk, lanes, replicas, mode):
+    """The same tensors and call shape as bench_decode, coded with interleaved
+    rANS instead of canonical Huffman."""
+    import torch
+
+    import entropy_coded_weight_canonical_amd as ent
+    from synth import tensor_specs, weights
+
+    spec = tensor_specs(workload)[0]
+    log(f"rANS-encoding {workload} ({spec.rows}x{spec.cols}, {bits}-bit {scheme}, C={chunk}, W={lanes})")
+    q, s, zp, chosen = ent.quantize(weights(spec), bits, scheme)
+    rc = RansCoded(q, s, zp, bits, chunk, lanes, spec.rows, spec.cols)
+    huff = Coded(q, s, zp, chosen, bits, 16 if bits == 8 else 12, chunk, lanes, spec.rows, spec.cols,
+                 args.refill_steps, args.refill_ahead)
+    log(f"rANS {rc.coded_bits_per_weight:.3f} bits/weight (Huffman {huff.coded_bits_per_weight:.3f}); "
+        f"uploading {replicas} replicas")
+    dts = [ent.DeviceRansTensor.upload(rc.table, rc.units, rc.offs, rc.n, chunk, lanes, bits) for _ in range(replicas)]
+    odt = torch.uint8 if mode == "u8" else torch.int16
+    outs = [torch.empty(rc.n, dtype=odt, device="cuda") for _ in range(replicas)]
+    status = torch.zeros(replicas, dtype=torch.int32, device="cuda")
+    descs = [d.desc for d in dts]
+    ptrs = [o.data_ptr() for o in outs]
+    fn = ent.rans_decode if mode == "u8" else ent.rans_decode_dequant
+
+    def step():
+        fn(descs, ptrs, status.data_ptr())
+
+    step()
+    torch.cuda.synchronize()
+    if int(status.abs().sum().item()) != 0:
+        raise SystemExit(f"stream flags set: {status.cpu().numpy()}")
+    log(f"timing {args.steps} steps after {args.warmup} warm-up")
+    _keep = flush_mall(torch)
+    total_ms, per_ms, wall = time_steps(step, args.steps, args.warmup)
+    ms = total_ms / args.steps
+    n_sym = rc.n * replicas
+    bytes_step = replicas * (rc.in_bytes + rc.n * (1 if mode == "u8" else 2))
+    launch_ms = float(np.mean(per_ms))
+    achieved = bytes_step / (launch_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(n_sym / (ms * 1e-3) / 1e9, 3),
+        "unit": "Gsym/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if mode == "bf16" else "u8",
+        "data": "synthetic",
+        "config": {"workload": f"{workload}: {spec.rows}x{spec.cols} {scheme} {bits}-bit, interleaved rANS "
+                               f"(M=4096, 16-bit units), C={chunk}, W={lanes}, x{replicas} replicas, "
+                               f"decode{'+dequant->bf16' if mode == 'bf16' else '->u8'}",
+                   "global_batch": replicas, "symbols_per_step": n_sym,
+                   "coded_bits_per_weight": round(rc.coded_bits_per_weight, 4),
+                   "huffman_coded_bits_per_weight": round(huff.coded_bits_per_weight, 4),
+                   "parallelism": "single GPU"},
+        "eff_GBps": round(bytes_step / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+        "kernel": {"name": "ecr_kernel", "launches_per_step": 1, "avg_launch_ms": round(launch_ms, 5),
+                   "algorithmic_bytes_per_launch": bytes_step, "src_sha": kernel_src_sha()},
+    }
+    return res, rc
 
 
 def bench_gemv(args, workload, batch, clip_sigma=0.0):
@@ -526,6 +644,8 @@ def main():
     ap.add_argument("--graph", action="store_true", help="GEMV workloads: replay each token as one HIP graph")
     ap.add_argument("--gemv-chunk", type=int, default=4096,
                     help="GEMV workloads: target chunk size in weights (rounded to whole rows)")
+    ap.add_argument("--coder", default="huffman", choices=["huffman", "rans"],
+                    help="tensor workloads: canonical Huffman (ECW v1) or interleaved rANS (ECR v1) streams")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -542,11 +662,14 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
     coded = None
+    if args.coder == "rans" and not args.workload.startswith("tensor_"):
+        raise SystemExit("--coder rans applies to the single-tensor workloads")
+    tensor_bench = bench_decode_rans if args.coder == "rans" else bench_decode
     if args.workload == "tensor_4096":
-        res, coded = bench_decode(args, "tensor_4096", 4, "unsigned", 8192, args.lanes or 32,
+        res, coded = tensor_bench(args, "tensor_4096", 4, "unsigned", 8192, args.lanes or 32,
                                   args.replicas or 16, "bf16")
     elif args.workload in ("tensor_2048", "tensor_2048_u8"):
-        res, coded = bench_decode(args, "tensor_2048", 8, "asymmetric", 4096, args.lanes or 32,
+        res, coded = tensor_bench(args, "tensor_2048", 8, "asymmetric", 4096, args.lanes or 32,
                                   args.replicas or 64, "u8" if args.workload.endswith("u8") else "bf16")
     elif args.workload in ("phi3_stack", "mistral_stack"):
         res = bench_gemv(args, args.workload, args.batch, args.clip_sigma)
@@ -557,7 +680,7 @@ def main():
     res["gpu"] = torch.cuda.get_device_name(0)
     if coded is not None and not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline(coded)
+        res["cpu_baseline"] = cpu_baseline_rans(coded) if args.coder == "rans" else cpu_baseline(coded)
     print(json.dumps(res), flush=True)
 
 

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libentro.so")
-SOURCES = ["entro_decode.hip", "entro_lut.cpp", "entro_encode.cpp", "entro_rans.cpp"]
+SOURCES = ["entro_decode.hip", "entro_rans.hip", "entro_lut.cpp", "entro_encode.cpp", "entro_rans.cpp"]
 ARCH = os.environ.get("ENTRO_OFFLOAD_ARCH", "gfx950")
 
 
