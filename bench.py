@@ -117,26 +117,49 @@ def code_tensor(spec, bits, scheme, chunk, lanes, refill_steps, clip_sigma=0.0, 
 # CPU baseline: the oracle, as it stands
 # --------------------------------------------------------------------------
 
-def cpu_baseline(coded: Coded, budget_s: float = 12.0):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(coded: Coded, budget_s: float = 12.0, single_budget_s: float = 4.0):
+    """The oracle's C decoder over host threads (the chunk-parallel CPU decode
+    of EntroLLM), plus numpy dequant; also one thread alone."""
     from oracle import ccodec
     from oracle.dequant import dequant_bf16
 
+    def rate(threads, budget):
+        n_done, reps, t_dec = 0, 0, 0.0
+        t0 = time.perf_counter()
+        while True:
+            ta = time.perf_counter()
+            q = ccodec.decode(coded.words, coded.offs, coded.lengths, coded.n, coded.chunk, coded.lanes,
+                              threads=threads, refill_steps=coded.refill_steps, ahead=coded.ahead)
+            t_dec += time.perf_counter() - ta
+            dequant_bf16(q, coded.scale, coded.zp)
+            n_done += coded.n
+            reps += 1
+            if time.perf_counter() - t0 >= budget:
+                break
+        dt = time.perf_counter() - t0
+        return n_done / dt / 1e9, n_done / t_dec / 1e9, reps, dt
+
     threads = min(16, os.cpu_count() or 1)
-    n_done = 0
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        q = ccodec.decode(coded.words, coded.offs, coded.lengths, coded.n, coded.chunk, coded.lanes,
-                          threads=threads, refill_steps=coded.refill_steps, ahead=coded.ahead)
-        dequant_bf16(q, coded.scale, coded.zp)
-        n_done += coded.n
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(n_done / dt / 1e9, 4), "unit": "Gsym/s", "cores": threads, "kind": "oracle",
+    v, vd, reps, dt = rate(threads, budget_s)
+    v1, vd1, reps1, dt1 = rate(1, single_budget_s)
+    return {"value": round(v, 4), "unit": "Gsym/s", "cores": threads, "kind": "oracle",
             "sample": f"{reps} x one {coded.rows}x{coded.cols} tensor ({coded.n} codes): bit-serial C decode "
-                      f"over {threads} host threads + numpy bf16 dequant, {dt:.1f} s wall"}
+                      f"over {threads} host threads + numpy bf16 dequant (one thread), {dt:.1f} s wall",
+            "decode_only_value": round(vd, 4),
+            "single_thread_value": round(v1, 4), "single_thread_decode_only_value": round(vd1, 4),
+            "single_thread_sample": f"{reps1} x the same tensor with the decode on 1 thread, {dt1:.1f} s wall",
+            "nproc": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 # --------------------------------------------------------------------------
@@ -144,6 +167,12 @@ def cpu_baseline(coded: Coded, budget_s: float = 12.0):
 # --------------------------------------------------------------------------
 
 def time_steps(step, steps, warmup):
+    """Warm-up, then the timed region: `steps` steps back to back between two
+    events on the launch stream, synchronized on both sides (-> total ms).
+    Then the same number of steps again, each between its own event pair, for
+    the per-launch durations: events between launches keep the next launch
+    from starting right behind the previous one, so they stay out of the
+    timed region."""
     import torch
 
     for _ in range(warmup):
@@ -152,10 +181,15 @@ def time_steps(step, steps, warmup):
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    per = []
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = ev0.elapsed_time(ev1)
+    per = []
     for _ in range(steps):
         e_a = torch.cuda.Event(enable_timing=True)
         e_b = torch.cuda.Event(enable_timing=True)
@@ -163,10 +197,7 @@ def time_steps(step, steps, warmup):
         step()
         e_b.record(stream)
         per.append((e_a, e_b))
-    ev1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = ev0.elapsed_time(ev1)
     per_ms = [a.elapsed_time(b) for a, b in per]
     return total_ms, per_ms, wall
 
@@ -176,6 +207,71 @@ def flush_mall(torch):
     buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
     return buf
+
+
+def launch_pct(per_ms):
+    p10, p50, p90 = np.percentile(np.asarray(per_ms, dtype=np.float64), [10, 50, 90])
+    return {"launch_ms_p10": round(float(p10), 5), "launch_ms_p50": round(float(p50), 5),
+            "launch_ms_p90": round(float(p90), 5)}
+
+
+def device_info(torch):
+    """GPU name, CU count (torch) and the agent's maximum clock (rocminfo)."""
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": torch.cuda.get_device_name(0), "compute_units": int(props.multi_processor_count),
+            "arch": getattr(props, "gcnArchName", "")}
+    try:
+        import subprocess
+
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+        gpu, clk = False, None
+        for line in out.splitlines():
+            t = line.strip()
+            if t.startswith("Name:") and "gfx" in t:
+                gpu = True
+            if gpu and t.startswith("Max Clock Freq. (MHz):"):
+                clk = int(t.split(":", 1)[1].split()[0])
+                break
+        info["max_clock_mhz"] = clk
+    except Exception as e:   # rocminfo missing or slow: the clock is context only
+        info["max_clock_mhz"] = None
+        info["clock_error"] = type(e).__name__
+    return info
+
+
+def device_copy_gbps(torch, nbytes=256 << 20, reps=10):
+    """A plain device-to-device copy of nbytes (read + write counted), median."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(5)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return 2.0 * nbytes / (float(np.median(ts)) * 1e-3) / 1e9
+
+
+def single_call_us(torch, step, reps=20):
+    """Latency of one call (median of reps, data warm in cache)."""
+    step()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return round(float(np.median(ts)) * 1e3, 2)
 
 
 # --------------------------------------------------------------------------
@@ -244,8 +340,10 @@ def bench_decode(args, workload, bits, scheme, chunk, lanes, replicas, mode):
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic / (launch_ms * 1e-3) / 1e9, 1)},
         "kernel": {"name": "ecw_decode_kernel", "launches_per_step": 1, "avg_launch_ms": round(launch_ms, 5),
-                   "algorithmic_bytes_per_launch": bytes_step, "src_sha": kernel_src_sha()},
+                   **launch_pct(per_ms), "algorithmic_bytes_per_launch": bytes_step, "src_sha": kernel_src_sha()},
     }
+    if args.single_latency:   # extra launches of the same kernel: kept out of the default (profiled) run
+        res["single_tensor_us"] = single_call_us(torch, lambda: fn(descs[:1], ptrs[:1], status.data_ptr()))
     return res, coded
 
 
@@ -360,8 +458,10 @@ def bench_decode_rans(args, workload, bits, scheme, chunk, lanes, replicas, mode
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
         "kernel": {"name": "ecr_kernel", "launches_per_step": 1, "avg_launch_ms": round(launch_ms, 5),
-                   "algorithmic_bytes_per_launch": bytes_step, "src_sha": kernel_src_sha()},
+                   **launch_pct(per_ms), "algorithmic_bytes_per_launch": bytes_step, "src_sha": kernel_src_sha()},
     }
+    if args.single_latency:
+        res["single_tensor_us"] = single_call_us(torch, lambda: fn(descs[:1], ptrs[:1], status.data_ptr()))
     return res, rc
 
 
@@ -525,6 +625,7 @@ def bench_gemv(args, workload, batch, clip_sigma=0.0):
         "hbm_bytes_per_token": int(hbm_bytes),
         "eff_GBps": round(hbm_bytes / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(hbm_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_ms_pct": {k.replace("launch_", "step_"): v for k, v in launch_pct(per_ms).items()},
     }
     return res
 
@@ -600,6 +701,7 @@ def bench_stack_decode(args, workload, mode):
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(bytes_step / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None},
         "kernel": {"name": "ecw_decode_kernel", "launches_per_step": launches, "avg_call_ms": round(call_ms, 5),
+                   **{k.replace("launch_", "call_"): v for k, v in launch_pct(per_ms).items()},
                    "algorithmic_bytes_per_step": bytes_step, "src_sha": kernel_src_sha()},
     }
     return res
@@ -646,6 +748,8 @@ def main():
                     help="GEMV workloads: target chunk size in weights (rounded to whole rows)")
     ap.add_argument("--coder", default="huffman", choices=["huffman", "rans"],
                     help="tensor workloads: canonical Huffman (ECW v1) or interleaved rANS (ECR v1) streams")
+    ap.add_argument("--single-latency", action="store_true",
+                    help="tensor workloads: also time one call on a single tensor (median of 20, warm)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -678,6 +782,12 @@ def main():
     else:
         raise SystemExit(f"unknown workload {args.workload}")
     res["gpu"] = torch.cuda.get_device_name(0)
+    res["device"] = device_info(torch)
+    copy = device_copy_gbps(torch)
+    res["device_copy_GBps"] = round(copy, 1)
+    ach = res.get("roofline", {}).get("achieved") or res.get("eff_GBps")
+    if ach:
+        res["frac_of_device_copy"] = round(float(ach) / copy, 4)
     if coded is not None and not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline_rans(coded) if args.coder == "rans" else cpu_baseline(coded)
