@@ -61,7 +61,7 @@ class Tensor(ctypes.Structure):
                 ("lanes", ctypes.c_uint32), ("sym_bits", ctypes.c_uint32),
                 ("max_len", ctypes.c_uint32), ("lut_bytes", ctypes.c_uint64),
                 ("max_chunk_words", ctypes.c_uint32), ("refill_steps", ctypes.c_uint32),
-                ("refill_ahead", ctypes.c_uint32)]
+                ("refill_ahead", ctypes.c_uint32), ("out_cached", ctypes.c_uint32)]
 
 
 class RansTensor(ctypes.Structure):

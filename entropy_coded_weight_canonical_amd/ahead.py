@@ -14,7 +14,10 @@ A block is a run of whole chunks: with row-aligned chunks (chunk a multiple
 of the row length) a block of chunks is a block of rows, decoded through a
 descriptor that covers only those chunks of the full stream.  Small blocks
 keep the staging buffers cache-resident between the decode and the multiply;
-``block_elems=None`` decodes whole matrices.
+``block_elems=None`` decodes whole matrices.  The staging decodes are issued
+with ``out_cached`` set (ordinary stores instead of the streaming stores of a
+standalone decode), so that the multiply finds the weights in L2 or the
+last-level cache.
 
 Every decode runs in the library's kernels (``decode_dequant``); this module
 only orders launches on torch streams (all at the default priority).  A whole
@@ -36,7 +39,14 @@ def chunk_range_view(desc: Tensor, c0: int, c1: int) -> Tensor:
         raise ValueError("empty or out-of-range chunk range")
     return Tensor(desc.d_lut, desc.d_words, int(desc.d_chunk_bit_off) + 8 * c0, desc.n_words, n,
                   desc.chunk_symbols, desc.lanes, desc.sym_bits, desc.max_len, desc.lut_bytes,
-                  desc.max_chunk_words, desc.refill_steps, desc.refill_ahead)
+                  desc.max_chunk_words, desc.refill_steps, desc.refill_ahead, desc.out_cached)
+
+
+def _staging(desc: Tensor) -> Tensor:
+    """The staged weights are read by the next matrix product right away:
+    decode them with ordinary stores, which leave them in the caches."""
+    desc.out_cached = 1
+    return desc
 
 
 class DecodeAhead:
@@ -61,15 +71,16 @@ class DecodeAhead:
             if int(d.n_symbols) != r * c:
                 raise ValueError(f"tensor of {d.n_symbols} symbols does not match shape {r}x{c}")
             chunk = int(d.chunk_symbols)
+            n_chunks = -(-r * c // chunk)
             if block_elems is None or chunk % c or r * c <= block_elems:
-                self.blocks.append((m, 0, r, d))
+                self.blocks.append((m, 0, r, _staging(chunk_range_view(d, 0, n_chunks))))
                 continue
             rows_per_chunk = chunk // c
-            n_chunks = -(-r * c // chunk)
             per = max(1, int(block_elems) // chunk)
             for c0 in range(0, n_chunks, per):
                 c1 = min(n_chunks, c0 + per)
-                self.blocks.append((m, c0 * rows_per_chunk, min(r, c1 * rows_per_chunk), chunk_range_view(d, c0, c1)))
+                self.blocks.append((m, c0 * rows_per_chunk, min(r, c1 * rows_per_chunk),
+                                    _staging(chunk_range_view(d, c0, c1))))
         self.depth = min(depth, len(self.blocks))
         elems = max((r1 - r0) * self.shapes[m][1] for m, r0, r1, _ in self.blocks)
         self.bufs = [torch.empty(elems, dtype=torch.bfloat16, device=device) for _ in range(self.depth)]

@@ -150,16 +150,22 @@ __device__ __forceinline__ uint32_t lookup(const uint32_t *lut, uint32_t hi, uin
   return e;
 }
 
-template <int MODE>
+template <int MODE, int CP>
 __device__ __forceinline__ void emit(void *base, uint64_t k, uint32_t e) {
-  if (MODE == kModeU8) __builtin_nontemporal_store((uint8_t)(e >> 16), static_cast<uint8_t *>(base) + k);
-  else __builtin_nontemporal_store((uint16_t)(e >> 16), static_cast<uint16_t *>(base) + k);
+  if (CP == kStoreCached) {
+    if (MODE == kModeU8) static_cast<uint8_t *>(base)[k] = (uint8_t)(e >> 16);
+    else static_cast<uint16_t *>(base)[k] = (uint16_t)(e >> 16);
+  } else if (MODE == kModeU8) {
+    __builtin_nontemporal_store((uint8_t)(e >> 16), static_cast<uint8_t *>(base) + k);
+  } else {
+    __builtin_nontemporal_store((uint16_t)(e >> 16), static_cast<uint16_t *>(base) + k);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // generic path: one wavefront task, words read from global memory, all checks
 // ---------------------------------------------------------------------------
-template <int MODE, int LOG2W, int BATCH>
+template <int MODE, int LOG2W, int BATCH, int CP>
 __device__ void task_generic(const TensorArg &d, const uint32_t *lut, uint32_t K, uint64_t task, uint32_t batch,
                              uint32_t l_min) {
   constexpr uint32_t W = 1u << LOG2W;
@@ -255,7 +261,7 @@ __device__ void task_generic(const TensorArg &d, const uint32_t *lut, uint32_t K
             }
           }
         } else {
-          emit<MODE>(d.out, sym0 + ((uint64_t)t << LOG2W) + j, e);
+          emit<MODE, CP>(d.out, sym0 + ((uint64_t)t << LOG2W) + j, e);
         }
       }
       if (MODE == kModeGemv) {
@@ -422,7 +428,7 @@ __device__ __forceinline__ void consume_pair(uint32_t &hi, uint32_t &lo, uint32_
   hi = nhi;
   n -= lab;
   if (PACK) {
-    store_pair<MODE>(outr, voff, soff, pack_ab<MODE>(eA, eB), sel);
+    store_pair<MODE, OutT::cp>(outr, voff, soff, pack_ab<MODE>(eA, eB), sel);
   } else {
     store_out<OutT>(outr, voff, soff, eA);
     store_out<OutT>(outr, voff, soff + boff, eB);
@@ -788,7 +794,7 @@ __device__ __forceinline__ uint32_t tab_pairs64(const uint32_t *lut, uint32_t K,
       lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
       hi = nhi;
       n = sub_len(n, e2.y);
-      store_pair<MODE>(outr, voffp, soff, e2.x, sel);
+      store_pair<MODE, OutT::cp>(outr, voffp, soff, e2.x, sel);
     }
     for (; soff != stop; soff += 2u * B) {
       u32x2 e2 = pair_lookup<MODE>(lut, K, hi, lo);
@@ -807,7 +813,7 @@ __device__ __forceinline__ uint32_t tab_pairs64(const uint32_t *lut, uint32_t K,
       lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
       hi = nhi;
       n = sub_len(n, e2.y);
-      store_pair<MODE>(outr, voffp, soff, e2.x, sel);
+      store_pair<MODE, OutT::cp>(outr, voffp, soff, e2.x, sel);
     }
   }
   if (steps & 1u) {   // last step alone
@@ -862,7 +868,7 @@ __device__ __forceinline__ uint32_t tab_pairs32(const uint32_t *lut, uint32_t K,
       lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
       hi = nhi;
       n = sub_len(n, e2.y);
-      store_pair<MODE>(outr, voffp, soff, e2.x, sel);
+      store_pair<MODE, OutT::cp>(outr, voffp, soff, e2.x, sel);
     }
     for (; soff != stop; soff += 2u * B) {
       u32x2 e2 = pair_lookup<MODE>(lut, K, hi, lo);
@@ -883,7 +889,7 @@ __device__ __forceinline__ uint32_t tab_pairs32(const uint32_t *lut, uint32_t K,
       lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
       hi = nhi;
       n = sub_len(n, e2.y);
-      store_pair<MODE>(outr, voffp, soff, e2.x, sel);
+      store_pair<MODE, OutT::cp>(outr, voffp, soff, e2.x, sel);
     }
   }
   if (steps & 1u) {
@@ -1181,7 +1187,7 @@ __device__ bool stage_task(const TensorArg &d, uint64_t task, uint32_t *stage, u
   return true;
 }
 
-template <int MODE, int LOG2W, int BATCH>
+template <int MODE, int LOG2W, int BATCH, int CP>
 __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K, const u32x2 *ptab,
                             uint64_t task, uint32_t *stage, uint32_t stage_words, uint32_t prio,
                             const uint32_t *xl, uint32_t batch, uint32_t l_min) {
@@ -1206,7 +1212,7 @@ __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K,
     return true;
   } else {
   const uint32_t steps = d.chunk >> LOG2W;
-  typedef typename std::conditional<MODE == kModeU8, uint8_t, uint16_t>::type OutT;
+  typedef OutElem<typename std::conditional<MODE == kModeU8, uint8_t, uint16_t>::type, CP> OutT;
   // output of the task: G full chunks from chunk c0 on
   OutT *outp = static_cast<OutT *>(d.out) + c0 * d.chunk;
   const uint32_t out_bytes = (uint32_t)min((uint64_t)G * d.chunk * sizeof(OutT), (uint64_t)0xFFFFFFF0u);
@@ -1251,7 +1257,7 @@ __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K,
 // occupancy query does not see this).  The budget below keeps two workgroups
 // per CU; the few values it pushes out are per-task setup, reloaded from
 // VGPR lanes outside the decode loops.
-template <int MODE, int LOG2W, int BATCH>
+template <int MODE, int LOG2W, int BATCH, int CP>
 __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKernelSgprs))) void ecw_kernel(
     const LaunchArgs a) {
   constexpr uint32_t G = 64u >> LOG2W;
@@ -1334,7 +1340,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
           gemv_sliced64<BATCH>(d, lut, K, have, stage + st.al, rfl(st.nw), xl, task * (d.chunk / d.cols), a.batch,
                                threadIdx.x & 63u, rfl(early_pairs(d.ahead, d.chunk >> 6, l_min)));
       if (flags) atomicOr(d.status, flags);
-      if (mine && !have) task_generic<MODE, LOG2W, BATCH>(d, lut, K, task, a.batch, l_min);
+      if (mine && !have) task_generic<MODE, LOG2W, BATCH, CP>(d, lut, K, task, a.batch, l_min);
       continue;
     }
     if (task >= d.n_tasks) continue;
@@ -1346,9 +1352,9 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
       // priority 3, 2 over the wavefront's first task, 1, 0 over the second
       const uint32_t k = bt - bt0, prio = k == 0u ? 3u : (k == 1u ? 1u : 0u);
       if (full)
-        done = task_staged<MODE, LOG2W, BATCH>(d, lut, K, ptab, task, stage, stage_words, prio, xl, a.batch, l_min);
+        done = task_staged<MODE, LOG2W, BATCH, CP>(d, lut, K, ptab, task, stage, stage_words, prio, xl, a.batch, l_min);
     }
-    if (!done) task_generic<MODE, LOG2W, BATCH>(d, lut, K, task, a.batch, l_min);
+    if (!done) task_generic<MODE, LOG2W, BATCH, CP>(d, lut, K, task, a.batch, l_min);
   }
 }
 
@@ -1595,7 +1601,7 @@ static entro_status check_tensor(const entro_tensor &t) {
   if (t.chunk_symbols == 0 || t.chunk_symbols % t.lanes || t.chunk_symbols > kMaxChunk) return ENTRO_E_FORMAT;
   if (t.sym_bits != 4 && t.sym_bits != 8) return ENTRO_E_FORMAT;
   if (t.max_len < 1 || t.max_len > kMaxCodeLen) return ENTRO_E_FORMAT;
-  if (t.refill_steps > 2 || t.refill_ahead > 1) return ENTRO_E_FORMAT;
+  if (t.refill_steps > 2 || t.refill_ahead > 1 || t.out_cached > 1) return ENTRO_E_FORMAT;
   if (t.n_symbols == 0) return ENTRO_OK;
   if (!t.d_lut || !t.d_words || !t.d_chunk_bit_off) return ENTRO_E_INVAL;
   const uint64_t nc = (t.n_symbols + t.chunk_symbols - 1) / t.chunk_symbols;
@@ -1603,9 +1609,9 @@ static entro_status check_tensor(const entro_tensor &t) {
   return ENTRO_OK;
 }
 
-template <int MODE, int L, int BATCH>
+template <int MODE, int L, int BATCH, int CP>
 static hipError_t launch_one(uint32_t total_btasks, LaunchArgs &a, size_t dyn, hipStream_t s) {
-  auto kern = ecw_kernel<MODE, L, BATCH>;
+  auto kern = ecw_kernel<MODE, L, BATCH, CP>;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
@@ -1625,21 +1631,21 @@ static hipError_t launch_one(uint32_t total_btasks, LaunchArgs &a, size_t dyn, h
   return hipGetLastError();
 }
 
-template <int MODE, int BATCH>
+template <int MODE, int BATCH, int CP>
 static hipError_t launch_w(uint32_t log2w, uint32_t total_btasks, LaunchArgs &a, size_t dyn, hipStream_t s) {
   switch (log2w) {
-    case 0: return launch_one<MODE, 0, BATCH>(total_btasks, a, dyn, s);
-    case 1: return launch_one<MODE, 1, BATCH>(total_btasks, a, dyn, s);
-    case 2: return launch_one<MODE, 2, BATCH>(total_btasks, a, dyn, s);
-    case 3: return launch_one<MODE, 3, BATCH>(total_btasks, a, dyn, s);
-    case 4: return launch_one<MODE, 4, BATCH>(total_btasks, a, dyn, s);
-    case 5: return launch_one<MODE, 5, BATCH>(total_btasks, a, dyn, s);
-    default: return launch_one<MODE, 6, BATCH>(total_btasks, a, dyn, s);
+    case 0: return launch_one<MODE, 0, BATCH, CP>(total_btasks, a, dyn, s);
+    case 1: return launch_one<MODE, 1, BATCH, CP>(total_btasks, a, dyn, s);
+    case 2: return launch_one<MODE, 2, BATCH, CP>(total_btasks, a, dyn, s);
+    case 3: return launch_one<MODE, 3, BATCH, CP>(total_btasks, a, dyn, s);
+    case 4: return launch_one<MODE, 4, BATCH, CP>(total_btasks, a, dyn, s);
+    case 5: return launch_one<MODE, 5, BATCH, CP>(total_btasks, a, dyn, s);
+    default: return launch_one<MODE, 6, BATCH, CP>(total_btasks, a, dyn, s);
   }
 }
 
 // Validate everything, then enqueue launches of up to 32 tensors that share
-// a lane count.
+// a lane count and an output cache policy.
 static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *outs,
                         const entro_gemv_item *g, uint32_t batch, uint32_t *d_status, hipStream_t s) {
   if (n == 0) return ENTRO_OK;
@@ -1670,6 +1676,7 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
     std::memset(&a, 0, sizeof a);
     a.batch = batch;
     uint32_t total = 0, log2w = 0, k = 0;
+    bool cached = false;   // output cache policy of the launch (GEMV: unused)
     uint64_t stage_need = 0, lut_need = 0, x_fit_words = 0;
     bool x_slices = false;
     bool stage_known = true, want_pairs = false;
@@ -1677,8 +1684,9 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
       const entro_tensor &x = t[i];
       if (x.n_symbols == 0) continue;
       const uint32_t lw = log2u(x.lanes);
-      if (k == 0) log2w = lw;
-      else if (lw != log2w) break;
+      const bool xc = mode != kModeGemv && x.out_cached;
+      if (k == 0) log2w = lw, cached = xc;
+      else if (lw != log2w || xc != cached) break;
       TensorArg &d = a.t[k];
       d.lut = static_cast<const uint32_t *>(x.d_lut);
       d.words = x.d_words;
@@ -1754,10 +1762,12 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
     a.state_word = (uint32_t)(dyn / 4u);
     dyn += 16u;
     hipError_t err;
-    if (mode == kModeU8) err = launch_w<kModeU8, 1>(log2w, total, a, dyn, s);
-    else if (mode == kModeBf16) err = launch_w<kModeBf16, 1>(log2w, total, a, dyn, s);
-    else if (batch == 1) err = launch_w<kModeGemv, 1>(log2w, total, a, dyn, s);
-    else err = launch_w<kModeGemv, 8>(log2w, total, a, dyn, s);
+    if (mode == kModeU8 && cached) err = launch_w<kModeU8, 1, kStoreCached>(log2w, total, a, dyn, s);
+    else if (mode == kModeU8) err = launch_w<kModeU8, 1, kStoreNT>(log2w, total, a, dyn, s);
+    else if (mode == kModeBf16 && cached) err = launch_w<kModeBf16, 1, kStoreCached>(log2w, total, a, dyn, s);
+    else if (mode == kModeBf16) err = launch_w<kModeBf16, 1, kStoreNT>(log2w, total, a, dyn, s);
+    else if (batch == 1) err = launch_w<kModeGemv, 1, kStoreNT>(log2w, total, a, dyn, s);
+    else err = launch_w<kModeGemv, 8, kStoreNT>(log2w, total, a, dyn, s);
     if (err != hipSuccess) return ENTRO_E_HIP;
   }
   return ENTRO_OK;

@@ -29,23 +29,38 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 
 __device__ __forceinline__ bool lds_at_zero() { return lds_addr(dyn_lds) == 0u; }
 
+// Output element of the decode kernels: the value's type and the cache
+// policy of its stores (kStoreNT or kStoreCached).
+template <typename T, int CP>
+struct OutElem {
+  T v;
+  static constexpr int cp = CP;
+};
+
 // One output element per lane through a buffer resource: per-lane byte
 // offset in a vector register, per-step offset in a scalar register.
 // The value sits in bits [31:16] ([23:16] for codes) of the table entry and
 // goes out with the d16_hi store forms, so no shift is spent on it.  (The
 // outputs are never read back by the kernel, so the compiler needs no
-// knowledge of these writes; they are streamed (nt) like every output
-// store, see kStoreNT.)  The compiler does not insert hazard wait
+// knowledge of these writes; they carry OutT's cache policy like every
+// output store.)  The compiler does not insert hazard wait
 // states around inline assembly, and a vector-memory instruction must not
 // read an SGPR in the 5 cycles after a VALU wrote it (as v_readlane does when
 // the resource comes back from a spill), hence the s_nop 4.
 template <typename OutT>
 __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t e) {
-  if (sizeof(OutT) == 1)
+  static_assert(OutT::cp == kStoreNT || OutT::cp == kStoreCached, "cache policy");
+  if (sizeof(OutT) == 1 && OutT::cp == kStoreNT)
     asm volatile("s_nop 4\n\tbuffer_store_byte_d16_hi %0, %1, %2, %3 offen nt"
                  : : "v"(e), "v"(voff), "s"(r), "s"(soff));
-  else
+  else if (sizeof(OutT) == 1)
+    asm volatile("s_nop 4\n\tbuffer_store_byte_d16_hi %0, %1, %2, %3 offen"
+                 : : "v"(e), "v"(voff), "s"(r), "s"(soff));
+  else if (OutT::cp == kStoreNT)
     asm volatile("s_nop 4\n\tbuffer_store_short_d16_hi %0, %1, %2, %3 offen nt"
+                 : : "v"(e), "v"(voff), "s"(r), "s"(soff));
+  else
+    asm volatile("s_nop 4\n\tbuffer_store_short_d16_hi %0, %1, %2, %3 offen"
                  : : "v"(e), "v"(voff), "s"(r), "s"(soff));
 }
 
@@ -66,13 +81,13 @@ __device__ __forceinline__ uint32_t pair_sel(uint32_t lane) {
   return (lane & 1u) ? 0x03020706u : 0x05040100u;
 }
 
-template <int MODE>
+template <int MODE, int CP>
 __device__ __forceinline__ void store_pair(__amdgpu_buffer_rsrc_t r, uint32_t voffp, uint32_t soff, uint32_t ab,
                                            uint32_t sel) {
   const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)ab, 0xB1, 0xF, 0xF, false);
   const uint32_t v = __builtin_amdgcn_perm(nb, ab, sel);
-  if (MODE == kModeU8) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, r, (int)voffp, (int)soff, kStoreNT);
-  else __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)voffp, (int)soff, kStoreNT);
+  if (MODE == kModeU8) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, r, (int)voffp, (int)soff, CP);
+  else __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)voffp, (int)soff, CP);
 }
 
 __device__ __forceinline__ uint32_t pair_voff(uint32_t lane_off, uint32_t lane, uint32_t W, uint32_t elem) {

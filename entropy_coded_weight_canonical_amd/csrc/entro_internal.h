@@ -58,6 +58,10 @@ constexpr uint32_t kStaticLds = 256u;            // margin for static LDS (the k
 // in the caches (measured on the 4096x4096 4-bit to bf16 workload: 131 ->
 // 115 us per launch).
 constexpr int kStoreNT = 2;
+// Ordinary stores, for outputs that a consumer reads right after the decode
+// (decode-ahead staging, entro_tensor.out_cached): they stay in L2 and the
+// last-level cache instead of going out to HBM first.
+constexpr int kStoreCached = 0;
 constexpr uint32_t kStageSlack = 72;            // words after each wavefront's staging area (reads of a well-formed stream stay within 64 words past its chunk)
 
 // A block task is kWaves consecutive wavefront tasks of one tensor; a

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
     const RansLaunch a) {
   constexpr uint32_t W = 1u << LOG2W;
   constexpr uint32_t G = 64u >> LOG2W;
-  typedef typename std::conditional<MODE == kModeU8, uint8_t, uint16_t>::type OutT;
+  typedef OutElem<typename std::conditional<MODE == kModeU8, uint8_t, uint16_t>::type, kStoreNT> OutT;
   u32x2 *tab = reinterpret_cast<u32x2 *>(dyn_lds);
   uint32_t &state = reinterpret_cast<uint32_t *>(dyn_lds)[a.state_word];
   const uint32_t wave = rfl(threadIdx.x >> 6);
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
       for (; t + 2u <= sfull; t += 2u) {
         const uint32_t eA = rans_step<LOG2W>(x, pu0, pu1, upper, true);
         const uint32_t eB = rans_step<LOG2W>(x, pu0, pu1, upper, true);
-        store_pair<MODE>(outr, voffp, t * B, pack_ab<MODE>(eA, eB), sel);
+        store_pair<MODE, kStoreNT>(outr, voffp, t * B, pack_ab<MODE>(eA, eB), sel);
       }
       if (t < sfull) store_out<OutT>(outr, lane_off * (uint32_t)sizeof(OutT), rfl(t * B),
                                      rans_step<LOG2W>(x, pu0, pu1, upper, true));

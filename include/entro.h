@@ -116,6 +116,11 @@ typedef struct {
   uint32_t refill_steps;          /* steps per refill decision the stream was encoded
                                      with: 1 or 2 (0 is read as 1)                       */
   uint32_t refill_ahead;          /* 1 if the stream was encoded refilling ahead, else 0 */
+  uint32_t out_cached;            /* decode entry points: 0 streams the outputs past the
+                                     caches (nothing reads them soon); 1 writes them with
+                                     ordinary stores, so that a consumer right after the
+                                     call (decode-ahead staging) finds them in L2 or the
+                                     last-level cache.  Values only; the GEMV ignores it */
 } entro_tensor;
 
 /* Operands of the fused GEMV for one tensor, read as a [rows][cols] row-major

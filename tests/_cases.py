@@ -59,11 +59,14 @@ def upload(case: Case, device="cuda"):
                                    case.max_len, device=device, refill_steps=case.refill_steps, ahead=case.ahead)
 
 
-def run_decode(cases, mode="u8", device="cuda"):
-    """Decode ``cases`` in one call; returns (outputs as numpy, status numpy)."""
+def run_decode(cases, mode="u8", device="cuda", cached=None):
+    """Decode ``cases`` in one call; returns (outputs as numpy, status numpy).
+    ``cached``: per case, the descriptor's ``out_cached`` flag (default 0)."""
     import torch
 
     dts = [upload(c, device) for c in cases]
+    for d, f in zip(dts, cached or []):
+        d.desc.out_cached = int(f)
     dtype = torch.uint8 if mode == "u8" else torch.int16
     outs = [torch.empty(max(c.n, 1), dtype=dtype, device=device) for c in cases]
     if mode == "u8":

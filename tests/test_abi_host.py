@@ -198,6 +198,7 @@ def test_device_entry_points_validate_before_launch(lib):
     assert dec(max_len=17) == 3
     assert dec(refill_steps=3) == 3
     assert dec(refill_ahead=2) == 3
+    assert dec(out_cached=2) == 3
     assert dec(d_words=None) == 1
     assert lib.entro_decode(arr, 1, None, st, None) == 1
     assert lib.entro_decode(arr, 1, outs, None, None) == 1

@@ -131,6 +131,28 @@ def test_more_tensors_than_one_launch_and_mixed_lanes():
         assert np.array_equal(o, c.expected_bf16())
 
 
+def test_cached_output_stores_mixed_with_streamed():
+    """out_cached = 1 selects ordinary output stores; tensors of both policies
+    in one call are split into separate launches and both decode exactly
+    (full tasks and ragged tails, every lane count)."""
+    cases, flags = [], []
+    for i in range(28):
+        lanes = [1, 2, 4, 8, 16, 32, 64][i % 7]
+        bits = 4 if i % 2 else 8
+        chunk = lanes * (8 + 3 * (i % 3))
+        n = chunk * (4 + i % 3) + (11 * i) % chunk
+        q = fuzz_codes(700 + i, n, bits, CODE_KINDS[i % len(CODE_KINDS)])
+        cases.append(make_case(q, bits, chunk, lanes, scale=0.002 * (i + 1), zp=i % 16,
+                               refill_steps=1 + (i % 4 == 1), ahead=(i % 4 == 1)))
+        flags.append((i // 7) % 2)
+    say("28 tensors, cached and streamed output stores")
+    for mode in ("u8", "bf16"):
+        outs, st = run_decode(cases, mode, cached=flags)
+        assert (st == 0).all(), st
+        for c, o in zip(cases, outs):
+            assert np.array_equal(o, c.q if mode == "u8" else c.expected_bf16())
+
+
 def test_faults_are_flagged_not_fatal():
     import entropy_coded_weight_canonical_amd as ent
 
