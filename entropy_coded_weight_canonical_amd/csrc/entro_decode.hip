@@ -1165,8 +1165,8 @@ __device__ bool stage_task(const TensorArg &d, uint64_t task, uint32_t *stage, u
   const uint64_t task_words = (o_last - o_first) >> 5;
   if (task_words + 3u > stage_words) return false;
 
-  // stage the task's words, 16 bytes per lane per load, from a 16-byte
-  // aligned start; bytes past the tensor's words read as zero
+  // stage the task's words, 16 bytes per lane per load straight into LDS,
+  // from a 16-byte aligned start; bytes past the tensor's words land as zero
   const uint64_t w_first = o_first >> 5;
   const uint32_t al = (uint32_t)(w_first & 3u);
   const uint64_t base_al = w_first - al;
@@ -1175,8 +1175,7 @@ __device__ bool stage_task(const TensorArg &d, uint64_t task, uint32_t *stage, u
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void *)(d.words + base_al), (short)0, (int)nrec, 0x00020000);
   const uint32_t nvec = (uint32_t)((al + task_words + 3u) >> 2);
-  u32x4 *st4 = reinterpret_cast<u32x4 *>(stage);
-  for (uint32_t v = lane; v < nvec; v += 64u) st4[v] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(v * 16u), 0, 0);
+  lds_copy16(rsrc, rfl(lds_addr(stage)), rfl(nvec), lane);
 
   const uint64_t og = __shfl(o, (int)grp, 64), og1 = __shfl(o_next, (int)grp, 64);
   const uint32_t cs = al + (uint32_t)((og - o_first) >> 5);
@@ -1184,6 +1183,7 @@ __device__ bool stage_task(const TensorArg &d, uint64_t task, uint32_t *stage, u
   st.al = al;
   st.cs = cs;
   st.nw = nw;
+  wait_lds_copy();
   return true;
 }
 
@@ -1265,9 +1265,6 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
   // constant), the code table (lut_cap entries, a multiple of 4), the staged
   // activations of the GEMV (x_words), then one 16-byte aligned staging area
   // per wavefront
-  // K | entries << 8 of the current table, or 0 if it is unusable (kept in
-  // dynamic LDS so that the workgroup has no static LDS and dyn_lds is at 0)
-  uint32_t &lut_state = reinterpret_cast<uint32_t *>(dyn_lds)[a.state_word];
   u32x2 *ptab_area = reinterpret_cast<u32x2 *>(dyn_lds);
   uint32_t *lut = reinterpret_cast<uint32_t *>(dyn_lds) + (a.pair_bits ? 2u << a.pair_bits : 0u);
   uint32_t *xl = lut + a.lut_cap;
@@ -1286,25 +1283,25 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
     const TensorArg &d = a.t[ti];
     if (ti != cur) {
       __syncthreads();
-      if (threadIdx.x == 0) {
-        uint32_t k = 0;
-        if (d.lut_words >= kLutHeaderWords) {
-          const uint32_t h0 = d.lut[0], h1 = d.lut[1], ne = d.lut[2], l1 = d.lut[3];
-          const uint32_t kk = h1 & 0xFFu;
-          const uint32_t lmin = h1 >> 24;
-          if (h0 == kLutMagic && (h1 & 0x00FFFF00u) == d.expect_hdr && kk >= 1 && kk <= kSingleLevelMax &&
-              l1 == (1u << kk) && ne >= l1 && ne <= a.lut_cap && ne <= d.lut_words - kLutHeaderWords &&
-              lmin >= 1u && lmin <= kMaxCodeLen)
-            k = kk | (ne << 8) | (lmin << 24);
-        }
-        if (!k) atomicOr(d.status, kFLut);
-        lut_state = k;
+      // every wavefront checks the table header itself (scalar loads of the
+      // same 16 bytes), so the entries are fetched without waiting for a
+      // verdict published through LDS
+      uint32_t k = 0;
+      if (d.lut_words >= kLutHeaderWords) {
+        const uint32_t h0 = d.lut[0], h1 = d.lut[1], ne = d.lut[2], l1 = d.lut[3];
+        const uint32_t kk = h1 & 0xFFu;
+        const uint32_t lmin = h1 >> 24;
+        if (h0 == kLutMagic && (h1 & 0x00FFFF00u) == d.expect_hdr && kk >= 1 && kk <= kSingleLevelMax &&
+            l1 == (1u << kk) && ne >= l1 && ne <= a.lut_cap && ne <= d.lut_words - kLutHeaderWords &&
+            lmin >= 1u && lmin <= kMaxCodeLen)
+          k = kk | (ne << 8) | (lmin << 24);
       }
-      __syncthreads();
-      const uint32_t ne = (lut_state >> 8) & 0xFFFFu;
+      k = rfl(k);
+      if (!k && threadIdx.x == 0) atomicOr(d.status, kFLut);
+      const uint32_t ne = (k >> 8) & 0xFFFFu;
       for (uint32_t i = threadIdx.x; i < ne; i += kBlockThreads) lut[i] = kernel_entry<MODE>(d.lut[kLutHeaderWords + i]);
-      K = rfl(lut_state & 0xFFu);
-      l_min = rfl(lut_state >> 24);
+      K = k & 0xFFu;
+      l_min = k >> 24;
       cur = ti;
       __syncthreads();
       // two-code table for 4-bit tensors decoded in pairs

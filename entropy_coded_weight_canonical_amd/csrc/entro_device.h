@@ -29,6 +29,31 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 
 __device__ __forceinline__ bool lds_at_zero() { return lds_addr(dyn_lds) == 0u; }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copy n16 16-byte vectors of a buffer resource (vector v at byte offset
+// 16 v) to LDS (at byte address lds + 16 v) with loads that write LDS
+// directly: lane l of an instruction fills the l-th 16-byte slot after the
+// instruction's LDS base, 1 KiB per wavefront and instruction, so every load
+// of the copy is in flight at once and no registers hold the data.  Dwords
+// past the resource's range land as zero; lanes past n16 write nothing.  The
+// wavefront must wait_lds_copy() before it reads the copy.
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t n16, uint32_t lane) {
+  for (uint32_t v0 = 0; v0 < n16; v0 += 64u) {
+    const uint32_t v = v0 + lane;
+    if (v < n16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(uintptr_t)(lds + 16u * v0), 16, 16u * v, 0, 0, 0);
+  }
+}
+
+// s_waitcnt vmcnt(0): the copies above have landed in LDS (and, the counter
+// being shared, earlier stores have completed); the compiler barrier keeps
+// later LDS reads below it.
+__device__ __forceinline__ void wait_lds_copy() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
+}
+
 // Output element of the decode kernels: the value's type and the cache
 // policy of its stores (kStoreNT or kStoreCached).
 template <typename T, int CP>

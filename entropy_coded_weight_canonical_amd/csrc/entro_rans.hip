@@ -154,25 +154,23 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
       if (lane == 0) atomicOr(d.status, kFOffsets);
       continue;
     }
-    // stage the units (16-byte loads from a 16-byte aligned start; past the
-    // tensor's units reads as zero)
+    // stage the units (16-byte loads straight into LDS from a 16-byte aligned
+    // start; past the tensor's units lands as zero)
     const uint32_t al = (uint32_t)(o_first & 7u);
     const uint64_t base_al = o_first - al;
     const uint64_t bytes_left = (d.n_units - base_al) * 2u;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(d.units + base_al), (short)0, (int)min(bytes_left, (uint64_t)0xFFFFFFF0u), 0x00020000);
     const uint32_t nvec = (uint32_t)((al + task_units + 7u) >> 3);
-    u32x4 *st4 = reinterpret_cast<u32x4 *>(stage);
-    for (uint32_t v = lane; v < nvec; v += 64u) st4[v] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(v * 16u), 0, 0);
+    lds_copy16(rsrc, rfl(lds_addr(stage)), rfl(nvec), lane);
+    wait_lds_copy();
     // the range check works per dword: with an odd unit count the tensor's
-    // last unit shares its dword with the end of the range and read as zero
-    // above, so it is fetched alone (same wavefront: LDS writes stay in order)
+    // last unit shares its dword with the end of the range and landed as
+    // zero above, so it is fetched alone, after the copy has landed
     if ((d.n_units & 1u) && o_last == d.n_units && lane == 0u) {
       const uint32_t li = (uint32_t)(d.n_units - 1u - base_al);
       stage[li] = __builtin_amdgcn_raw_buffer_load_b16(rsrc, (int)(2u * li), 0, 0);
     }
-    // the units are read back as 16-bit values: keep the compiler from
-    // moving those reads above the vector stores (different types)
     asm volatile("" ::: "memory");
     // this lane's chunk: units [cs, cs + nu) of the staging area
     const uint64_t og = __shfl(o, (int)min(grp, nck - 1u), 64), og1 = __shfl(o_next, (int)min(grp, nck - 1u), 64);

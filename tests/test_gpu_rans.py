@@ -144,3 +144,29 @@ def test_odd_unit_counts_read_the_last_unit():
         assert (st == 0).all(), st
         for c, o in zip(cases, outs):
             assert np.array_equal(o, c.q if mode == "u8" else dequant_bf16(c.q, c.scale, c.zp))
+
+
+def test_edge_cases_in_one_call():
+    """An empty tensor between others, fewer codes than lanes, exactly one
+    step, a tensor of one code value (every state stays at L), chunks of one
+    step each, both lane counts, both code widths."""
+    one = np.full(300, 9, dtype=np.uint8)
+    cases = [RCase(fuzz_codes(31, 5, 4, "uniform"), 4, 64, 64),        # 5 codes, 64 lanes
+             RCase(fuzz_codes(32, 32, 8, "skewed"), 8, 32, 32),        # one full step
+             RCase(one, 4, 128, 32),                                   # a single code value
+             RCase(fuzz_codes(33, 64 * 7 + 3, 8, "peaked"), 8, 64, 64),  # one step per chunk, ragged tail
+             RCase(fuzz_codes(34, 33, 4, "skewed"), 4, 32, 32)]        # one step and one code
+    empty = RCase.__new__(RCase)
+    empty.q = np.zeros(0, dtype=np.uint8)
+    empty.bits, empty.chunk, empty.lanes, empty.scale, empty.zp = 4, 64, 32, np.float32(0.5), 8
+    empty.freqs = cases[0].freqs
+    empty.units, empty.offs = np.zeros(0, dtype=np.uint16), np.zeros(1, dtype=np.uint64)
+    empty.table = cases[0].table
+    cases.insert(2, empty)
+    say("rANS edge cases")
+    for mode in ("u8", "bf16"):
+        outs, st = run(cases, mode)
+        assert (st == 0).all(), st
+        for c, o in zip(cases, outs):
+            assert o.size == c.n
+            assert np.array_equal(o, c.q if mode == "u8" else dequant_bf16(c.q, c.scale, c.zp))
