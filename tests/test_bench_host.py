@@ -1,0 +1,84 @@
+"""Host-side pieces of bench.py: the one-GPU guard, launch statistics, the
+gate that keeps a stale traffic profile out of the JSON line, the coded-size
+accounting of both coders, and the CPU-baseline record (no GPU needed)."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert p.returncode == 2
+    msg = json.loads(p.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
+
+
+def test_launch_percentiles():
+    pct = bench.launch_pct([1.0, 2.0, 3.0, 4.0, 5.0, 6.0, 7.0, 8.0, 9.0, 10.0, 11.0])
+    assert pct == {"launch_ms_p10": 2.0, "launch_ms_p50": 6.0, "launch_ms_p90": 10.0}
+
+
+def test_traffic_profile_is_used_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_src_sha", lambda: "abc123")
+    (prof / "traffic_w_m.txt").write_text("# header: with a colon\nkernel_src_sha: abc123\n"
+                                          "hbm_bytes_per_launch: 1234567\n")
+    assert bench.read_traffic("w_m") == 1234567.0
+    (prof / "traffic_w_m.txt").write_text("kernel_src_sha: other\nhbm_bytes_per_launch: 1234567\n")
+    assert bench.read_traffic("w_m") is None
+    assert bench.read_traffic("missing") is None
+
+
+def test_kernel_source_hash_covers_every_kernel_source():
+    for p in bench.KERNEL_SOURCES:
+        assert os.path.exists(os.path.join(ROOT, p)), p
+    assert len(bench.kernel_src_sha()) == 16
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import entropy_coded_weight_canonical_amd as ent
+
+    try:
+        ent.load()
+    except ent.LibraryNotBuilt:
+        pytest.skip("library not built")
+    return ent
+
+
+def test_coded_size_accounting(lib):
+    """in_bytes counts the stream and the chunk offsets, as the roofline's
+    algorithmic bytes do; bits per weight follow from it."""
+    rng = np.random.default_rng(5)
+    q = np.clip(np.rint(rng.laplace(8, 1.2, size=(64, 512))), 0, 15).astype(np.uint8)
+    c = bench.Coded(q, np.float32(0.01), 8, "unsigned", 4, 12, 4096, 32, 64, 512, 2, ahead=True)
+    assert c.n_chunks == 8
+    assert c.in_bytes == 4 * c.words.size + 8 * 9
+    assert c.coded_bits_per_weight == pytest.approx(8.0 * c.in_bytes / q.size)
+    r = bench.RansCoded(q, np.float32(0.01), 8, 4, 4096, 32, 64, 512)
+    assert r.n_chunks == 8
+    assert r.in_bytes == 2 * r.units.size + 8 * 9
+    # each chunk carries at least its 32 lane states (two units each)
+    assert r.units.size >= 8 * 64
+
+
+def test_cpu_baseline_record(lib):
+    rng = np.random.default_rng(6)
+    q = np.clip(np.rint(rng.laplace(8, 1.0, size=(32, 256))), 0, 15).astype(np.uint8)
+    c = bench.Coded(q, np.float32(0.02), 8, "unsigned", 4, 12, 1024, 32, 32, 256, 2, ahead=True)
+    rec = bench.cpu_baseline(c, budget_s=0.2, single_budget_s=0.1)
+    assert rec["kind"] == "oracle" and rec["unit"] == "Gsym/s"
+    assert rec["value"] > 0 and rec["single_thread_value"] > 0 and rec["decode_only_value"] > 0
+    assert rec["cores"] >= 1 and rec["nproc"] >= 1 and isinstance(rec["cpu_model"], str)
