@@ -89,6 +89,14 @@ def load():
     if not os.path.exists(_LIB_PATH):
         raise LibraryNotBuilt(
             f"{_LIB_PATH} is missing; build it with `python -m entropy_coded_weight_canonical_amd.build`")
+    # The device entry points take torch's device pointers and streams, and
+    # torch ships its own HIP runtime (same soname).  Load torch first, so that
+    # the library binds to that runtime: loaded the other way round, the
+    # process holds two HIP runtimes and torch's pointers are foreign to ours.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(_LIB_PATH)
     P, U32, U64, SZ = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_size_t
     lib.entro_lut_bytes.argtypes = [P]

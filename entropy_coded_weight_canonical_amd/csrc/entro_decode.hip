@@ -1284,8 +1284,12 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
     if (ti != cur) {
       __syncthreads();
       // every wavefront checks the table header itself (scalar loads of the
-      // same 16 bytes), so the entries are fetched without waiting for a
-      // verdict published through LDS
+      // same 16 bytes), and the entries are fetched together with it, as many
+      // as the caller's table holds (at most the launch's table capacity): a
+      // table whose header fails the checks is then not used
+      const uint32_t ne_fetch = min(a.lut_cap, d.lut_words > kLutHeaderWords ? d.lut_words - kLutHeaderWords : 0u);
+      for (uint32_t i = threadIdx.x; i < ne_fetch; i += kBlockThreads)
+        lut[i] = kernel_entry<MODE>(d.lut[kLutHeaderWords + i]);
       uint32_t k = 0;
       if (d.lut_words >= kLutHeaderWords) {
         const uint32_t h0 = d.lut[0], h1 = d.lut[1], ne = d.lut[2], l1 = d.lut[3];
@@ -1298,8 +1302,6 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
       }
       k = rfl(k);
       if (!k && threadIdx.x == 0) atomicOr(d.status, kFLut);
-      const uint32_t ne = (k >> 8) & 0xFFFFu;
-      for (uint32_t i = threadIdx.x; i < ne; i += kBlockThreads) lut[i] = kernel_entry<MODE>(d.lut[kLutHeaderWords + i]);
       K = k & 0xFFu;
       l_min = k >> 24;
       cur = ti;
@@ -1624,6 +1626,9 @@ static hipError_t launch_one(uint32_t total_btasks, LaunchArgs &a, size_t dyn, h
   const uint32_t per_block = (uint32_t)((total_btasks + slots - 1) / slots);
   a.btasks_per_block = per_block < 1 ? 1 : per_block;
   const uint32_t grid = (total_btasks + a.btasks_per_block - 1) / a.btasks_per_block;
+  // clear an error left by an earlier call (ours, such as a failed occupancy
+  // query, or the caller's): the check below then sees this launch alone
+  (void)hipGetLastError();
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlockThreads), dyn, s, a);
   return hipGetLastError();
 }
@@ -1785,6 +1790,9 @@ static hipError_t launch_gemm(GemmArgs &a, size_t dyn, hipStream_t s) {
   const uint32_t per_block = (uint32_t)((a.total_tiles + slots - 1) / slots);
   a.tiles_per_block = per_block < 1 ? 1 : per_block;
   const uint32_t grid = (a.total_tiles + a.tiles_per_block - 1) / a.tiles_per_block;
+  // clear an error left by an earlier call (ours, such as a failed occupancy
+  // query, or the caller's): the check below then sees this launch alone
+  (void)hipGetLastError();
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlockThreads), dyn, s, a);
   return hipGetLastError();
 }

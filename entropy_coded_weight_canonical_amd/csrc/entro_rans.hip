@@ -306,6 +306,9 @@ static entro_status run_rans(int mode, const entro_rans_tensor *t, size_t n, voi
     const uint32_t per_block = (uint32_t)((total + slots - 1) / slots);
     a.btasks_per_block = per_block < 1 ? 1 : per_block;
     const uint32_t grid = (total + a.btasks_per_block - 1) / a.btasks_per_block;
+    // clear an error left by an earlier call (ours, such as a failed occupancy
+    // query, or the caller's): the check below then sees this launch alone
+    (void)hipGetLastError();
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlockThreads), dyn, s, a);
     if (hipGetLastError() != hipSuccess) return ENTRO_E_HIP;
   }

@@ -342,3 +342,34 @@ def test_gemv_mistral_shapes_sampled_layer(batch, refill_steps):
     for c, x, y in zip(cases, xs, ys):
         ref = ogemv.gemv_f64(c.expected_bf16().reshape(c.rows, c.cols), x)
         assert ogemv.rel_err(y, ref) <= 1e-2
+
+
+def test_library_loaded_before_torch_shares_torchs_runtime():
+    """Loading the library before importing torch must not leave the process
+    with a second HIP runtime (torch ships its own): a child process loads
+    the library first, then decodes a small tensor from torch memory."""
+    import subprocess
+
+    code = r"""
+import numpy as np
+import entropy_coded_weight_canonical_amd as ent
+ent.load()
+import torch
+from oracle import ccodec, huffman, quant
+from synth import fuzz_codes
+q = fuzz_codes(9, 5000, 4, "skewed")
+L = huffman.code_lengths(quant.histogram(q, 4), 12)
+lut = ent.lut_build(L, 4, 12, np.float32(0.01), 8)
+w, o = ccodec.encode(q, L, 1024, 32)
+t = ent.DeviceTensor.upload(lut, w, o, q.size, 1024, 32, 4, 12)
+out = torch.empty(q.size, dtype=torch.uint8, device="cuda")
+st = torch.zeros(1, dtype=torch.int32, device="cuda")
+ent.decode([t.desc], [out.data_ptr()], st.data_ptr())
+torch.cuda.synchronize()
+assert int(st.item()) == 0 and np.array_equal(out.cpu().numpy(), q)
+print("child ok")
+"""
+    root = __import__("os").path.dirname(__import__("os").path.dirname(__import__("os").path.abspath(__file__)))
+    say("library loaded before torch, in a child process")
+    p = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert p.returncode == 0 and "child ok" in p.stdout, p.stderr[-2000:]
