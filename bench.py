@@ -36,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MAX_TENSORS_PER_LAUNCH = 32   # the library batches up to 32 tensors per kernel launch
 METRIC = "decoded Gsym/s + effective HBM GB/s (% of peak); fused decode+GEMV ms/token"
 KERNEL_SOURCES = ["entropy_coded_weight_canonical_amd/csrc/entro_decode.hip",
                   "entropy_coded_weight_canonical_amd/csrc/entro_device.h",
@@ -168,11 +169,12 @@ def cpu_baseline(coded: Coded, budget_s: float = 12.0, single_budget_s: float = 
 
 def time_steps(step, steps, warmup):
     """Warm-up, then the timed region: `steps` steps back to back between two
-    events on the launch stream, synchronized on both sides (-> total ms).
-    Then the same number of steps again, each between its own event pair, for
-    the per-launch durations: events between launches keep the next launch
-    from starting right behind the previous one, so they stay out of the
-    timed region."""
+    events on the launch stream, synchronized on both sides (-> total ms; its
+    average per launch is what the roofline uses).  Then the same number of
+    steps again, each between its own event pair, for the spread of single
+    launches (p10/p50/p90): events between launches keep the next launch from
+    starting right behind the previous one and add a few microseconds each,
+    so they stay out of the timed region."""
     import torch
 
     for _ in range(warmup):
@@ -313,8 +315,9 @@ def bench_decode(args, workload, bits, scheme, chunk, lanes, replicas, mode):
     n_sym = coded.n * replicas
     out_b = coded.n * (1 if mode == "u8" else 2)
     bytes_step = replicas * (coded.in_bytes + out_b)
-    launch_ms = float(np.mean(per_ms))
-    achieved = bytes_step / (launch_ms * 1e-3) / 1e9
+    launches = -(-replicas // MAX_TENSORS_PER_LAUNCH)
+    launch_ms = ms / launches   # the timed region's average launch
+    achieved = (bytes_step / launches) / (launch_ms * 1e-3) / 1e9   # per launch
     traffic = read_traffic(f"{workload}_{mode}")
     res = {
         "metric": METRIC,
@@ -339,8 +342,9 @@ def bench_decode(args, workload, bits, scheme, chunk, lanes, replicas, mode):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic / (launch_ms * 1e-3) / 1e9, 1)},
-        "kernel": {"name": "ecw_decode_kernel", "launches_per_step": 1, "avg_launch_ms": round(launch_ms, 5),
-                   **launch_pct(per_ms), "algorithmic_bytes_per_launch": bytes_step, "src_sha": kernel_src_sha()},
+        "kernel": {"name": "ecw_decode_kernel", "launches_per_step": launches, "avg_launch_ms": round(launch_ms, 5),
+                   **{"event_bracketed_" + k.replace("launch_", "step_"): v for k, v in launch_pct(per_ms).items()},
+                   "algorithmic_bytes_per_launch": bytes_step // launches, "src_sha": kernel_src_sha()},
     }
     if args.single_latency:   # extra launches of the same kernel: kept out of the default (profiled) run
         res["single_tensor_us"] = single_call_us(torch, lambda: fn(descs[:1], ptrs[:1], status.data_ptr()))
@@ -433,8 +437,9 @@ def bench_decode_rans(args, workload, bits, scheme, chunk, lanes, replicas, mode
     ms = total_ms / args.steps
     n_sym = rc.n * replicas
     bytes_step = replicas * (rc.in_bytes + rc.n * (1 if mode == "u8" else 2))
-    launch_ms = float(np.mean(per_ms))
-    achieved = bytes_step / (launch_ms * 1e-3) / 1e9
+    launches = -(-replicas // MAX_TENSORS_PER_LAUNCH)
+    launch_ms = ms / launches   # the timed region's average launch
+    achieved = (bytes_step / launches) / (launch_ms * 1e-3) / 1e9   # per launch
     res = {
         "metric": METRIC,
         "value": round(n_sym / (ms * 1e-3) / 1e9, 3),
@@ -457,8 +462,9 @@ def bench_decode_rans(args, workload, bits, scheme, chunk, lanes, replicas, mode
         "hbm_frac": round(bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
-        "kernel": {"name": "ecr_kernel", "launches_per_step": 1, "avg_launch_ms": round(launch_ms, 5),
-                   **launch_pct(per_ms), "algorithmic_bytes_per_launch": bytes_step, "src_sha": kernel_src_sha()},
+        "kernel": {"name": "ecr_kernel", "launches_per_step": launches, "avg_launch_ms": round(launch_ms, 5),
+                   **{"event_bracketed_" + k.replace("launch_", "step_"): v for k, v in launch_pct(per_ms).items()},
+                   "algorithmic_bytes_per_launch": bytes_step // launches, "src_sha": kernel_src_sha()},
     }
     if args.single_latency:
         res["single_tensor_us"] = single_call_us(torch, lambda: fn(descs[:1], ptrs[:1], status.data_ptr()))
@@ -675,8 +681,8 @@ def bench_stack_decode(args, workload, mode):
     _keep = flush_mall(torch)
     total_ms, per_ms, wall = time_steps(step, args.steps, args.warmup)
     ms = total_ms / args.steps
-    call_ms = float(np.mean(per_ms))
-    launches = -(-len(specs) // 32)   # one lane count: up to 32 tensors per launch
+    call_ms = ms   # one call per step: the timed region's average call
+    launches = -(-len(specs) // MAX_TENSORS_PER_LAUNCH)   # one lane count in the stack
     bits = 8.0 * sum(c.in_bytes for c in coded.values()) / sum(c.n for c in coded.values())
     res = {
         "metric": METRIC,
@@ -701,7 +707,7 @@ def bench_stack_decode(args, workload, mode):
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(bytes_step / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None},
         "kernel": {"name": "ecw_decode_kernel", "launches_per_step": launches, "avg_call_ms": round(call_ms, 5),
-                   **{k.replace("launch_", "call_"): v for k, v in launch_pct(per_ms).items()},
+                   **{"event_bracketed_" + k.replace("launch_", "call_"): v for k, v in launch_pct(per_ms).items()},
                    "algorithmic_bytes_per_step": bytes_step, "src_sha": kernel_src_sha()},
     }
     return res
