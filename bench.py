@@ -760,7 +760,7 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU only; --gpus must be 1"}))
         raise SystemExit(2)
     import torch
 
