@@ -16,6 +16,11 @@ ecw        chunked, lane-interleaved stream: pure-Python encoder and a
 ccodec     the same encoder / decoder in plain C (``codec.c``) for full sizes
 dequant    code -> fp32 -> bf16 (round to nearest even)
 gemv       float64 GEMV on dequantized weights, and the error metric
+rans       interleaved rANS coder of the same codes: frequency quantizer,
+           encoder and lockstep decoder (small inputs)
+groupwise  group-wise quantizer, for the tensor-level versus group-wise study
+entropy_study  code entropy, Huffman mean length and side information of
+           every workload under both quantizers
 
 Parity status (what pins each function; see the tests named in each module):
 every function listed above is pinned by tests that do not call it back
