@@ -1140,11 +1140,13 @@ struct Staged {
   uint32_t al, cs, nw;
 };
 
-// Copy the words of wavefront task `task` (64 / W consecutive chunks) into
-// the wavefront's LDS area; false (nothing usable staged) if the offsets are
-// malformed or the words do not fit.
+// Start copying the words of wavefront task `task` (64 / W consecutive
+// chunks) into the wavefront's LDS area; false (nothing usable staged) if the
+// offsets are malformed or the words do not fit.  The copy is in flight on
+// return: wait_lds_copy() before reading it (stage_task does both).
 template <int LOG2W>
-__device__ bool stage_task(const TensorArg &d, uint64_t task, uint32_t *stage, uint32_t stage_words, Staged &st) {
+__device__ bool stage_task_issue(const TensorArg &d, uint64_t task, uint32_t *stage, uint32_t stage_words,
+                                 Staged &st) {
   constexpr uint32_t W = 1u << LOG2W;
   constexpr uint32_t G = 64u / W;
   const uint32_t lane = threadIdx.x & 63u;
@@ -1183,14 +1185,20 @@ __device__ bool stage_task(const TensorArg &d, uint64_t task, uint32_t *stage, u
   st.al = al;
   st.cs = cs;
   st.nw = nw;
-  wait_lds_copy();
   return true;
+}
+
+template <int LOG2W>
+__device__ bool stage_task(const TensorArg &d, uint64_t task, uint32_t *stage, uint32_t stage_words, Staged &st) {
+  const bool ok = stage_task_issue<LOG2W>(d, task, stage, stage_words, st);
+  wait_lds_copy();
+  return ok;
 }
 
 template <int MODE, int LOG2W, int BATCH, int CP>
 __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K, const u32x2 *ptab,
                             uint64_t task, uint32_t *stage, uint32_t stage_words, uint32_t prio,
-                            const uint32_t *xl, uint32_t batch, uint32_t l_min) {
+                            const uint32_t *xl, uint32_t batch, uint32_t l_min, int pre, const Staged &pst) {
   constexpr uint32_t W = 1u << LOG2W;
   constexpr uint32_t G = 64u / W;
   const uint32_t lane = threadIdx.x & 63u;
@@ -1199,8 +1207,14 @@ __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K,
   const uint64_t c0 = task * G;
   const uint64_t n_words = d.n_words;
 
-  Staged st;
-  if (!stage_task<LOG2W>(d, task, stage, stage_words, st)) return false;
+  // the staging may have been issued before the table switch (pre >= 0)
+  Staged st = pst;
+  if (pre < 0) {
+    if (!stage_task<LOG2W>(d, task, stage, stage_words, st)) return false;
+  } else {
+    wait_lds_copy();
+    if (!pre) return false;
+  }
   const uint32_t al = st.al, cs = st.cs, nw = st.nw;
   if constexpr (MODE == kModeGemv) {
     // one chunk (LOG2W == 6) of d.chunk / cols whole rows
@@ -1281,6 +1295,19 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
     uint32_t ti = 0;
     while (ti + 1 < a.n_tensors && a.btask_begin[ti + 1] <= bt) ++ti;
     const TensorArg &d = a.t[ti];
+    // On a table switch, start staging this wavefront's task first: its loads
+    // are in flight while the workgroup fetches and builds the tables (the
+    // staging area is the wavefront's own; if the task later takes another
+    // path the copy is simply not used, and copies land in issue order).
+    int pre = -1;
+    Staged pst{0u, 0u, 0u};
+    if (ti != cur && stage_words) {
+      const uint64_t t0 = (uint64_t)(bt - a.btask_begin[ti]) * kWaves + wave;
+      const bool sliced = MODE == kModeGemv && BATCH != 1 && a.x_slice &&
+                          (uint64_t)(d.cols >> 1) * XSlots<BATCH>::n > a.x_words;
+      const bool full = t0 < d.n_tasks && (t0 + 1) * G <= d.n_chunks && (t0 + 1) * G * (uint64_t)d.chunk <= d.n_symbols;
+      if (full && !sliced) pre = stage_task_issue<LOG2W>(d, t0, stage, stage_words, pst) ? 1 : 0;
+    }
     if (ti != cur) {
       __syncthreads();
       // every wavefront checks the table header itself (scalar loads of the
@@ -1351,10 +1378,14 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
       // priority 3, 2 over the wavefront's first task, 1, 0 over the second
       const uint32_t k = bt - bt0, prio = k == 0u ? 3u : (k == 1u ? 1u : 0u);
       if (full)
-        done = task_staged<MODE, LOG2W, BATCH, CP>(d, lut, K, ptab, task, stage, stage_words, prio, xl, a.batch, l_min);
+        done = task_staged<MODE, LOG2W, BATCH, CP>(d, lut, K, ptab, task, stage, stage_words, prio, xl, a.batch, l_min,
+                                                   pre, pst);
     }
     if (!done) task_generic<MODE, LOG2W, BATCH, CP>(d, lut, K, task, a.batch, l_min);
   }
+  // a copy issued ahead for a task that took another path may still be in
+  // flight: let it land while the workgroup's LDS is still its own
+  wait_lds_copy();
 }
 
 // ---------------------------------------------------------------------------
