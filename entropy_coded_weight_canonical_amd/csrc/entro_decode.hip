@@ -1155,15 +1155,36 @@ __device__ bool stage_task_issue(const TensorArg &d, uint64_t task, uint32_t *st
   const uint64_t n_words = d.n_words;
   (void)W;
 
-  // offsets of the task's G + 1 chunk boundaries: lane l < G holds the start
-  // of chunk c0 + l, the end of the task is loaded once for all lanes
-  const uint64_t o = d.offs[c0 + min(lane, G - 1u)];
-  const uint64_t o_last = rfl64(d.offs[c0 + G]);
-  const uint64_t o_down = __shfl_down(o, 1, 64);
-  const uint64_t o_next = lane + 1u < G ? o_down : o_last;
-  const bool bad = lane < G && ((o & 31u) || (o_next & 31u) || o_next < o || (o_next >> 5) > n_words);
-  if (__ballot(bad)) return false;
-  const uint64_t o_first = rfl64(__shfl(o, 0, 64));
+  // offsets of the task's G + 1 chunk boundaries
+  uint64_t o_first, o_last, og, og1;
+  if constexpr (G <= 2) {
+    // at most three, the same for every lane: scalar loads (read through the
+    // constant address space, which the offsets are for the kernel).  Their
+    // wait counter is not the vector-memory one, so waiting for them does not
+    // also wait for the stores of the wavefront's previous task.
+    const __attribute__((address_space(4))) uint64_t *co =
+        (const __attribute__((address_space(4))) uint64_t *)(uintptr_t)d.offs;
+    const uint64_t oA = co[c0], oB = co[c0 + 1u], oC = G == 2 ? co[c0 + 2u] : oB;
+    const bool bad = (oA & 31u) || (oB & 31u) || oB < oA || (oB >> 5) > n_words ||
+                     (G == 2 && ((oC & 31u) || oC < oB || (oC >> 5) > n_words));
+    if (bad) return false;
+    o_first = oA;
+    o_last = G == 2 ? oC : oB;
+    og = grp ? oB : oA;
+    og1 = grp ? oC : oB;
+  } else {
+    // lane l < G holds the start of chunk c0 + l, the end of the task is
+    // loaded once for all lanes
+    const uint64_t o = d.offs[c0 + min(lane, G - 1u)];
+    o_last = rfl64(d.offs[c0 + G]);
+    const uint64_t o_down = __shfl_down(o, 1, 64);
+    const uint64_t o_next = lane + 1u < G ? o_down : o_last;
+    const bool bad = lane < G && ((o & 31u) || (o_next & 31u) || o_next < o || (o_next >> 5) > n_words);
+    if (__ballot(bad)) return false;
+    o_first = rfl64(__shfl(o, 0, 64));
+    og = __shfl(o, (int)grp, 64);
+    og1 = __shfl(o_next, (int)grp, 64);
+  }
   const uint64_t task_words = (o_last - o_first) >> 5;
   if (task_words + 3u > stage_words) return false;
 
@@ -1179,7 +1200,6 @@ __device__ bool stage_task_issue(const TensorArg &d, uint64_t task, uint32_t *st
   const uint32_t nvec = (uint32_t)((al + task_words + 3u) >> 2);
   lds_copy16(rsrc, rfl(lds_addr(stage)), rfl(nvec), lane);
 
-  const uint64_t og = __shfl(o, (int)grp, 64), og1 = __shfl(o_next, (int)grp, 64);
   const uint32_t cs = al + (uint32_t)((og - o_first) >> 5);
   const uint32_t nw = (uint32_t)((og1 - og) >> 5);
   st.al = al;
