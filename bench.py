@@ -55,9 +55,10 @@ def kernel_src_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(name: str):
+def read_traffic(name: str, config: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None
-    if the kernel source changed since the counters were taken."""
+    if the kernel source changed since the counters were taken or the summary
+    was taken on another configuration (lanes, chunk, refill options, replicas)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
     if not os.path.exists(path):
         return None
@@ -67,12 +68,17 @@ def read_traffic(name: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_src_sha") != kernel_src_sha():
+    if kv.get("kernel_src_sha") != kernel_src_sha() or kv.get("config") != config:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def traffic_config(chunk, lanes, args, replicas) -> str:
+    """The configuration a traffic summary applies to (recorded in it)."""
+    return f"C={chunk} W={lanes} refill_steps={args.refill_steps} ahead={int(args.refill_ahead)} replicas={replicas}"
 
 
 # --------------------------------------------------------------------------
@@ -318,7 +324,7 @@ def bench_decode(args, workload, bits, scheme, chunk, lanes, replicas, mode):
     launches = -(-replicas // MAX_TENSORS_PER_LAUNCH)
     launch_ms = ms / launches   # the timed region's average launch
     achieved = (bytes_step / launches) / (launch_ms * 1e-3) / 1e9   # per launch
-    traffic = read_traffic(f"{workload}_{mode}")
+    traffic = read_traffic(f"{workload}_{mode}", traffic_config(chunk, lanes, args, replicas))
     res = {
         "metric": METRIC,
         "value": round(n_sym / (ms * 1e-3) / 1e9, 3),

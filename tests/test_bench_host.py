@@ -33,12 +33,23 @@ def test_traffic_profile_is_used_only_for_the_sources_it_was_taken_on(tmp_path, 
     prof.mkdir()
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "kernel_src_sha", lambda: "abc123")
-    (prof / "traffic_w_m.txt").write_text("# header: with a colon\nkernel_src_sha: abc123\n"
+    (prof / "traffic_w_m.txt").write_text("# header: with a colon\nconfig: C=1 W=2\nkernel_src_sha: abc123\n"
                                           "hbm_bytes_per_launch: 1234567\n")
-    assert bench.read_traffic("w_m") == 1234567.0
-    (prof / "traffic_w_m.txt").write_text("kernel_src_sha: other\nhbm_bytes_per_launch: 1234567\n")
-    assert bench.read_traffic("w_m") is None
-    assert bench.read_traffic("missing") is None
+    assert bench.read_traffic("w_m", "C=1 W=2") == 1234567.0
+    assert bench.read_traffic("w_m", "C=1 W=4") is None          # taken on another configuration
+    (prof / "traffic_w_m.txt").write_text("config: C=1 W=2\nkernel_src_sha: other\nhbm_bytes_per_launch: 1234567\n")
+    assert bench.read_traffic("w_m", "C=1 W=2") is None          # taken on other kernel sources
+    assert bench.read_traffic("missing", "C=1 W=2") is None
+
+
+def test_committed_traffic_summary_matches_the_default_command():
+    """The committed summary applies to the configuration bench.py runs by
+    default (it is null in the JSON line otherwise)."""
+    import argparse
+
+    a = argparse.Namespace(refill_steps=2, refill_ahead=1)
+    text = open(os.path.join(ROOT, "profiles", "traffic_tensor_4096_bf16.txt")).read()
+    assert f"config: {bench.traffic_config(8192, 32, a, 16)}" in text
 
 
 def test_kernel_source_hash_covers_every_kernel_source():
