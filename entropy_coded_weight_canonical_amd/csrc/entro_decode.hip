@@ -25,8 +25,8 @@
 // Two paths share that step:
 //   * staged: the workgroup is persistent and walks block tasks; a wavefront
 //     copies all words of its task (64/W consecutive chunks, contiguous in
-//     memory) into its LDS area with 16-byte buffer loads, then decodes from
-//     LDS.  The bit buffer is two 32-bit registers, left-aligned; refill and
+//     memory) into its LDS area with 16-byte loads that write LDS directly,
+//     then decodes from LDS.  The bit buffer is two 32-bit registers, left-aligned; refill and
 //     consume are v_alignbit / shift / or; the loop keeps word pointers and
 //     output addresses in scalar registers.
 //   * generic: any task (ragged last chunk, words beyond the staging area,
@@ -1812,8 +1812,6 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
       a.stage_words = (uint32_t)sw;
       dyn += (size_t)kWaves * (sw + kStageSlack) * 4u;
     }
-    a.state_word = (uint32_t)(dyn / 4u);
-    dyn += 16u;
     hipError_t err;
     if (mode == kModeU8 && cached) err = launch_w<kModeU8, 1, kStoreCached>(log2w, total, a, dyn, s);
     else if (mode == kModeU8) err = launch_w<kModeU8, 1, kStoreNT>(log2w, total, a, dyn, s);

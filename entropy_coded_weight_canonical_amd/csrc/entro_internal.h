@@ -76,7 +76,6 @@ struct LaunchArgs {
   uint32_t stage_words;                            // staging words per wavefront (0: none)
   uint32_t lut_cap;                                // table entries reserved in LDS
   uint32_t pair_bits;                              // index bits of the two-code table (0: none)
-  uint32_t state_word;                             // LDS word (from the dynamic base) of the table state
   uint32_t x_words;                                // LDS words of staged GEMV activations (0: none)
   uint32_t x_slice;                                // 1: activations too large for x_words go in slices
 };
