@@ -958,15 +958,12 @@ __device__ __forceinline__ float wave_sum63(float v) {
 template <int BATCH>
 struct XSlots { static constexpr uint32_t n = BATCH == 1 ? 1u : 8u; };
 
-// x[b][cols] (bf16, global) -> LDS.  One slot: dword q*64 + j holds
-// x[128q + j] | x[128q + 64 + j] << 16.  Eight slots: 16-byte unit
-// (2q + h)*64 + j holds that dword for b = 4h .. 4h+3, so a lane reads its
-// four slots with one conflict-free 16-byte read.
 // x[b][cols] (bf16, global) -> LDS for the pairs [q0, q0 + np) of a row.
 // One slot: dword (q - q0)*64 + j holds x[128q + j] | x[128q + 64 + j] << 16.
 // Eight slots: 16-byte unit (2(q - q0) + h)*64 + j holds that dword for
 // b = 4h .. 4h+3, so a lane reads its four slots with one conflict-free
-// 16-byte read.
+// 16-byte read.  This copy reads x two bytes at a time and works at any
+// alignment of x.
 template <int BATCH>
 __device__ void stage_x(uint32_t *xl, const uint16_t *x, uint32_t cols, uint32_t batch, uint32_t q0, uint32_t np) {
   const uint32_t units = np * 64u;
@@ -985,6 +982,71 @@ __device__ void stage_x(uint32_t *xl, const uint16_t *x, uint32_t cols, uint32_t
         }
         reinterpret_cast<u32x4 *>(xl)[(2u * q + h) * 64u + j] = v;
       }
+    }
+  }
+}
+
+// The same layout from a 16-byte aligned x (its rows then are too, cols
+// being a multiple of 128), in two halves so that the loads are in flight
+// while the workgroup does other work: x_load issues them into registers,
+// x_store writes the LDS layout.  Item s is eight consecutive columns of one
+// batch row in both halves of a 128-column block: columns 8g .. 8g + 7 and
+// 64 + 8g .. 64 + 8g + 7 (g = s & 7) of block q = s / (8 SB), slot
+// b = (s >> 3) % SB.  A thread holds at most kXItems items.
+constexpr uint32_t kXItems = 2;
+static_assert(kGemvXMaxBytes / 32u <= kXItems * kBlockThreads, "staged x: items per thread");
+static_assert(kGemvSlicePairs * 64u <= kXItems * kBlockThreads, "x slice: items per thread");
+
+struct XRegs {
+  u32x4 lo[kXItems], hi[kXItems];
+};
+
+__device__ __forceinline__ bool x_vec_ok(const uint16_t *x) { return ((uintptr_t)x & 15u) == 0u; }
+
+template <int BATCH>
+__device__ __forceinline__ void x_load(XRegs &r, const uint16_t *x, uint32_t cols, uint32_t batch, uint32_t q0,
+                                       uint32_t np) {
+  constexpr uint32_t SB = XSlots<BATCH>::n;
+  const uint32_t items = np * 8u * SB;
+#pragma unroll
+  for (uint32_t k = 0; k < kXItems; ++k) {
+    const uint32_t s = threadIdx.x + k * kBlockThreads;
+    const uint32_t g = s & 7u, b = (s >> 3) % SB, q = s / (8u * SB);
+    u32x4 va = {0u, 0u, 0u, 0u}, vb = va;
+    if (s < items && b < batch) {
+      const u32x4 *p = reinterpret_cast<const u32x4 *>(x + (uint64_t)b * cols + (q0 + q) * 128u + 8u * g);
+      va = p[0];
+      vb = p[8];   // 64 columns on
+    }
+    r.lo[k] = va;
+    r.hi[k] = vb;
+  }
+}
+
+template <int BATCH>
+__device__ __forceinline__ void x_store(uint32_t *xl, const XRegs &r, uint32_t np) {
+  constexpr uint32_t SB = XSlots<BATCH>::n;
+  const uint32_t items = np * 8u * SB;
+#pragma unroll
+  for (uint32_t k = 0; k < kXItems; ++k) {
+    const uint32_t s = threadIdx.x + k * kBlockThreads;
+    if (s >= items) continue;
+    const uint32_t g = s & 7u, b = (s >> 3) % SB, q = s / (8u * SB);
+    // dword for column 8g + m of the block: x[.. + 8g + m] | x[.. + 64 + 8g + m] << 16
+    uint32_t w[8];
+#pragma unroll
+    for (uint32_t m = 0; m < 4u; ++m) {
+      w[2u * m] = (r.lo[k][m] & 0xFFFFu) | (r.hi[k][m] << 16);
+      w[2u * m + 1u] = (r.lo[k][m] >> 16) | (r.hi[k][m] & 0xFFFF0000u);
+    }
+    if (SB == 1) {
+      u32x4 *dst = reinterpret_cast<u32x4 *>(xl + q * 64u + 8u * g);
+      dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+      dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+    } else {
+      uint32_t *dst = xl + ((2u * q + (b >> 2)) * 64u + 8u * g) * 4u + (b & 3u);
+#pragma unroll
+      for (uint32_t m = 0; m < 8u; ++m) dst[4u * m] = w[m];
     }
   }
 }
@@ -1109,10 +1171,24 @@ __device__ uint32_t gemv_sliced64(const TensorArg &d, const uint32_t *lut, uint3
   g.pa = lds_addr(sw);
 #pragma unroll
   for (uint32_t b = 0; b < SB; ++b) g.acc[b] = 0.f;
-  stage_x<BATCH>(xb, x, cols, batch, 0u, min(S, ppr));
-  if (total > 1u) {
-    const uint32_t s1 = 1u % nsl;
-    stage_x<BATCH>(xb + BUF, x, cols, batch, s1 * S, min(S, ppr - s1 * S));
+  // with x 16-byte aligned, the loads of slice gi + 2 are issued before the
+  // decode of slice gi + 1 and written to LDS after it
+  const bool vec = x_vec_ok(x);
+  XRegs xr;
+  const uint32_t s1 = 1u % nsl;
+  if (vec) {
+    XRegs x1;
+    x_load<BATCH>(xr, x, cols, batch, 0u, min(S, ppr));
+    if (total > 1u) x_load<BATCH>(x1, x, cols, batch, s1 * S, min(S, ppr - s1 * S));
+    x_store<BATCH>(xb, xr, min(S, ppr));
+    if (total > 1u) x_store<BATCH>(xb + BUF, x1, min(S, ppr - s1 * S));
+    if (total > 2u) {
+      const uint32_t s2 = 2u % nsl;
+      x_load<BATCH>(xr, x, cols, batch, s2 * S, min(S, ppr - s2 * S));
+    }
+  } else {
+    stage_x<BATCH>(xb, x, cols, batch, 0u, min(S, ppr));
+    if (total > 1u) stage_x<BATCH>(xb + BUF, x, cols, batch, s1 * S, min(S, ppr - s1 * S));
   }
   __syncthreads();
   for (uint32_t gi = 0; gi < total; ++gi) {
@@ -1127,7 +1203,15 @@ __device__ uint32_t gemv_sliced64(const TensorArg &d, const uint32_t *lut, uint3
     __syncthreads();
     if (gi + 2u < total) {
       const uint32_t s2 = (gi + 2u) % nsl;
-      stage_x<BATCH>(xb + (gi & 1u) * BUF, x, cols, batch, s2 * S, min(S, ppr - s2 * S));
+      if (vec) {
+        x_store<BATCH>(xb + (gi & 1u) * BUF, xr, min(S, ppr - s2 * S));
+        if (gi + 3u < total) {
+          const uint32_t s3 = (gi + 3u) % nsl;
+          x_load<BATCH>(xr, x, cols, batch, s3 * S, min(S, ppr - s3 * S));
+        }
+      } else {
+        stage_x<BATCH>(xb + (gi & 1u) * BUF, x, cols, batch, s2 * S, min(S, ppr - s2 * S));
+      }
     }
   }
   return have ? gemv_end_flags<BATCH>(g, lds_addr(sw), nw) : 0u;
@@ -1329,14 +1413,37 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
       if (full && !sliced) pre = stage_task_issue<LOG2W>(d, t0, stage, stage_words, pst) ? 1 : 0;
     }
     if (ti != cur) {
+      // activations of a GEMV tensor that may take the LDS path (W = 64,
+      // pairs, an even number of steps per row, all of x within its area):
+      // from an aligned x, loaded before the barrier and written to LDS
+      // after it, in flight together with the table fetch
+      const bool x_fit = MODE == kModeGemv && LOG2W == 6 && a.pair_bits && stage_words && (d.cols & 127u) == 0u &&
+                         (uint64_t)(d.cols >> 1) * XSlots<BATCH>::n <= a.x_words;
+      const bool x_vec = x_fit && x_vec_ok(d.x);
+      XRegs xr;
+      if (x_vec) x_load<BATCH>(xr, d.x, d.cols, a.batch, 0u, d.cols >> 7);
       __syncthreads();
       // every wavefront checks the table header itself (scalar loads of the
       // same 16 bytes), and the entries are fetched together with it, as many
       // as the caller's table holds (at most the launch's table capacity): a
       // table whose header fails the checks is then not used
       const uint32_t ne_fetch = min(a.lut_cap, d.lut_words > kLutHeaderWords ? d.lut_words - kLutHeaderWords : 0u);
-      for (uint32_t i = threadIdx.x; i < ne_fetch; i += kBlockThreads)
-        lut[i] = kernel_entry<MODE>(d.lut[kLutHeaderWords + i]);
+      if (((uintptr_t)d.lut & 15u) == 0u) {
+        // 16 bytes per load from an aligned table (the header is 16 bytes)
+        const uint32_t nv = ne_fetch >> 2;
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(d.lut + kLutHeaderWords);
+        for (uint32_t v = threadIdx.x; v < nv; v += kBlockThreads) {
+          const u32x4 e = src[v];
+          reinterpret_cast<u32x4 *>(lut)[v] =
+              u32x4{kernel_entry<MODE>(e[0]), kernel_entry<MODE>(e[1]), kernel_entry<MODE>(e[2]), kernel_entry<MODE>(e[3])};
+        }
+        for (uint32_t i = 4u * nv + threadIdx.x; i < ne_fetch; i += kBlockThreads)
+          lut[i] = kernel_entry<MODE>(d.lut[kLutHeaderWords + i]);
+      } else {
+        for (uint32_t i = threadIdx.x; i < ne_fetch; i += kBlockThreads)
+          lut[i] = kernel_entry<MODE>(d.lut[kLutHeaderWords + i]);
+      }
+      if (x_vec) x_store<BATCH>(xl, xr, d.cols >> 7);
       uint32_t k = 0;
       if (d.lut_words >= kLutHeaderWords) {
         const uint32_t h0 = d.lut[0], h1 = d.lut[1], ne = d.lut[2], l1 = d.lut[3];
@@ -1365,8 +1472,8 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
       // fits its area, else slices of it (eight batch slots)
       x_staged = x_sliced = false;
       if (MODE == kModeGemv && LOG2W == 6 && ptab && stage_words && (d.cols & 127u) == 0u) {
-        if ((uint64_t)(d.cols >> 1) * XSlots<BATCH>::n <= a.x_words) {
-          stage_x<BATCH>(xl, d.x, d.cols, a.batch, 0u, d.cols >> 7);
+        if (x_fit) {
+          if (!x_vec) stage_x<BATCH>(xl, d.x, d.cols, a.batch, 0u, d.cols >> 7);
           x_staged = true;
         } else if (BATCH != 1 && a.x_slice) {
           x_sliced = true;

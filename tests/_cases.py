@@ -59,12 +59,26 @@ def upload(case: Case, device="cuda"):
                                    case.max_len, device=device, refill_steps=case.refill_steps, ahead=case.ahead)
 
 
-def run_decode(cases, mode="u8", device="cuda", cached=None):
+def _offset_lut(dt, case: Case, offset: int, device):
+    """Point ``dt``'s descriptor at a copy of its table ``offset`` words into
+    a fresh allocation; returns the allocation (keep it alive)."""
+    import torch
+
+    buf = torch.zeros(case.lut.size + offset, dtype=torch.int32, device=device)
+    buf[offset:] = torch.from_numpy(np.ascontiguousarray(case.lut).view(np.int32)).to(device)
+    dt.desc.d_lut = buf.data_ptr() + 4 * offset
+    return buf
+
+
+def run_decode(cases, mode="u8", device="cuda", cached=None, lut_offset=0):
     """Decode ``cases`` in one call; returns (outputs as numpy, status numpy).
-    ``cached``: per case, the descriptor's ``out_cached`` flag (default 0)."""
+    ``cached``: per case, the descriptor's ``out_cached`` flag (default 0).
+    ``lut_offset`` (words) places the decode tables that far past a 256-byte
+    aligned allocation."""
     import torch
 
     dts = [upload(c, device) for c in cases]
+    keep = [_offset_lut(d, c, lut_offset, device) for d, c in zip(dts, cases)] if lut_offset else []
     for d, f in zip(dts, cached or []):
         d.desc.out_cached = int(f)
     dtype = torch.uint8 if mode == "u8" else torch.int16
@@ -86,12 +100,20 @@ def run_decode(cases, mode="u8", device="cuda", cached=None):
     return res, status.cpu().numpy().view(np.uint32)
 
 
-def run_gemv(cases, xs, batch, device="cuda"):
-    """Fused GEMV of ``cases`` (each with rows/cols) on bf16 inputs ``xs``."""
+def run_gemv(cases, xs, batch, device="cuda", x_offset=0, lut_offset=0):
+    """Fused GEMV of ``cases`` (each with rows/cols) on bf16 inputs ``xs``.
+    ``x_offset`` (elements) and ``lut_offset`` (words) place x and the decode
+    table that far past a 256-byte aligned allocation."""
     import torch
 
     dts = [upload(c, device) for c in cases]
-    dx = [torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device) for x in xs]
+    keep = [_offset_lut(d, c, lut_offset, device) for d, c in zip(dts, cases)] if lut_offset else []
+    dx = []
+    for x in xs:
+        flat = np.ascontiguousarray(x).view(np.int16).ravel()
+        buf = torch.zeros(flat.size + x_offset, dtype=torch.int16, device=device)
+        buf[x_offset:] = torch.from_numpy(flat).to(device)
+        dx.append(buf[x_offset:])
     dy = [torch.full((batch, max(c.rows, 1)), float("nan"), dtype=torch.float32, device=device) for c in cases]
     items = [ent.GemvItem(c.rows, c.cols, x.data_ptr(), y.data_ptr()) for c, x, y in zip(cases, dx, dy)]
     status = torch.zeros(len(cases), dtype=torch.int32, device=device)

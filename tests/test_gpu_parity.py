@@ -116,6 +116,25 @@ def test_edge_cases_in_one_batch():
             assert np.array_equal(o, exp)
 
 
+@pytest.mark.parametrize("lut_offset", [1, 2, 3])
+def test_decode_tables_at_any_word_alignment(lut_offset):
+    """Decode tables 4, 8 and 12 bytes past 16-byte alignment are fetched
+    entry by entry (aligned ones 16 bytes at a time): W = 32 and 64 with the
+    two-code table, 8-bit codes, a table whose entry count is not a multiple
+    of four, and the same outputs as from aligned tables."""
+    cases = [make_case(fuzz_codes(80, 8192 * 5 + 77, 4, "skewed"), 4, 8192, 32, refill_steps=2, ahead=True),
+             make_case(fuzz_codes(81, 4096 * 3, 4, "skewed"), 4, 4096, 64, refill_steps=2),
+             make_case(fuzz_codes(82, 30_001, 8, "peaked"), 8, 4096, 32),
+             make_case(fuzz_codes(83, 5000, 8, "uniform"), 8, 1024, 16)]
+    say(f"decode tables at word offset {lut_offset}")
+    for mode in ("u8", "bf16"):
+        outs, st = run_decode(cases, mode, lut_offset=lut_offset)
+        assert (st == 0).all(), st
+        for c, o in zip(cases, outs):
+            exp = c.q if mode == "u8" else c.expected_bf16()
+            assert np.array_equal(o, exp)
+
+
 def test_more_tensors_than_one_launch_and_mixed_lanes():
     cases = []
     for i in range(45):
@@ -297,6 +316,27 @@ def test_gemv_sliced_activations(batch, ahead):
     for c, x, y in zip(cases, xs, ys):
         ref = ogemv.gemv_f64(c.expected_bf16().reshape(c.rows, c.cols), x)
         assert ogemv.rel_err(y, ref) <= 1e-4
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_gemv_activations_and_tables_at_any_alignment(batch):
+    """x 2 bytes and the decode table 4 bytes past 16-byte alignment take the
+    element-wise copies; x at 16 bytes past it takes the 16-byte loads.  The
+    LDS path with all of x staged, the column-sliced path (batch 8, 5120
+    columns), an 8-bit tensor on the generic path, all within 1e-4 of the
+    float64 oracle at every placement."""
+    cases = [_gemv_case(37, 1024, 4, 71, refill_steps=2, ahead=True),
+             _gemv_case(70, 5120, 4, 72, refill_steps=2, ahead=True),
+             _gemv_case(33, 4096, 4, 73, rows_per_chunk=2, refill_steps=2),
+             _gemv_case(20, 512, 8, 74, refill_steps=2, ahead=True)]
+    xs = [activations_bf16("mistral_stack", 70 + i, c.cols, batch) for i, c in enumerate(cases)]
+    refs = [ogemv.gemv_f64(c.expected_bf16().reshape(c.rows, c.cols), x) for c, x in zip(cases, xs)]
+    for x_offset, lut_offset in [(1, 1), (1, 0), (0, 3), (8, 4), (0, 0)]:
+        say(f"gemv batch={batch} x offset {x_offset} table offset {lut_offset}")
+        ys, st = run_gemv(cases, xs, batch, x_offset=x_offset, lut_offset=lut_offset)
+        assert (st == 0).all(), st
+        for y, ref in zip(ys, refs):
+            assert ogemv.rel_err(y, ref) <= 1e-4
 
 
 @pytest.mark.parametrize("batch", [1, 3, 8])
