@@ -1309,7 +1309,6 @@ __device__ bool task_staged(const TensorArg &d, const uint32_t *lut, uint32_t K,
   const uint32_t grp = lane >> LOG2W;
   const uint32_t j = lane & (W - 1u);
   const uint64_t c0 = task * G;
-  const uint64_t n_words = d.n_words;
 
   // the staging may have been issued before the table switch (pre >= 0)
   Staged st = pst;
@@ -1391,14 +1390,24 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
   uint32_t *stage = xl + a.x_words + wave * (stage_words + kStageSlack);
   const u32x2 *ptab = nullptr;
   bool x_staged = false, x_sliced = false;
-  const uint32_t bt0 = blockIdx.x * a.btasks_per_block;
-  const uint32_t bt1 = min(bt0 + a.btasks_per_block, a.total_btasks);
+  // The workgroup's tasks: [g0, g1) of the launch's task space (the first
+  // tasks_r workgroups take one more than tasks_q), walked in rounds of up to
+  // kWaves tasks that stay within one tensor; wavefront w takes the w-th task
+  // of a round.  Workgroups thus differ by at most one task, and within one
+  // the wavefronts of each SIMD (w mod 4) share the tasks evenly.
+  const uint32_t b = blockIdx.x;
+  const uint32_t g0 = b * a.tasks_q + min(b, a.tasks_r);
+  const uint32_t g1 = g0 + a.tasks_q + (b < a.tasks_r ? 1u : 0u);
   uint32_t cur = 0xFFFFFFFFu;
   uint32_t K = 0, l_min = 1;
-  for (uint32_t bt = bt0; bt < bt1; ++bt) {
-    uint32_t ti = 0;
-    while (ti + 1 < a.n_tensors && a.btask_begin[ti + 1] <= bt) ++ti;
+  uint32_t ti = 0, round = 0;
+  for (uint32_t g = g0; g < g1; ++round) {
+    while (ti + 1 < a.n_tensors && a.task_begin[ti + 1] <= g) ++ti;
     const TensorArg &d = a.t[ti];
+    const uint32_t n_here = min(min(g1, a.task_begin[ti + 1]) - g, (uint32_t)kWaves);
+    const uint64_t task = (uint64_t)(g - a.task_begin[ti]) + wave;   // within the tensor
+    const bool mine = wave < n_here;
+    g += n_here;
     // On a table switch, start staging this wavefront's task first: its loads
     // are in flight while the workgroup fetches and builds the tables (the
     // staging area is the wavefront's own; if the task later takes another
@@ -1406,11 +1415,10 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
     int pre = -1;
     Staged pst{0u, 0u, 0u};
     if (ti != cur && stage_words) {
-      const uint64_t t0 = (uint64_t)(bt - a.btask_begin[ti]) * kWaves + wave;
       const bool sliced = MODE == kModeGemv && BATCH != 1 && a.x_slice &&
                           (uint64_t)(d.cols >> 1) * XSlots<BATCH>::n > a.x_words;
-      const bool full = t0 < d.n_tasks && (t0 + 1) * G <= d.n_chunks && (t0 + 1) * G * (uint64_t)d.chunk <= d.n_symbols;
-      if (full && !sliced) pre = stage_task_issue<LOG2W>(d, t0, stage, stage_words, pst) ? 1 : 0;
+      const bool full = mine && (task + 1) * G <= d.n_chunks && (task + 1) * G * (uint64_t)d.chunk <= d.n_symbols;
+      if (full && !sliced) pre = stage_task_issue<LOG2W>(d, task, stage, stage_words, pst) ? 1 : 0;
     }
     if (ti != cur) {
       // activations of a GEMV tensor that may take the LDS path (W = 64,
@@ -1482,10 +1490,8 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
       __syncthreads();
     }
     if (!K) continue;
-    const uint64_t task = (uint64_t)(bt - a.btask_begin[ti]) * kWaves + wave;
     if (MODE == kModeGemv && x_sliced) {
       // every wavefront of the workgroup takes part in the sliced walk
-      const bool mine = task < d.n_tasks;
       const bool full = mine && (task + 1) * G <= d.n_chunks && (task + 1) * G * (uint64_t)d.chunk <= d.n_symbols;
       Staged st{0u, 0u, 0u};
       const bool have = full && stage_task<LOG2W>(d, task, stage, stage_words, st);
@@ -1496,14 +1502,14 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
       if (mine && !have) task_generic<MODE, LOG2W, BATCH, CP>(d, lut, K, task, a.batch, l_min);
       continue;
     }
-    if (task >= d.n_tasks) continue;
+    if (!mine) continue;
     bool done = false;
     // streams encoded refilling ahead: the pair loops for W = 32, 64
     const bool ahead_ok = !d.ahead || (d.refill_steps == 2u && LOG2W >= 5);
     if (stage_words && (MODE != kModeGemv || x_staged) && ahead_ok) {
       const bool full = (task + 1) * G <= d.n_chunks && (task + 1) * G * (uint64_t)d.chunk <= d.n_symbols;
       // priority 3, 2 over the wavefront's first task, 1, 0 over the second
-      const uint32_t k = bt - bt0, prio = k == 0u ? 3u : (k == 1u ? 1u : 0u);
+      const uint32_t prio = round == 0u ? 3u : (round == 1u ? 1u : 0u);
       if (full)
         done = task_staged<MODE, LOG2W, BATCH, CP>(d, lut, K, ptab, task, stage, stage_words, prio, xl, a.batch, l_min,
                                                    pre, pst);
@@ -1767,7 +1773,7 @@ static entro_status check_tensor(const entro_tensor &t) {
 }
 
 template <int MODE, int L, int BATCH, int CP>
-static hipError_t launch_one(uint32_t total_btasks, LaunchArgs &a, size_t dyn, hipStream_t s) {
+static hipError_t launch_one(uint32_t total_tasks, LaunchArgs &a, size_t dyn, hipStream_t s) {
   auto kern = ecw_kernel<MODE, L, BATCH, CP>;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
@@ -1780,10 +1786,12 @@ static hipError_t launch_one(uint32_t total_btasks, LaunchArgs &a, size_t dyn, h
   const int lds_fit = (int)((kLdsPerCu - kLdsPlanReserve) / (dyn + kStaticLds));
   if (lds_fit >= 1 && per_cu > lds_fit) per_cu = lds_fit;
   if (cus < 1) cus = 1;
+  // one workgroup per slot (fewer if there are fewer tasks), the tasks
+  // spread over them evenly
   const uint64_t slots = (uint64_t)cus * (uint64_t)per_cu;
-  const uint32_t per_block = (uint32_t)((total_btasks + slots - 1) / slots);
-  a.btasks_per_block = per_block < 1 ? 1 : per_block;
-  const uint32_t grid = (total_btasks + a.btasks_per_block - 1) / a.btasks_per_block;
+  const uint32_t grid = (uint32_t)std::min<uint64_t>(slots, total_tasks);
+  a.tasks_q = total_tasks / grid;
+  a.tasks_r = total_tasks % grid;
   // clear an error left by an earlier call (ours, such as a failed occupancy
   // query, or the caller's): the check below then sees this launch alone
   (void)hipGetLastError();
@@ -1792,15 +1800,15 @@ static hipError_t launch_one(uint32_t total_btasks, LaunchArgs &a, size_t dyn, h
 }
 
 template <int MODE, int BATCH, int CP>
-static hipError_t launch_w(uint32_t log2w, uint32_t total_btasks, LaunchArgs &a, size_t dyn, hipStream_t s) {
+static hipError_t launch_w(uint32_t log2w, uint32_t total_tasks, LaunchArgs &a, size_t dyn, hipStream_t s) {
   switch (log2w) {
-    case 0: return launch_one<MODE, 0, BATCH, CP>(total_btasks, a, dyn, s);
-    case 1: return launch_one<MODE, 1, BATCH, CP>(total_btasks, a, dyn, s);
-    case 2: return launch_one<MODE, 2, BATCH, CP>(total_btasks, a, dyn, s);
-    case 3: return launch_one<MODE, 3, BATCH, CP>(total_btasks, a, dyn, s);
-    case 4: return launch_one<MODE, 4, BATCH, CP>(total_btasks, a, dyn, s);
-    case 5: return launch_one<MODE, 5, BATCH, CP>(total_btasks, a, dyn, s);
-    default: return launch_one<MODE, 6, BATCH, CP>(total_btasks, a, dyn, s);
+    case 0: return launch_one<MODE, 0, BATCH, CP>(total_tasks, a, dyn, s);
+    case 1: return launch_one<MODE, 1, BATCH, CP>(total_tasks, a, dyn, s);
+    case 2: return launch_one<MODE, 2, BATCH, CP>(total_tasks, a, dyn, s);
+    case 3: return launch_one<MODE, 3, BATCH, CP>(total_tasks, a, dyn, s);
+    case 4: return launch_one<MODE, 4, BATCH, CP>(total_tasks, a, dyn, s);
+    case 5: return launch_one<MODE, 5, BATCH, CP>(total_tasks, a, dyn, s);
+    default: return launch_one<MODE, 6, BATCH, CP>(total_tasks, a, dyn, s);
   }
 }
 
@@ -1847,6 +1855,11 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
       const bool xc = mode != kModeGemv && x.out_cached;
       if (k == 0) log2w = lw, cached = xc;
       else if (lw != log2w || xc != cached) break;
+      // the launch's task space stays below 2^31 tasks
+      const uint64_t chunks_per_wave = 64u >> lw;
+      const uint64_t tasks = ((x.n_symbols + x.chunk_symbols - 1) / x.chunk_symbols + chunks_per_wave - 1) / chunks_per_wave;
+      if (tasks > 0x7FFFFFFFull) return ENTRO_E_UNSUPPORTED;
+      if ((uint64_t)total + tasks > 0x7FFFFFFFull) break;
       TensorArg &d = a.t[k];
       d.lut = static_cast<const uint32_t *>(x.d_lut);
       d.words = x.d_words;
@@ -1874,13 +1887,9 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
       } else {
         d.out = outs[i];
       }
-      const uint64_t chunks_per_wave = 64u >> lw;
-      const uint64_t tasks = (d.n_chunks + chunks_per_wave - 1) / chunks_per_wave;
       d.n_tasks = (uint32_t)tasks;
-      const uint64_t nb = (tasks + kWaves - 1) / kWaves;
-      if ((uint64_t)total + nb > 0x7FFFFFFFull) return ENTRO_E_UNSUPPORTED;
-      a.btask_begin[k] = total;
-      total += (uint32_t)nb;
+      a.task_begin[k] = total;
+      total += (uint32_t)tasks;
       lut_need = std::max<uint64_t>(lut_need, d.lut_words > kLutHeaderWords ? d.lut_words - kLutHeaderWords : 0);
       if (x.max_chunk_words) stage_need = std::max<uint64_t>(stage_need, chunks_per_wave * x.max_chunk_words);
       else stage_known = false, stage_need = std::max<uint64_t>(stage_need, (x.n_words + tasks - 1) / tasks * 5 / 4 + 64);
@@ -1888,8 +1897,7 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
     }
     if (k == 0) continue;
     a.n_tensors = k;
-    a.total_btasks = total;
-    for (uint32_t r = k; r <= (uint32_t)kMaxTensorsPerLaunch; ++r) a.btask_begin[r] = total;
+    for (uint32_t r = k; r <= (uint32_t)kMaxTensorsPerLaunch; ++r) a.task_begin[r] = total;
     (void)stage_known;
     // LDS: the largest table of the launch, then the staging areas (room for
     // the largest task plus 16-byte alignment), within 160 KiB

@@ -64,15 +64,17 @@ constexpr int kStoreNT = 2;
 constexpr int kStoreCached = 0;
 constexpr uint32_t kStageSlack = 72;            // words after each wavefront's staging area (reads of a well-formed stream stay within 64 words past its chunk)
 
-// A block task is kWaves consecutive wavefront tasks of one tensor; a
-// wavefront task is 64 / lanes consecutive chunks.
+// A wavefront task is 64 / lanes consecutive chunks.  The tasks of the
+// launch's tensors, one after another, form its task space; workgroup b
+// takes tasks_q of them (one more if b < tasks_r), from task
+// b * tasks_q + min(b, tasks_r) on.
 struct LaunchArgs {
   TensorArg t[kMaxTensorsPerLaunch];
-  uint32_t btask_begin[kMaxTensorsPerLaunch + 1];  // first block task of each tensor
+  uint32_t task_begin[kMaxTensorsPerLaunch + 1];   // first task of each tensor (then the total)
   uint32_t n_tensors;
   uint32_t batch;                                  // GEMV rows of x / y
-  uint32_t total_btasks;
-  uint32_t btasks_per_block;
+  uint32_t tasks_q;
+  uint32_t tasks_r;
   uint32_t stage_words;                            // staging words per wavefront (0: none)
   uint32_t lut_cap;                                // table entries reserved in LDS
   uint32_t pair_bits;                              // index bits of the two-code table (0: none)
