@@ -1065,6 +1065,16 @@ template <int BATCH>
 __device__ __forceinline__ void gemv_pair(GemvLane<BATCH> &g, const uint32_t *lut, uint32_t K, uint32_t early,
                                           const uint32_t *xp) {
   constexpr uint32_t SB = XSlots<BATCH>::n;
+  // the x pair first: its LDS reads do not depend on the decode and land
+  // while the table lookups do
+  uint32_t x1s = 0u;
+  u32x4 x0, x1;
+  if (SB == 1) {
+    x1s = xp[0];
+  } else {
+    x0 = *reinterpret_cast<const u32x4 *>(xp);
+    x1 = *reinterpret_cast<const u32x4 *>(xp + 256);
+  }
   u32x2 e2;
   if (g.kk < early) {
     e2 = early_pair64<kModeGemv>(lut, K, g.hi, g.lo, g.n, g.pa);
@@ -1088,10 +1098,8 @@ __device__ __forceinline__ void gemv_pair(GemvLane<BATCH> &g, const uint32_t *lu
   g.hi = nhi;
   g.n = sub_len(g.n, e2.y);
   if (SB == 1) {
-    g.acc[0] = dot2(e2.x, xp[0], g.acc[0]);
+    g.acc[0] = dot2(e2.x, x1s, g.acc[0]);
   } else {
-    const u32x4 x0 = *reinterpret_cast<const u32x4 *>(xp);
-    const u32x4 x1 = *reinterpret_cast<const u32x4 *>(xp + 256);
 #pragma unroll
     for (uint32_t i = 0; i < 4u; ++i) {
       g.acc[i] = dot2(e2.x, x0[i], g.acc[i]);
