@@ -1429,40 +1429,44 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
       if (full && !sliced) pre = stage_task_issue<LOG2W>(d, task, stage, stage_words, pst) ? 1 : 0;
     }
     if (ti != cur) {
-      // activations of a GEMV tensor that may take the LDS path (W = 64,
-      // pairs, an even number of steps per row, all of x within its area):
-      // from an aligned x, loaded before the barrier and written to LDS
-      // after it, in flight together with the table fetch
+      // The table switch issues its loads before the workgroup barrier, after
+      // the staging above (whose copy should not queue behind them; issued
+      // ahead of it, they were slower), and writes LDS after it: the activations of a GEMV tensor that may take
+      // the LDS path (W = 64, pairs, an even number of steps per row, all of
+      // x within its area) from an aligned x, the table's entries (16 bytes
+      // per thread from an aligned table, whose header is 16 bytes) and its
+      // header.  Every wavefront checks the header itself, and the entries
+      // are fetched together with it, as many as the caller's table holds (at
+      // most the launch's table capacity): a table whose header fails the
+      // checks is then not used.
       const bool x_fit = MODE == kModeGemv && LOG2W == 6 && a.pair_bits && stage_words && (d.cols & 127u) == 0u &&
                          (uint64_t)(d.cols >> 1) * XSlots<BATCH>::n <= a.x_words;
       const bool x_vec = x_fit && x_vec_ok(d.x);
       XRegs xr;
       if (x_vec) x_load<BATCH>(xr, d.x, d.cols, a.batch, 0u, d.cols >> 7);
-      __syncthreads();
-      // every wavefront checks the table header itself (scalar loads of the
-      // same 16 bytes), and the entries are fetched together with it, as many
-      // as the caller's table holds (at most the launch's table capacity): a
-      // table whose header fails the checks is then not used
+      static_assert(kLutMaxEntries / 4u <= (uint32_t)kBlockThreads, "table fetch: one 16-byte load per thread");
       const uint32_t ne_fetch = min(a.lut_cap, d.lut_words > kLutHeaderWords ? d.lut_words - kLutHeaderWords : 0u);
-      if (((uintptr_t)d.lut & 15u) == 0u) {
-        // 16 bytes per load from an aligned table (the header is 16 bytes)
-        const uint32_t nv = ne_fetch >> 2;
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(d.lut + kLutHeaderWords);
-        for (uint32_t v = threadIdx.x; v < nv; v += kBlockThreads) {
-          const u32x4 e = src[v];
-          reinterpret_cast<u32x4 *>(lut)[v] =
-              u32x4{kernel_entry<MODE>(e[0]), kernel_entry<MODE>(e[1]), kernel_entry<MODE>(e[2]), kernel_entry<MODE>(e[3])};
-        }
-        for (uint32_t i = 4u * nv + threadIdx.x; i < ne_fetch; i += kBlockThreads)
-          lut[i] = kernel_entry<MODE>(d.lut[kLutHeaderWords + i]);
-      } else {
-        for (uint32_t i = threadIdx.x; i < ne_fetch; i += kBlockThreads)
-          lut[i] = kernel_entry<MODE>(d.lut[kLutHeaderWords + i]);
-      }
+      const uint32_t nv = ((uintptr_t)d.lut & 15u) == 0u ? ne_fetch >> 2 : 0u;
+      u32x4 lv = {0u, 0u, 0u, 0u};
+      uint32_t h0 = 0, h1 = 0, hne = 0, hl1 = 0;
+      auto fetch_table = [&]() {
+        if (threadIdx.x < nv) lv = reinterpret_cast<const u32x4 *>(d.lut + kLutHeaderWords)[threadIdx.x];
+        if (d.lut_words >= kLutHeaderWords) h0 = d.lut[0], h1 = d.lut[1], hne = d.lut[2], hl1 = d.lut[3];
+      };
+      // with eight batch slots the activations' loads fill this window
+      // already: the table follows the barrier there (measured faster)
+      if (BATCH == 1) fetch_table();
+      __syncthreads();
+      if (BATCH != 1) fetch_table();
+      if (threadIdx.x < nv)
+        reinterpret_cast<u32x4 *>(lut)[threadIdx.x] =
+            u32x4{kernel_entry<MODE>(lv[0]), kernel_entry<MODE>(lv[1]), kernel_entry<MODE>(lv[2]), kernel_entry<MODE>(lv[3])};
+      for (uint32_t i = 4u * nv + threadIdx.x; i < ne_fetch; i += kBlockThreads)
+        lut[i] = kernel_entry<MODE>(d.lut[kLutHeaderWords + i]);
       if (x_vec) x_store<BATCH>(xl, xr, d.cols >> 7);
       uint32_t k = 0;
       if (d.lut_words >= kLutHeaderWords) {
-        const uint32_t h0 = d.lut[0], h1 = d.lut[1], ne = d.lut[2], l1 = d.lut[3];
+        const uint32_t ne = hne, l1 = hl1;
         const uint32_t kk = h1 & 0xFFu;
         const uint32_t lmin = h1 >> 24;
         if (h0 == kLutMagic && (h1 & 0x00FFFF00u) == d.expect_hdr && kk >= 1 && kk <= kSingleLevelMax &&

@@ -42,12 +42,15 @@ struct RansArg {
   uint32_t n_tasks;
 };
 
+// Tasks as for the Huffman decoder: the launch's task space is the tensors'
+// wavefront tasks one after another; workgroup b takes tasks_q of them (one
+// more if b < tasks_r) from task b * tasks_q + min(b, tasks_r) on.
 struct RansLaunch {
   RansArg t[kMaxTensorsPerLaunch];
-  uint32_t btask_begin[kMaxTensorsPerLaunch + 1];
+  uint32_t task_begin[kMaxTensorsPerLaunch + 1];   // first task of each tensor (then the total)
   uint32_t n_tensors;
-  uint32_t total_btasks;
-  uint32_t btasks_per_block;
+  uint32_t tasks_q;
+  uint32_t tasks_r;
   uint32_t stage_units;      // staging units per wavefront (a multiple of 8)
   uint32_t state_word;       // LDS word of the table state
 };
@@ -107,14 +110,20 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
       for (uint32_t i = 0; i < a.n_tensors; ++i) atomicOr(a.t[i].status, kFLut);
     return;
   }
-  const uint32_t bt0 = blockIdx.x * a.btasks_per_block;
-  const uint32_t bt1 = min(bt0 + a.btasks_per_block, a.total_btasks);
+  // rounds of up to kWaves tasks within one tensor; wavefront w takes the
+  // w-th task of a round
+  const uint32_t b = blockIdx.x;
+  const uint32_t g0 = b * a.tasks_q + min(b, a.tasks_r);
+  const uint32_t g1 = g0 + a.tasks_q + (b < a.tasks_r ? 1u : 0u);
   uint32_t cur = 0xFFFFFFFFu;
-  uint32_t ok = 0;
-  for (uint32_t bt = bt0; bt < bt1; ++bt) {
-    uint32_t ti = 0;
-    while (ti + 1 < a.n_tensors && a.btask_begin[ti + 1] <= bt) ++ti;
+  uint32_t ok = 0, ti = 0;
+  for (uint32_t g = g0; g < g1;) {
+    while (ti + 1 < a.n_tensors && a.task_begin[ti + 1] <= g) ++ti;
     const RansArg &d = a.t[ti];
+    const uint32_t n_here = min(min(g1, a.task_begin[ti + 1]) - g, (uint32_t)kWaves);
+    const uint64_t task = (uint64_t)(g - a.task_begin[ti]) + wave;   // within the tensor
+    const bool mine = wave < n_here;
+    g += n_here;
     if (ti != cur) {
       __syncthreads();
       if (threadIdx.x == 0) {
@@ -137,9 +146,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
       cur = ti;
       __syncthreads();
     }
-    if (!ok) continue;
-    const uint64_t task = (uint64_t)(bt - a.btask_begin[ti]) * kWaves + wave;
-    if (task >= d.n_tasks) continue;
+    if (!ok || !mine) continue;
     // chunk offsets of the task: lane l < G holds chunk c0 + l's start
     const uint64_t c0 = task * G;
     const uint32_t nck = (uint32_t)min((uint64_t)G, (uint64_t)d.n_chunks - c0);
@@ -256,6 +263,10 @@ static entro_status run_rans(int mode, const entro_rans_tensor *t, size_t n, voi
       if (x.n_symbols == 0) continue;
       if (k == 0) lanes = x.lanes;
       else if (x.lanes != lanes) break;
+      // the launch's task space stays below 2^31 tasks
+      const uint64_t tasks = ((x.n_symbols + x.chunk_symbols - 1) / x.chunk_symbols + 64u / x.lanes - 1) / (64u / x.lanes);
+      if (tasks > 0x7FFFFFFFull) return ENTRO_E_UNSUPPORTED;
+      if ((uint64_t)total + tasks > 0x7FFFFFFFull) break;
       RansArg &d = a.t[k];
       d.table = static_cast<const uint32_t *>(x.d_table);
       d.units = x.d_units;
@@ -270,18 +281,15 @@ static entro_status run_rans(int mode, const entro_rans_tensor *t, size_t n, voi
       d.table_words = (uint32_t)(entro_rans_table_bytes() / 4u);
       const uint32_t g = 64u / x.lanes;
       d.n_tasks = (d.n_chunks + g - 1) / g;
-      const uint64_t nb = (d.n_tasks + kWaves - 1) / kWaves;
-      if ((uint64_t)total + nb > 0x7FFFFFFFull) return ENTRO_E_UNSUPPORTED;
-      a.btask_begin[k] = total;
-      total += (uint32_t)nb;
+      a.task_begin[k] = total;
+      total += d.n_tasks;
       const uint64_t mcu = x.max_chunk_units ? x.max_chunk_units : (x.n_units + d.n_chunks - 1) / d.n_chunks * 2u;
       stage_need = std::max<uint64_t>(stage_need, (uint64_t)g * mcu);
       ++k;
     }
     if (k == 0) continue;
     a.n_tensors = k;
-    a.total_btasks = total;
-    for (uint32_t r = k; r <= (uint32_t)kMaxTensorsPerLaunch; ++r) a.btask_begin[r] = total;
+    for (uint32_t r = k; r <= (uint32_t)kMaxTensorsPerLaunch; ++r) a.task_begin[r] = total;
     // LDS: the slot table (32 KiB, at 0), the state word, then one staging
     // area per wavefront (the largest task plus alignment)
     size_t dyn = (size_t)kRansSlots * 8u;
@@ -302,10 +310,12 @@ static entro_status run_rans(int mode, const entro_rans_tensor *t, size_t n, voi
     const int lds_fit = (int)((kLdsPerCu - kLdsPlanReserve) / (dyn + kStaticLds));
     if (lds_fit >= 1 && per_cu > lds_fit) per_cu = lds_fit;
     if (cus < 1) cus = 1;
+    // one workgroup per slot (fewer if there are fewer tasks), the tasks
+    // spread over them evenly
     const uint64_t slots = (uint64_t)cus * (uint64_t)per_cu;
-    const uint32_t per_block = (uint32_t)((total + slots - 1) / slots);
-    a.btasks_per_block = per_block < 1 ? 1 : per_block;
-    const uint32_t grid = (total + a.btasks_per_block - 1) / a.btasks_per_block;
+    const uint32_t grid = (uint32_t)std::min<uint64_t>(slots, total);
+    a.tasks_q = total / grid;
+    a.tasks_r = total % grid;
     // clear an error left by an earlier call (ours, such as a failed occupancy
     // query, or the caller's): the check below then sees this launch alone
     (void)hipGetLastError();
