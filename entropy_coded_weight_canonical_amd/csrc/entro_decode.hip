@@ -1798,10 +1798,14 @@ static hipError_t launch_one(uint32_t total_tasks, LaunchArgs &a, size_t dyn, hi
   const int lds_fit = (int)((kLdsPerCu - kLdsPlanReserve) / (dyn + kStaticLds));
   if (lds_fit >= 1 && per_cu > lds_fit) per_cu = lds_fit;
   if (cus < 1) cus = 1;
-  // one workgroup per slot (fewer if there are fewer tasks), the tasks
-  // spread over them evenly
-  const uint64_t slots = (uint64_t)cus * (uint64_t)per_cu;
-  const uint32_t grid = (uint32_t)std::min<uint64_t>(slots, total_tasks);
+  // k workgroups per CU on every CU, k the fewest that give each wavefront
+  // a task (at most per_cu; fewer workgroups than CUs if there are fewer
+  // tasks), the tasks spread over them evenly.  A second workgroup per CU
+  // only when the first ones are full leaves room on the CUs for work on
+  // other streams (decoding ahead of a consumer).
+  const uint64_t k = std::min<uint64_t>((uint64_t)per_cu,
+                                        (total_tasks + (uint64_t)kWaves * cus - 1) / ((uint64_t)kWaves * cus));
+  const uint32_t grid = (uint32_t)std::min<uint64_t>((uint64_t)cus * std::max<uint64_t>(k, 1), total_tasks);
   a.tasks_q = total_tasks / grid;
   a.tasks_r = total_tasks % grid;
   // clear an error left by an earlier call (ours, such as a failed occupancy
