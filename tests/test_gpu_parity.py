@@ -150,6 +150,32 @@ def test_more_tensors_than_one_launch_and_mixed_lanes():
         assert np.array_equal(o, c.expected_bf16())
 
 
+def test_workgroup_task_ranges_cross_tensor_boundaries():
+    """Workgroups take an even share of the launch's tasks, in rounds that
+    stay within one tensor, so a share can span several tensors: 32 tensors
+    of 40 to 269 tasks (more tasks in all than 16 per CU, so that CUs take
+    a second workgroup), lanes 32 (two chunks per task) with a ragged last
+    task, then half of the codes with 64 lanes (fewer tasks than that)."""
+    cases = []
+    for i in range(32):
+        n_tasks = 40 + (i * 37) % 230
+        n = n_tasks * 2 * 1024 - (i % 3) * 100
+        bits = 4 if i % 4 else 8
+        q = fuzz_codes(90 + i, n, bits, CODE_KINDS[i % len(CODE_KINDS)])
+        cases.append(make_case(q, bits, 1024, 32, refill_steps=2, ahead=bool(i % 2)))
+    say("32 tensors, task ranges across tensor boundaries (W 32)")
+    outs, st = run_decode(cases, "bf16")
+    assert (st == 0).all(), st
+    for c, o in zip(cases, outs):
+        assert np.array_equal(o, c.expected_bf16())
+    cases64 = [make_case(c.q, c.bits, 1024, 64, refill_steps=2) for c in cases[:16]]
+    say("16 tensors, task ranges across tensor boundaries (W 64)")
+    outs, st = run_decode(cases64, "u8")
+    assert (st == 0).all(), st
+    for c, o in zip(cases64, outs):
+        assert np.array_equal(o, c.q)
+
+
 def test_cached_output_stores_mixed_with_streamed():
     """out_cached = 1 selects ordinary output stores; tensors of both policies
     in one call are split into separate launches and both decode exactly
@@ -337,6 +363,27 @@ def test_gemv_activations_and_tables_at_any_alignment(batch):
         assert (st == 0).all(), st
         for y, ref in zip(ys, refs):
             assert ogemv.rel_err(y, ref) <= 1e-4
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_gemv_task_ranges_cross_tensor_boundaries(batch):
+    """Many GEMV tensors in one launch whose row counts do not line up with
+    the workgroups' even shares of the tasks: the LDS path (1024 columns)
+    and, at batch 8, the column-sliced path (5120 columns), where every
+    wavefront of a workgroup takes part in each round, with or without a
+    row of its own."""
+    cases = []
+    for i in range(20):
+        cols = 5120 if i % 5 == 0 else 1024
+        rows = 90 + (i * 53) % 170
+        cases.append(_gemv_case(rows, cols, 4, 200 + i, refill_steps=2, ahead=bool(i % 2)))
+    xs = [activations_bf16("mistral_stack", 90 + i, c.cols, batch) for i, c in enumerate(cases)]
+    say(f"gemv 20 tensors, task ranges across tensor boundaries, batch={batch}")
+    ys, st = run_gemv(cases, xs, batch)
+    assert (st == 0).all(), st
+    for c, x, y in zip(cases, xs, ys):
+        ref = ogemv.gemv_f64(c.expected_bf16().reshape(c.rows, c.cols), x)
+        assert ogemv.rel_err(y, ref) <= 1e-4
 
 
 @pytest.mark.parametrize("batch", [1, 3, 8])
