@@ -25,6 +25,32 @@ def test_golden_tiny():
     assert quant.quantize_mixed(w, bits).scheme == g["mixed"][0][0]
 
 
+
+def test_golden_mixed_choice_when_entropies_differ():
+    """Two hand-derived cases where the schemes' code entropies differ: the
+    one-sided tensor goes to unsigned (fewer distinct codes), the lopsided one
+    to asymmetric."""
+    _, rows = load("quant_mixed_tiny.txt")
+    cases, cur = [], None
+    for r in rows:
+        if r[0] == "case":
+            cur = {}
+            cases.append(cur)
+        else:
+            cur[r[0]] = r[1:]
+    assert len(cases) == 2
+    for c in cases:
+        w = np.array([float(x) for x in c["w"]], dtype=np.float32)
+        a = quant.quantize_asymmetric(w, 4)
+        u = quant.quantize_unsigned(w, 4)
+        assert a.zero_point == int(c["asym_zp"][0])
+        assert a.q.tolist() == [int(x) for x in c["asym_q"]]
+        assert u.zero_point == 8 and u.q.tolist() == [int(x) for x in c["unsigned_q"]]
+        m = quant.quantize_mixed(w, 4)
+        assert m.scheme == c["mixed"][0]
+        assert m.q.tolist() == (u.q if m.scheme == "unsigned" else a.q).tolist()
+
+
 def _rand_w(seed, n=200_000, dist="normal"):
     rng = np.random.default_rng(seed)
     if dist == "normal":
