@@ -43,6 +43,7 @@
 #include <algorithm>
 #include <cstring>
 #include <type_traits>
+#include <vector>
 
 #include "entro.h"
 #include "entro_device.h"
@@ -1828,8 +1829,17 @@ static hipError_t launch_w(uint32_t log2w, uint32_t total_tasks, LaunchArgs &a, 
   }
 }
 
-// Validate everything, then enqueue launches of up to 32 tensors that share
-// a lane count and an output cache policy.
+// One planned launch: its arguments, dynamic LDS bytes and task count.
+struct LaunchPlan {
+  LaunchArgs a;
+  size_t dyn;
+  uint32_t total, log2w;
+  bool cached;
+};
+
+// Validate everything and plan every launch (groups of up to 32 tensors that
+// share a lane count and an output cache policy), then enqueue them: a call
+// that fails validation or planning enqueues nothing.
 static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *outs,
                         const entro_gemv_item *g, uint32_t batch, uint32_t *d_status, hipStream_t s) {
   if (n == 0) return ENTRO_OK;
@@ -1854,10 +1864,13 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
       if (!outs[i] || (reinterpret_cast<uintptr_t>(outs[i]) & (align - 1u))) return ENTRO_E_INVAL;
     }
   }
+  std::vector<LaunchPlan> plans;
   size_t i = 0;
   while (i < n) {
-    LaunchArgs a;
-    std::memset(&a, 0, sizeof a);
+    plans.emplace_back();
+    LaunchPlan &pl = plans.back();
+    std::memset(&pl, 0, sizeof pl);
+    LaunchArgs &a = pl.a;
     a.batch = batch;
     uint32_t total = 0, log2w = 0, k = 0;
     bool cached = false;   // output cache policy of the launch (GEMV: unused)
@@ -1911,7 +1924,10 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
       else stage_known = false, stage_need = std::max<uint64_t>(stage_need, (x.n_words + tasks - 1) / tasks * 5 / 4 + 64);
       ++k;
     }
-    if (k == 0) continue;
+    if (k == 0) {
+      plans.pop_back();
+      continue;
+    }
     a.n_tensors = k;
     for (uint32_t r = k; r <= (uint32_t)kMaxTensorsPerLaunch; ++r) a.task_begin[r] = total;
     (void)stage_known;
@@ -1943,10 +1959,19 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
       a.stage_words = (uint32_t)sw;
       dyn += (size_t)kWaves * (sw + kStageSlack) * 4u;
     }
+    pl.dyn = dyn;
+    pl.total = total;
+    pl.log2w = log2w;
+    pl.cached = cached;
+  }
+  for (LaunchPlan &pl : plans) {
     hipError_t err;
-    if (mode == kModeU8 && cached) err = launch_w<kModeU8, 1, kStoreCached>(log2w, total, a, dyn, s);
+    const uint32_t log2w = pl.log2w, total = pl.total;
+    const size_t dyn = pl.dyn;
+    LaunchArgs &a = pl.a;
+    if (mode == kModeU8 && pl.cached) err = launch_w<kModeU8, 1, kStoreCached>(log2w, total, a, dyn, s);
     else if (mode == kModeU8) err = launch_w<kModeU8, 1, kStoreNT>(log2w, total, a, dyn, s);
-    else if (mode == kModeBf16 && cached) err = launch_w<kModeBf16, 1, kStoreCached>(log2w, total, a, dyn, s);
+    else if (mode == kModeBf16 && pl.cached) err = launch_w<kModeBf16, 1, kStoreCached>(log2w, total, a, dyn, s);
     else if (mode == kModeBf16) err = launch_w<kModeBf16, 1, kStoreNT>(log2w, total, a, dyn, s);
     else if (batch == 1) err = launch_w<kModeGemv, 1, kStoreNT>(log2w, total, a, dyn, s);
     else err = launch_w<kModeGemv, 8, kStoreNT>(log2w, total, a, dyn, s);
@@ -1992,9 +2017,13 @@ static entro_status run_gemm(const entro_tensor *t, size_t n, const entro_gemv_i
     if (t[i].lanes != 64u || t[i].sym_bits != 4u || t[i].refill_steps != 2u || t[i].max_chunk_words == 0u)
       return ENTRO_E_UNSUPPORTED;
   }
+  // plan every launch first (a row too long for the staging fails the call
+  // before anything is enqueued), then launch
+  std::vector<std::pair<GemmArgs, size_t>> plans;
   size_t i = 0;
   while (i < n) {
-    GemmArgs a;
+    plans.emplace_back();
+    GemmArgs &a = plans.back().first;
     std::memset(&a, 0, sizeof a);
     a.n_tokens = n_tokens;
     uint32_t total = 0, k = 0;
@@ -2028,7 +2057,10 @@ static entro_status run_gemm(const entro_tensor *t, size_t n, const entro_gemv_i
       stage_need = std::max<uint64_t>(stage_need, x.max_chunk_words);
       ++k;
     }
-    if (k == 0) continue;
+    if (k == 0) {
+      plans.pop_back();
+      continue;
+    }
     a.n_tensors = k;
     a.total_tiles = total;
     for (uint32_t r = k; r <= (uint32_t)kMaxTensorsPerLaunch; ++r) a.tile_begin[r] = total;
@@ -2052,8 +2084,10 @@ static entro_status run_gemm(const entro_tensor *t, size_t n, const entro_gemv_i
     if (sw > cap) return ENTRO_E_UNSUPPORTED;
     a.stage_words = (uint32_t)sw;
     dyn += (size_t)kWaves * (sw + kStageSlack) * 4u;
-    if (launch_gemm(a, dyn, s) != hipSuccess) return ENTRO_E_HIP;
+    plans.back().second = dyn;
   }
+  for (auto &pl : plans)
+    if (launch_gemm(pl.first, pl.second, s) != hipSuccess) return ENTRO_E_HIP;
   return ENTRO_OK;
 }
 

@@ -72,6 +72,19 @@ def _split(nc: int, threads: int):
     return [(bounds[i], bounds[i + 1]) for i in range(threads)]
 
 
+def layout(q: np.ndarray, lengths: np.ndarray, chunk: int, lanes: int):
+    """Chunk offsets and word count of the stream, without writing it ->
+    ``(chunk_bit_off uint64, n_words)``; the same offsets as ``encode``."""
+    lib = _load()
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.uint8).ravel())
+    ln = np.ascontiguousarray(np.asarray(lengths, dtype=np.uint8))
+    n = q.size
+    offs = np.zeros(-(-n // chunk) + 1, dtype=np.uint64)
+    nw = np.zeros(1, dtype=np.uint64)
+    _check(lib.oc_layout(_ptr(q), n, _ptr(ln), ln.size, chunk, lanes, _ptr(offs), _ptr(nw)), "layout")
+    return offs, int(nw[0])
+
+
 def encode(q: np.ndarray, lengths: np.ndarray, chunk: int, lanes: int, threads: int = 1, refill_steps: int = 1,
            ahead: bool = False):
     """Encode -> ``(words uint32, chunk_bit_off uint64)``; same result as ``oracle.ecw.encode``."""

@@ -40,6 +40,12 @@ WORKLOAD_IDS = {
 }
 
 
+# Clip factor of the Mistral-shaped workload's unsigned 4-bit codes: each
+# tensor's range end is MISTRAL_CLIP_SIGMA * std(w), so that the stack, coded
+# in one-row chunks of 64 lanes, takes 3.90 bits per weight (found by
+# ``python -m oracle.clip_calibration``; 3.9006 on layer 0, 3.9005 on layer 1).
+MISTRAL_CLIP_SIGMA = 1.9219
+
 @dataclass(frozen=True)
 class TensorSpec:
     """One weight matrix of a workload: ``rows`` = out features, ``cols`` = in."""

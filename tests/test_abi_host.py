@@ -243,6 +243,21 @@ def test_gemm_entry_point_validates_before_launch(lib):
     assert lib.entro_decode_gemm((ent.Tensor * 1)(), 0, None, 16, st, None) == 0
 
 
+def test_a_call_that_fails_planning_enqueues_nothing(lib):
+    """The tensors of a call go out in launches of up to 32; a tensor that a
+    later launch cannot take must fail the whole call before the earlier
+    launches are enqueued.  On this machine (no GPU) an enqueued launch would
+    report ENTRO_E_HIP (5), so ENTRO_E_UNSUPPORTED (4) shows that planning
+    rejected the call first."""
+    st = ctypes.c_void_p(1)
+    good = [ent.Tensor(1, 1, 1, 10, 2 * 128, 128, 64, 4, 12, 64, 8, 2, 1) for _ in range(40)]
+    bad = list(good)
+    bad[35] = ent.Tensor(1, 1, 1, 10, 2 * 128, 128, 64, 4, 12, 64, 1 << 20, 2, 1)   # row beyond the staging
+    g = (ent.GemvItem * 40)(*[ent.GemvItem(2, 128, 0x1000, 0x2000) for _ in range(40)])
+    assert lib.entro_decode_gemm((ent.Tensor * 40)(*bad), 40, g, 16, st, None) == 4
+    assert lib.entro_decode_gemm((ent.Tensor * 40)(*good), 40, g, 16, st, None) == 5
+
+
 # --------------------------------------------------------------------------
 # the library's offline encoder against the oracle
 # --------------------------------------------------------------------------

@@ -1,0 +1,240 @@
+"""GPU parity of the five workloads at full size, encoded and launched the way
+the benchmark runs them (the settings come from bench.WORKLOADS: chunk size,
+lanes, refill every two steps, refilling ahead).
+
+Streams, code lengths and every expected value come from the oracle; the
+library contributes its decode-table builder and the kernels under test.
+Codes and bf16 values must be bit-exact; fused GEMV outputs within 1e-2 of
+the float64 oracle (floor-guarded relative error).
+
+* configs[0] (tensor_2048): 64 replicas in one call, u8 and bf16, at the
+  benchmark's lane count and at the other one.
+* configs[1] (tensor_4096): covered in test_gpu_parity (16 replicas).
+* configs[2] (smollm_stack): the whole 169-tensor call, layers 2..23 device
+  copies of layers 0 and 1; layers 0, 1 and the 49152 x 2048 embedding
+  compared element by element with the oracle, every copy with its source.
+* configs[3] (phi3_stack): one full layer through the fused GEMV, batch 1.
+* configs[4] (mistral_stack): one full layer at the stated rate (clipped
+  unsigned 4-bit, 3.90 bits per weight) at batch 1 and batch 8.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from oracle import gemv as ogemv  # noqa: E402
+from oracle import quant  # noqa: E402
+from oracle.dequant import dequant_bf16  # noqa: E402
+from synth import MISTRAL_CLIP_SIGMA, TensorSpec, activations_bf16, tensor_specs, weights  # noqa: E402
+from tests._cases import make_case, upload  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import entropy_coded_weight_canonical_amd as ent
+
+    ent.load()
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+def _quantize(spec, workload):
+    """The oracle's quantizer with the workload's scheme (and clip)."""
+    cfg = bench.WORKLOADS[workload]
+    w = weights(spec)
+    bits = cfg["bits"]
+    if cfg["scheme"] == "mixed":
+        return quant.quantize_mixed(w, bits)
+    if cfg["scheme"] == "asymmetric":
+        return quant.quantize_asymmetric(w, bits)
+    c = cfg.get("clip_sigma")
+    c = MISTRAL_CLIP_SIGMA if c is None else c
+    return quant.quantize_unsigned(w, bits, clip=c * float(np.std(w, dtype=np.float64)) if c else None)
+
+
+def _case(spec, workload, chunk=None, lanes=None):
+    cfg = bench.WORKLOADS[workload]
+    qz = _quantize(spec, workload)
+    chunk = chunk or cfg.get("chunk") or bench.gemv_chunk(spec.cols, cfg["chunk_target"])
+    return make_case(qz.q, cfg["bits"], chunk, lanes or cfg["lanes"], scale=qz.scale, zp=qz.zero_point,
+                     rows=spec.rows, cols=spec.cols, refill_steps=bench.REFILL_STEPS, ahead=bench.REFILL_AHEAD)
+
+
+def _decode_on_device(dts, ns, mode):
+    """One call over every descriptor; the outputs stay on the device."""
+    import torch
+
+    import entropy_coded_weight_canonical_amd as ent
+
+    dtype = torch.uint8 if mode == "u8" else torch.int16
+    outs = [torch.full((max(n, 1),), 0x5A if mode == "u8" else 0x5A5A, dtype=dtype, device="cuda") for n in ns]
+    status = torch.zeros(len(dts), dtype=torch.int32, device="cuda")
+    fn = ent.decode if mode == "u8" else ent.decode_dequant
+    fn([d.desc for d in dts], [o.data_ptr() for o in outs], status.data_ptr())
+    torch.cuda.synchronize()
+    return outs, status.cpu().numpy().view(np.uint32)
+
+
+def _expected_on_device(case, mode):
+    import torch
+
+    exp = case.q if mode == "u8" else case.expected_bf16().view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(exp)).cuda()
+
+
+# --------------------------------------------------------------------------
+# configs[0]: 2048 x 2048 N(0, 0.02), asymmetric 8-bit, 4096-code chunks
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lanes", sorted({bench.WORKLOADS["tensor_2048"]["lanes"], 32, 64}))
+def test_config1_tensor_2048_replicas_as_benchmarked(lanes):
+    import torch
+
+    cfg = bench.WORKLOADS["tensor_2048"]
+    c = _case(TensorSpec("tensor_2048", 0, -1, "w", 2048, 2048, "w"), "tensor_2048", lanes=lanes)
+    dts = [upload(c) for _ in range(cfg["replicas"])]
+    for mode in ("u8", "bf16"):
+        say(f"tensor_2048 x{cfg['replicas']} W={lanes} {mode}")
+        outs, st = _decode_on_device(dts, [c.n] * len(dts), mode)
+        assert (st == 0).all(), st
+        exp = _expected_on_device(c, mode)
+        assert np.array_equal(outs[0].cpu().numpy()[: c.n], exp.cpu().numpy())
+        for o in outs:
+            assert torch.equal(o[: c.n], exp)
+
+
+# --------------------------------------------------------------------------
+# configs[2]: SmolLM-shaped stack, 169 tensors, mixed 8-bit, decode all
+# --------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def smollm_cases():
+    specs = tensor_specs("smollm_stack")
+    cases = {}
+    for s in specs:
+        key = (s.layer, s.name.split(".", 1)[-1]) if s.layer >= 0 else ("x", s.name)
+        if s.layer in (0, 1) or s.layer < 0:
+            cases[key] = _case(s, "smollm_stack")
+    return specs, cases
+
+
+@pytest.mark.parametrize("mode", ["u8", "bf16"])
+def test_config3_smollm_stack_decode_all_in_one_call(smollm_cases, mode):
+    import torch
+
+    specs, cases = smollm_cases
+    lengths_max = max(int(c.lengths.max()) for c in cases.values())
+    srcs, dts = [], []
+    for s in specs:
+        key = (s.layer % 2, s.name.split(".", 1)[-1]) if s.layer >= 0 else ("x", s.name)
+        srcs.append(key)
+        dts.append(upload(cases[key]))
+    say(f"smollm_stack {len(specs)} tensors in one call, {mode} (longest code {lengths_max} bits)")
+    outs, st = _decode_on_device(dts, [cases[k].n for k in srcs], mode)
+    assert (st == 0).all(), st
+    first = {}
+    for key, o in zip(srcs, outs):
+        c = cases[key]
+        if key not in first:
+            got = o.cpu().numpy()[: c.n]
+            exp = c.q if mode == "u8" else c.expected_bf16().view(np.int16)
+            assert np.array_equal(got, exp), key
+            first[key] = o
+        else:
+            assert torch.equal(o, first[key]), key
+    assert len(first) == 15   # 2 x 7 matrices + the embedding
+
+
+# --------------------------------------------------------------------------
+# fused GEMV of whole layers, one call per group of matrices sharing x
+# --------------------------------------------------------------------------
+
+def _gemv_layer(workload, layer, batch, cases=None):
+    """Run the fused GEMV over one layer as the benchmark groups it; returns
+    [(case, x, y)]."""
+    import torch
+
+    import entropy_coded_weight_canonical_amd as ent
+
+    specs = [s for s in tensor_specs(workload) if s.layer == layer]
+    cases = cases or [_case(s, workload) for s in specs]
+    groups = {}
+    for s, c in zip(specs, cases):
+        groups.setdefault(s.group, []).append((s, c))
+    res = []
+    for gi, (gname, members) in enumerate(groups.items()):
+        cols = members[0][0].cols
+        x = activations_bf16(workload, gi, cols, batch)
+        dx = torch.from_numpy(x.view(np.int16)).cuda()
+        dts, items, ys = [], [], []
+        for s, c in members:
+            dts.append(upload(c))
+            y = torch.full((batch, s.rows), float("nan"), dtype=torch.float32, device="cuda")
+            ys.append(y)
+            items.append(ent.GemvItem(s.rows, s.cols, dx.data_ptr(), y.data_ptr()))
+        status = torch.zeros(len(dts), dtype=torch.int32, device="cuda")
+        say(f"{workload} layer {layer} group {gname} ({len(dts)} matrices, {cols} columns) batch {batch}")
+        ent.decode_gemv([d.desc for d in dts], items, batch, status.data_ptr())
+        torch.cuda.synchronize()
+        st = status.cpu().numpy()
+        assert (st == 0).all(), (gname, st)
+        for (s, c), y in zip(members, ys):
+            res.append((c, x, y.cpu().numpy()))
+    return res
+
+
+def test_config4_phi3_layer_fused_gemv_batch1():
+    for c, x, y in _gemv_layer("phi3_stack", 0, 1):
+        ref = ogemv.gemv_f64(c.expected_bf16().reshape(c.rows, c.cols), x)
+        err = ogemv.rel_err(y, ref)
+        assert err <= 1e-2, err
+        assert err <= 1e-4, err   # fp32 accumulation
+
+
+@pytest.fixture(scope="module")
+def mistral_layer_cases():
+    specs = [s for s in tensor_specs("mistral_stack") if s.layer == 0]
+    cases = [_case(s, "mistral_stack") for s in specs]
+    n = sum(c.n for c in cases)
+    bits = 8.0 * sum(4 * c.words.size + 8 * c.offs.size for c in cases) / n
+    return cases, bits
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_config5_mistral_layer_at_stated_rate_fused_gemv(mistral_layer_cases, batch):
+    """The stated rate: 3.90 +- 0.05 bits per weight; the 14336-column down
+    rows are the longest chunks the GEMV stages."""
+    cases, bits = mistral_layer_cases
+    assert abs(bits - 3.90) <= 0.05, bits
+    assert max(int(c.lengths.max()) for c in cases) <= 12
+    for c, x, y in _gemv_layer("mistral_stack", 0, batch, cases):
+        ref = ogemv.gemv_f64(c.expected_bf16().reshape(c.rows, c.cols), x)
+        err = ogemv.rel_err(y, ref)
+        assert err <= 1e-2, err
+        assert err <= 1e-4, err
+
+
+def test_config5_mistral_layer_decodes_bit_exact(mistral_layer_cases):
+    """The same layer through the standalone decode (u8 and bf16), so that the
+    codes themselves are pinned at the stated rate, not only the products."""
+    cases, _ = mistral_layer_cases
+    dts = [upload(c) for c in cases]
+    for mode in ("u8", "bf16"):
+        say(f"mistral_stack layer 0 at 3.90 bits, decode {mode}")
+        outs, st = _decode_on_device(dts, [c.n for c in cases], mode)
+        assert (st == 0).all(), st
+        for c, o in zip(cases, outs):
+            exp = c.q if mode == "u8" else c.expected_bf16().view(np.int16)
+            assert np.array_equal(o.cpu().numpy()[: c.n], exp)
