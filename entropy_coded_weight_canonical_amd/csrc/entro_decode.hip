@@ -669,26 +669,27 @@ __device__ __forceinline__ uint32_t pairs_small(const uint32_t *lut, uint32_t K,
 }
 
 // Two-code table, built in LDS from the code table when a 4-bit tensor is
-// decoded in pairs: entry i (the next kPairBits stream bits) holds, in its
-// first word, the pair's two output values packed as by pack_ab and, in the
-// second, the pair's summed length in byte 1 and its alignbit shift in bits
-// [4:0], so that one 8-byte read gives a whole pair.  Indices whose A and B
-// do not both fit in kPairBits bits carry kPairFallback in byte 0 (length 0);
-// lanes that hit one look the two codes up in the code table instead.
+// decoded in pairs: entry i (the next PB stream bits, PB = kPairBits or
+// kPairBitsWide) holds, in its first word, the pair's two output values
+// packed as by pack_ab and, in the second, the pair's summed length in byte 1
+// and its alignbit shift in bits [4:0], so that one 8-byte read gives a whole
+// pair.  Indices whose A and B do not both fit in PB bits carry
+// kPairFallback in byte 0 (length 0); lanes that hit one look the two codes
+// up in the code table instead.
 __device__ __forceinline__ uint32_t pair_word(uint32_t lab) { return (lab << 8) | ((32u - lab) & 31u); }
 
-template <int MODE>
+template <int MODE, uint32_t PB = kPairBits>
 __device__ u32x2 build_pair_entry(const uint32_t *lut, uint32_t K, uint32_t i) {
-  const uint32_t hi = i << (32u - kPairBits);
+  const uint32_t hi = i << (32u - PB);
   const uint32_t eA = lookup(lut, hi, K);
   const uint32_t lA = entry_len(eA);
   u32x2 r;
   r.x = 0u;
   r.y = kPairFallback | 0xFF00u;   // length byte above any loaded count
-  if (lA <= kPairBits) {
+  if (lA <= PB) {
     const uint32_t eB = lookup(lut, hi << lA, K);
     const uint32_t lB = entry_len(eB);
-    if (lA + lB <= kPairBits) {
+    if (lA + lB <= PB) {
       r.x = pack_ab<MODE>(eA, eB);
       r.y = pair_word(lA + lB);
     }
@@ -696,9 +697,9 @@ __device__ u32x2 build_pair_entry(const uint32_t *lut, uint32_t K, uint32_t i) {
   return r;
 }
 
-template <int MODE>
+template <int MODE, uint32_t PB = kPairBits>
 __device__ __forceinline__ u32x2 pair_lookup(const uint32_t *lut, uint32_t K, uint32_t hi, uint32_t lo) {
-  u32x2 e2 = *(lds_u32x2 *)(uintptr_t)((hi >> (32u - kPairBits)) << 3);   // table at LDS address 0
+  u32x2 e2 = *(lds_u32x2 *)(uintptr_t)((hi >> (32u - PB)) << 3);   // table at LDS address 0
   const uint64_t fb = pointer_mask(e2.y);
   if (fb) {
     if (__builtin_amdgcn_inverse_ballot_w64(fb)) {
@@ -1224,6 +1225,400 @@ __device__ uint32_t gemv_sliced64(const TensorArg &d, const uint32_t *lut, uint3
     }
   }
   return have ? gemv_end_flags<BATCH>(g, lds_addr(sw), nw) : 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Fused GEMV, streamed: W = 64 chunks of whole rows, 4-bit codes decoded in
+// pairs through a two-code table of kPairBitsWide index bits, 128 | cols.
+//
+// A workgroup takes a contiguous share of the launch's chunks and splits the
+// part of it that lies in one tensor into kWaves contiguous ranges, one per
+// wavefront.  A wavefront's chunks are consecutive, so their words form one
+// run of the stream, which it streams through a ring of kRingBlocks blocks in
+// its LDS area (copies with 16-byte loads that write LDS directly).  Block k
+// of the run (words [k B, (k + 1) B) from the run's block-aligned base) sits
+// in ring slot k mod kRingBlocks.  When the word pointer P enters block k,
+// slot k - 1 is free (all its words lie below P) and block k + 3 is copied
+// into it; a step reads words [P, P + 64), within blocks k and k + 1, so the
+// two newest copies may stay in flight (s_waitcnt vmcnt(2); vector-memory
+// loads complete in order).  The buffer resource ends at the run's last
+// word, so copies past it read zeros without touching memory.  No other
+// vector-memory access happens while a run streams: the rows' y values are
+// collected in registers and stored at most every 64 rows.
+// ---------------------------------------------------------------------------
+
+// The run of one wavefront: the buffer resource over its words (from the
+// block-aligned base on), the word pointer P as a byte offset from the base,
+// and the chunks' end offsets (lane i: byte offset of the end of chunk cb + i from the base, for
+// the 64 chunks from chunk c64 on).
+struct Run {
+  __amdgpu_buffer_rsrc_t r;
+  uint64_t base;     // first word of block 0 (stream word index)
+  uint32_t p4;       // byte offset of P from the base
+  uint32_t klast;    // the run's last block
+  uint32_t ends;     // per lane: end of chunk c64 + lane (byte offset from the base)
+};
+
+// Copy block k of the run into its ring slot.  A ring of 2^RL words holds
+// four blocks of 2^RL bytes: with RL = 10 one 16-byte copy per lane (64 lanes
+// x 16 bytes), with RL = 9 two 4-byte copies per lane (2 x 64 lanes x 4
+// bytes), so that every lane takes part in every copy.  A block past the
+// run's end is never read; its slot receives the run's last block again
+// instead, so that every copy reads memory.  (The waits count copies in
+// flight and rely on copies completing in the order they were issued; a
+// copy wholly outside the buffer resource reads no memory and could
+// complete ahead of earlier ones.)
+template <uint32_t RL>
+__device__ __forceinline__ void ring_copy(const Run &R, uint32_t ring_base, uint32_t k, uint32_t lane) {
+  const uint32_t dst = ring_base + ((k << RL) & ((4u << RL) - 1u));
+  const uint32_t src = min(k, R.klast) << RL;
+  if (RL == 10) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(R.r, (lds_void *)(uintptr_t)rfl(dst), 16, lane * 16u, rfl(src), 0, 0);
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(R.r, (lds_void *)(uintptr_t)rfl(dst), 4, lane * 4u, rfl(src), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(R.r, (lds_void *)(uintptr_t)rfl(dst + 256u), 4, lane * 4u,
+                                             rfl(src + 256u), 0, 0);
+  }
+}
+
+// Copy instructions per block
+template <uint32_t RL>
+struct RingCopies { static constexpr uint32_t n = RL == 10 ? 1u : 2u; };
+
+// Wait until at most two blocks' copies are in flight (every block up to the
+// one after P's has landed), then keep later LDS reads below the wait.
+template <uint32_t RL>
+__device__ __forceinline__ void ring_wait2() {
+  if (RingCopies<RL>::n == 1) __builtin_amdgcn_s_waitcnt(0x0F72);   // vmcnt(2)
+  else __builtin_amdgcn_s_waitcnt(0x0F74);                          // vmcnt(4)
+  asm volatile("" ::: "memory");
+}
+
+// End offsets of chunks [c, min(c + 64, ce)) relative to the run's base, one
+// per lane (a vector load, so that no scalar load is pending in the decode
+// loop); lanes past ce hold the last one.  False if any is malformed (not a
+// multiple of 32 bits, below the run's start, past the words).
+__device__ __forceinline__ bool load_ends(const TensorArg &d, const Run &R, uint32_t c, uint32_t ce,
+                                          uint64_t o_start, uint32_t lane, uint32_t &ends) {
+  const uint32_t i = min(c + 1u + lane, ce);
+  const uint64_t o = d.offs[i];
+  const bool bad = (o & 31u) || o < o_start || (o >> 5) > d.n_words;
+  ends = (uint32_t)((o >> 5) - R.base) * 4u;
+  return __ballot(bad) == 0ull;
+}
+
+// Start the run of chunks [cb, ce) (cb < ce): the copies of its first four
+// blocks, issued whether or not the offsets turn out valid (with malformed
+// offsets the buffer resource is empty and the copies read zeros), so that
+// every launch issues exactly four here.  False if the offsets are malformed.
+template <uint32_t RL>
+__device__ __forceinline__ bool run_start(const TensorArg &d, uint32_t cb, uint32_t ce, uint32_t ring_base,
+                                          uint32_t lane, Run &R) {
+  constexpr uint32_t log2r = RL;
+  const __attribute__((address_space(4))) uint64_t *co =
+      (const __attribute__((address_space(4))) uint64_t *)(uintptr_t)d.offs;
+  const uint64_t o0 = co[cb], o1 = co[ce];
+  const bool ok = !((o0 & 31u) || (o1 & 31u) || o1 < o0 || (o1 >> 5) > d.n_words);
+  const uint32_t log2b = log2r - 2u;
+  const uint64_t s0 = o0 >> 5, s1 = o1 >> 5;
+  R.base = ok ? (s0 >> log2b) << log2b : 0u;
+  const uint32_t bytes = ok ? (uint32_t)(s1 - R.base) * 4u : 0u;   // the host keeps streams below 4 GiB
+  R.klast = rfl(bytes ? (bytes - 1u) >> log2r : 0u);
+  R.r = __builtin_amdgcn_make_buffer_rsrc((void *)(d.words + R.base), (short)0, (int)bytes, 0x00020000);
+  const bool ends_ok = load_ends(d, R, cb, ce, o0, lane, R.ends);
+#pragma unroll
+  for (uint32_t k = 0; k < kRingBlocks; ++k) ring_copy<RL>(R, ring_base, k, lane);
+  R.p4 = rfl((uint32_t)(s0 - R.base) * 4u);
+  return ok && ends_ok;
+}
+
+// After P moved from byte offset p_old on (by at most 256 bytes, less than a
+// block): on entering a new block k, copy block k + 3 into the freed slot.
+// The block index is P's, so the ring needs no state of its own.
+template <uint32_t RL>
+__device__ __forceinline__ void ring_advance(const Run &R, uint32_t p_old, uint32_t ring_base, uint32_t lane) {
+  if ((p_old ^ R.p4) >> RL) {
+    ring_copy<RL>(R, ring_base, (R.p4 >> RL) + (kRingBlocks - 1u), lane);
+    ring_wait2<RL>();
+  }
+}
+
+// P += 4 * (lanes of m), on the scalar unit
+__device__ __forceinline__ void p4_add(uint32_t &p4, uint64_t m) {
+  uint32_t r;
+  asm("s_lshl2_add_u32 %0, %1, %2" : "=s"(r) : "s"((uint32_t)__popcll(m)), "s"(rfl(p4)) : "scc");
+  p4 = r;
+}
+
+// Lanes of mask m take the next words of the run: word P + (lower lanes of m)
+// from the ring (ring_v: the ring's LDS byte address, a multiple of its size,
+// in a vector register), merged into the bit buffer at its end.
+__device__ __forceinline__ void ring_fetch(uint64_t m, uint32_t &hi, uint32_t &lo, uint32_t &n, uint32_t p4,
+                                           uint32_t ring_v, uint32_t rmask4) {
+  const uint32_t idx = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  uint32_t a;
+  asm("v_lshl_add_u32 %0, %1, 2, %2\n\tv_and_or_b32 %0, %0, %3, %4"
+      : "=&v"(a) : "v"(idx), "s"(p4), "s"(rmask4), "v"(ring_v));
+  const uint32_t w = *(lds_u32 *)(uintptr_t)a;
+  hi |= w >> n;
+  lo = __builtin_amdgcn_alignbit(w, 0u, n);
+  n += 32u;
+}
+
+template <bool NOFB>
+__device__ __forceinline__ u32x2 wide_pair(const uint32_t *lut, uint32_t K, uint32_t hi, uint32_t lo) {
+  if (NOFB) return *(lds_u32x2 *)(uintptr_t)((hi >> (32u - kPairBitsWide)) << 3);
+  return pair_lookup<kModeGemv, kPairBitsWide>(lut, K, hi, lo);
+}
+
+// One pair of steps of a run's chunk, in the early phase of a stream encoded
+// refilling ahead (fetch iff fewer than 32 bits are held, decided before the
+// lookup, so that the word and the pair are read together) or on demand.
+// With NOFB every index of the two-code table holds a whole pair of at most
+// 12 bits (codes of at most 6 bits); in the early phase at least 32 - 12 = 20
+// bits are held before each pair (32 after the chunk's first word), so the
+// lookup made before the fetch is exact.
+template <bool EARLY, bool NOFB>
+__device__ __forceinline__ u32x2 stream_pair(const uint32_t *lut, uint32_t K, uint32_t &hi, uint32_t &lo,
+                                             uint32_t &n, uint32_t &p4, uint32_t ring_v, uint32_t rmask4) {
+  u32x2 e2;
+  if (EARLY) {
+    const uint64_t m = gt_mask(32u, n);
+    e2 = *(lds_u32x2 *)(uintptr_t)((hi >> (32u - kPairBitsWide)) << 3);
+    const uint32_t n0 = n;
+    if (__builtin_amdgcn_inverse_ballot_w64(m)) ring_fetch(m, hi, lo, n, p4, ring_v, rmask4);
+    p4_add(p4, m);
+    if (!NOFB) {
+      const uint64_t bad = need_mask(e2.y, n0);
+      if (bad) {
+        if (__builtin_amdgcn_inverse_ballot_w64(bad)) e2 = wide_pair<false>(lut, K, hi, lo);
+      }
+    }
+  } else {
+    e2 = wide_pair<NOFB>(lut, K, hi, lo);
+    const uint64_t m = need_mask(e2.y, n);
+    if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+      ring_fetch(m, hi, lo, n, p4, ring_v, rmask4);
+      e2 = wide_pair<NOFB>(lut, K, hi, lo);
+    }
+    p4_add(p4, m);
+  }
+  const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e2.y);
+  lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
+  hi = nhi;
+  n = sub_len(n, e2.y);
+  return e2;
+}
+
+// Pairs [q0, q1) of a row: decode, one v_dot2_f32_bf16 per batch slot with
+// the staged x pair, and the ring kept ahead.
+template <int BATCH, bool EARLY, bool NOFB, uint32_t RL>
+__device__ __forceinline__ void stream_pairs(const uint32_t *lut, uint32_t K, uint32_t q0, uint32_t q1,
+                                             const uint32_t *xl, uint32_t lane, float *acc, uint32_t &hi,
+                                             uint32_t &lo, uint32_t &n, Run &R, uint32_t ring_base,
+                                             uint32_t ring_v, uint32_t rmask4) {
+  constexpr uint32_t SB = XSlots<BATCH>::n;
+  const uint32_t *xp = xl + lane * (SB == 1 ? 1u : 4u) + q0 * 64u * SB;
+  for (uint32_t q = q0; q < q1; ++q, xp += 64u * SB) {
+    uint32_t x1s = 0u;
+    u32x4 x0, x1;
+    if (SB == 1) {
+      x1s = xp[0];
+    } else {
+      x0 = *reinterpret_cast<const u32x4 *>(xp);
+      x1 = *reinterpret_cast<const u32x4 *>(xp + 256);
+    }
+    const uint32_t p_old = R.p4;
+    const u32x2 e2 = stream_pair<EARLY, NOFB>(lut, K, hi, lo, n, R.p4, ring_v, rmask4);
+    if (SB == 1) {
+      acc[0] = dot2(e2.x, x1s, acc[0]);
+    } else {
+#pragma unroll
+      for (uint32_t i = 0; i < 4u; ++i) {
+        acc[i] = dot2(e2.x, x0[i], acc[i]);
+        acc[4u + i] = dot2(e2.x, x1[i], acc[4u + i]);
+      }
+    }
+    ring_advance<RL>(R, p_old, ring_base, lane);
+  }
+}
+
+// Decode the run's chunks [cb, ce) (each of d.chunk / cols whole rows) and
+// write y of their rows; returns the stream flags.
+template <int BATCH, bool NOFB, uint32_t RL>
+__device__ uint32_t stream_run(const TensorArg &d, const uint32_t *lut, uint32_t K, uint32_t l_min, Run &R,
+                               uint32_t cb, uint32_t ce, const uint32_t *xl, uint32_t batch, uint32_t lane,
+                               uint32_t ring_base) {
+  constexpr uint32_t log2r = RL;
+  constexpr uint32_t SB = XSlots<BATCH>::n;
+  const uint32_t cols = d.cols, ppr = cols >> 7, rpc = d.chunk / cols, rows = d.rows;
+  uint32_t ring_v;   // the ring's address in a vector register (an operand of v_and_or_b32)
+  asm volatile("v_mov_b32 %0, %1" : "=v"(ring_v) : "s"(ring_base));
+  const uint32_t rmask4 = rfl((4u << log2r) - 1u);
+  float *y = static_cast<float *>(d.out);
+  uint32_t flags = 0;
+  uint64_t yrow0 = (uint64_t)cb * rpc;   // first row of the y values held
+  uint32_t ycnt = 0;
+  float yv[SB];
+#pragma unroll
+  for (uint32_t b = 0; b < SB; ++b) yv[b] = 0.f;
+  ring_wait2<RL>();   // blocks 0 and 1 of the run
+  for (uint32_t c = cb; c < ce; ++c) {
+    if (c != cb && ((c - cb) & 63u) == 0u) {   // the next 64 chunk ends
+      const uint64_t o_start = R.base * 32u + R.p4 * 8u;
+      if (!load_ends(d, R, c, ce, o_start, lane, R.ends)) {
+        flags |= kFOffsets;
+        break;
+      }
+    }
+    const uint32_t end4 = __builtin_amdgcn_readlane(R.ends, (int)((c - cb) & 63u));
+    // rows of this chunk (the last chunk of a tensor may hold fewer) and the
+    // pairs of its early phase
+    const uint32_t nr = (uint32_t)min((uint64_t)rpc, (uint64_t)rows - (uint64_t)c * rpc);
+    const uint32_t early_n = rfl(early_pairs(d.ahead, nr * (cols >> 6), l_min));
+    // the chunk's first decision point: every lane takes one word (both
+    // refill rules agree there: no bits are held)
+    uint32_t hi = 0, lo = 0, n = 0;
+    ring_fetch(~0ull, hi, lo, n, R.p4, ring_v, rmask4);
+    const uint32_t p_old = R.p4;
+    R.p4 = rfl(R.p4 + 256u);
+    ring_advance<RL>(R, p_old, ring_base, lane);
+    uint32_t kk = 0;   // pairs of the chunk done
+    for (uint32_t r = 0; r < nr; ++r, kk += ppr) {
+      float acc[SB];
+#pragma unroll
+      for (uint32_t b = 0; b < SB; ++b) acc[b] = 0.f;
+      const uint32_t qe = early_n > kk ? min(early_n - kk, ppr) : 0u;
+      stream_pairs<BATCH, true, NOFB, RL>(lut, K, 0u, qe, xl, lane, acc, hi, lo, n, R, ring_base, ring_v, rmask4);
+      stream_pairs<BATCH, false, NOFB, RL>(lut, K, qe, ppr, xl, lane, acc, hi, lo, n, R, ring_base, ring_v, rmask4);
+      // row end: the row's sums (lane 63 after the reduction) go to lane ycnt
+#pragma unroll
+      for (uint32_t b = 0; b < SB; ++b) {
+        const float s =
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_sum63(acc[b])), 63));
+        yv[b] = lane == ycnt ? s : yv[b];
+      }
+      if (++ycnt == 64u) {
+#pragma unroll
+        for (uint32_t b = 0; b < SB; ++b)
+          if (b < batch) y[(uint64_t)b * rows + yrow0 + lane] = yv[b];
+        yrow0 += 64u;
+        ycnt = 0;
+      }
+    }
+    if (R.p4 != end4) flags |= R.p4 < end4 ? kFUnderrun : kFOverrun;
+    if (hi | lo) flags |= kFPadding;
+    if (R.p4 != end4) break;   // malformed: the rest of the run is not decoded
+  }
+  if (ycnt) {
+#pragma unroll
+    for (uint32_t b = 0; b < SB; ++b)
+      if (b < batch && lane < ycnt) y[(uint64_t)b * rows + yrow0 + lane] = yv[b];
+  }
+  return flags;
+}
+
+// The 64-SGPR budget lets two 16-wave workgroups share a CU where the LDS
+// allows it (with 84 SGPRs only one was resident: 3.86 against 3.38 ms per
+// token on the Mistral-shaped stack at 3.9 bits per weight, batch 1).
+template <int BATCH, uint32_t RL>
+__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKernelSgprs))) void ecw_gemv_stream_kernel(
+    const StreamArgs a) {
+  constexpr uint32_t SB = XSlots<BATCH>::n;
+  // dynamic LDS: the two-code table (kPairBitsWide index bits, at LDS address
+  // 0), the code table (lut_cap entries), the staged activations (x_words),
+  // the table-state word, then one ring per wavefront
+  u32x2 *ptab = reinterpret_cast<u32x2 *>(dyn_lds);
+  uint32_t *lut = reinterpret_cast<uint32_t *>(dyn_lds) + (2u << kPairBitsWide);
+  uint32_t *xl = lut + a.lut_cap;
+  uint32_t *state = reinterpret_cast<uint32_t *>(dyn_lds) + a.flag_word;
+  const uint32_t wave = rfl(threadIdx.x >> 6);
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t ring_base = rfl(lds_addr(dyn_lds) + a.ring_off + (wave << (RL + 2u)));
+  if (!lds_at_zero()) {   // the two-code table is addressed from LDS address 0
+    if (threadIdx.x == 0)
+      for (uint32_t i = 0; i < a.n_tensors; ++i) atomicOr(a.t[i].status, kFLut);
+    return;
+  }
+  const uint32_t b = blockIdx.x;
+  const uint32_t g0 = b * a.chunks_q + min(b, a.chunks_r);
+  const uint32_t g1 = g0 + a.chunks_q + (b < a.chunks_r ? 1u : 0u);
+  uint32_t ti = 0;
+  for (uint32_t g = g0; g < g1;) {
+    while (ti + 1 < a.n_tensors && a.chunk_begin[ti + 1] <= g) ++ti;
+    const TensorArg &d = a.t[ti];
+    const uint32_t seg_end = min(g1, a.chunk_begin[ti + 1]);
+    const uint32_t len = seg_end - g;
+    const uint32_t c0 = g - a.chunk_begin[ti];
+    const uint32_t cb = c0 + (wave * len) / kWaves, ce = c0 + ((wave + 1u) * len) / kWaves;
+    g = seg_end;
+    // table switch: activations and table entries into registers, the run's
+    // first copies in flight, then (after the barrier) the LDS writes
+    const bool x_vec = x_vec_ok(d.x);
+    XRegs xr;
+    if (x_vec) x_load<BATCH>(xr, d.x, d.cols, a.batch, 0u, d.cols >> 7);
+    const uint32_t ne_fetch = min(a.lut_cap, d.lut_words > kLutHeaderWords ? d.lut_words - kLutHeaderWords : 0u);
+    const uint32_t nv = ((uintptr_t)d.lut & 15u) == 0u ? ne_fetch >> 2 : 0u;
+    u32x4 lv = {0u, 0u, 0u, 0u};
+    uint32_t h0 = 0, h1 = 0, hne = 0, hl1 = 0;
+    if (threadIdx.x < nv) lv = reinterpret_cast<const u32x4 *>(d.lut + kLutHeaderWords)[threadIdx.x];
+    if (d.lut_words >= kLutHeaderWords) {   // scalar loads: nothing to wait for among the vector loads
+      const __attribute__((address_space(4))) uint32_t *ch =
+          (const __attribute__((address_space(4))) uint32_t *)(uintptr_t)d.lut;
+      h0 = ch[0], h1 = ch[1], hne = ch[2], hl1 = ch[3];
+    }
+    Run R;
+    const bool have = cb < ce;
+    const bool run_ok = have && run_start<RL>(d, cb, ce, ring_base, lane, R);
+    __syncthreads();
+    if (threadIdx.x == 0) *state = 0u;
+    if (threadIdx.x < nv)
+      reinterpret_cast<u32x4 *>(lut)[threadIdx.x] =
+          u32x4{kernel_entry<kModeGemv>(lv[0]), kernel_entry<kModeGemv>(lv[1]), kernel_entry<kModeGemv>(lv[2]),
+                kernel_entry<kModeGemv>(lv[3])};
+    for (uint32_t i = 4u * nv + threadIdx.x; i < ne_fetch; i += kBlockThreads)
+      lut[i] = kernel_entry<kModeGemv>(d.lut[kLutHeaderWords + i]);
+    if (x_vec) x_store<BATCH>(xl, xr, d.cols >> 7);
+    else stage_x<BATCH>(xl, d.x, d.cols, a.batch, 0u, d.cols >> 7);
+    uint32_t k = 0;
+    if (d.lut_words >= kLutHeaderWords) {
+      const uint32_t kk = h1 & 0xFFu, lmin = h1 >> 24;
+      if (h0 == kLutMagic && (h1 & 0x00FFFF00u) == d.expect_hdr && kk >= 1 && kk <= kSingleLevelMax &&
+          hl1 == (1u << kk) && hne >= hl1 && hne <= a.lut_cap && hne <= d.lut_words - kLutHeaderWords &&
+          lmin >= 1u && lmin <= kMaxCodeLen)
+        k = kk | (lmin << 24);
+    }
+    k = rfl(k);
+    if (!k && threadIdx.x == 0) atomicOr(d.status, kFLut);
+    const uint32_t K = k & 0xFFu, l_min = k >> 24;
+    __syncthreads();
+    // two-code table; does any index miss a whole pair?
+    bool miss = false;
+    if (K) {
+      for (uint32_t i = threadIdx.x; i < (1u << kPairBitsWide); i += kBlockThreads) {
+        const u32x2 e = build_pair_entry<kModeGemv, kPairBitsWide>(lut, K, i);
+        ptab[i] = e;
+        miss |= (e.y & kPairFallback) != 0u;
+      }
+    }
+    if (__ballot(miss) && lane == 0) atomicOr(state, 1u);
+    __syncthreads();
+    const bool nofb = rfl(*state) == 0u;
+    if (!K) {
+      wait_lds_copy();   // the run's first copies land before the ring is reused
+      continue;
+    }
+    uint32_t flags = 0;
+    if (have && !run_ok) flags = kFOffsets;
+    else if (run_ok)
+      flags = nofb ? stream_run<BATCH, true, RL>(d, lut, K, l_min, R, cb, ce, xl, a.batch, lane, ring_base)
+                   : stream_run<BATCH, false, RL>(d, lut, K, l_min, R, cb, ce, xl, a.batch, lane, ring_base);
+    if (flags && lane == 0) atomicOr(d.status, flags);
+    // copies past the run's end may still be in flight into this ring
+    wait_lds_copy();
+  }
+  wait_lds_copy();
+  (void)SB;
 }
 
 // Where a staged task's words sit in its LDS area: chunk of lane group g
@@ -1829,6 +2224,151 @@ static hipError_t launch_w(uint32_t log2w, uint32_t total_tasks, LaunchArgs &a, 
   }
 }
 
+// Streamed GEMV launches (ecw_gemv_stream_kernel): tensors with 64 lanes,
+// 4-bit codes, refill every two steps, 128 | cols, a stream below 4 GiB,
+// and activations that fit the LDS block (eight batch slots when batch > 1).
+// Rings of 1024 words (blocks of 64 lanes x 16 bytes), or of 512 words
+// (blocks of 2 x 64 lanes x 4 bytes) where that lets two workgroups share a
+// CU or is needed to fit at all.
+constexpr uint32_t kStreamLog2Ring = 10;
+constexpr uint32_t kStreamLog2RingSmall = 9;
+
+// LDS bytes of a streamed launch (code table of lut_cap entries, x_words of
+// activations, rings of 2^log2r words); sets the layout fields of a if given.
+static size_t stream_lds_bytes(uint64_t lut_cap, uint64_t x_words, uint32_t log2r, StreamArgs *a = nullptr) {
+  size_t dyn = ((size_t)8u << kPairBitsWide) + (size_t)lut_cap * 4u + (size_t)x_words * 4u;
+  if (a) a->flag_word = (uint32_t)(dyn / 4u);
+  dyn += 16u;
+  const size_t ring_bytes = (size_t)4u << log2r;
+  dyn = (dyn + ring_bytes - 1u) / ring_bytes * ring_bytes;
+  if (a) a->ring_off = (uint32_t)dyn, a->log2_ring = log2r;
+  return dyn + (size_t)kWaves * ring_bytes;
+}
+
+static bool stream_fits(uint64_t lut_cap, uint64_t x_words, uint32_t log2r = kStreamLog2RingSmall) {
+  return stream_lds_bytes((lut_cap + 3) & ~3ull, (x_words + 3) & ~3ull, log2r) + kStaticLds <=
+         kLdsPerCu - kLdsPlanReserve;
+}
+
+// Ring size of a launch: 512 words if that gives two workgroups per CU where
+// 1024 give one, or if 1024 do not fit; else 1024.
+static uint32_t stream_ring(uint64_t lut_cap, uint64_t x_words) {
+  const size_t budget = kLdsPerCu - kLdsPlanReserve;
+  const size_t big = stream_lds_bytes(lut_cap, x_words, kStreamLog2Ring) + kStaticLds;
+  const size_t small = stream_lds_bytes(lut_cap, x_words, kStreamLog2RingSmall) + kStaticLds;
+  if (big > budget) return kStreamLog2RingSmall;
+  if (2u * big > budget && 2u * small <= budget) return kStreamLog2RingSmall;
+  return kStreamLog2Ring;
+}
+
+static uint64_t stream_lut_entries(const entro_tensor &t) {
+  const uint64_t w = std::min<uint64_t>(t.lut_bytes / 4, kLutHeaderWords + kLutMaxEntries);
+  return w > kLutHeaderWords ? w - kLutHeaderWords : 0;
+}
+
+static uint64_t stream_x_words(const entro_gemv_item &g, uint32_t batch) {
+  return (uint64_t)(g.cols >> 1) * (batch == 1 ? 1u : 8u);
+}
+
+static bool stream_ok(const entro_tensor &t, const entro_gemv_item &g, uint32_t batch) {
+  if (t.n_symbols == 0 || t.lanes != 64u || t.sym_bits != 4u || t.refill_steps != 2u) return false;
+  if (g.cols == 0 || (g.cols & 127u) || t.chunk_symbols % g.cols) return false;
+  if (t.n_words >= (1ull << 30)) return false;
+  const uint64_t xw = stream_x_words(g, batch);   // the activation staging moves at most kGemvXMaxBytes
+  return xw * 4u <= kGemvXMaxBytes && stream_fits(stream_lut_entries(t), xw);
+}
+
+struct StreamPlan {
+  StreamArgs a;
+  size_t dyn;
+  uint32_t total;
+};
+
+template <int BATCH>
+static hipError_t launch_stream(StreamPlan &pl, hipStream_t s) {
+  auto kern = pl.a.log2_ring == kStreamLog2Ring ? ecw_gemv_stream_kernel<BATCH, kStreamLog2Ring>
+                                                : ecw_gemv_stream_kernel<BATCH, kStreamLog2RingSmall>;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBlockThreads, pl.dyn) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int lds_fit = (int)((kLdsPerCu - kLdsPlanReserve) / (pl.dyn + kStaticLds));
+  if (lds_fit >= 1 && per_cu > lds_fit) per_cu = lds_fit;
+  if (cus < 1) cus = 1;
+  // as for the decode kernel: the fewest workgroups per CU that give every
+  // wavefront a chunk, the chunks spread evenly
+  const uint64_t k = std::min<uint64_t>((uint64_t)per_cu,
+                                        (pl.total + (uint64_t)kWaves * cus - 1) / ((uint64_t)kWaves * cus));
+  const uint32_t grid = (uint32_t)std::min<uint64_t>((uint64_t)cus * std::max<uint64_t>(k, 1), pl.total);
+  pl.a.chunks_q = pl.total / grid;
+  pl.a.chunks_r = pl.total % grid;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlockThreads), pl.dyn, s, pl.a);
+  return hipGetLastError();
+}
+
+// Plan the streamed launches of the tensors marked in `take` (groups of up to
+// 32).
+static entro_status plan_stream(const entro_tensor *t, size_t n, const entro_gemv_item *g, uint32_t batch,
+                                uint32_t *d_status, const std::vector<char> &take, std::vector<StreamPlan> &plans) {
+  size_t i = 0;
+  while (i < n) {
+    plans.emplace_back();
+    StreamPlan &pl = plans.back();
+    std::memset(&pl, 0, sizeof pl);
+    StreamArgs &a = pl.a;
+    a.batch = batch;
+    uint32_t total = 0, k = 0;
+    uint64_t lut_need = 0, x_need = 0;
+    for (; i < n && k < (uint32_t)kMaxTensorsPerLaunch; ++i) {
+      if (!take[i]) continue;
+      const entro_tensor &x = t[i];
+      const uint64_t nc = (x.n_symbols + x.chunk_symbols - 1) / x.chunk_symbols;
+      if ((uint64_t)total + nc > 0x7FFFFFFFull) break;
+      // a tensor whose table or activations would overflow this launch's LDS
+      // starts the next one (each fits alone: stream_ok)
+      if (k && !stream_fits(std::max(lut_need, stream_lut_entries(x)), std::max(x_need, stream_x_words(g[i], batch))))
+        break;
+      TensorArg &d = a.t[k];
+      d.lut = static_cast<const uint32_t *>(x.d_lut);
+      d.words = x.d_words;
+      d.offs = x.d_chunk_bit_off;
+      d.status = d_status + i;
+      d.n_words = x.n_words;
+      d.n_symbols = x.n_symbols;
+      d.chunk = x.chunk_symbols;
+      d.n_chunks = (uint32_t)nc;
+      d.expect_hdr = (x.sym_bits << 8) | (x.max_len << 16);
+      d.lut_words = (uint32_t)std::min<uint64_t>(x.lut_bytes / 4, kLutHeaderWords + kLutMaxEntries);
+      d.refill_steps = 2u;
+      d.ahead = x.refill_ahead;
+      d.out = g[i].d_y;
+      d.x = g[i].d_x;
+      d.rows = g[i].rows;
+      d.cols = g[i].cols;
+      d.n_tasks = (uint32_t)nc;
+      a.chunk_begin[k] = total;
+      total += (uint32_t)nc;
+      lut_need = std::max<uint64_t>(lut_need, stream_lut_entries(x));
+      x_need = std::max<uint64_t>(x_need, stream_x_words(g[i], batch));
+      ++k;
+    }
+    if (k == 0) {
+      plans.pop_back();
+      continue;
+    }
+    a.n_tensors = k;
+    for (uint32_t r = k; r <= (uint32_t)kMaxTensorsPerLaunch; ++r) a.chunk_begin[r] = total;
+    a.lut_cap = (uint32_t)((lut_need + 3) & ~3ull);
+    a.x_words = (uint32_t)((x_need + 3) & ~3ull);
+    pl.dyn = stream_lds_bytes(a.lut_cap, a.x_words, stream_ring(a.lut_cap, a.x_words), &a);
+    if (pl.dyn + kStaticLds > kLdsPerCu - kLdsPlanReserve) return ENTRO_E_UNSUPPORTED;   // not reached (stream_ok)
+    pl.total = total;
+  }
+  return ENTRO_OK;
+}
+
 // One planned launch: its arguments, dynamic LDS bytes and task count.
 struct LaunchPlan {
   LaunchArgs a;
@@ -1864,6 +2404,17 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
       if (!outs[i] || (reinterpret_cast<uintptr_t>(outs[i]) & (align - 1u))) return ENTRO_E_INVAL;
     }
   }
+  // GEMV tensors of the streamed layout take the streamed kernel
+  std::vector<char> take(n, 0);
+  std::vector<StreamPlan> splans;
+  if (mode == kModeGemv) {
+    bool any = false;
+    for (size_t j = 0; j < n; ++j) any |= (take[j] = stream_ok(t[j], g[j], batch) ? 1 : 0) != 0;
+    if (any) {
+      const entro_status st = plan_stream(t, n, g, batch, d_status, take, splans);
+      if (st != ENTRO_OK) return st;
+    }
+  }
   std::vector<LaunchPlan> plans;
   size_t i = 0;
   while (i < n) {
@@ -1879,7 +2430,7 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
     bool stage_known = true, want_pairs = false;
     for (; i < n && k < (uint32_t)kMaxTensorsPerLaunch; ++i) {
       const entro_tensor &x = t[i];
-      if (x.n_symbols == 0) continue;
+      if (x.n_symbols == 0 || take[i]) continue;
       const uint32_t lw = log2u(x.lanes);
       const bool xc = mode != kModeGemv && x.out_cached;
       if (k == 0) log2w = lw, cached = xc;
@@ -1963,6 +2514,10 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
     pl.total = total;
     pl.log2w = log2w;
     pl.cached = cached;
+  }
+  for (StreamPlan &sp : splans) {
+    const hipError_t err = batch == 1 ? launch_stream<1>(sp, s) : launch_stream<8>(sp, s);
+    if (err != hipSuccess) return ENTRO_E_HIP;
   }
   for (LaunchPlan &pl : plans) {
     hipError_t err;

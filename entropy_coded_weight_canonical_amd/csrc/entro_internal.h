@@ -106,7 +106,28 @@ struct GemmArgs {
   uint32_t state_word;                             // LDS word of the table state
 };
 
+// Streamed fused GEMV (W = 64, 4-bit codes in pairs, chunks of whole rows,
+// 128 | cols): workgroup b takes chunks_q chunks of the launch's chunk space
+// (the tensors' chunks one after another; one more if b < chunks_r), from
+// chunk b * chunks_q + min(b, chunks_r) on.  Each wavefront streams the words
+// of its chunks through a ring of kRingBlocks blocks in LDS.
+constexpr uint32_t kRingBlocks = 4;
+
+struct StreamArgs {
+  TensorArg t[kMaxTensorsPerLaunch];
+  uint32_t chunk_begin[kMaxTensorsPerLaunch + 1];  // first chunk of each tensor (then the total)
+  uint32_t n_tensors;
+  uint32_t batch;
+  uint32_t chunks_q, chunks_r;
+  uint32_t lut_cap;        // code-table entries reserved in LDS (a multiple of 4)
+  uint32_t x_words;        // LDS words of the staged activations
+  uint32_t flag_word;      // LDS word index of the workgroup's table-state word
+  uint32_t ring_off;       // LDS byte offset of the first ring (a multiple of the ring's bytes)
+  uint32_t log2_ring;      // log2 of a ring's words (a block is a quarter of it)
+};
+
 constexpr uint32_t kPairBits = 10;                 // two-code table: 1024 entries of 8 bytes
+constexpr uint32_t kPairBitsWide = 12;             // streamed GEMV: 4096 entries of 8 bytes
 constexpr uint32_t kPairFallback = 0x80u;          // flag (byte 0 of the second word): no pair
 
 }  // namespace entro
