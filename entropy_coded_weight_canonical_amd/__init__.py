@@ -18,7 +18,8 @@ import numpy as np
 __all__ = [
     "LibraryNotBuilt", "EntroError", "library_path", "load",
     "Codebook", "Tensor", "GemvItem", "RansTensor", "FLAGS",
-    "lut_bytes", "lut_build", "decode", "decode_dequant", "decode_gemv", "decode_gemm", "status_str",
+    "lut_bytes", "lut_build", "decode", "decode_dequant", "decode_gemv", "GemvCall", "decode_gemm",
+    "status_str",
     "quantize", "code_lengths", "encode_layout", "encode",
     "rans_freqs", "rans_table_build", "rans_encode", "rans_decode", "rans_decode_dequant",
     "SCHEME_ASYMMETRIC", "SCHEME_UNSIGNED", "SCHEME_MIXED",
@@ -215,6 +216,26 @@ def decode_gemv(tensors, items, batch: int, d_status: int, stream=None) -> None:
     _check(load().entro_decode_gemv(ta, len(tensors), ia, int(batch), ctypes.c_void_p(d_status),
                                     ctypes.c_void_p(_stream_handle(stream))), "entro_decode_gemv")
 
+
+
+class GemvCall:
+    """``entro_decode_gemv`` over a fixed set of tensors and items, with the
+    ctypes argument arrays built once (a caller that repeats the same call,
+    such as a per-token loop, then pays no marshalling per call)."""
+
+    def __init__(self, tensors, items, batch: int, d_status: int):
+        self._t = _tensor_array(tensors)
+        self._i = (GemvItem * len(items))()
+        for i, it in enumerate(items):
+            self._i[i] = it
+        self._n = len(tensors)
+        self._batch = int(batch)
+        self._st = ctypes.c_void_p(d_status)
+        self._fn = load().entro_decode_gemv
+
+    def __call__(self, stream=None) -> None:
+        _check(self._fn(self._t, self._n, self._i, self._batch, self._st, ctypes.c_void_p(_stream_handle(stream))),
+               "entro_decode_gemv")
 
 def decode_gemm(tensors, items, n_tokens: int, d_status: int, stream=None) -> None:
     """``entro_decode_gemm``: like ``decode_gemv`` for ``n_tokens`` (1..512)

@@ -93,3 +93,34 @@ def test_cpu_baseline_record(lib):
     assert rec["kind"] == "oracle" and rec["unit"] == "Gsym/s"
     assert rec["value"] > 0 and rec["single_thread_value"] > 0 and rec["decode_only_value"] > 0
     assert rec["cores"] >= 1 and rec["nproc"] >= 1 and isinstance(rec["cpu_model"], str)
+
+
+def test_profiles_apply_only_to_their_sources_and_configuration(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_src_sha", lambda: "abc123")
+    (prof / "counters_k.txt").write_text("config: cfg A\nkernel_src_sha: abc123\n"
+                                         "valu_lane_ops_per_symbol: 8.0   # a comment\n")
+    r = bench.gemv_roofline("k", "cfg A", 2e12, 1e9, 1.0)
+    assert r["bound"] == "alu" and r["valu_lane_ops_per_symbol"] == 8.0
+    assert r["achieved"] == pytest.approx(16000.0) and r["frac"] == pytest.approx(16000.0 / r["peak"], rel=1e-3)
+    assert r["peak"] == pytest.approx(256 * 4 * 16 * 2.4)
+    assert r["hbm"]["achieved"] == pytest.approx(1000.0) and r["hbm"]["frac"] == pytest.approx(0.125)
+    r = bench.gemv_roofline("k", "cfg B", 2e12, 1e9, 1.0)       # taken on another configuration
+    assert r["achieved"] is None and r["frac"] is None and r["hbm"]["frac"] == pytest.approx(0.125)
+
+
+def test_workload_table_matches_the_stated_configurations():
+    """configs[0..4] in order: sizes and code widths as stated; GEMV chunks
+    hold whole rows."""
+    w = bench.WORKLOADS
+    assert [w[k]["config"] for k in ("tensor_2048", "tensor_4096", "smollm_stack", "phi3_stack", "mistral_stack")] \
+        == [1, 2, 3, 4, 5]
+    assert (w["tensor_2048"]["bits"], w["tensor_2048"]["scheme"], w["tensor_2048"]["chunk"]) == (8, "asymmetric", 4096)
+    assert (w["tensor_4096"]["bits"], w["tensor_4096"]["scheme"], w["tensor_4096"]["chunk"],
+            w["tensor_4096"]["lanes"]) == (4, "unsigned", 8192, 32)
+    assert w["smollm_stack"]["bits"] == 8 and w["phi3_stack"]["bits"] == 4 and w["mistral_stack"]["bits"] == 4
+    for cols in (1024, 3072, 4096, 8192, 14336):
+        c = bench.gemv_chunk(cols, 4096)
+        assert c % cols == 0 and c >= cols
