@@ -1518,12 +1518,8 @@ __device__ uint32_t stream_run(const TensorArg &d, const uint32_t *lut, uint32_t
   return flags;
 }
 
-// The 64-SGPR budget lets two 16-wave workgroups share a CU where the LDS
-// allows it (with 84 SGPRs only one was resident: 3.86 against 3.38 ms per
-// token on the Mistral-shaped stack at 3.9 bits per weight, batch 1).
 template <int BATCH, uint32_t RL>
-__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKernelSgprs))) void ecw_gemv_stream_kernel(
-    const StreamArgs a) {
+__device__ __forceinline__ void gemv_stream(const StreamArgs &a) {
   constexpr uint32_t SB = XSlots<BATCH>::n;
   // dynamic LDS: the two-code table (kPairBitsWide index bits, at LDS address
   // 0), the code table (lut_cap entries), the staged activations (x_words),
@@ -1619,6 +1615,20 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
   }
   wait_lds_copy();
   (void)SB;
+}
+
+// Batch 1: two 16-wave workgroups share a CU where the LDS allows it, which
+// takes at most 64 SGPRs and 64 VGPRs per wavefront (8 wavefronts per SIMD).
+// Batch 8: its activations leave room for one workgroup per CU; no budget.
+template <uint32_t RL>
+__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKernelSgprs), amdgpu_waves_per_eu(8)))
+void ecw_gemv_stream_kernel(const StreamArgs a) {
+  gemv_stream<1, RL>(a);
+}
+
+template <uint32_t RL>
+__global__ __launch_bounds__(kBlockThreads) void ecw_gemv8_stream_kernel(const StreamArgs a) {
+  gemv_stream<8, RL>(a);
 }
 
 // Where a staged task's words sit in its LDS area: chunk of lane group g
@@ -2286,8 +2296,10 @@ struct StreamPlan {
 
 template <int BATCH>
 static hipError_t launch_stream(StreamPlan &pl, hipStream_t s) {
-  auto kern = pl.a.log2_ring == kStreamLog2Ring ? ecw_gemv_stream_kernel<BATCH, kStreamLog2Ring>
-                                                : ecw_gemv_stream_kernel<BATCH, kStreamLog2RingSmall>;
+  auto kern = BATCH == 1 ? (pl.a.log2_ring == kStreamLog2Ring ? ecw_gemv_stream_kernel<kStreamLog2Ring>
+                                                              : ecw_gemv_stream_kernel<kStreamLog2RingSmall>)
+                         : (pl.a.log2_ring == kStreamLog2Ring ? ecw_gemv8_stream_kernel<kStreamLog2Ring>
+                                                              : ecw_gemv8_stream_kernel<kStreamLog2RingSmall>);
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
