@@ -114,6 +114,8 @@ def load():
     lib.entro_rans_encode.argtypes = [P, U64, P, U32, U32, U32, P, P, U64, P, U32]
     for name in ("entro_rans_decode", "entro_rans_decode_dequant"):
         getattr(lib, name).argtypes = [P, SZ, P, P, P]
+    lib.entro_set_max_workgroups.argtypes = [U32]
+    lib.entro_set_max_workgroups.restype = U32
     lib.entro_status_str.argtypes = [ctypes.c_int]
     lib.entro_status_str.restype = ctypes.c_char_p
     lib.entro_quantize.argtypes = [P, U64, U32, ctypes.c_int, ctypes.c_float, P, P, P, P]
@@ -246,6 +248,12 @@ def decode_gemm(tensors, items, n_tokens: int, d_status: int, stream=None) -> No
         ia[i] = it
     _check(load().entro_decode_gemm(ta, len(tensors), ia, int(n_tokens), ctypes.c_void_p(d_status),
                                     ctypes.c_void_p(_stream_handle(stream))), "entro_decode_gemm")
+
+
+def set_max_workgroups(n: int) -> int:
+    """``entro_set_max_workgroups``: cap the workgroups of later launches (0:
+    no cap); returns the previous cap."""
+    return int(load().entro_set_max_workgroups(int(n)))
 
 
 def _rans_array(tensors):

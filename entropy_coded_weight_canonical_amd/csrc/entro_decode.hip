@@ -41,6 +41,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <type_traits>
 #include <vector>
@@ -1256,28 +1257,38 @@ struct Run {
   uint64_t base;     // first word of block 0 (stream word index)
   uint32_t p4;       // byte offset of P from the base
   uint32_t klast;    // the run's last block
+  uint32_t bytes;    // the run's bytes from the base (the buffer resource's range)
   uint32_t ends;     // per lane: end of chunk c64 + lane (byte offset from the base)
 };
 
 // Copy block k of the run into its ring slot.  A ring of 2^RL words holds
 // four blocks of 2^RL bytes: with RL = 10 one 16-byte copy per lane (64 lanes
 // x 16 bytes), with RL = 9 two 4-byte copies per lane (2 x 64 lanes x 4
-// bytes), so that every lane takes part in every copy.  A block past the
-// run's end is never read; its slot receives the run's last block again
-// instead, so that every copy reads memory.  (The waits count copies in
-// flight and rely on copies completing in the order they were issued; a
-// copy wholly outside the buffer resource reads no memory and could
-// complete ahead of earlier ones.)
+// bytes), so that every lane takes part in every copy.  Every copy
+// instruction reads memory: a block past the run's end is never read, and
+// its slot receives the run's last block again instead; likewise the second
+// half of the last block, where it lies wholly past the run's end, is
+// replaced by the first.  (The waits count copies in flight and rely on
+// copies completing in the order they were issued; a copy wholly outside
+// the buffer resource reads no memory and can complete ahead of earlier
+// ones.)  The copy's LDS write does not pass through the LDS instruction
+// queue, so it can land before an LDS read of the slot that was issued
+// earlier (the chunk's first fetch reads the block being left when the copy
+// is issued); the wavefront's LDS reads are waited for first.
 template <uint32_t RL>
 __device__ __forceinline__ void ring_copy(const Run &R, uint32_t ring_base, uint32_t k, uint32_t lane) {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  asm volatile("" ::: "memory");
   const uint32_t dst = ring_base + ((k << RL) & ((4u << RL) - 1u));
   const uint32_t src = min(k, R.klast) << RL;
   if (RL == 10) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(R.r, (lds_void *)(uintptr_t)rfl(dst), 16, lane * 16u, rfl(src), 0, 0);
   } else {
+    const uint32_t src2 = src + 256u < R.bytes ? src + 256u : src;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(R.r, (lds_void *)(uintptr_t)rfl(dst), 4, lane * 4u, rfl(src), 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(R.r, (lds_void *)(uintptr_t)rfl(dst + 256u), 4, lane * 4u,
-                                             rfl(src + 256u), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(R.r, (lds_void *)(uintptr_t)rfl(dst + 256u), 4, lane * 4u, rfl(src2),
+                                             0, 0);
   }
 }
 
@@ -1308,9 +1319,9 @@ __device__ __forceinline__ bool load_ends(const TensorArg &d, const Run &R, uint
 }
 
 // Start the run of chunks [cb, ce) (cb < ce): the copies of its first four
-// blocks, issued whether or not the offsets turn out valid (with malformed
-// offsets the buffer resource is empty and the copies read zeros), so that
-// every launch issues exactly four here.  False if the offsets are malformed.
+// blocks.  False if the offsets are malformed; then no copy is issued (the
+// buffer resource would be empty, and a copy that reads no memory can
+// complete out of order), and the run is not decoded.
 template <uint32_t RL>
 __device__ __forceinline__ bool run_start(const TensorArg &d, uint32_t cb, uint32_t ce, uint32_t ring_base,
                                           uint32_t lane, Run &R) {
@@ -1324,10 +1335,13 @@ __device__ __forceinline__ bool run_start(const TensorArg &d, uint32_t cb, uint3
   R.base = ok ? (s0 >> log2b) << log2b : 0u;
   const uint32_t bytes = ok ? (uint32_t)(s1 - R.base) * 4u : 0u;   // the host keeps streams below 4 GiB
   R.klast = rfl(bytes ? (bytes - 1u) >> log2r : 0u);
+  R.bytes = rfl(bytes);
   R.r = __builtin_amdgcn_make_buffer_rsrc((void *)(d.words + R.base), (short)0, (int)bytes, 0x00020000);
   const bool ends_ok = load_ends(d, R, cb, ce, o0, lane, R.ends);
+  if (bytes) {
 #pragma unroll
-  for (uint32_t k = 0; k < kRingBlocks; ++k) ring_copy<RL>(R, ring_base, k, lane);
+    for (uint32_t k = 0; k < kRingBlocks; ++k) ring_copy<RL>(R, ring_base, k, lane);
+  }
   R.p4 = rfl((uint32_t)(s0 - R.base) * 4u);
   return ok && ends_ok;
 }
@@ -2166,8 +2180,362 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
 }
 
 // ---------------------------------------------------------------------------
+// Fused GEMV of 2..8 activation rows on the matrix cores: the streamed layout
+// (W = 64, 4-bit codes, refill every two steps) with one row per chunk,
+// 512 | cols and cols >= 1024.
+//
+// A workgroup takes whole tiles of 16 consecutive rows.  Over the T tiles of
+// its share that lie in one tensor, wavefront w takes the T consecutive rows
+// [16 T' + w T, ...) of that range, one contiguous run of the stream that it
+// streams through its ring exactly as the batch-1 kernel does; at step r the
+// r-th rows of the 16 wavefronts form a tile.  The wavefronts advance in
+// lockstep by slices of four pair steps (512 columns):
+// - decode: wavefront m writes each pair it decodes, as the lane holds it
+//   (the bf16 weights of columns 128q + j and 128q + 64 + j in one dword),
+//   into row m of an LDS tile of 16 rows x 256 dwords (two such tiles);
+// - barrier;
+// - multiply: wavefront w takes dwords [16w, 16w + 16) of every tile row,
+//   i.e. 32 columns, as the A operand of v_mfma_f32_16x16x32_bf16 and the
+//   same columns of x, paired the same way, as B (token n in column n,
+//   tokens >= batch zero), accumulating 16 rows x 16 tokens in fp32.
+// At a row end the 16 wavefronts' partial tiles go to LDS and, after the next
+// barrier, wavefront m adds the 16 partials of its own row; the sums of up to
+// 64 rows wait in registers (lane i: the wavefront's i-th row) before their
+// store.  x streams through LDS as well: three buffers of one 512-column
+// slice per token, which wavefront n (< batch) fills for token n two slices
+// ahead with 16-byte copies that write LDS directly.  Every weight is decoded
+// once; the matrix cores do every multiplication.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kTileRowBytes = 1040;   // one A row: 256 dwords, then 16 bytes that skew the banks
+constexpr uint32_t kTileXBytes = 1056;     // one token's x slice: 512 bf16, then 32 bytes that skew the banks
+constexpr uint32_t kTileXBufs = 3;
+constexpr uint32_t kTileLog2Ring = 9;
+
+typedef __attribute__((address_space(3))) uint32_t lds_w32;
+typedef __attribute__((address_space(3))) u32x4 lds_w32x4;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+
+// s_waitcnt vmcnt(n) for a wavefront-uniform n (above 15: vmcnt(15), which
+// waits for more than asked)
+__device__ __forceinline__ void wait_vm(uint32_t n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
+    case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
+  }
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier over LDS only: this wavefront's LDS accesses have
+// completed (lgkmcnt(0)), and its vector-memory operations in flight (ring
+// and x copies) stay in flight, unlike __syncthreads(), whose fence waits
+// for them all.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Pairs [q0, q1) of the slice: decode, write to the wavefront's tile row
+// (arow: its LDS byte address plus 4 lane), keep the ring ahead; ops counts
+// the copy instructions issued.
+template <bool EARLY, bool NOFB, uint32_t RL>
+__device__ __forceinline__ void tile_pairs(const uint32_t *lut, uint32_t K, uint32_t q0, uint32_t q1, uint32_t arow,
+                                           uint32_t &hi, uint32_t &lo, uint32_t &n, Run &R, uint32_t ring_base,
+                                           uint32_t ring_v, uint32_t rmask4, uint32_t lane, uint32_t &ops) {
+  for (uint32_t q = q0; q < q1; ++q) {
+    const uint32_t p_old = R.p4;
+    const u32x2 e2 = stream_pair<EARLY, NOFB>(lut, K, hi, lo, n, R.p4, ring_v, rmask4);
+    *(lds_w32 *)(uintptr_t)(arow + 256u * q) = e2.x;
+    if ((p_old ^ R.p4) >> RL) {
+      ring_copy<RL>(R, ring_base, (R.p4 >> RL) + (kRingBlocks - 1u), lane);
+      ring_wait2<RL>();
+      ops += RingCopies<RL>::n;
+    }
+  }
+}
+
+// The 512 columns of slice sl of token tok's activations into LDS (x_lds:
+// that token's place in the buffer), one 16-byte copy per lane.
+__device__ __forceinline__ void tile_x_copy(__amdgpu_buffer_rsrc_t xr, uint32_t x_lds, uint32_t cols, uint32_t tok,
+                                            uint32_t sl, uint32_t lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)(uintptr_t)rfl(x_lds), 16, lane * 16u,
+                                           rfl(tok * cols * 2u + sl * 1024u), 0, 0);
+}
+
+// One slice's product for wavefront w: A = dwords [16w, 16w + 16) of the 16
+// tile rows (lane: row lane mod 16, dwords 16w + 4 (lane / 16) .. + 3), B =
+// the same columns of x for token lane mod 16 (zero past the batch), paired
+// as the weights are: dword i holds columns c + i and c + 64 + i.
+__device__ __forceinline__ f32x4 tile_mma(uint32_t a_lds, uint32_t x_lds, uint32_t wave, uint32_t lane,
+                                          uint32_t batch, f32x4 acc) {
+  const uint32_t m = lane & 15u, g = lane >> 4;
+  const u32x4 av = *(lds_u32x4 *)(uintptr_t)(a_lds + m * kTileRowBytes + 4u * (16u * wave + 4u * g));
+  u32x4 bv = {0u, 0u, 0u, 0u};
+  if (m < batch) {
+    const uint32_t c = 128u * (wave >> 2) + 16u * (wave & 3u) + 4u * g;   // column within the slice
+    const u32x2 lo = *(lds_u32x2 *)(uintptr_t)(x_lds + m * kTileXBytes + 2u * c);
+    const u32x2 hi = *(lds_u32x2 *)(uintptr_t)(x_lds + m * kTileXBytes + 2u * (c + 64u));
+    bv[0] = (lo.x & 0xFFFFu) | (hi.x << 16);
+    bv[1] = (lo.x >> 16) | (hi.x & 0xFFFF0000u);
+    bv[2] = (lo.y & 0xFFFFu) | (hi.y << 16);
+    bv[3] = (lo.y >> 16) | (hi.y & 0xFFFF0000u);
+  }
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc,
+                                                 0, 0, 0);
+}
+
+// Wavefront w's rows [cb, ce) (ce - cb <= T, possibly none) in lockstep with
+// the workgroup's T rows per wavefront; returns the stream flags.  live: the
+// run started (cb < ce and valid offsets).
+template <bool NOFB, uint32_t RL>
+__device__ uint32_t tile_run(const TensorArg &d, const uint32_t *lut, uint32_t K, uint32_t l_min, Run &R, bool live,
+                             uint32_t cb, uint32_t ce, uint32_t T, uint32_t batch, uint32_t wave, uint32_t lane,
+                             uint32_t ring_base, uint32_t a_lds, uint32_t x_lds, uint32_t red_lds) {
+  const uint32_t cols = d.cols, spr = cols >> 9, rows = d.rows;
+  const uint32_t nsl = T * spr;
+  const uint32_t xbuf = batch * kTileXBytes;
+  uint32_t ring_v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(ring_v) : "s"(ring_base));
+  const uint32_t rmask4 = rfl((4u << RL) - 1u);
+  const uint32_t early_n = rfl(early_pairs(d.ahead, cols >> 6, l_min));
+  float *y = static_cast<float *>(d.out);
+  // x: wavefront `wave` < batch copies token `wave`; o_a (o_b) counts the
+  // vector-memory instructions issued after the oldest (newest) copy in flight
+  const bool xw = wave < batch;
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc((void *)d.x, (short)0, (int)(batch * cols * 2u), 0x00020000);
+  uint32_t o_a = 0, o_b = 0, nx = 0;
+  if (xw) {
+    tile_x_copy(xr, x_lds + wave * kTileXBytes, cols, wave, 0u, lane);
+    ++nx;
+    if (nsl > 1u) {
+      tile_x_copy(xr, x_lds + xbuf + wave * kTileXBytes, cols, wave, 1u % spr, lane);
+      ++nx;
+      o_a = 1u;
+    }
+  }
+  if (live) wait_vm(2u * RingCopies<RL>::n + nx);   // blocks 0 and 1 of the run have landed
+  uint32_t flags = 0;
+  bool dead = !live;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  uint32_t hi = 0, lo = 0, n = 0, end4 = 0;
+  uint32_t ycnt = 0;
+  uint64_t yrow0 = cb;
+  float yv[8];
+#pragma unroll
+  for (uint32_t b = 0; b < 8u; ++b) yv[b] = 0.f;
+  bool pend = false, pend_row = false, row_live = false;
+  // the 16 partial sums of this wavefront's row (lane n: token n) into lane
+  // ycnt's registers, and the store of every 64 rows
+  auto take_row = [&](bool store) {
+    float s = 0.f;
+    if (lane < batch) {
+      const uint32_t src = red_lds + (16u * (wave >> 2) + lane) * 16u + 4u * (wave & 3u);
+#pragma unroll
+      for (uint32_t v = 0; v < (uint32_t)kWaves; ++v) s += __builtin_bit_cast(float, *(lds_u32 *)(uintptr_t)(src + v * 1024u));
+    }
+    if (!store) return;
+#pragma unroll
+    for (uint32_t b = 0; b < 8u; ++b) {
+      const float sb = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), (int)b));
+      yv[b] = lane == ycnt ? sb : yv[b];
+    }
+    if (++ycnt == 64u) {
+#pragma unroll
+      for (uint32_t b = 0; b < 8u; ++b)
+        if (b < batch) y[(uint64_t)b * rows + yrow0 + lane] = yv[b];
+      yrow0 += 64u;
+      ycnt = 0;
+    }
+  };
+  uint32_t r = 0, sl = 0;
+  for (uint32_t t = 0; t < nsl; ++t) {
+    const uint32_t arow = a_lds + (t & 1u) * (16u * kTileRowBytes) + wave * kTileRowBytes + 4u * lane;
+    if (sl == 0u) {
+      row_live = !dead && cb + r < ce;
+      if (row_live && r != 0u && (r & 63u) == 0u) {   // the next 64 rows' end offsets
+        const uint64_t o_start = R.base * 32u + R.p4 * 8u;
+        if (!load_ends(d, R, cb + r, ce, o_start, lane, R.ends)) {
+          flags |= kFOffsets;
+          dead = true, row_live = false;
+        }
+      }
+    }
+    if (row_live) {
+      if (sl == 0u) {
+        end4 = __builtin_amdgcn_readlane(R.ends, (int)(r & 63u));
+        hi = 0, lo = 0, n = 0;
+        ring_fetch(~0ull, hi, lo, n, R.p4, ring_v, rmask4);
+        const uint32_t p_old = R.p4;
+        R.p4 = rfl(R.p4 + 256u);
+        if ((p_old ^ R.p4) >> RL) {
+          ring_copy<RL>(R, ring_base, (R.p4 >> RL) + (kRingBlocks - 1u), lane);
+          ring_wait2<RL>();
+          o_a += RingCopies<RL>::n, o_b += RingCopies<RL>::n;
+        }
+      }
+      const uint32_t q0 = 4u * sl;
+      const uint32_t qe = early_n > q0 ? min(early_n - q0, 4u) : 0u;
+      uint32_t ops = 0;
+      tile_pairs<true, NOFB, RL>(lut, K, 0u, qe, arow, hi, lo, n, R, ring_base, ring_v, rmask4, lane, ops);
+      tile_pairs<false, NOFB, RL>(lut, K, qe, 4u, arow, hi, lo, n, R, ring_base, ring_v, rmask4, lane, ops);
+      o_a += ops, o_b += ops;
+      if (sl == spr - 1u) {
+        if (R.p4 != end4) flags |= R.p4 < end4 ? kFUnderrun : kFOverrun;
+        if (hi | lo) flags |= kFPadding;
+        if (R.p4 != end4) dead = true;   // malformed: the rest of the run is not decoded
+      }
+    } else {
+#pragma unroll
+      for (uint32_t q = 0; q < 4u; ++q) *(lds_w32 *)(uintptr_t)(arow + 256u * q) = 0u;
+    }
+    if (xw) wait_vm(o_a);   // this slice's x has landed
+    lds_barrier();
+    o_a = o_b, o_b = 0;
+    if (xw && t + 2u < nsl) {
+      tile_x_copy(xr, x_lds + ((t + 2u) % kTileXBufs) * xbuf + wave * kTileXBytes, cols, wave, (t + 2u) % spr, lane);
+      o_a += 1u;
+    }
+    if (pend) {
+      take_row(pend_row);
+      pend = false;
+    }
+    acc = tile_mma(a_lds + (t & 1u) * (16u * kTileRowBytes), x_lds + (t % kTileXBufs) * xbuf, wave, lane, batch, acc);
+    if (++sl == spr) {
+      *(lds_w32x4 *)(uintptr_t)(red_lds + (wave * 64u + lane) * 16u) = __builtin_bit_cast(u32x4, acc);
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      pend = true, pend_row = row_live;
+      sl = 0, ++r;
+    }
+  }
+  lds_barrier();
+  if (pend) take_row(pend_row);
+  if (ycnt) {
+#pragma unroll
+    for (uint32_t b = 0; b < 8u; ++b)
+      if (b < batch && lane < ycnt) y[(uint64_t)b * rows + yrow0 + lane] = yv[b];
+  }
+  return flags;
+}
+
+template <uint32_t RL>
+__global__ __launch_bounds__(kBlockThreads) void ecw_gemv_tile_kernel(const StreamArgs a) {
+  // dynamic LDS: the two-code table (at LDS address 0), the code table
+  // (lut_cap entries), the table-state word, the two A tiles, the x buffers,
+  // the partial sums of a row end, then one ring per wavefront
+  u32x2 *ptab = reinterpret_cast<u32x2 *>(dyn_lds);
+  uint32_t *lut = reinterpret_cast<uint32_t *>(dyn_lds) + (2u << kPairBitsWide);
+  uint32_t *state = reinterpret_cast<uint32_t *>(dyn_lds) + a.flag_word;
+  const uint32_t wave = rfl(threadIdx.x >> 6);
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t lds0 = lds_addr(dyn_lds);
+  const uint32_t ring_base = rfl(lds0 + a.ring_off + (wave << (RL + 2u)));
+  const uint32_t a_lds = rfl(lds0 + a.tile_a_off), x_lds = rfl(lds0 + a.tile_x_off), red_lds = rfl(lds0 + a.tile_red_off);
+  if (!lds_at_zero()) {
+    if (threadIdx.x == 0)
+      for (uint32_t i = 0; i < a.n_tensors; ++i) atomicOr(a.t[i].status, kFLut);
+    return;
+  }
+  // tiles [g0, g1) of the launch (chunk_begin counts tiles here)
+  const uint32_t b = blockIdx.x;
+  const uint32_t g0 = b * a.chunks_q + min(b, a.chunks_r);
+  const uint32_t g1 = g0 + a.chunks_q + (b < a.chunks_r ? 1u : 0u);
+  uint32_t ti = 0;
+  for (uint32_t g = g0; g < g1;) {
+    while (ti + 1 < a.n_tensors && a.chunk_begin[ti + 1] <= g) ++ti;
+    const TensorArg &d = a.t[ti];
+    const uint32_t seg_end = min(g1, a.chunk_begin[ti + 1]);
+    const uint32_t T = seg_end - g;
+    const uint32_t r0 = (g - a.chunk_begin[ti]) * 16u;                     // first row of the segment
+    const uint32_t r1 = min(r0 + 16u * T, d.n_chunks);
+    const uint32_t cb = min(r0 + wave * T, r1), ce = min(cb + T, r1);
+    g = seg_end;
+    // table switch, as in the batch-1 kernel (no activations staged here)
+    const uint32_t ne_fetch = min(a.lut_cap, d.lut_words > kLutHeaderWords ? d.lut_words - kLutHeaderWords : 0u);
+    const uint32_t nv = ((uintptr_t)d.lut & 15u) == 0u ? ne_fetch >> 2 : 0u;
+    u32x4 lv = {0u, 0u, 0u, 0u};
+    uint32_t h0 = 0, h1 = 0, hne = 0, hl1 = 0;
+    if (threadIdx.x < nv) lv = reinterpret_cast<const u32x4 *>(d.lut + kLutHeaderWords)[threadIdx.x];
+    if (d.lut_words >= kLutHeaderWords) {
+      const __attribute__((address_space(4))) uint32_t *ch =
+          (const __attribute__((address_space(4))) uint32_t *)(uintptr_t)d.lut;
+      h0 = ch[0], h1 = ch[1], hne = ch[2], hl1 = ch[3];
+    }
+    Run R;
+    const bool have = cb < ce;
+    const bool run_ok = have && run_start<RL>(d, cb, ce, ring_base, lane, R);
+    __syncthreads();
+    if (threadIdx.x == 0) *state = 0u;
+    if (threadIdx.x < nv)
+      reinterpret_cast<u32x4 *>(lut)[threadIdx.x] =
+          u32x4{kernel_entry<kModeGemv>(lv[0]), kernel_entry<kModeGemv>(lv[1]), kernel_entry<kModeGemv>(lv[2]),
+                kernel_entry<kModeGemv>(lv[3])};
+    for (uint32_t i = 4u * nv + threadIdx.x; i < ne_fetch; i += kBlockThreads)
+      lut[i] = kernel_entry<kModeGemv>(d.lut[kLutHeaderWords + i]);
+    uint32_t k = 0;
+    if (d.lut_words >= kLutHeaderWords) {
+      const uint32_t kk = h1 & 0xFFu, lmin = h1 >> 24;
+      if (h0 == kLutMagic && (h1 & 0x00FFFF00u) == d.expect_hdr && kk >= 1 && kk <= kSingleLevelMax &&
+          hl1 == (1u << kk) && hne >= hl1 && hne <= a.lut_cap && hne <= d.lut_words - kLutHeaderWords &&
+          lmin >= 1u && lmin <= kMaxCodeLen)
+        k = kk | (lmin << 24);
+    }
+    k = rfl(k);
+    if (!k && threadIdx.x == 0) atomicOr(d.status, kFLut);
+    const uint32_t K = k & 0xFFu, l_min = k >> 24;
+    __syncthreads();
+    bool miss = false;
+    if (K) {
+      for (uint32_t i = threadIdx.x; i < (1u << kPairBitsWide); i += kBlockThreads) {
+        const u32x2 e = build_pair_entry<kModeGemv, kPairBitsWide>(lut, K, i);
+        ptab[i] = e;
+        miss |= (e.y & kPairFallback) != 0u;
+      }
+    }
+    if (__ballot(miss) && lane == 0) atomicOr(state, 1u);
+    __syncthreads();
+    const bool nofb = rfl(*state) == 0u;
+    if (!K) {
+      wait_lds_copy();
+      continue;
+    }
+    uint32_t flags = have && !run_ok ? kFOffsets : 0u;
+    flags |= nofb ? tile_run<true, RL>(d, lut, K, l_min, R, run_ok, cb, ce, T, a.batch, wave, lane, ring_base, a_lds,
+                                       x_lds, red_lds)
+                  : tile_run<false, RL>(d, lut, K, l_min, R, run_ok, cb, ce, T, a.batch, wave, lane, ring_base, a_lds,
+                                        x_lds, red_lds);
+    if (flags && lane == 0) atomicOr(d.status, flags);
+    wait_lds_copy();
+  }
+  wait_lds_copy();
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+
+// Workgroup cap of every launch (entro_set_max_workgroups; 0: none).
+static std::atomic<uint32_t> g_max_workgroups{0};
+
+static uint64_t cap_grid(uint64_t grid) {
+  const uint32_t cap = g_max_workgroups.load(std::memory_order_relaxed);
+  return cap && grid > cap ? cap : grid;
+}
 
 static bool pow2_lanes(uint32_t w) { return w >= 1 && w <= 64 && (w & (w - 1)) == 0; }
 
@@ -2211,7 +2579,7 @@ static hipError_t launch_one(uint32_t total_tasks, LaunchArgs &a, size_t dyn, hi
   // other streams (decoding ahead of a consumer).
   const uint64_t k = std::min<uint64_t>((uint64_t)per_cu,
                                         (total_tasks + (uint64_t)kWaves * cus - 1) / ((uint64_t)kWaves * cus));
-  const uint32_t grid = (uint32_t)std::min<uint64_t>((uint64_t)cus * std::max<uint64_t>(k, 1), total_tasks);
+  const uint32_t grid = (uint32_t)cap_grid(std::min<uint64_t>((uint64_t)cus * std::max<uint64_t>(k, 1), total_tasks));
   a.tasks_q = total_tasks / grid;
   a.tasks_r = total_tasks % grid;
   // clear an error left by an earlier call (ours, such as a failed occupancy
@@ -2288,6 +2656,10 @@ static bool stream_ok(const entro_tensor &t, const entro_gemv_item &g, uint32_t 
   return xw * 4u <= kGemvXMaxBytes && stream_fits(stream_lut_entries(t), xw);
 }
 
+// How a GEMV tensor is launched: the matrix-core kernel, the streamed one,
+// or (0) the staged or generic paths of ecw_kernel.
+constexpr char kTakeStream = 1, kTakeTile = 2;
+
 struct StreamPlan {
   StreamArgs a;
   size_t dyn;
@@ -2312,7 +2684,7 @@ static hipError_t launch_stream(StreamPlan &pl, hipStream_t s) {
   // wavefront a chunk, the chunks spread evenly
   const uint64_t k = std::min<uint64_t>((uint64_t)per_cu,
                                         (pl.total + (uint64_t)kWaves * cus - 1) / ((uint64_t)kWaves * cus));
-  const uint32_t grid = (uint32_t)std::min<uint64_t>((uint64_t)cus * std::max<uint64_t>(k, 1), pl.total);
+  const uint32_t grid = (uint32_t)cap_grid(std::min<uint64_t>((uint64_t)cus * std::max<uint64_t>(k, 1), pl.total));
   pl.a.chunks_q = pl.total / grid;
   pl.a.chunks_r = pl.total % grid;
   (void)hipGetLastError();
@@ -2322,6 +2694,28 @@ static hipError_t launch_stream(StreamPlan &pl, hipStream_t s) {
 
 // Plan the streamed launches of the tensors marked in `take` (groups of up to
 // 32).
+// The tensor arguments of a streamed or matrix-core GEMV launch.
+static void stream_tensor_arg(TensorArg &d, const entro_tensor &x, const entro_gemv_item &gi, uint32_t *status,
+                              uint64_t nc) {
+  d.lut = static_cast<const uint32_t *>(x.d_lut);
+  d.words = x.d_words;
+  d.offs = x.d_chunk_bit_off;
+  d.status = status;
+  d.n_words = x.n_words;
+  d.n_symbols = x.n_symbols;
+  d.chunk = x.chunk_symbols;
+  d.n_chunks = (uint32_t)nc;
+  d.expect_hdr = (x.sym_bits << 8) | (x.max_len << 16);
+  d.lut_words = (uint32_t)std::min<uint64_t>(x.lut_bytes / 4, kLutHeaderWords + kLutMaxEntries);
+  d.refill_steps = 2u;
+  d.ahead = x.refill_ahead;
+  d.out = gi.d_y;
+  d.x = gi.d_x;
+  d.rows = gi.rows;
+  d.cols = gi.cols;
+  d.n_tasks = (uint32_t)nc;
+}
+
 static entro_status plan_stream(const entro_tensor *t, size_t n, const entro_gemv_item *g, uint32_t batch,
                                 uint32_t *d_status, const std::vector<char> &take, std::vector<StreamPlan> &plans) {
   size_t i = 0;
@@ -2334,7 +2728,7 @@ static entro_status plan_stream(const entro_tensor *t, size_t n, const entro_gem
     uint32_t total = 0, k = 0;
     uint64_t lut_need = 0, x_need = 0;
     for (; i < n && k < (uint32_t)kMaxTensorsPerLaunch; ++i) {
-      if (!take[i]) continue;
+      if (take[i] != kTakeStream) continue;
       const entro_tensor &x = t[i];
       const uint64_t nc = (x.n_symbols + x.chunk_symbols - 1) / x.chunk_symbols;
       if ((uint64_t)total + nc > 0x7FFFFFFFull) break;
@@ -2342,24 +2736,7 @@ static entro_status plan_stream(const entro_tensor *t, size_t n, const entro_gem
       // starts the next one (each fits alone: stream_ok)
       if (k && !stream_fits(std::max(lut_need, stream_lut_entries(x)), std::max(x_need, stream_x_words(g[i], batch))))
         break;
-      TensorArg &d = a.t[k];
-      d.lut = static_cast<const uint32_t *>(x.d_lut);
-      d.words = x.d_words;
-      d.offs = x.d_chunk_bit_off;
-      d.status = d_status + i;
-      d.n_words = x.n_words;
-      d.n_symbols = x.n_symbols;
-      d.chunk = x.chunk_symbols;
-      d.n_chunks = (uint32_t)nc;
-      d.expect_hdr = (x.sym_bits << 8) | (x.max_len << 16);
-      d.lut_words = (uint32_t)std::min<uint64_t>(x.lut_bytes / 4, kLutHeaderWords + kLutMaxEntries);
-      d.refill_steps = 2u;
-      d.ahead = x.refill_ahead;
-      d.out = g[i].d_y;
-      d.x = g[i].d_x;
-      d.rows = g[i].rows;
-      d.cols = g[i].cols;
-      d.n_tasks = (uint32_t)nc;
+      stream_tensor_arg(a.t[k], x, g[i], d_status + i, nc);
       a.chunk_begin[k] = total;
       total += (uint32_t)nc;
       lut_need = std::max<uint64_t>(lut_need, stream_lut_entries(x));
@@ -2376,6 +2753,100 @@ static entro_status plan_stream(const entro_tensor *t, size_t n, const entro_gem
     a.x_words = (uint32_t)((x_need + 3) & ~3ull);
     pl.dyn = stream_lds_bytes(a.lut_cap, a.x_words, stream_ring(a.lut_cap, a.x_words), &a);
     if (pl.dyn + kStaticLds > kLdsPerCu - kLdsPlanReserve) return ENTRO_E_UNSUPPORTED;   // not reached (stream_ok)
+    pl.total = total;
+  }
+  return ENTRO_OK;
+}
+
+// Matrix-core GEMV launches (ecw_gemv_tile_kernel): batch 2..8, tensors of
+// the streamed layout with one row per chunk, 512 | cols, cols >= 1024, and x
+// 16-byte aligned (its slices are copied 16 bytes a lane).
+
+// LDS bytes of a matrix-core launch (code table of lut_cap entries); sets the
+// layout fields of a if given.
+static size_t tile_lds_bytes(uint64_t lut_cap, uint32_t batch, StreamArgs *a = nullptr) {
+  size_t dyn = ((size_t)8u << kPairBitsWide) + (size_t)lut_cap * 4u;
+  if (a) a->flag_word = (uint32_t)(dyn / 4u);
+  dyn = (dyn + 16u + 15u) & ~(size_t)15u;
+  if (a) a->tile_a_off = (uint32_t)dyn;
+  dyn += 2u * 16u * kTileRowBytes;
+  if (a) a->tile_x_off = (uint32_t)dyn;
+  dyn += (size_t)kTileXBufs * batch * kTileXBytes;
+  if (a) a->tile_red_off = (uint32_t)dyn;
+  dyn += (size_t)kWaves * 64u * 16u;
+  const size_t ring_bytes = (size_t)4u << kTileLog2Ring;
+  dyn = (dyn + ring_bytes - 1u) / ring_bytes * ring_bytes;
+  if (a) a->ring_off = (uint32_t)dyn, a->log2_ring = kTileLog2Ring;
+  return dyn + (size_t)kWaves * ring_bytes;
+}
+
+static bool tile_fits(uint64_t lut_cap, uint32_t batch) {
+  return tile_lds_bytes((lut_cap + 3) & ~3ull, batch) + kStaticLds <= kLdsPerCu - kLdsPlanReserve;
+}
+
+static bool tile_ok(const entro_tensor &t, const entro_gemv_item &g, uint32_t batch) {
+  if (batch < 2u || batch > 8u) return false;
+  if (t.n_symbols == 0 || t.lanes != 64u || t.sym_bits != 4u || t.refill_steps != 2u) return false;
+  if (g.cols < 1024u || (g.cols & 511u) || t.chunk_symbols != g.cols) return false;
+  if (t.n_words >= (1ull << 30) || (reinterpret_cast<uintptr_t>(g.d_x) & 15u)) return false;
+  if ((uint64_t)batch * g.cols * 2u > 0x7FFFFFFFull) return false;
+  return tile_fits(stream_lut_entries(t), batch);
+}
+
+static hipError_t launch_tile(StreamPlan &pl, hipStream_t s) {
+  auto kern = ecw_gemv_tile_kernel<kTileLog2Ring>;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBlockThreads, pl.dyn) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int lds_fit = (int)((kLdsPerCu - kLdsPlanReserve) / (pl.dyn + kStaticLds));
+  if (lds_fit >= 1 && per_cu > lds_fit) per_cu = lds_fit;
+  if (cus < 1) cus = 1;
+  // every workgroup resident at once, the tiles spread evenly
+  const uint32_t grid = (uint32_t)cap_grid(std::min<uint64_t>((uint64_t)cus * (uint64_t)per_cu, pl.total));
+  pl.a.chunks_q = pl.total / grid;
+  pl.a.chunks_r = pl.total % grid;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlockThreads), pl.dyn, s, pl.a);
+  return hipGetLastError();
+}
+
+// Plan the matrix-core launches of the tensors marked in `take` (groups of up
+// to 32; chunk_begin counts tiles of 16 rows).
+static entro_status plan_tile(const entro_tensor *t, size_t n, const entro_gemv_item *g, uint32_t batch,
+                              uint32_t *d_status, const std::vector<char> &take, std::vector<StreamPlan> &plans) {
+  size_t i = 0;
+  while (i < n) {
+    plans.emplace_back();
+    StreamPlan &pl = plans.back();
+    std::memset(&pl, 0, sizeof pl);
+    StreamArgs &a = pl.a;
+    a.batch = batch;
+    uint32_t total = 0, k = 0;
+    uint64_t lut_need = 0;
+    for (; i < n && k < (uint32_t)kMaxTensorsPerLaunch; ++i) {
+      if (take[i] != kTakeTile) continue;
+      const entro_tensor &x = t[i];
+      const uint64_t nc = (x.n_symbols + x.chunk_symbols - 1) / x.chunk_symbols;
+      const uint64_t tiles = (nc + 15u) / 16u;
+      if ((uint64_t)total + tiles > 0x7FFFFFFFull) break;
+      if (k && !tile_fits(std::max(lut_need, stream_lut_entries(x)), batch)) break;
+      stream_tensor_arg(a.t[k], x, g[i], d_status + i, nc);
+      a.chunk_begin[k] = total;
+      total += (uint32_t)tiles;
+      lut_need = std::max<uint64_t>(lut_need, stream_lut_entries(x));
+      ++k;
+    }
+    if (k == 0) {
+      plans.pop_back();
+      continue;
+    }
+    a.n_tensors = k;
+    for (uint32_t r = k; r <= (uint32_t)kMaxTensorsPerLaunch; ++r) a.chunk_begin[r] = total;
+    a.lut_cap = (uint32_t)((lut_need + 3) & ~3ull);
+    pl.dyn = tile_lds_bytes(a.lut_cap, batch, &a);
+    if (pl.dyn + kStaticLds > kLdsPerCu - kLdsPlanReserve) return ENTRO_E_UNSUPPORTED;   // not reached (tile_ok)
     pl.total = total;
   }
   return ENTRO_OK;
@@ -2417,12 +2888,20 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
     }
   }
   // GEMV tensors of the streamed layout take the streamed kernel
+  // (batch 2..8: the matrix-core kernel where it applies)
   std::vector<char> take(n, 0);
-  std::vector<StreamPlan> splans;
+  std::vector<StreamPlan> splans, tplans;
   if (mode == kModeGemv) {
-    bool any = false;
-    for (size_t j = 0; j < n; ++j) any |= (take[j] = stream_ok(t[j], g[j], batch) ? 1 : 0) != 0;
-    if (any) {
+    bool any_s = false, any_t = false;
+    for (size_t j = 0; j < n; ++j) {
+      if (tile_ok(t[j], g[j], batch)) take[j] = kTakeTile, any_t = true;
+      else if (stream_ok(t[j], g[j], batch)) take[j] = kTakeStream, any_s = true;
+    }
+    if (any_t) {
+      const entro_status st = plan_tile(t, n, g, batch, d_status, take, tplans);
+      if (st != ENTRO_OK) return st;
+    }
+    if (any_s) {
       const entro_status st = plan_stream(t, n, g, batch, d_status, take, splans);
       if (st != ENTRO_OK) return st;
     }
@@ -2527,6 +3006,8 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
     pl.log2w = log2w;
     pl.cached = cached;
   }
+  for (StreamPlan &tp : tplans)
+    if (launch_tile(tp, s) != hipSuccess) return ENTRO_E_HIP;
   for (StreamPlan &sp : splans) {
     const hipError_t err = batch == 1 ? launch_stream<1>(sp, s) : launch_stream<8>(sp, s);
     if (err != hipSuccess) return ENTRO_E_HIP;
@@ -2558,7 +3039,7 @@ static hipError_t launch_gemm(GemmArgs &a, size_t dyn, hipStream_t s) {
   const int lds_fit = (int)((kLdsPerCu - kLdsPlanReserve) / (dyn + kStaticLds));
   if (lds_fit >= 1 && per_cu > lds_fit) per_cu = lds_fit;
   if (cus < 1) cus = 1;
-  const uint64_t slots = (uint64_t)cus * (uint64_t)per_cu;
+  const uint64_t slots = cap_grid((uint64_t)cus * (uint64_t)per_cu);
   const uint32_t per_block = (uint32_t)((a.total_tiles + slots - 1) / slots);
   a.tiles_per_block = per_block < 1 ? 1 : per_block;
   const uint32_t grid = (a.total_tiles + a.tiles_per_block - 1) / a.tiles_per_block;
@@ -2681,3 +3162,5 @@ extern "C" entro_status entro_decode_gemm(const entro_tensor *t, size_t n, const
                                           uint32_t n_tokens, uint32_t *d_status, hipStream_t stream) {
   return run_gemm(t, n, g, n_tokens, d_status, stream);
 }
+
+extern "C" uint32_t entro_set_max_workgroups(uint32_t n) { return g_max_workgroups.exchange(n); }

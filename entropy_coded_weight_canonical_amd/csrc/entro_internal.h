@@ -124,6 +124,9 @@ struct StreamArgs {
   uint32_t flag_word;      // LDS word index of the workgroup's table-state word
   uint32_t ring_off;       // LDS byte offset of the first ring (a multiple of the ring's bytes)
   uint32_t log2_ring;      // log2 of a ring's words (a block is a quarter of it)
+  uint32_t tile_a_off;     // matrix-core GEMV: LDS byte offsets of the A tiles,
+  uint32_t tile_x_off;     //   the x buffers
+  uint32_t tile_red_off;   //   and the row-end partial sums
 };
 
 constexpr uint32_t kPairBits = 10;                 // two-code table: 1024 entries of 8 bytes

@@ -205,6 +205,13 @@ entro_status entro_decode_gemv(const entro_tensor *t, size_t n, const entro_gemv
 entro_status entro_decode_gemm(const entro_tensor *t, size_t n, const entro_gemv_item *g,
                                uint32_t n_tokens, uint32_t *d_status, hipStream_t stream);
 
+/* Cap the workgroups of every later launch of this library in this process
+ * (0, the default: no cap).  A launch then spreads its chunks, tasks or tiles
+ * over at most n workgroups, which leaves CUs free for work on other streams
+ * and gives each wavefront a longer run; results do not depend on it.  A
+ * launch setting, not part of the method; returns the previous cap. */
+uint32_t entro_set_max_workgroups(uint32_t n);
+
 /* Static English text for a status code. */
 const char *entro_status_str(entro_status s);
 
