@@ -2888,14 +2888,15 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
     }
   }
   // GEMV tensors of the streamed layout take the streamed kernel
-  // (batch 2..8: the matrix-core kernel where it applies)
+  // (batch 2..8: where the activations do not fit the streamed kernel's LDS
+  // block, the matrix-core kernel, which streams them in slices)
   std::vector<char> take(n, 0);
   std::vector<StreamPlan> splans, tplans;
   if (mode == kModeGemv) {
     bool any_s = false, any_t = false;
     for (size_t j = 0; j < n; ++j) {
-      if (tile_ok(t[j], g[j], batch)) take[j] = kTakeTile, any_t = true;
-      else if (stream_ok(t[j], g[j], batch)) take[j] = kTakeStream, any_s = true;
+      if (stream_ok(t[j], g[j], batch)) take[j] = kTakeStream, any_s = true;
+      else if (tile_ok(t[j], g[j], batch)) take[j] = kTakeTile, any_t = true;
     }
     if (any_t) {
       const entro_status st = plan_tile(t, n, g, batch, d_status, take, tplans);

@@ -1,7 +1,9 @@
-"""GPU parity of the streamed fused GEMV kernels: the batch-1 kernel (pairs
-multiplied on the vector ALUs) and the matrix-core kernel for 2..8
-activation rows (one row per chunk, 512 | cols, cols >= 1024), which the
-library picks by itself for tensors of that layout.
+"""GPU parity of the streamed fused GEMV kernels: the kernel that multiplies
+decoded pairs on the vector ALUs with activations staged whole in LDS
+(batch 1, and batches 2..8 while 8 batch slots of x fit, cols <= 4096), and
+the matrix-core kernel for 2..8 activation rows whose x is streamed in
+512-column slices (one row per chunk, 512 | cols, wider rows).  The library
+picks the kernel by itself; the shapes below reach both, often in one call.
 
 Every stream, code length and expected value comes from the oracle; outputs
 must lie within 1e-4 (relative, floor-guarded) of the float64 oracle GEMV
@@ -76,7 +78,8 @@ def _check(cases, xs, ys, st, tol=1e-4):
 @pytest.mark.parametrize("ahead", [False, True])
 @pytest.mark.parametrize("batch", [1, 2, 3, 5, 8])
 def test_streamed_gemv_shapes_in_one_call(batch, ahead):
-    shapes = [(1, 1024), (15, 1536), (16, 2048), (17, 1024), (37, 5120), (300, 1024), (64, 3072)]
+    shapes = [(1, 1024), (15, 1536), (16, 2048), (17, 4608), (37, 5120), (300, 1024), (64, 3072), (20, 8192),
+              (33, 14336), (1, 6144)]
     cases = [_rows_case(r, c, 100 + i, ahead=ahead) for i, (r, c) in enumerate(shapes)]
     xs = [activations_bf16("mistral_stack", 200 + i, c.cols, batch) for i, c in enumerate(cases)]
     say(f"streamed gemv shapes batch={batch} ahead={ahead}")
@@ -102,7 +105,8 @@ def test_streamed_gemv_runs_past_64_rows_per_wavefront(batch, cap):
     every 64 rows."""
     import entropy_coded_weight_canonical_amd as ent
 
-    cases = [_rows_case(16 * 70 * cap + 5, 1024, 11, ahead=True), _rows_case(33, 2048, 12)]
+    cases = [_rows_case(16 * 70 * cap + 5, 1024, 11, ahead=True), _rows_case(33, 2048, 12),
+             _rows_case(16 * 70 * cap + 3, 4608, 13)]
     xs = [activations_bf16("mistral_stack", 400 + i, c.cols, batch) for i, c in enumerate(cases)]
     say(f"streamed gemv cap={cap} batch={batch} rows={cases[0].rows}")
     prev = ent.set_max_workgroups(cap)
@@ -117,7 +121,7 @@ def test_streamed_gemv_runs_past_64_rows_per_wavefront(batch, cap):
 def test_streamed_gemv_results_do_not_depend_on_the_grid(batch):
     import entropy_coded_weight_canonical_amd as ent
 
-    cases = [_rows_case(500, 1024, 21), _rows_case(77, 4096, 22, ahead=True)]
+    cases = [_rows_case(500, 1024, 21), _rows_case(77, 4096, 22, ahead=True), _rows_case(60, 5120, 23)]
     xs = [activations_bf16("mistral_stack", 500 + i, c.cols, batch) for i, c in enumerate(cases)]
     say(f"streamed gemv grid independence batch={batch}")
     ys0, st0 = run_gemv(cases, xs, batch)
@@ -134,14 +138,15 @@ def test_streamed_gemv_results_do_not_depend_on_the_grid(batch):
 
 @pytest.mark.parametrize("batch", [1, 8])
 def test_streamed_gemv_malformed_stream_is_flagged(batch):
-    good = _rows_case(48, 1024, 31)
-    bad = _rows_case(48, 1024, 32)
-    words = bad.words.copy()
-    words[len(words) // 3:] ^= np.uint32(0x5A5A5A5A)   # the later rows' words no longer decode to their ends
-    bad.words = words
-    cases = [good, bad, _rows_case(20, 2048, 33)]
+    cases = [_rows_case(48, 1024, 31), _rows_case(48, 1024, 32), _rows_case(20, 2048, 33),
+             _rows_case(48, 5120, 34), _rows_case(16, 6144, 35)]
+    for i in (1, 3):
+        words = cases[i].words.copy()
+        words[len(words) // 3:] ^= np.uint32(0x5A5A5A5A)   # the later rows' words no longer decode to their ends
+        cases[i].words = words
     xs = [activations_bf16("mistral_stack", 600 + i, c.cols, batch) for i, c in enumerate(cases)]
     say(f"streamed gemv malformed stream batch={batch}")
     ys, st = run_gemv(cases, xs, batch)
-    assert st[1] != 0, st
-    _check([cases[0], cases[2]], [xs[0], xs[2]], [ys[0], ys[2]], st[[0, 2]])
+    assert st[1] != 0 and st[3] != 0, st
+    ok = [0, 2, 4]
+    _check([cases[i] for i in ok], [xs[i] for i in ok], [ys[i] for i in ok], st[ok])
