@@ -62,7 +62,8 @@ class Tensor(ctypes.Structure):
                 ("lanes", ctypes.c_uint32), ("sym_bits", ctypes.c_uint32),
                 ("max_len", ctypes.c_uint32), ("lut_bytes", ctypes.c_uint64),
                 ("max_chunk_words", ctypes.c_uint32), ("refill_steps", ctypes.c_uint32),
-                ("refill_ahead", ctypes.c_uint32), ("out_cached", ctypes.c_uint32)]
+                ("refill_ahead", ctypes.c_uint32), ("out_cached", ctypes.c_uint32),
+                ("d_pair_lut", ctypes.c_void_p)]
 
 
 class RansTensor(ctypes.Structure):
@@ -103,6 +104,9 @@ def load():
     lib.entro_lut_bytes.argtypes = [P]
     lib.entro_lut_bytes.restype = SZ
     lib.entro_lut_build.argtypes = [P, P, SZ]
+    lib.entro_pair_lut_bytes.argtypes = []
+    lib.entro_pair_lut_bytes.restype = SZ
+    lib.entro_pair_lut_build.argtypes = [P, SZ, P, SZ]
     for name in ("entro_decode", "entro_decode_dequant"):
         getattr(lib, name).argtypes = [P, SZ, P, P, P]
     lib.entro_decode_gemv.argtypes = [P, SZ, P, U32, P, P]
@@ -122,7 +126,7 @@ def load():
     lib.entro_code_lengths.argtypes = [P, U64, U32, U32, P]
     lib.entro_encode_layout.argtypes = [P, U64, P, U32, U32, U32, P, P]
     lib.entro_encode.argtypes = [P, U64, P, U32, U32, U32, U32, U32, P, P, U32]
-    for name in ("entro_lut_build", "entro_decode", "entro_decode_dequant", "entro_decode_gemv",
+    for name in ("entro_lut_build", "entro_pair_lut_build", "entro_decode", "entro_decode_dequant", "entro_decode_gemv",
                  "entro_decode_gemm", "entro_quantize", "entro_code_lengths", "entro_encode_layout", "entro_encode",
                  "entro_rans_freqs", "entro_rans_table_build", "entro_rans_encode", "entro_rans_decode",
                  "entro_rans_decode_dequant"):
@@ -173,6 +177,16 @@ def lut_build(code_len, sym_bits: int, max_len: int, scale: float, zero_point: i
 # --------------------------------------------------------------------------
 # device entry points
 # --------------------------------------------------------------------------
+
+def pair_lut_build(lut: np.ndarray) -> np.ndarray:
+    """``entro_pair_lut_build``: the two-code table of a 4-bit decode table
+    (``lut_build`` output), as uint32 words."""
+    lib = load()
+    t = np.ascontiguousarray(lut, dtype=np.uint32)
+    out = np.zeros(lib.entro_pair_lut_bytes() // 4, dtype=np.uint32)
+    _check(lib.entro_pair_lut_build(_np_ptr(t), t.nbytes, _np_ptr(out), out.nbytes), "entro_pair_lut_build")
+    return out
+
 
 def _stream_handle(stream) -> int:
     if stream is None:
@@ -395,11 +409,15 @@ class DeviceTensor:
     words: object
     offs: object
     desc: Tensor
+    pair_lut: object = None
 
     @classmethod
     def upload(cls, lut: np.ndarray, words: np.ndarray, offs: np.ndarray, n_symbols: int,
                chunk: int, lanes: int, sym_bits: int, max_len: int, device="cuda", refill_steps: int = 1,
-               ahead: bool = False):
+               ahead: bool = False, pair_lut: bool = True):
+        """``pair_lut``: for 4-bit tensors, also build the two-code table on
+        the host and upload it (``d_pair_lut``); the fused GEMV then loads it
+        instead of building it on chip."""
         import torch
 
         d_lut = torch.from_numpy(np.ascontiguousarray(lut).view(np.int32)).to(device)
@@ -411,4 +429,8 @@ class DeviceTensor:
         desc = Tensor(d_lut.data_ptr(), d_words.data_ptr(), d_offs.data_ptr(), int(w.size), int(n_symbols),
                       int(chunk), int(lanes), int(sym_bits), int(max_len), int(np.asarray(lut).nbytes),
                       max_cw, int(refill_steps), int(ahead))
-        return cls(d_lut, d_words, d_offs, desc)
+        d_pair = None
+        if pair_lut and int(sym_bits) == 4:
+            d_pair = torch.from_numpy(pair_lut_build(lut).view(np.int32)).to(device)
+            desc.d_pair_lut = d_pair.data_ptr()
+        return cls(d_lut, d_words, d_offs, desc, d_pair)

@@ -1532,6 +1532,18 @@ __device__ uint32_t stream_run(const TensorArg &d, const uint32_t *lut, uint32_t
   return flags;
 }
 
+// The host-built two-code table of a tensor into LDS [0, 32 KiB): wavefront
+// w copies bytes [2 KiB w, 2 KiB (w + 1)) with two 16-byte copies per lane.
+__device__ __forceinline__ void ptab_copy(const uint32_t *plut, uint32_t wave, uint32_t lane) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(plut + kPairLutHeaderWords), (short)0, (int)(8u << kPairBitsWide), 0x00020000);
+  const uint32_t b = wave * 2048u;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(uintptr_t)rfl(b), 16, lane * 16u, rfl(b), 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(uintptr_t)rfl(b + 1024u), 16, lane * 16u,
+                                           rfl(b + 1024u), 0, 0);
+}
+static_assert((8u << kPairBitsWide) == 2048u * kWaves, "two-code table copy: 2 KiB per wavefront");
+
 template <int BATCH, uint32_t RL>
 __device__ __forceinline__ void gemv_stream(const StreamArgs &a) {
   constexpr uint32_t SB = XSlots<BATCH>::n;
@@ -1561,6 +1573,7 @@ __device__ __forceinline__ void gemv_stream(const StreamArgs &a) {
     const uint32_t len = seg_end - g;
     const uint32_t c0 = g - a.chunk_begin[ti];
     const uint32_t cb = c0 + (wave * len) / kWaves, ce = c0 + ((wave + 1u) * len) / kWaves;
+    const bool first = g == g0;
     g = seg_end;
     // table switch: activations and table entries into registers, the run's
     // first copies in flight, then (after the barrier) the LDS writes
@@ -1577,10 +1590,21 @@ __device__ __forceinline__ void gemv_stream(const StreamArgs &a) {
           (const __attribute__((address_space(4))) uint32_t *)(uintptr_t)d.lut;
       h0 = ch[0], h1 = ch[1], hne = ch[2], hl1 = ch[3];
     }
+    // the host-built two-code table: copied now if nothing reads that LDS
+    // yet (the workgroup's first tensor), else after the barrier
+    const bool pt = d.plut != nullptr;
+    uint32_t p0 = 0, p1 = 0, p2 = 0;
+    if (pt) {
+      const __attribute__((address_space(4))) uint32_t *cp =
+          (const __attribute__((address_space(4))) uint32_t *)(uintptr_t)d.plut;
+      p0 = cp[0], p1 = cp[1], p2 = cp[2];
+      if (first) ptab_copy(d.plut, wave, lane);
+    }
     Run R;
     const bool have = cb < ce;
     const bool run_ok = have && run_start<RL>(d, cb, ce, ring_base, lane, R);
     __syncthreads();
+    if (pt && !first) ptab_copy(d.plut, wave, lane);
     if (threadIdx.x == 0) *state = 0u;
     if (threadIdx.x < nv)
       reinterpret_cast<u32x4 *>(lut)[threadIdx.x] =
@@ -1598,22 +1622,26 @@ __device__ __forceinline__ void gemv_stream(const StreamArgs &a) {
           lmin >= 1u && lmin <= kMaxCodeLen)
         k = kk | (lmin << 24);
     }
+    if (pt && (p0 != kPairLutMagic || p2 != h1)) k = 0u;   // not this code's two-code table
     k = rfl(k);
     if (!k && threadIdx.x == 0) atomicOr(d.status, kFLut);
     const uint32_t K = k & 0xFFu, l_min = k >> 24;
     __syncthreads();
-    // two-code table; does any index miss a whole pair?
-    bool miss = false;
-    if (K) {
-      for (uint32_t i = threadIdx.x; i < (1u << kPairBitsWide); i += kBlockThreads) {
-        const u32x2 e = build_pair_entry<kModeGemv, kPairBitsWide>(lut, K, i);
-        ptab[i] = e;
-        miss |= (e.y & kPairFallback) != 0u;
+    // two-code table (unless copied); does any index miss a whole pair?
+    bool nofb = (p1 & kPairLutWhole) != 0u;
+    if (!pt) {
+      bool miss = false;
+      if (K) {
+        for (uint32_t i = threadIdx.x; i < (1u << kPairBitsWide); i += kBlockThreads) {
+          const u32x2 e = build_pair_entry<kModeGemv, kPairBitsWide>(lut, K, i);
+          ptab[i] = e;
+          miss |= (e.y & kPairFallback) != 0u;
+        }
       }
+      if (__ballot(miss) && lane == 0) atomicOr(state, 1u);
+      __syncthreads();
+      nofb = rfl(*state) == 0u;
     }
-    if (__ballot(miss) && lane == 0) atomicOr(state, 1u);
-    __syncthreads();
-    const bool nofb = rfl(*state) == 0u;
     if (!K) {
       wait_lds_copy();   // the run's first copies land before the ring is reused
       continue;
@@ -2464,6 +2492,7 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_gemv_tile_kernel(const Stre
     const uint32_t r0 = (g - a.chunk_begin[ti]) * 16u;                     // first row of the segment
     const uint32_t r1 = min(r0 + 16u * T, d.n_chunks);
     const uint32_t cb = min(r0 + wave * T, r1), ce = min(cb + T, r1);
+    const bool first = g == g0;
     g = seg_end;
     // table switch, as in the batch-1 kernel (no activations staged here)
     const uint32_t ne_fetch = min(a.lut_cap, d.lut_words > kLutHeaderWords ? d.lut_words - kLutHeaderWords : 0u);
@@ -2476,10 +2505,21 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_gemv_tile_kernel(const Stre
           (const __attribute__((address_space(4))) uint32_t *)(uintptr_t)d.lut;
       h0 = ch[0], h1 = ch[1], hne = ch[2], hl1 = ch[3];
     }
+    // the host-built two-code table: copied now if nothing reads that LDS
+    // yet (the workgroup's first tensor), else after the barrier
+    const bool pt = d.plut != nullptr;
+    uint32_t p0 = 0, p1 = 0, p2 = 0;
+    if (pt) {
+      const __attribute__((address_space(4))) uint32_t *cp =
+          (const __attribute__((address_space(4))) uint32_t *)(uintptr_t)d.plut;
+      p0 = cp[0], p1 = cp[1], p2 = cp[2];
+      if (first) ptab_copy(d.plut, wave, lane);
+    }
     Run R;
     const bool have = cb < ce;
     const bool run_ok = have && run_start<RL>(d, cb, ce, ring_base, lane, R);
     __syncthreads();
+    if (pt && !first) ptab_copy(d.plut, wave, lane);
     if (threadIdx.x == 0) *state = 0u;
     if (threadIdx.x < nv)
       reinterpret_cast<u32x4 *>(lut)[threadIdx.x] =
@@ -2495,21 +2535,26 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_gemv_tile_kernel(const Stre
           lmin >= 1u && lmin <= kMaxCodeLen)
         k = kk | (lmin << 24);
     }
+    if (pt && (p0 != kPairLutMagic || p2 != h1)) k = 0u;   // not this code's two-code table
     k = rfl(k);
     if (!k && threadIdx.x == 0) atomicOr(d.status, kFLut);
     const uint32_t K = k & 0xFFu, l_min = k >> 24;
     __syncthreads();
-    bool miss = false;
-    if (K) {
-      for (uint32_t i = threadIdx.x; i < (1u << kPairBitsWide); i += kBlockThreads) {
-        const u32x2 e = build_pair_entry<kModeGemv, kPairBitsWide>(lut, K, i);
-        ptab[i] = e;
-        miss |= (e.y & kPairFallback) != 0u;
+    // two-code table (unless copied); does any index miss a whole pair?
+    bool nofb = (p1 & kPairLutWhole) != 0u;
+    if (!pt) {
+      bool miss = false;
+      if (K) {
+        for (uint32_t i = threadIdx.x; i < (1u << kPairBitsWide); i += kBlockThreads) {
+          const u32x2 e = build_pair_entry<kModeGemv, kPairBitsWide>(lut, K, i);
+          ptab[i] = e;
+          miss |= (e.y & kPairFallback) != 0u;
+        }
       }
+      if (__ballot(miss) && lane == 0) atomicOr(state, 1u);
+      __syncthreads();
+      nofb = rfl(*state) == 0u;
     }
-    if (__ballot(miss) && lane == 0) atomicOr(state, 1u);
-    __syncthreads();
-    const bool nofb = rfl(*state) == 0u;
     if (!K) {
       wait_lds_copy();
       continue;
@@ -2698,6 +2743,8 @@ static hipError_t launch_stream(StreamPlan &pl, hipStream_t s) {
 static void stream_tensor_arg(TensorArg &d, const entro_tensor &x, const entro_gemv_item &gi, uint32_t *status,
                               uint64_t nc) {
   d.lut = static_cast<const uint32_t *>(x.d_lut);
+  d.plut = (reinterpret_cast<uintptr_t>(x.d_pair_lut) & 15u) == 0u ? static_cast<const uint32_t *>(x.d_pair_lut)
+                                                                    : nullptr;
   d.words = x.d_words;
   d.offs = x.d_chunk_bit_off;
   d.status = status;

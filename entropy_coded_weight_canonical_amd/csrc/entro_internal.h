@@ -26,6 +26,7 @@ enum Mode : int { kModeU8 = 0, kModeBf16 = 1, kModeGemv = 2 };
 // One tensor of a launch.
 struct TensorArg {
   const uint32_t *lut;     // header + entries
+  const uint32_t *plut;    // host-built two-code table (header + entries) or null
   const uint32_t *words;
   const uint64_t *offs;
   void *out;               // u8 / bf16 codes, or fp32 y for the GEMV
@@ -132,5 +133,8 @@ struct StreamArgs {
 constexpr uint32_t kPairBits = 10;                 // two-code table: 1024 entries of 8 bytes
 constexpr uint32_t kPairBitsWide = 12;             // streamed GEMV: 4096 entries of 8 bytes
 constexpr uint32_t kPairFallback = 0x80u;          // flag (byte 0 of the second word): no pair
+constexpr uint32_t kPairLutMagic = 0x31504345u;    // "ECP1", little-endian
+constexpr uint32_t kPairLutHeaderWords = 4;        // magic, flags, the code table's header word 1, 0
+constexpr uint32_t kPairLutWhole = 1u;             // flags: every index holds a whole pair
 
 }  // namespace entro

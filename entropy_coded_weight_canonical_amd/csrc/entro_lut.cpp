@@ -193,3 +193,73 @@ extern "C" const char *entro_status_str(entro_status s) {
   }
   return "unknown status";
 }
+
+// ---------------------------------------------------------------------------
+// Two-code table for the fused GEMV of 4-bit tensors, built on the host from
+// a decode table: entry i (the next kPairBitsWide stream bits, MSB first)
+// holds the bf16 values of the two codewords those bits begin with (first
+// word: A | B << 16), and in the second word their summed length in byte 1
+// and the alignbit shift 32 - length in bits [4:0]; where the two codewords
+// do not both lie within the index bits, or the bits begin no codeword, the
+// entry is {0, kPairFallback | 0xFF00}.  The lookups follow the decode table
+// exactly as the kernels do (first level by the top K bits, pointer entries
+// to the subtable of the next bits).
+// ---------------------------------------------------------------------------
+
+namespace entro {
+
+static uint32_t raw_lookup(const uint32_t *ent, uint32_t n_ent, uint32_t K, uint32_t hi) {
+  uint32_t e = ent[hi >> (32u - K)];
+  if (e & kEntryPointer) {
+    const uint32_t sb = (e >> 8) & 31u;
+    const uint32_t i2 = sb ? (hi << K) >> (32u - sb) : 0u;
+    const uint32_t j = (e >> 16) + i2;
+    e = j < n_ent ? ent[j] : 0u;
+    if (e & kEntryPointer) e = 0u;   // two levels at most
+  }
+  return e;
+}
+
+}  // namespace entro
+
+extern "C" size_t entro_pair_lut_bytes(void) {
+  return sizeof(uint32_t) * (kPairLutHeaderWords + (2u << kPairBitsWide));
+}
+
+extern "C" entro_status entro_pair_lut_build(const void *host_lut, size_t lut_bytes, void *host_out, size_t cap) {
+  if (!host_lut || !host_out || ((uintptr_t)host_lut & 3u) || ((uintptr_t)host_out & 3u)) return ENTRO_E_INVAL;
+  if (cap < entro_pair_lut_bytes() || lut_bytes < sizeof(uint32_t) * kLutHeaderWords) return ENTRO_E_INVAL;
+  const uint32_t *h = static_cast<const uint32_t *>(host_lut);
+  const uint32_t K = h[1] & 0xFFu, sym_bits = (h[1] >> 8) & 0xFFu, n_ent = h[2];
+  if (h[0] != kLutMagic || K < 1 || K > kSingleLevelMax || h[3] != (1u << K) || n_ent < h[3] ||
+      n_ent > kLutMaxEntries || (uint64_t)n_ent + kLutHeaderWords > lut_bytes / 4)
+    return ENTRO_E_INVAL;
+  if (sym_bits != 4) return ENTRO_E_UNSUPPORTED;
+  const uint32_t *ent = h + kLutHeaderWords;
+  uint32_t *out = static_cast<uint32_t *>(host_out);
+  uint32_t *pe = out + kPairLutHeaderWords;
+  bool whole = true;
+  for (uint32_t i = 0; i < (1u << kPairBitsWide); ++i) {
+    const uint32_t hi = i << (32u - kPairBitsWide);
+    uint32_t x = 0u, y = kPairFallback | 0xFF00u;
+    const uint32_t eA = raw_lookup(ent, n_ent, K, hi);
+    const uint32_t lA = eA & 31u;
+    if (lA && lA <= kPairBitsWide) {
+      const uint32_t eB = raw_lookup(ent, n_ent, K, hi << lA);
+      const uint32_t lB = eB & 31u;
+      if (lB && lA + lB <= kPairBitsWide) {
+        const uint32_t lab = lA + lB;
+        x = (eA >> 16) | (eB & 0xFFFF0000u);
+        y = (lab << 8) | ((32u - lab) & 31u);
+      }
+    }
+    whole &= (y & kPairFallback) == 0u;
+    pe[2u * i] = x;
+    pe[2u * i + 1u] = y;
+  }
+  out[0] = kPairLutMagic;
+  out[1] = whole ? kPairLutWhole : 0u;
+  out[2] = h[1];
+  out[3] = 0u;
+  return ENTRO_OK;
+}

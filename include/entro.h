@@ -121,6 +121,13 @@ typedef struct {
                                      ordinary stores, so that a consumer right after the
                                      call (decode-ahead staging) finds them in L2 or the
                                      last-level cache.  Values only; the GEMV ignores it */
+  const void *d_pair_lut;         /* optional, fused GEMV of 4-bit tensors: the two-code
+                                     table entro_pair_lut_build made from this tensor's
+                                     decode table, copied to the device 16-byte aligned;
+                                     each workgroup then loads it instead of building it
+                                     on chip.  NULL (or unaligned): built on chip.  A table
+                                     whose header does not match the decode table sets
+                                     ENTRO_F_LUT and the tensor is not decoded          */
 } entro_tensor;
 
 /* Operands of the fused GEMV for one tensor, read as a [rows][cols] row-major
@@ -153,6 +160,26 @@ size_t entro_lut_bytes(const entro_codebook *cb);
  * ENTRO_E_FORMAT (sym_bits not 4/8, max_len not in 1..16),
  * ENTRO_E_UNSUPPORTED (table larger than 16 KiB of entries). */
 entro_status entro_lut_build(const entro_codebook *cb, void *host_lut, size_t cap);
+
+/* Size in bytes of a two-code table (entro_pair_lut_build): a 16-byte header
+ * and 4096 entries of 8 bytes. */
+size_t entro_pair_lut_bytes(void);
+
+/* Build the two-code table of a 4-bit decode table (host_lut: lut_bytes of
+ * entro_lut_build output) into host_out (cap bytes, 4-byte aligned).  Entry i
+ * is indexed by the next 12 stream bits (MSB first): the bf16 values of the
+ * two codewords those bits begin with, their summed length and the matching
+ * shift, or a mark that the two codewords do not both lie within the 12 bits
+ * (then the decoder looks them up one at a time).  The header records
+ * whether every entry holds a whole pair and repeats the decode table's
+ * header word that names the code (first-level width, alphabet, length cap,
+ * shortest length).  The entry layout is the library's own; upload the bytes
+ * as they are.  Defined by: the same canonical code and dequantization as
+ * entro_lut_build; the pages leave the decoder's table structure open, and
+ * two codewords per lookup is this library's design.  Errors:
+ * ENTRO_E_INVAL (null pointers, cap too small, a malformed decode table),
+ * ENTRO_E_UNSUPPORTED (not a 4-bit table). */
+entro_status entro_pair_lut_build(const void *host_lut, size_t lut_bytes, void *host_out, size_t cap);
 
 /* Decode n tensors to their codes: d_out[i] receives t[i].n_symbols bytes.
  * Defined by: EntroLLM's parallel decoding of independent chunks

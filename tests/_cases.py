@@ -54,9 +54,10 @@ def make_case(q, bits, chunk, lanes, scale=0.0123, zp=None, max_len=None, length
                 lanes, words, offs, lut, rows, cols, refill_steps, bool(ahead))
 
 
-def upload(case: Case, device="cuda"):
+def upload(case: Case, device="cuda", pair_lut=True):
     return ent.DeviceTensor.upload(case.lut, case.words, case.offs, case.n, case.chunk, case.lanes, case.bits,
-                                   case.max_len, device=device, refill_steps=case.refill_steps, ahead=case.ahead)
+                                   case.max_len, device=device, refill_steps=case.refill_steps, ahead=case.ahead,
+                                   pair_lut=pair_lut)
 
 
 def _offset_lut(dt, case: Case, offset: int, device):
@@ -100,13 +101,18 @@ def run_decode(cases, mode="u8", device="cuda", cached=None, lut_offset=0):
     return res, status.cpu().numpy().view(np.uint32)
 
 
-def run_gemv(cases, xs, batch, device="cuda", x_offset=0, lut_offset=0):
+def run_gemv(cases, xs, batch, device="cuda", x_offset=0, lut_offset=0, pair_lut=True, edit=None):
     """Fused GEMV of ``cases`` (each with rows/cols) on bf16 inputs ``xs``.
     ``x_offset`` (elements) and ``lut_offset`` (words) place x and the decode
-    table that far past a 256-byte aligned allocation."""
+    table that far past a 256-byte aligned allocation; ``pair_lut``: upload
+    the host-built two-code tables of 4-bit tensors; ``edit(i, dt)`` may
+    change descriptor i before the call."""
     import torch
 
-    dts = [upload(c, device) for c in cases]
+    dts = [upload(c, device, pair_lut=pair_lut) for c in cases]
+    for i, d in enumerate(dts):
+        if edit:
+            edit(i, d)
     keep = [_offset_lut(d, c, lut_offset, device) for d, c in zip(dts, cases)] if lut_offset else []
     dx = []
     for x in xs:

@@ -107,6 +107,72 @@ def test_lut_matches_oracle_code(seed):
     check_lut(lut, lengths, bits, max_len, scale, zp)
 
 
+def check_pair_lut(p, lut, lengths, scale, zp):
+    """Every entry of a two-code table against the oracle's canonical code:
+    the two codewords the 12 index bits begin with (zeros after them), or the
+    fallback mark where they do not both lie within the 12 bits."""
+    codes = canonical_codes(lengths)
+    vals = dequant_bf16(np.arange(16), scale, zp)
+    assert p.size == 4 + 2 * 4096 and p[0] == 0x31504345 and p[2] == lut[1] and p[3] == 0
+    whole = True
+    for i in range(4096):
+        bits = format(i, "012b") + "0" * 20
+        a = _expected_entry(lengths, codes, vals, bits)
+        b = None
+        if a is not None and a[0] <= 12:
+            b = _expected_entry(lengths, codes, vals, bits[a[0]:] + "0" * a[0])
+        if a is None or b is None or a[0] + b[0] > 12:
+            exp = (0, 0x80 | 0xFF00)
+            whole = False
+        else:
+            lab = a[0] + b[0]
+            exp = (a[2] | (b[2] << 16), (lab << 8) | ((32 - lab) & 31))
+        assert (int(p[4 + 2 * i]), int(p[5 + 2 * i])) == exp, i
+    assert int(p[1]) == (1 if whole else 0)
+    return whole
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_pair_lut_matches_oracle_code(seed):
+    """entro_pair_lut_build over 4-bit codes of every kind: short codes (every
+    index a whole pair), long ones (up to the 12-bit cap, two-level decode
+    tables) and incomplete codes (indices that begin no codeword)."""
+    rng = np.random.default_rng(100 + seed)
+    kind = ["skewed", "peaked", "uniform", "sparse"][seed % 4]
+    q = fuzz_codes(seed, 20000, 4, kind)
+    lengths = huffman.code_lengths(quant.histogram(q, 4), 12)
+    if seed >= 4:   # geometric counts: lengths up to the cap
+        counts = (2.0 ** np.arange(16, 0, -1)).astype(np.int64)
+        lengths = huffman.code_lengths(counts if seed < 6 else counts[::-1].copy(), 12 if seed % 2 else 9)
+    scale = np.float32(rng.uniform(1e-4, 1e-1))
+    zp = int(rng.integers(0, 16))
+    lut = ent.lut_build(lengths, 4, 12, scale, zp)
+    check_pair_lut(ent.pair_lut_build(lut), lut, lengths, scale, zp)
+
+
+def test_pair_lut_cases_and_rejections(lib):
+    # uniform 4-bit code: every index holds a whole pair
+    lengths = np.full(16, 4, dtype=np.uint8)
+    lut = ent.lut_build(lengths, 4, 12, np.float32(0.5), 8)
+    assert check_pair_lut(ent.pair_lut_build(lut), lut, lengths, np.float32(0.5), 8)
+    # a 12-bit codeword: indices that begin it cannot hold a pair
+    counts = (2.0 ** np.arange(16, 0, -1)).astype(np.int64)
+    lengths = huffman.code_lengths(counts, 12)
+    assert lengths.max() == 12
+    lut = ent.lut_build(lengths, 4, 12, np.float32(0.5), 8)
+    assert not check_pair_lut(ent.pair_lut_build(lut), lut, lengths, np.float32(0.5), 8)
+    out = np.zeros(4 + 8192, dtype=np.uint32)
+    P = ctypes.c_void_p
+    bad = lut.copy()
+    bad[0] ^= 1
+    assert lib.entro_pair_lut_build(P(bad.ctypes.data), bad.nbytes, P(out.ctypes.data), out.nbytes) == 1
+    assert lib.entro_pair_lut_build(P(lut.ctypes.data), lut.nbytes, P(out.ctypes.data), out.nbytes - 4) == 1
+    assert lib.entro_pair_lut_build(P(lut.ctypes.data), 8, P(out.ctypes.data), out.nbytes) == 1
+    lut8 = ent.lut_build(np.full(256, 8, dtype=np.uint8), 8, 16, np.float32(0.5), 8)
+    assert lib.entro_pair_lut_build(P(lut8.ctypes.data), lut8.nbytes, P(out.ctypes.data), out.nbytes) == 4
+    assert lib.entro_pair_lut_bytes() == 16 + 8 * 4096
+
+
 def test_lut_two_level_with_longest_codes():
     # geometric counts force the 16-bit cap to bind on 8-bit codes
     counts = np.zeros(256, dtype=np.int64)

@@ -75,26 +75,63 @@ def _check(cases, xs, ys, st, tol=1e-4):
         assert err <= tol, (c.rows, c.cols, err)
 
 
+@pytest.mark.parametrize("pair_lut", [True, False])
 @pytest.mark.parametrize("ahead", [False, True])
 @pytest.mark.parametrize("batch", [1, 2, 3, 5, 8])
-def test_streamed_gemv_shapes_in_one_call(batch, ahead):
+def test_streamed_gemv_shapes_in_one_call(batch, ahead, pair_lut):
+    """pair_lut: two-code tables built on the host and loaded, or (False)
+    built on chip by every workgroup."""
     shapes = [(1, 1024), (15, 1536), (16, 2048), (17, 4608), (37, 5120), (300, 1024), (64, 3072), (20, 8192),
               (33, 14336), (1, 6144)]
     cases = [_rows_case(r, c, 100 + i, ahead=ahead) for i, (r, c) in enumerate(shapes)]
     xs = [activations_bf16("mistral_stack", 200 + i, c.cols, batch) for i, c in enumerate(cases)]
-    say(f"streamed gemv shapes batch={batch} ahead={ahead}")
-    ys, st = run_gemv(cases, xs, batch)
+    say(f"streamed gemv shapes batch={batch} ahead={ahead} pair_lut={pair_lut}")
+    ys, st = run_gemv(cases, xs, batch, pair_lut=pair_lut)
     _check(cases, xs, ys, st)
 
 
+@pytest.mark.parametrize("pair_lut", [True, False])
 @pytest.mark.parametrize("batch", [1, 4, 8])
-def test_streamed_gemv_codes_longer_than_six_bits(batch):
-    cases = [_long_code_case(40, 1024, 7, ahead=True), _long_code_case(23, 2560, 8)]
+def test_streamed_gemv_codes_longer_than_six_bits(batch, pair_lut):
+    cases = [_long_code_case(40, 1024, 7, ahead=True), _long_code_case(23, 2560, 8),
+             _long_code_case(19, 5120, 9, ahead=True)]
     assert max(int(c.lengths.max()) for c in cases) > 6
     xs = [activations_bf16("mistral_stack", 300 + i, c.cols, batch) for i, c in enumerate(cases)]
-    say(f"streamed gemv long codes batch={batch}")
-    ys, st = run_gemv(cases, xs, batch)
+    say(f"streamed gemv long codes batch={batch} pair_lut={pair_lut}")
+    ys, st = run_gemv(cases, xs, batch, pair_lut=pair_lut)
     _check(cases, xs, ys, st)
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_streamed_gemv_mismatched_two_code_table_is_flagged(batch):
+    """A host-built two-code table of another code is refused (ENTRO_F_LUT,
+    tensor not decoded); a misaligned one is ignored (built on chip); the
+    other tensors of the call stay exact."""
+    cases = [_rows_case(32, 1024, 41), _rows_case(32, 1024, 42), _long_code_case(21, 5120, 43),
+             _rows_case(18, 6144, 44)]
+    keep = []
+
+    def edit(i, dt):
+        import torch
+
+        if i == 1:   # the long-code table of case 2, whose header names another code
+            dt.desc.d_pair_lut = None
+            p = torch.from_numpy(__import__("entropy_coded_weight_canonical_amd").pair_lut_build(cases[2].lut)
+                                 .view(np.int32)).cuda()
+            keep.append(p)
+            dt.desc.d_pair_lut = p.data_ptr()
+        if i == 3:   # an unaligned copy: the kernels build the table themselves
+            p = torch.zeros(4 + 8196, dtype=torch.int32, device="cuda")
+            p[2:8198] = dt.pair_lut
+            keep.append(p)
+            dt.desc.d_pair_lut = p.data_ptr() + 8
+
+    xs = [activations_bf16("mistral_stack", 700 + i, c.cols, batch) for i, c in enumerate(cases)]
+    say(f"streamed gemv mismatched two-code table batch={batch}")
+    ys, st = run_gemv(cases, xs, batch, edit=edit)
+    assert st[1] == 0x20, st
+    ok = [0, 2, 3]
+    _check([cases[i] for i in ok], [xs[i] for i in ok], [ys[i] for i in ok], st[ok])
 
 
 @pytest.mark.parametrize("cap", [1, 3])
