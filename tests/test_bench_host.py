@@ -121,6 +121,8 @@ def test_workload_table_matches_the_stated_configurations():
     assert (w["tensor_4096"]["bits"], w["tensor_4096"]["scheme"], w["tensor_4096"]["chunk"],
             w["tensor_4096"]["lanes"]) == (4, "unsigned", 8192, 32)
     assert w["smollm_stack"]["bits"] == 8 and w["phi3_stack"]["bits"] == 4 and w["mistral_stack"]["bits"] == 4
+    # no lane count is stated for configs[0] and [2]: 64, the faster layout
+    assert w["tensor_2048"]["lanes"] == 64 and w["smollm_stack"]["lanes"] == 64
     for cols in (1024, 3072, 4096, 8192, 14336):
         c = bench.gemv_chunk(cols, 4096)
         assert c % cols == 0 and c >= cols
