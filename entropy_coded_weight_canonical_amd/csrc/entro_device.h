@@ -37,8 +37,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 // instruction's LDS base, 1 KiB per wavefront and instruction, so every load
 // of the copy is in flight at once and no registers hold the data.  Dwords
 // past the resource's range land as zero; lanes past n16 write nothing.  The
-// wavefront must wait_lds_copy() before it reads the copy.
+// wavefront must wait_lds_copy() before it reads the copy.  The copy's LDS
+// writes do not pass through the LDS instruction queue and can land before
+// an LDS read of the area that the wavefront issued earlier: its LDS reads
+// are waited for first.
 __device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t n16, uint32_t lane) {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  asm volatile("" ::: "memory");
   for (uint32_t v0 = 0; v0 < n16; v0 += 64u) {
     const uint32_t v = v0 + lane;
     if (v < n16)
