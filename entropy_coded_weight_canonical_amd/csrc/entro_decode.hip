@@ -1562,9 +1562,14 @@ __device__ __forceinline__ void gemv_stream(const StreamArgs &a) {
       for (uint32_t i = 0; i < a.n_tensors; ++i) atomicOr(a.t[i].status, kFLut);
     return;
   }
+  // the workgroup's share: an even part of one tensor's chunks
   const uint32_t b = blockIdx.x;
-  const uint32_t g0 = b * a.chunks_q + min(b, a.chunks_r);
-  const uint32_t g1 = g0 + a.chunks_q + (b < a.chunks_r ? 1u : 0u);
+  uint32_t tw = 0;
+  while (tw + 1 < a.n_tensors && a.wg_begin[tw + 1] <= b) ++tw;
+  const uint32_t nwg = a.wg_begin[tw + 1] - a.wg_begin[tw], bl = b - a.wg_begin[tw];
+  const uint32_t n_t = a.chunk_begin[tw + 1] - a.chunk_begin[tw];
+  const uint32_t g0 = a.chunk_begin[tw] + bl * (n_t / nwg) + min(bl, n_t % nwg);
+  const uint32_t g1 = g0 + n_t / nwg + (bl < n_t % nwg ? 1u : 0u);
   uint32_t ti = 0;
   for (uint32_t g = g0; g < g1;) {
     while (ti + 1 < a.n_tensors && a.chunk_begin[ti + 1] <= g) ++ti;
@@ -2479,10 +2484,15 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_gemv_tile_kernel(const Stre
       for (uint32_t i = 0; i < a.n_tensors; ++i) atomicOr(a.t[i].status, kFLut);
     return;
   }
-  // tiles [g0, g1) of the launch (chunk_begin counts tiles here)
+  // the workgroup's tiles: an even part of one tensor's (chunk_begin counts
+  // tiles here)
   const uint32_t b = blockIdx.x;
-  const uint32_t g0 = b * a.chunks_q + min(b, a.chunks_r);
-  const uint32_t g1 = g0 + a.chunks_q + (b < a.chunks_r ? 1u : 0u);
+  uint32_t tw = 0;
+  while (tw + 1 < a.n_tensors && a.wg_begin[tw + 1] <= b) ++tw;
+  const uint32_t nwg = a.wg_begin[tw + 1] - a.wg_begin[tw], bl = b - a.wg_begin[tw];
+  const uint32_t n_t = a.chunk_begin[tw + 1] - a.chunk_begin[tw];
+  const uint32_t g0 = a.chunk_begin[tw] + bl * (n_t / nwg) + min(bl, n_t % nwg);
+  const uint32_t g1 = g0 + n_t / nwg + (bl < n_t % nwg ? 1u : 0u);
   uint32_t ti = 0;
   for (uint32_t g = g0; g < g1;) {
     while (ti + 1 < a.n_tensors && a.chunk_begin[ti + 1] <= g) ++ti;
@@ -2701,6 +2711,41 @@ static bool stream_ok(const entro_tensor &t, const entro_gemv_item &g, uint32_t 
   return xw * 4u <= kGemvXMaxBytes && stream_fits(stream_lut_entries(t), xw);
 }
 
+// The workgroups of a streamed or matrix-core launch, split by tensor, so
+// that no workgroup's share straddles two tensors (a straddling workgroup
+// decodes its two parts one after the other, each after a table switch,
+// while the others decode one).  Tensor i gets floor(grid n_i / total)
+// workgroups, at least one and at most its n_i chunks or tiles; the rest of
+// the grid goes to the largest remainders.  The split stays within grid (the
+// resident workgroups) unless there are more tensors than that.  Returns the
+// launch's grid.
+static uint32_t split_grid(StreamArgs &a, uint32_t total, uint64_t grid) {
+  const uint32_t nt = a.n_tensors;
+  uint64_t w[kMaxTensorsPerLaunch], rem[kMaxTensorsPerLaunch], n[kMaxTensorsPerLaunch];
+  uint64_t used = 0;
+  for (uint32_t i = 0; i < nt; ++i) {
+    n[i] = a.chunk_begin[i + 1] - a.chunk_begin[i];
+    w[i] = std::max<uint64_t>(1, std::min<uint64_t>(n[i] * grid / total, n[i]));
+    rem[i] = (n[i] * grid) % total;
+    used += w[i];
+  }
+  while (used < grid) {   // the largest remainder among tensors with a chunk to spare
+    int best = -1;
+    for (uint32_t i = 0; i < nt; ++i)
+      if (w[i] < n[i] && (best < 0 || rem[i] > rem[best])) best = (int)i;
+    if (best < 0) break;
+    ++w[best], ++used;
+    rem[best] = 0;
+  }
+  uint32_t wb = 0;
+  for (uint32_t i = 0; i < nt; ++i) {
+    a.wg_begin[i] = wb;
+    wb += (uint32_t)w[i];
+  }
+  for (uint32_t r = nt; r <= (uint32_t)kMaxTensorsPerLaunch; ++r) a.wg_begin[r] = wb;
+  return wb;
+}
+
 // How a GEMV tensor is launched: the matrix-core kernel, the streamed one,
 // or (0) the staged or generic paths of ecw_kernel.
 constexpr char kTakeStream = 1, kTakeTile = 2;
@@ -2729,9 +2774,8 @@ static hipError_t launch_stream(StreamPlan &pl, hipStream_t s) {
   // wavefront a chunk, the chunks spread evenly
   const uint64_t k = std::min<uint64_t>((uint64_t)per_cu,
                                         (pl.total + (uint64_t)kWaves * cus - 1) / ((uint64_t)kWaves * cus));
-  const uint32_t grid = (uint32_t)cap_grid(std::min<uint64_t>((uint64_t)cus * std::max<uint64_t>(k, 1), pl.total));
-  pl.a.chunks_q = pl.total / grid;
-  pl.a.chunks_r = pl.total % grid;
+  const uint32_t grid = split_grid(pl.a, pl.total,
+                                  cap_grid(std::min<uint64_t>((uint64_t)cus * std::max<uint64_t>(k, 1), pl.total)));
   (void)hipGetLastError();
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlockThreads), pl.dyn, s, pl.a);
   return hipGetLastError();
@@ -2851,9 +2895,8 @@ static hipError_t launch_tile(StreamPlan &pl, hipStream_t s) {
   if (lds_fit >= 1 && per_cu > lds_fit) per_cu = lds_fit;
   if (cus < 1) cus = 1;
   // every workgroup resident at once, the tiles spread evenly
-  const uint32_t grid = (uint32_t)cap_grid(std::min<uint64_t>((uint64_t)cus * (uint64_t)per_cu, pl.total));
-  pl.a.chunks_q = pl.total / grid;
-  pl.a.chunks_r = pl.total % grid;
+  const uint32_t grid =
+      split_grid(pl.a, pl.total, cap_grid(std::min<uint64_t>((uint64_t)cus * (uint64_t)per_cu, pl.total)));
   (void)hipGetLastError();
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlockThreads), pl.dyn, s, pl.a);
   return hipGetLastError();

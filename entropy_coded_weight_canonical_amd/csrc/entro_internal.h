@@ -108,18 +108,18 @@ struct GemmArgs {
 };
 
 // Streamed fused GEMV (W = 64, 4-bit codes in pairs, chunks of whole rows,
-// 128 | cols): workgroup b takes chunks_q chunks of the launch's chunk space
-// (the tensors' chunks one after another; one more if b < chunks_r), from
-// chunk b * chunks_q + min(b, chunks_r) on.  Each wavefront streams the words
-// of its chunks through a ring of kRingBlocks blocks in LDS.
+// 128 | cols): the launch's workgroups [wg_begin[i], wg_begin[i + 1]) split
+// tensor i's chunks (or tiles) into even parts, one per workgroup.  Each
+// wavefront streams the words of its chunks through a ring of kRingBlocks
+// blocks in LDS.
 constexpr uint32_t kRingBlocks = 4;
 
 struct StreamArgs {
   TensorArg t[kMaxTensorsPerLaunch];
   uint32_t chunk_begin[kMaxTensorsPerLaunch + 1];  // first chunk of each tensor (then the total)
+  uint32_t wg_begin[kMaxTensorsPerLaunch + 1];     // first workgroup of each tensor (then the grid)
   uint32_t n_tensors;
   uint32_t batch;
-  uint32_t chunks_q, chunks_r;
   uint32_t lut_cap;        // code-table entries reserved in LDS (a multiple of 4)
   uint32_t x_words;        // LDS words of the staged activations
   uint32_t flag_word;      // LDS word index of the workgroup's table-state word
@@ -129,6 +129,7 @@ struct StreamArgs {
   uint32_t tile_x_off;     //   the x buffers
   uint32_t tile_red_off;   //   and the row-end partial sums
 };
+static_assert(sizeof(StreamArgs) <= 4096, "kernel arguments: at most 4 KiB");
 
 constexpr uint32_t kPairBits = 10;                 // two-code table: 1024 entries of 8 bytes
 constexpr uint32_t kPairBitsWide = 12;             // streamed GEMV: 4096 entries of 8 bytes

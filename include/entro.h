@@ -234,9 +234,10 @@ entro_status entro_decode_gemm(const entro_tensor *t, size_t n, const entro_gemv
 
 /* Cap the workgroups of every later launch of this library in this process
  * (0, the default: no cap).  A launch then spreads its chunks, tasks or tiles
- * over at most n workgroups, which leaves CUs free for work on other streams
- * and gives each wavefront a longer run; results do not depend on it.  A
- * launch setting, not part of the method; returns the previous cap. */
+ * over at most n workgroups (the fused GEMV's streamed launches: at least one
+ * per tensor), which leaves CUs free for work on other streams and gives
+ * each wavefront a longer run; results do not depend on it.  A launch
+ * setting, not part of the method; returns the previous cap. */
 uint32_t entro_set_max_workgroups(uint32_t n);
 
 /* Static English text for a status code. */
