@@ -1318,17 +1318,17 @@ __device__ __forceinline__ bool load_ends(const TensorArg &d, const Run &R, uint
   return __ballot(bad) == 0ull;
 }
 
-// Start the run of chunks [cb, ce) (cb < ce): the copies of its first four
-// blocks.  False if the offsets are malformed; then no copy is issued (the
-// buffer resource would be empty, and a copy that reads no memory can
-// complete out of order), and the run is not decoded.
-template <uint32_t RL>
-__device__ __forceinline__ bool run_start(const TensorArg &d, uint32_t cb, uint32_t ce, uint32_t ring_base,
-                                          uint32_t lane, Run &R) {
+// Start the run of chunks [cb, ce) (cb < ce): the copies of its first NFILL
+// blocks (the rest of the ring: ring_fill_rest).  False if the offsets are
+// malformed; then no copy is issued (the buffer resource would be empty, and
+// a copy that reads no memory can complete out of order), and the run is not
+// decoded.
+// run_begin takes the run's bounding offsets o0 = offs[cb], o1 = offs[ce],
+// read beforehand.
+template <uint32_t RL, uint32_t NFILL = kRingBlocks>
+__device__ __forceinline__ bool run_begin(const TensorArg &d, uint32_t cb, uint32_t ce, uint64_t o0, uint64_t o1,
+                                          uint32_t ring_base, uint32_t lane, Run &R) {
   constexpr uint32_t log2r = RL;
-  const __attribute__((address_space(4))) uint64_t *co =
-      (const __attribute__((address_space(4))) uint64_t *)(uintptr_t)d.offs;
-  const uint64_t o0 = co[cb], o1 = co[ce];
   const bool ok = !((o0 & 31u) || (o1 & 31u) || o1 < o0 || (o1 >> 5) > d.n_words);
   const uint32_t log2b = log2r - 2u;
   const uint64_t s0 = o0 >> 5, s1 = o1 >> 5;
@@ -1337,13 +1337,31 @@ __device__ __forceinline__ bool run_start(const TensorArg &d, uint32_t cb, uint3
   R.klast = rfl(bytes ? (bytes - 1u) >> log2r : 0u);
   R.bytes = rfl(bytes);
   R.r = __builtin_amdgcn_make_buffer_rsrc((void *)(d.words + R.base), (short)0, (int)bytes, 0x00020000);
-  const bool ends_ok = load_ends(d, R, cb, ce, o0, lane, R.ends);
   if (bytes) {
 #pragma unroll
-    for (uint32_t k = 0; k < kRingBlocks; ++k) ring_copy<RL>(R, ring_base, k, lane);
+    for (uint32_t k = 0; k < NFILL; ++k) ring_copy<RL>(R, ring_base, k, lane);
   }
+  // the end offsets after the copies, so that their load does not delay them
+  const bool ends_ok = load_ends(d, R, cb, ce, o0, lane, R.ends);
   R.p4 = rfl((uint32_t)(s0 - R.base) * 4u);
   return ok && ends_ok;
+}
+
+template <uint32_t RL, uint32_t NFILL = kRingBlocks>
+__device__ __forceinline__ bool run_start(const TensorArg &d, uint32_t cb, uint32_t ce, uint32_t ring_base,
+                                          uint32_t lane, Run &R) {
+  const __attribute__((address_space(4))) uint64_t *co =
+      (const __attribute__((address_space(4))) uint64_t *)(uintptr_t)d.offs;
+  return run_begin<RL, NFILL>(d, cb, ce, co[cb], co[ce], ring_base, lane, R);
+}
+
+// The ring's blocks NFILL.. of a run started with run_start<RL, NFILL>.
+template <uint32_t RL, uint32_t NFILL>
+__device__ __forceinline__ void ring_fill_rest(const Run &R, uint32_t ring_base, uint32_t lane) {
+  if (R.bytes) {
+#pragma unroll
+    for (uint32_t k = NFILL; k < kRingBlocks; ++k) ring_copy<RL>(R, ring_base, k, lane);
+  }
 }
 
 // After P moved from byte offset p_old on (by at most 256 bytes, less than a
@@ -1532,6 +1550,17 @@ __device__ uint32_t stream_run(const TensorArg &d, const uint32_t *lut, uint32_t
   return flags;
 }
 
+// The tensor whose workgroups include workgroup b, that tensor's workgroup
+// count nwg, and b's index bl among them (from the host's per-workgroup
+// table).
+__device__ __forceinline__ uint32_t wg_tensor(const StreamArgs &a, uint32_t b, uint32_t &nwg, uint32_t &bl) {
+  const uint32_t info = (a.wg_info_w[b >> 1] >> ((b & 1u) * 16u)) & 0xFFFFu;
+  const uint32_t tw = info >> 12;
+  nwg = (a.wg_count_w[tw >> 1] >> ((tw & 1u) * 16u)) & 0xFFFFu;
+  bl = info & 0xFFFu;
+  return tw;
+}
+
 // The host-built two-code table of a tensor into LDS [0, 32 KiB): wavefront
 // w copies bytes [2 KiB w, 2 KiB (w + 1)) with two 16-byte copies per lane.
 __device__ __forceinline__ void ptab_copy(const uint32_t *plut, uint32_t wave, uint32_t lane) {
@@ -1550,66 +1579,63 @@ __device__ __forceinline__ void gemv_stream(const StreamArgs &a) {
   // dynamic LDS: the two-code table (kPairBitsWide index bits, at LDS address
   // 0), the code table (lut_cap entries), the staged activations (x_words),
   // the table-state word, then one ring per wavefront
+  // Setup in four dependent rounds, each issued before anything waits on it
+  // (kernel argument reads stay in the first block, ahead of every branch):
+  // the workgroup split and the LDS layout; the tensor's fields and chunk
+  // range; its table headers, run offsets, activations and table entries;
+  // the ring's and the two-code table's copies.
+  const uint32_t lut_cap = a.lut_cap, flag_word = a.flag_word, ring_off = a.ring_off, batch = a.batch;
+  const uint32_t b = blockIdx.x;
+  uint32_t nwg, bl;
+  const uint32_t tw = wg_tensor(a, b, nwg, bl);
+  const TensorArg d = a.t[tw];
+  const uint32_t n_t = a.chunk_begin[tw + 1] - a.chunk_begin[tw];
   u32x2 *ptab = reinterpret_cast<u32x2 *>(dyn_lds);
   uint32_t *lut = reinterpret_cast<uint32_t *>(dyn_lds) + (2u << kPairBitsWide);
-  uint32_t *xl = lut + a.lut_cap;
-  uint32_t *state = reinterpret_cast<uint32_t *>(dyn_lds) + a.flag_word;
+  uint32_t *xl = lut + lut_cap;
+  uint32_t *state = reinterpret_cast<uint32_t *>(dyn_lds) + flag_word;
   const uint32_t wave = rfl(threadIdx.x >> 6);
   const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t ring_base = rfl(lds_addr(dyn_lds) + a.ring_off + (wave << (RL + 2u)));
-  if (!lds_at_zero()) {   // the two-code table is addressed from LDS address 0
-    if (threadIdx.x == 0)
-      for (uint32_t i = 0; i < a.n_tensors; ++i) atomicOr(a.t[i].status, kFLut);
-    return;
-  }
-  // the workgroup's share: an even part of one tensor's chunks
-  const uint32_t b = blockIdx.x;
-  uint32_t tw = 0;
-  while (tw + 1 < a.n_tensors && a.wg_begin[tw + 1] <= b) ++tw;
-  const uint32_t nwg = a.wg_begin[tw + 1] - a.wg_begin[tw], bl = b - a.wg_begin[tw];
-  const uint32_t n_t = a.chunk_begin[tw + 1] - a.chunk_begin[tw];
-  const uint32_t g0 = a.chunk_begin[tw] + bl * (n_t / nwg) + min(bl, n_t % nwg);
-  const uint32_t g1 = g0 + n_t / nwg + (bl < n_t % nwg ? 1u : 0u);
-  uint32_t ti = 0;
-  for (uint32_t g = g0; g < g1;) {
-    while (ti + 1 < a.n_tensors && a.chunk_begin[ti + 1] <= g) ++ti;
-    const TensorArg &d = a.t[ti];
-    const uint32_t seg_end = min(g1, a.chunk_begin[ti + 1]);
-    const uint32_t len = seg_end - g;
-    const uint32_t c0 = g - a.chunk_begin[ti];
+  const uint32_t ring_base = rfl(lds_addr(dyn_lds) + ring_off + (wave << (RL + 2u)));
+  // the workgroup's share, an even part of one tensor's chunks (the host
+  // gives every tensor its own workgroups, each at least one chunk)
+  const uint32_t c0 = bl * (n_t / nwg) + min(bl, n_t % nwg);   // chunks of tensor tw
+  const uint32_t len = n_t / nwg + (bl < n_t % nwg ? 1u : 0u);
+  {
     const uint32_t cb = c0 + (wave * len) / kWaves, ce = c0 + ((wave + 1u) * len) / kWaves;
-    const bool first = g == g0;
-    g = seg_end;
-    // table switch: activations and table entries into registers, the run's
-    // first copies in flight, then (after the barrier) the LDS writes
+    // the headers of both tables (in place of a missing or short table, the
+    // first 16 bytes of the chunk offsets are read and ignored)
+    const bool hv = d.lut_words >= kLutHeaderWords;
+    const bool pt = d.plut != nullptr;
+    const uint32_t *const offs32 = reinterpret_cast<const uint32_t *>(d.offs);
+    const u32x4 hh = *(const __attribute__((address_space(4))) u32x4 *)(uintptr_t)(hv ? d.lut : offs32);
+    const u32x4 ph = *(const __attribute__((address_space(4))) u32x4 *)(uintptr_t)(pt ? d.plut : offs32);
+    const uint32_t h0 = hh[0], h1 = hh[1], hne = hh[2], hl1 = hh[3];
+    const uint32_t p0 = ph[0], p1 = ph[1], p2 = ph[2];
+    const __attribute__((address_space(4))) uint64_t *co =
+        (const __attribute__((address_space(4))) uint64_t *)(uintptr_t)d.offs;
+    const uint64_t o0 = co[cb], o1 = co[ce];   // the run's bounds (cb == ce reads one twice)
+    if (!lds_at_zero()) {   // the two-code table is addressed from LDS address 0
+      if (threadIdx.x == 0) atomicOr(d.status, kFLut);
+      return;
+    }
+    // the two-code table's copy (nothing reads that LDS yet), activations
+    // and table entries into registers (written to LDS after the barrier),
+    // all in flight while the run's bounds arrive
+    if (pt) ptab_copy(d.plut, wave, lane);
     const bool x_vec = x_vec_ok(d.x);
     XRegs xr;
-    if (x_vec) x_load<BATCH>(xr, d.x, d.cols, a.batch, 0u, d.cols >> 7);
-    const uint32_t ne_fetch = min(a.lut_cap, d.lut_words > kLutHeaderWords ? d.lut_words - kLutHeaderWords : 0u);
+    if (x_vec) x_load<BATCH>(xr, d.x, d.cols, batch, 0u, d.cols >> 7);
+    const uint32_t ne_fetch = min(lut_cap, d.lut_words > kLutHeaderWords ? d.lut_words - kLutHeaderWords : 0u);
     const uint32_t nv = ((uintptr_t)d.lut & 15u) == 0u ? ne_fetch >> 2 : 0u;
     u32x4 lv = {0u, 0u, 0u, 0u};
-    uint32_t h0 = 0, h1 = 0, hne = 0, hl1 = 0;
     if (threadIdx.x < nv) lv = reinterpret_cast<const u32x4 *>(d.lut + kLutHeaderWords)[threadIdx.x];
-    if (d.lut_words >= kLutHeaderWords) {   // scalar loads: nothing to wait for among the vector loads
-      const __attribute__((address_space(4))) uint32_t *ch =
-          (const __attribute__((address_space(4))) uint32_t *)(uintptr_t)d.lut;
-      h0 = ch[0], h1 = ch[1], hne = ch[2], hl1 = ch[3];
-    }
-    // the host-built two-code table: copied now if nothing reads that LDS
-    // yet (the workgroup's first tensor), else after the barrier
-    const bool pt = d.plut != nullptr;
-    uint32_t p0 = 0, p1 = 0, p2 = 0;
-    if (pt) {
-      const __attribute__((address_space(4))) uint32_t *cp =
-          (const __attribute__((address_space(4))) uint32_t *)(uintptr_t)d.plut;
-      p0 = cp[0], p1 = cp[1], p2 = cp[2];
-      if (first) ptab_copy(d.plut, wave, lane);
-    }
+    // blocks 0 and 1 of the run now, 2 and 3 after the barriers: the copies
+    // that every wavefront waits for at the barrier are half the ring
     Run R;
     const bool have = cb < ce;
-    const bool run_ok = have && run_start<RL>(d, cb, ce, ring_base, lane, R);
+    const bool run_ok = have && run_begin<RL, 2u>(d, cb, ce, o0, o1, ring_base, lane, R);
     __syncthreads();
-    if (pt && !first) ptab_copy(d.plut, wave, lane);
     if (threadIdx.x == 0) *state = 0u;
     if (threadIdx.x < nv)
       reinterpret_cast<u32x4 *>(lut)[threadIdx.x] =
@@ -1618,12 +1644,12 @@ __device__ __forceinline__ void gemv_stream(const StreamArgs &a) {
     for (uint32_t i = 4u * nv + threadIdx.x; i < ne_fetch; i += kBlockThreads)
       lut[i] = kernel_entry<kModeGemv>(d.lut[kLutHeaderWords + i]);
     if (x_vec) x_store<BATCH>(xl, xr, d.cols >> 7);
-    else stage_x<BATCH>(xl, d.x, d.cols, a.batch, 0u, d.cols >> 7);
+    else stage_x<BATCH>(xl, d.x, d.cols, batch, 0u, d.cols >> 7);
     uint32_t k = 0;
-    if (d.lut_words >= kLutHeaderWords) {
+    if (hv) {
       const uint32_t kk = h1 & 0xFFu, lmin = h1 >> 24;
       if (h0 == kLutMagic && (h1 & 0x00FFFF00u) == d.expect_hdr && kk >= 1 && kk <= kSingleLevelMax &&
-          hl1 == (1u << kk) && hne >= hl1 && hne <= a.lut_cap && hne <= d.lut_words - kLutHeaderWords &&
+          hl1 == (1u << kk) && hne >= hl1 && hne <= lut_cap && hne <= d.lut_words - kLutHeaderWords &&
           lmin >= 1u && lmin <= kMaxCodeLen)
         k = kk | (lmin << 24);
     }
@@ -1648,18 +1674,20 @@ __device__ __forceinline__ void gemv_stream(const StreamArgs &a) {
       nofb = rfl(*state) == 0u;
     }
     if (!K) {
-      wait_lds_copy();   // the run's first copies land before the ring is reused
-      continue;
+      wait_lds_copy();   // the run's first copies land before the workgroup ends
+      return;
     }
     uint32_t flags = 0;
-    if (have && !run_ok) flags = kFOffsets;
-    else if (run_ok)
-      flags = nofb ? stream_run<BATCH, true, RL>(d, lut, K, l_min, R, cb, ce, xl, a.batch, lane, ring_base)
-                   : stream_run<BATCH, false, RL>(d, lut, K, l_min, R, cb, ce, xl, a.batch, lane, ring_base);
+    if (have && !run_ok) {
+      flags = kFOffsets;
+    } else if (run_ok) {
+      ring_fill_rest<RL, 2u>(R, ring_base, lane);
+      flags = nofb ? stream_run<BATCH, true, RL>(d, lut, K, l_min, R, cb, ce, xl, batch, lane, ring_base)
+                   : stream_run<BATCH, false, RL>(d, lut, K, l_min, R, cb, ce, xl, batch, lane, ring_base);
+    }
     if (flags && lane == 0) atomicOr(d.status, flags);
-    // copies past the run's end may still be in flight into this ring
-    wait_lds_copy();
   }
+  // copies past the run's end may still be in flight into the ring
   wait_lds_copy();
   (void)SB;
 }
@@ -2487,9 +2515,8 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_gemv_tile_kernel(const Stre
   // the workgroup's tiles: an even part of one tensor's (chunk_begin counts
   // tiles here)
   const uint32_t b = blockIdx.x;
-  uint32_t tw = 0;
-  while (tw + 1 < a.n_tensors && a.wg_begin[tw + 1] <= b) ++tw;
-  const uint32_t nwg = a.wg_begin[tw + 1] - a.wg_begin[tw], bl = b - a.wg_begin[tw];
+  uint32_t nwg, bl;
+  const uint32_t tw = wg_tensor(a, b, nwg, bl);
   const uint32_t n_t = a.chunk_begin[tw + 1] - a.chunk_begin[tw];
   const uint32_t g0 = a.chunk_begin[tw] + bl * (n_t / nwg) + min(bl, n_t % nwg);
   const uint32_t g1 = g0 + n_t / nwg + (bl < n_t % nwg ? 1u : 0u);
@@ -2721,7 +2748,8 @@ static bool stream_ok(const entro_tensor &t, const entro_gemv_item &g, uint32_t 
 // launch's grid.
 static uint32_t split_grid(StreamArgs &a, uint32_t total, uint64_t grid) {
   const uint32_t nt = a.n_tensors;
-  uint64_t w[kMaxTensorsPerLaunch], rem[kMaxTensorsPerLaunch], n[kMaxTensorsPerLaunch];
+  grid = std::min<uint64_t>(grid, (uint64_t)(kMaxStreamWgs - kMaxStreamTensors));   // the workgroup table
+  uint64_t w[kMaxStreamTensors], rem[kMaxStreamTensors], n[kMaxStreamTensors];
   uint64_t used = 0;
   for (uint32_t i = 0; i < nt; ++i) {
     n[i] = a.chunk_begin[i + 1] - a.chunk_begin[i];
@@ -2739,10 +2767,10 @@ static uint32_t split_grid(StreamArgs &a, uint32_t total, uint64_t grid) {
   }
   uint32_t wb = 0;
   for (uint32_t i = 0; i < nt; ++i) {
-    a.wg_begin[i] = wb;
+    a.wg_count[i] = (uint16_t)w[i];
+    for (uint32_t j = 0; j < (uint32_t)w[i]; ++j) a.wg_info[wb + j] = (uint16_t)(i << 12 | j);
     wb += (uint32_t)w[i];
   }
-  for (uint32_t r = nt; r <= (uint32_t)kMaxTensorsPerLaunch; ++r) a.wg_begin[r] = wb;
   return wb;
 }
 
@@ -2818,7 +2846,7 @@ static entro_status plan_stream(const entro_tensor *t, size_t n, const entro_gem
     a.batch = batch;
     uint32_t total = 0, k = 0;
     uint64_t lut_need = 0, x_need = 0;
-    for (; i < n && k < (uint32_t)kMaxTensorsPerLaunch; ++i) {
+    for (; i < n && k < (uint32_t)kMaxStreamTensors; ++i) {
       if (take[i] != kTakeStream) continue;
       const entro_tensor &x = t[i];
       const uint64_t nc = (x.n_symbols + x.chunk_symbols - 1) / x.chunk_symbols;
@@ -2839,7 +2867,7 @@ static entro_status plan_stream(const entro_tensor *t, size_t n, const entro_gem
       continue;
     }
     a.n_tensors = k;
-    for (uint32_t r = k; r <= (uint32_t)kMaxTensorsPerLaunch; ++r) a.chunk_begin[r] = total;
+    for (uint32_t r = k; r <= (uint32_t)kMaxStreamTensors; ++r) a.chunk_begin[r] = total;
     a.lut_cap = (uint32_t)((lut_need + 3) & ~3ull);
     a.x_words = (uint32_t)((x_need + 3) & ~3ull);
     pl.dyn = stream_lds_bytes(a.lut_cap, a.x_words, stream_ring(a.lut_cap, a.x_words), &a);
@@ -2903,7 +2931,7 @@ static hipError_t launch_tile(StreamPlan &pl, hipStream_t s) {
 }
 
 // Plan the matrix-core launches of the tensors marked in `take` (groups of up
-// to 32; chunk_begin counts tiles of 16 rows).
+// to kMaxStreamTensors; chunk_begin counts tiles of 16 rows).
 static entro_status plan_tile(const entro_tensor *t, size_t n, const entro_gemv_item *g, uint32_t batch,
                               uint32_t *d_status, const std::vector<char> &take, std::vector<StreamPlan> &plans) {
   size_t i = 0;
@@ -2915,7 +2943,7 @@ static entro_status plan_tile(const entro_tensor *t, size_t n, const entro_gemv_
     a.batch = batch;
     uint32_t total = 0, k = 0;
     uint64_t lut_need = 0;
-    for (; i < n && k < (uint32_t)kMaxTensorsPerLaunch; ++i) {
+    for (; i < n && k < (uint32_t)kMaxStreamTensors; ++i) {
       if (take[i] != kTakeTile) continue;
       const entro_tensor &x = t[i];
       const uint64_t nc = (x.n_symbols + x.chunk_symbols - 1) / x.chunk_symbols;
@@ -2933,7 +2961,7 @@ static entro_status plan_tile(const entro_tensor *t, size_t n, const entro_gemv_
       continue;
     }
     a.n_tensors = k;
-    for (uint32_t r = k; r <= (uint32_t)kMaxTensorsPerLaunch; ++r) a.chunk_begin[r] = total;
+    for (uint32_t r = k; r <= (uint32_t)kMaxStreamTensors; ++r) a.chunk_begin[r] = total;
     a.lut_cap = (uint32_t)((lut_need + 3) & ~3ull);
     pl.dyn = tile_lds_bytes(a.lut_cap, batch, &a);
     if (pl.dyn + kStaticLds > kLdsPerCu - kLdsPlanReserve) return ENTRO_E_UNSUPPORTED;   // not reached (tile_ok)

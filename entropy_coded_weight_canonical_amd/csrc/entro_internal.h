@@ -108,16 +108,28 @@ struct GemmArgs {
 };
 
 // Streamed fused GEMV (W = 64, 4-bit codes in pairs, chunks of whole rows,
-// 128 | cols): the launch's workgroups [wg_begin[i], wg_begin[i + 1]) split
-// tensor i's chunks (or tiles) into even parts, one per workgroup.  Each
-// wavefront streams the words of its chunks through a ring of kRingBlocks
-// blocks in LDS.
+// 128 | cols): the launch's workgroups are split by tensor, and tensor i's
+// wg_count[i] workgroups split its chunks (or tiles) into even parts, one
+// per workgroup.  Each wavefront streams the words of its chunks through a
+// ring of kRingBlocks blocks in LDS.
 constexpr uint32_t kRingBlocks = 4;
+constexpr int kMaxStreamTensors = 16;
+constexpr uint32_t kMaxStreamWgs = 1024;   // at most 4096: wg_info keeps 12 bits of index
 
 struct StreamArgs {
-  TensorArg t[kMaxTensorsPerLaunch];
-  uint32_t chunk_begin[kMaxTensorsPerLaunch + 1];  // first chunk of each tensor (then the total)
-  uint32_t wg_begin[kMaxTensorsPerLaunch + 1];     // first workgroup of each tensor (then the grid)
+  TensorArg t[kMaxStreamTensors];
+  uint32_t chunk_begin[kMaxStreamTensors + 1];  // first chunk of each tensor (then the total)
+  // workgroup b works on tensor wg_info[b] >> 12 as its workgroup
+  // wg_info[b] & 0xFFF of wg_count[that tensor]: one scalar load each (as
+  // 32-bit words), so that a workgroup finds its share in two round trips
+  union {
+    uint16_t wg_count[kMaxStreamTensors];
+    uint32_t wg_count_w[kMaxStreamTensors / 2];
+  };
+  union {
+    uint16_t wg_info[kMaxStreamWgs];
+    uint32_t wg_info_w[kMaxStreamWgs / 2];
+  };
   uint32_t n_tensors;
   uint32_t batch;
   uint32_t lut_cap;        // code-table entries reserved in LDS (a multiple of 4)

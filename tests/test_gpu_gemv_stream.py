@@ -12,7 +12,8 @@ workgroup count, rows not multiples of 16, several tensors per call (tiles of
 one workgroup in two tensors), codes longer than 6 bits (two-code table
 entries that fall back), refilling ahead, wavefronts with more than 64 rows
 (with a workgroup cap), results independent of the cap, and a malformed
-stream that is flagged while the other tensors of the call stay exact.
+stream that is flagged while the other tensors of the call stay exact,
+and calls of more tensors than one launch holds.
 """
 import os
 import sys
@@ -151,6 +152,18 @@ def test_streamed_gemv_runs_past_64_rows_per_wavefront(batch, cap):
         ys, st = run_gemv(cases, xs, batch)
     finally:
         ent.set_max_workgroups(prev)
+    _check(cases, xs, ys, st)
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_streamed_gemv_calls_of_more_tensors_than_one_launch_holds(batch):
+    """20 tensors in one call: the streamed and matrix-core launches hold at
+    most 16 each, so the call is split into several launches."""
+    shapes = [(17 + 3 * i, (1024, 2048, 4096, 5120)[i % 4]) for i in range(20)]
+    cases = [_rows_case(r, c, 900 + i, ahead=i % 2 == 0) for i, (r, c) in enumerate(shapes)]
+    xs = [activations_bf16("mistral_stack", 910 + i, c.cols, batch) for i, c in enumerate(cases)]
+    say(f"streamed gemv 20 tensors batch={batch}")
+    ys, st = run_gemv(cases, xs, batch)
     _check(cases, xs, ys, st)
 
 
