@@ -2496,67 +2496,62 @@ __device__ uint32_t tile_run(const TensorArg &d, const uint32_t *lut, uint32_t K
 
 template <uint32_t RL>
 __global__ __launch_bounds__(kBlockThreads) void ecw_gemv_tile_kernel(const StreamArgs a) {
-  // dynamic LDS: the two-code table (at LDS address 0), the code table
-  // (lut_cap entries), the table-state word, the two A tiles, the x buffers,
-  // the partial sums of a row end, then one ring per wavefront
-  u32x2 *ptab = reinterpret_cast<u32x2 *>(dyn_lds);
-  uint32_t *lut = reinterpret_cast<uint32_t *>(dyn_lds) + (2u << kPairBitsWide);
-  uint32_t *state = reinterpret_cast<uint32_t *>(dyn_lds) + a.flag_word;
-  const uint32_t wave = rfl(threadIdx.x >> 6);
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t lds0 = lds_addr(dyn_lds);
-  const uint32_t ring_base = rfl(lds0 + a.ring_off + (wave << (RL + 2u)));
-  const uint32_t a_lds = rfl(lds0 + a.tile_a_off), x_lds = rfl(lds0 + a.tile_x_off), red_lds = rfl(lds0 + a.tile_red_off);
-  if (!lds_at_zero()) {
-    if (threadIdx.x == 0)
-      for (uint32_t i = 0; i < a.n_tensors; ++i) atomicOr(a.t[i].status, kFLut);
-    return;
-  }
-  // the workgroup's tiles: an even part of one tensor's (chunk_begin counts
-  // tiles here)
+  // Setup in dependent rounds, each issued before anything waits on it, as
+  // in the streamed kernel.  Dynamic LDS: the two-code table (at LDS address
+  // 0), the code table (lut_cap entries), the table-state word, the two A
+  // tiles, the x buffers, the partial sums of a row end, then one ring per
+  // wavefront.
+  const uint32_t lut_cap = a.lut_cap, flag_word = a.flag_word, ring_off = a.ring_off, batch = a.batch;
+  const uint32_t tile_a_off = a.tile_a_off, tile_x_off = a.tile_x_off, tile_red_off = a.tile_red_off;
   const uint32_t b = blockIdx.x;
   uint32_t nwg, bl;
   const uint32_t tw = wg_tensor(a, b, nwg, bl);
-  const uint32_t n_t = a.chunk_begin[tw + 1] - a.chunk_begin[tw];
-  const uint32_t g0 = a.chunk_begin[tw] + bl * (n_t / nwg) + min(bl, n_t % nwg);
-  const uint32_t g1 = g0 + n_t / nwg + (bl < n_t % nwg ? 1u : 0u);
-  uint32_t ti = 0;
-  for (uint32_t g = g0; g < g1;) {
-    while (ti + 1 < a.n_tensors && a.chunk_begin[ti + 1] <= g) ++ti;
-    const TensorArg &d = a.t[ti];
-    const uint32_t seg_end = min(g1, a.chunk_begin[ti + 1]);
-    const uint32_t T = seg_end - g;
-    const uint32_t r0 = (g - a.chunk_begin[ti]) * 16u;                     // first row of the segment
-    const uint32_t r1 = min(r0 + 16u * T, d.n_chunks);
-    const uint32_t cb = min(r0 + wave * T, r1), ce = min(cb + T, r1);
-    const bool first = g == g0;
-    g = seg_end;
-    // table switch, as in the batch-1 kernel (no activations staged here)
-    const uint32_t ne_fetch = min(a.lut_cap, d.lut_words > kLutHeaderWords ? d.lut_words - kLutHeaderWords : 0u);
+  const TensorArg d = a.t[tw];
+  const uint32_t n_t = a.chunk_begin[tw + 1] - a.chunk_begin[tw];   // tiles of 16 rows
+  u32x2 *ptab = reinterpret_cast<u32x2 *>(dyn_lds);
+  uint32_t *lut = reinterpret_cast<uint32_t *>(dyn_lds) + (2u << kPairBitsWide);
+  uint32_t *state = reinterpret_cast<uint32_t *>(dyn_lds) + flag_word;
+  const uint32_t wave = rfl(threadIdx.x >> 6);
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t lds0 = lds_addr(dyn_lds);
+  const uint32_t ring_base = rfl(lds0 + ring_off + (wave << (RL + 2u)));
+  const uint32_t a_lds = rfl(lds0 + tile_a_off), x_lds = rfl(lds0 + tile_x_off), red_lds = rfl(lds0 + tile_red_off);
+  // the workgroup's tiles [t0, t0 + T), an even part of tensor tw's; wavefront
+  // w takes rows r0 + w T .. of them
+  const uint32_t t0 = bl * (n_t / nwg) + min(bl, n_t % nwg);
+  const uint32_t T = n_t / nwg + (bl < n_t % nwg ? 1u : 0u);
+  const uint32_t r0 = t0 * 16u;
+  const uint32_t r1 = min(r0 + 16u * T, d.n_chunks);
+  const uint32_t cb = min(r0 + wave * T, r1), ce = min(cb + T, r1);
+  {
+    // the headers of both tables (in place of a missing or short table, the
+    // first 16 bytes of the chunk offsets are read and ignored), the run's
+    // bounds
+    const bool hv = d.lut_words >= kLutHeaderWords;
+    const bool pt = d.plut != nullptr;
+    const uint32_t *const offs32 = reinterpret_cast<const uint32_t *>(d.offs);
+    const u32x4 hh = *(const __attribute__((address_space(4))) u32x4 *)(uintptr_t)(hv ? d.lut : offs32);
+    const u32x4 ph = *(const __attribute__((address_space(4))) u32x4 *)(uintptr_t)(pt ? d.plut : offs32);
+    const uint32_t h0 = hh[0], h1 = hh[1], hne = hh[2], hl1 = hh[3];
+    const uint32_t p0 = ph[0], p1 = ph[1], p2 = ph[2];
+    const __attribute__((address_space(4))) uint64_t *co =
+        (const __attribute__((address_space(4))) uint64_t *)(uintptr_t)d.offs;
+    const uint64_t o0 = co[cb], o1 = co[ce];
+    if (!lds_at_zero()) {   // the two-code table is addressed from LDS address 0
+      if (threadIdx.x == 0) atomicOr(d.status, kFLut);
+      return;
+    }
+    // the two-code table's copy (nothing reads that LDS yet) and the table
+    // entries into registers, in flight while the run's bounds arrive
+    if (pt) ptab_copy(d.plut, wave, lane);
+    const uint32_t ne_fetch = min(lut_cap, d.lut_words > kLutHeaderWords ? d.lut_words - kLutHeaderWords : 0u);
     const uint32_t nv = ((uintptr_t)d.lut & 15u) == 0u ? ne_fetch >> 2 : 0u;
     u32x4 lv = {0u, 0u, 0u, 0u};
-    uint32_t h0 = 0, h1 = 0, hne = 0, hl1 = 0;
     if (threadIdx.x < nv) lv = reinterpret_cast<const u32x4 *>(d.lut + kLutHeaderWords)[threadIdx.x];
-    if (d.lut_words >= kLutHeaderWords) {
-      const __attribute__((address_space(4))) uint32_t *ch =
-          (const __attribute__((address_space(4))) uint32_t *)(uintptr_t)d.lut;
-      h0 = ch[0], h1 = ch[1], hne = ch[2], hl1 = ch[3];
-    }
-    // the host-built two-code table: copied now if nothing reads that LDS
-    // yet (the workgroup's first tensor), else after the barrier
-    const bool pt = d.plut != nullptr;
-    uint32_t p0 = 0, p1 = 0, p2 = 0;
-    if (pt) {
-      const __attribute__((address_space(4))) uint32_t *cp =
-          (const __attribute__((address_space(4))) uint32_t *)(uintptr_t)d.plut;
-      p0 = cp[0], p1 = cp[1], p2 = cp[2];
-      if (first) ptab_copy(d.plut, wave, lane);
-    }
     Run R;
     const bool have = cb < ce;
-    const bool run_ok = have && run_start<RL>(d, cb, ce, ring_base, lane, R);
+    const bool run_ok = have && run_begin<RL>(d, cb, ce, o0, o1, ring_base, lane, R);
     __syncthreads();
-    if (pt && !first) ptab_copy(d.plut, wave, lane);
     if (threadIdx.x == 0) *state = 0u;
     if (threadIdx.x < nv)
       reinterpret_cast<u32x4 *>(lut)[threadIdx.x] =
@@ -2565,10 +2560,10 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_gemv_tile_kernel(const Stre
     for (uint32_t i = 4u * nv + threadIdx.x; i < ne_fetch; i += kBlockThreads)
       lut[i] = kernel_entry<kModeGemv>(d.lut[kLutHeaderWords + i]);
     uint32_t k = 0;
-    if (d.lut_words >= kLutHeaderWords) {
+    if (hv) {
       const uint32_t kk = h1 & 0xFFu, lmin = h1 >> 24;
       if (h0 == kLutMagic && (h1 & 0x00FFFF00u) == d.expect_hdr && kk >= 1 && kk <= kSingleLevelMax &&
-          hl1 == (1u << kk) && hne >= hl1 && hne <= a.lut_cap && hne <= d.lut_words - kLutHeaderWords &&
+          hl1 == (1u << kk) && hne >= hl1 && hne <= lut_cap && hne <= d.lut_words - kLutHeaderWords &&
           lmin >= 1u && lmin <= kMaxCodeLen)
         k = kk | (lmin << 24);
     }
@@ -2593,16 +2588,15 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_gemv_tile_kernel(const Stre
       nofb = rfl(*state) == 0u;
     }
     if (!K) {
-      wait_lds_copy();
-      continue;
+      wait_lds_copy();   // the run's first copies land before the workgroup ends
+      return;
     }
     uint32_t flags = have && !run_ok ? kFOffsets : 0u;
-    flags |= nofb ? tile_run<true, RL>(d, lut, K, l_min, R, run_ok, cb, ce, T, a.batch, wave, lane, ring_base, a_lds,
+    flags |= nofb ? tile_run<true, RL>(d, lut, K, l_min, R, run_ok, cb, ce, T, batch, wave, lane, ring_base, a_lds,
                                        x_lds, red_lds)
-                  : tile_run<false, RL>(d, lut, K, l_min, R, run_ok, cb, ce, T, a.batch, wave, lane, ring_base, a_lds,
+                  : tile_run<false, RL>(d, lut, K, l_min, R, run_ok, cb, ce, T, batch, wave, lane, ring_base, a_lds,
                                         x_lds, red_lds);
     if (flags && lane == 0) atomicOr(d.status, flags);
-    wait_lds_copy();
   }
   wait_lds_copy();
 }
