@@ -3232,17 +3232,22 @@ static entro_status run_gemm(const entro_tensor *t, size_t n, const entro_gemv_i
     dyn = (dyn + 15u) & ~(size_t)15u;
     a.slice_byte = (uint32_t)dyn;
     dyn += 2u * kGemmSliceBytes;
-    // short prompts: the activations of each slice staged in LDS as well
+    // short prompts: the activations of each slice staged in LDS as well,
+    // where the staging areas still hold the longest row (else x is read
+    // from L2 by every tile, as for long prompts)
+    const uint64_t sw = (stage_need + 3 + 3) & ~3ull;
+    auto stage_cap = [](size_t d) -> uint64_t {
+      const uint64_t words = (kLdsPerCu - kStaticLds) / 4u - (d + 16u) / 4u;
+      return words / kWaves > kStageSlack ? words / kWaves - kStageSlack : 0u;
+    };
     const uint32_t tok_pad = (n_tokens + 15u) & ~15u;
-    if (n_tokens <= kGemmXlTokens) {
+    if (n_tokens <= kGemmXlTokens && sw <= stage_cap(dyn + 2u * (size_t)tok_pad * kGemmRowStride * 2u)) {
       a.xslice_bytes = tok_pad * kGemmRowStride * 2u;
       dyn += 2u * (size_t)a.xslice_bytes;
     }
     a.state_word = (uint32_t)(dyn / 4u);
+    if (sw > stage_cap(dyn)) return ENTRO_E_UNSUPPORTED;
     dyn += 16u;
-    const uint64_t sw = (stage_need + 3 + 3) & ~3ull;
-    const uint64_t cap = ((kLdsPerCu - kStaticLds) / 4u - dyn / 4u) / kWaves - kStageSlack;
-    if (sw > cap) return ENTRO_E_UNSUPPORTED;
     a.stage_words = (uint32_t)sw;
     dyn += (size_t)kWaves * (sw + kStageSlack) * 4u;
     plans.back().second = dyn;
