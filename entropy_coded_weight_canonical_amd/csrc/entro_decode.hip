@@ -1264,7 +1264,8 @@ struct Run {
 // Copy block k of the run into its ring slot.  A ring of 2^RL words holds
 // four blocks of 2^RL bytes: with RL = 10 one 16-byte copy per lane (64 lanes
 // x 16 bytes), with RL = 9 two 4-byte copies per lane (2 x 64 lanes x 4
-// bytes), so that every lane takes part in every copy.  Every copy
+// bytes), with RL = 8 one 4-byte copy per lane, so that every lane takes part
+// in every copy.  Every copy
 // instruction reads memory: a block past the run's end is never read, and
 // its slot receives the run's last block again instead; likewise the second
 // half of the last block, where it lies wholly past the run's end, is
@@ -1282,8 +1283,11 @@ __device__ __forceinline__ void ring_copy(const Run &R, uint32_t ring_base, uint
   asm volatile("" ::: "memory");
   const uint32_t dst = ring_base + ((k << RL) & ((4u << RL) - 1u));
   const uint32_t src = min(k, R.klast) << RL;
+  static_assert(RL >= 8u && RL <= 10u, "ring blocks of 64, 128 or 256 words");
   if (RL == 10) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(R.r, (lds_void *)(uintptr_t)rfl(dst), 16, lane * 16u, rfl(src), 0, 0);
+  } else if (RL == 8) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(R.r, (lds_void *)(uintptr_t)rfl(dst), 4, lane * 4u, rfl(src), 0, 0);
   } else {
     const uint32_t src2 = src + 256u < R.bytes ? src + 256u : src;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(R.r, (lds_void *)(uintptr_t)rfl(dst), 4, lane * 4u, rfl(src), 0, 0);
@@ -1294,7 +1298,7 @@ __device__ __forceinline__ void ring_copy(const Run &R, uint32_t ring_base, uint
 
 // Copy instructions per block
 template <uint32_t RL>
-struct RingCopies { static constexpr uint32_t n = RL == 10 ? 1u : 2u; };
+struct RingCopies { static constexpr uint32_t n = RL == 9 ? 2u : 1u; };
 
 // Wait until at most two blocks' copies are in flight (every block up to the
 // one after P's has landed), then keep later LDS reads below the wait.
@@ -2014,6 +2018,17 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
   wait_lds_copy();
 }
 
+// Workgroup barrier over LDS only: this wavefront's LDS accesses have
+// completed (lgkmcnt(0)), and its vector-memory operations in flight (ring
+// and x copies) stay in flight, unlike __syncthreads(), whose fence waits
+// for them all.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // decode + GEMM (prefill, n_tokens up to kGemmMaxTokens):
 //   y[t][o] = sum_k deq(W[o][k]) * x[t][k]
@@ -2184,23 +2199,49 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
     // grp * 16 + lane % 16 of the x slice, same column pattern as A
     const uint32_t xunits = tok_groups * 256u;
     const uint32_t b_addr = xslices + ((lane & 15u) * kGemmRowStride + 8u * (lane >> 4)) * 2u;
-    XSliceRegs xr;
+    // Activations stay in flight across the slice barriers, which wait for
+    // LDS accesses only (a __syncthreads() would wait for every load in
+    // flight, a memory round trip per slice): staged prompts load slice
+    // q + 2 into registers while slice q is multiplied and store slice q + 1;
+    // longer prompts load the B operands of slice q + 1 into registers
+    // during slice q.
+    XSliceRegs xr, xr2;
     if (XL) {
       gemm_x_load(xr, d.x, cols, a.n_tokens, xunits, 0u);
       gemm_x_store(xr, xslices, xunits);
+      if (q_n > 1u) gemm_x_load(xr, d.x, cols, a.n_tokens, xunits, kGemmSliceCols);
     }
+    u32x4 bn[NT][4];
+    auto b_load = [&](u32x4 (&bo)[NT][4], uint32_t q) {
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        const uint32_t tok = (wave + (uint32_t)tt * (uint32_t)kWaves) * 16u + (lane & 15u);
+#pragma unroll
+        for (uint32_t ks = 0; ks < 4u; ++ks)
+          bo[tt][ks] = __builtin_bit_cast(
+              u32x4, gemm_x8(d.x, cols, tok, a.n_tokens, q * kGemmSliceCols + ks * 32u + 8u * (lane >> 4)));
+      }
+    };
+    if (!XL) b_load(bn, 0u);
     if (have) gemm_put(my_row_addr, lane, gemm_pair(g, lut, K, early).x);
-    __syncthreads();
+    lds_barrier();
     for (uint32_t q = 0; q < q_n; ++q) {
       const uint32_t buf = (q & 1u) * kGemmSliceBytes;
       const bool next = q + 1u < q_n;
-      if (XL && next) gemm_x_load(xr, d.x, cols, a.n_tokens, xunits, (q + 1u) * kGemmSliceCols);
+      if (XL && q + 2u < q_n) gemm_x_load(xr2, d.x, cols, a.n_tokens, xunits, (q + 2u) * kGemmSliceCols);
+      u32x4 bc[NT][4];
+      if (!XL) {
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+          for (uint32_t ks = 0; ks < 4u; ++ks) bc[tt][ks] = bn[tt][ks];
+        if (next) b_load(bn, q + 1u);
+      }
       if (have && next) gemm_put(my_row_addr + (kGemmSliceBytes - buf), lane, gemm_pair(g, lut, K, early).x);
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
         const uint32_t grp = wave + (uint32_t)tt * (uint32_t)kWaves;
         if (grp < tok_groups) {
-          const uint32_t tok = grp * 16u + (lane & 15u);
 #pragma unroll
           for (uint32_t ks = 0; ks < 4u; ++ks) {
             const bf16x8 av = __builtin_bit_cast(
@@ -2211,13 +2252,16 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKern
                                                   b_addr + (q & 1u) * a.xslice_bytes + grp * 16u * kGemmRowStride * 2u +
                                                   ks * 64u));
             else
-              bv = gemm_x8(d.x, cols, tok, a.n_tokens, q * kGemmSliceCols + ks * 32u + 8u * (lane >> 4));
+              bv = __builtin_bit_cast(bf16x8, bc[tt][ks]);
             acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[tt], 0, 0, 0);
           }
         }
       }
-      if (XL && next) gemm_x_store(xr, xslices + ((q + 1u) & 1u) * a.xslice_bytes, xunits);
-      __syncthreads();
+      if (XL && next) {
+        gemm_x_store(xr, xslices + ((q + 1u) & 1u) * a.xslice_bytes, xunits);
+        xr = xr2;
+      }
+      lds_barrier();
     }
     if (have) {
       const uint32_t flags = gemv_end_flags<1>(g, lds_addr(stage + st.al), rfl(st.nw));
@@ -2297,17 +2341,6 @@ __device__ __forceinline__ void wait_vm(uint32_t n) {
     case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
     default: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
   }
-  asm volatile("" ::: "memory");
-}
-
-// Workgroup barrier over LDS only: this wavefront's LDS accesses have
-// completed (lgkmcnt(0)), and its vector-memory operations in flight (ring
-// and x copies) stay in flight, unlike __syncthreads(), whose fence waits
-// for them all.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
@@ -2599,6 +2632,270 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_gemv_tile_kernel(const Stre
     if (flags && lane == 0) atomicOr(d.status, flags);
   }
   wait_lds_copy();
+}
+
+// ---------------------------------------------------------------------------
+// decode + GEMM in 64-row tiles (prompts; y[t][o] = sum_k deq(W[o][k]) x[t][k])
+//
+// A workgroup owns tiles of 64 consecutive rows.  Wavefront w decodes rows
+// w, 16 + w, 32 + w and 48 + w of a tile (chains 0..3), each streamed
+// through a ring of four 64-word blocks in LDS, one pair of steps (128
+// columns) per chain and slice, into a double-buffered LDS slice of 64 rows.
+// After an LDS-only barrier each wavefront multiplies the slice on the
+// matrix cores for its token groups (w and w + 16): its x operands are
+// loaded into registers one slice ahead, read once per workgroup and slice,
+// and reused by the four 16-row blocks of the tile.  A 16-row tile read x
+// four times as often, and that traffic bounded long prompts.
+//
+// Ring waits: a pair step reads at most 64 words, one block, so a chain
+// enters at most one new block per slice; the block after the one entered
+// was copied when the chain entered the block two before it, at least two
+// slices earlier.  At the start of each slice the wavefront therefore waits
+// only for the copies (and x loads) issued before the previous slice.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kGemmRingLog2 = 8;       // rings of 256 words, blocks of 64
+constexpr uint32_t kGemmChains = 4;         // rows per wavefront in a tile
+constexpr uint32_t kGemmTileRows = kGemmChains * kWaves;
+constexpr uint32_t kGemmTileSliceBytes = kGemmTileRows * kGemmRowStride * 2u;
+
+struct GemmChain {
+  Run R;
+  uint32_t hi, lo, n;
+  uint32_t end4;
+};
+
+// One pair step of chain C; returns the pair's packed weights (0 if the
+// chain has no row) and counts a ring copy in ops.
+template <bool EARLY, bool NOFB>
+__device__ __forceinline__ uint32_t gemm_chain_pair(const uint32_t *lut, uint32_t K, GemmChain &C, bool live,
+                                                    uint32_t ring_base, uint32_t ring_v, uint32_t rmask4,
+                                                    uint32_t lane, uint32_t &ops) {
+  if (!live) return 0u;
+  const uint32_t p_old = C.R.p4;
+  const u32x2 e2 = stream_pair<EARLY, NOFB>(lut, K, C.hi, C.lo, C.n, C.R.p4, ring_v, rmask4);
+  if ((p_old ^ C.R.p4) >> kGemmRingLog2) {
+    ring_copy<kGemmRingLog2>(C.R, ring_base, (C.R.p4 >> kGemmRingLog2) + (kRingBlocks - 1u), lane);
+    ops += RingCopies<kGemmRingLog2>::n;
+  }
+  return e2.x;
+}
+
+template <int NT>
+__device__ __forceinline__ void gemm_b_load(u32x4 (&bo)[NT][4], const uint16_t *x, uint32_t cols, uint32_t n_tokens,
+                                            uint32_t wave, uint32_t lane, uint32_t q) {
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const uint32_t tok = (wave + (uint32_t)tt * (uint32_t)kWaves) * 16u + (lane & 15u);
+#pragma unroll
+    for (uint32_t ks = 0; ks < 4u; ++ks)
+      bo[tt][ks] = __builtin_bit_cast(
+          u32x4, gemm_x8(x, cols, tok, n_tokens, q * kGemmSliceCols + ks * 32u + 8u * (lane >> 4)));
+  }
+}
+
+// The tile of rows [r0, r0 + 64) (rows < d.rows): decode, multiply, write y.
+template <int NT, bool NOFB>
+__device__ uint32_t gemm_tile(const TensorArg &d, const uint32_t *lut, uint32_t K, uint32_t l_min, uint32_t r0,
+                              uint32_t n_tokens, uint32_t wave, uint32_t lane, uint32_t ring0, uint32_t slices) {
+  const uint32_t cols = d.cols, rows = d.rows, q_n = cols / kGemmSliceCols;
+  const uint32_t tok_groups = (n_tokens + 15u) >> 4;
+  const uint32_t rmask4 = rfl((4u << kGemmRingLog2) - 1u);
+  const uint32_t early_n = rfl(early_pairs(d.ahead, cols >> 6, l_min));
+  uint32_t flags = 0;
+  // the chains' runs (one row each) and their first four blocks
+  GemmChain C[kGemmChains];
+  bool live[kGemmChains];
+  uint32_t ring_b[kGemmChains], ring_vv[kGemmChains];
+#pragma unroll
+  for (uint32_t c = 0; c < kGemmChains; ++c) {
+    const uint32_t row = r0 + 16u * c + wave;
+    ring_b[c] = rfl(ring0 + c * (4u << kGemmRingLog2));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(ring_vv[c]) : "s"(ring_b[c]));
+    live[c] = row < rows;
+    C[c].hi = C[c].lo = C[c].n = 0u;
+    C[c].end4 = 0u;
+    if (live[c]) {
+      const __attribute__((address_space(4))) uint64_t *co =
+          (const __attribute__((address_space(4))) uint64_t *)(uintptr_t)d.offs;
+      const bool ok = run_begin<kGemmRingLog2>(d, row, row + 1u, co[row], co[row + 1u], ring_b[c], lane, C[c].R);
+      if (!ok) {
+        flags |= kFOffsets;
+        live[c] = false;
+      } else {
+        C[c].end4 = __builtin_amdgcn_readlane(C[c].R.ends, 0);
+      }
+    }
+  }
+  wait_vm(0u);   // every ring's first four blocks
+  // each row's first decision point: every lane takes one word
+#pragma unroll
+  for (uint32_t c = 0; c < kGemmChains; ++c) {
+    if (!live[c]) continue;
+    ring_fetch(~0ull, C[c].hi, C[c].lo, C[c].n, C[c].R.p4, ring_vv[c], rmask4);
+    const uint32_t p_old = C[c].R.p4;
+    C[c].R.p4 = rfl(C[c].R.p4 + 256u);
+    if ((p_old ^ C[c].R.p4) >> kGemmRingLog2)
+      ring_copy<kGemmRingLog2>(C[c].R, ring_b[c], (C[c].R.p4 >> kGemmRingLog2) + (kRingBlocks - 1u), lane);
+  }
+  f32x4 acc[kGemmChains][NT];
+#pragma unroll
+  for (uint32_t c = 0; c < kGemmChains; ++c)
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // x operands of slice q + 1 in flight (bn) while slice q is multiplied
+  // (two slices ahead measured slower)
+  u32x4 bn[NT][4];
+  gemm_b_load<NT>(bn, d.x, cols, n_tokens, wave, lane, 0u);
+  uint32_t ops_prev = 0;
+  for (uint32_t q = 0; q < q_n; ++q) {
+    wait_vm(ops_prev);   // copies and loads issued before the previous slice
+    u32x4 bc[NT][4];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (uint32_t ks = 0; ks < 4u; ++ks) bc[tt][ks] = bn[tt][ks];
+    uint32_t ops = 0;
+    if (q + 1u < q_n) {
+      gemm_b_load<NT>(bn, d.x, cols, n_tokens, wave, lane, q + 1u);
+      ops += 4u * NT;
+    }
+    const uint32_t buf = slices + (q & 1u) * kGemmTileSliceBytes;
+#pragma unroll
+    for (uint32_t c = 0; c < kGemmChains; ++c) {
+      const uint32_t ab = q < early_n
+                              ? gemm_chain_pair<true, NOFB>(lut, K, C[c], live[c], ring_b[c], ring_vv[c], rmask4,
+                                                            lane, ops)
+                              : gemm_chain_pair<false, NOFB>(lut, K, C[c], live[c], ring_b[c], ring_vv[c], rmask4,
+                                                             lane, ops);
+      gemm_put(buf + (16u * c + wave) * kGemmRowStride * 2u, lane, ab);
+    }
+    lds_barrier();
+    // A: rows 16c + lane mod 16 of the slice, columns 32 ks + 8 (lane / 16)
+    const uint32_t a_addr = buf + ((lane & 15u) * kGemmRowStride + 8u * (lane >> 4)) * 2u;
+#pragma unroll
+    for (uint32_t ks = 0; ks < 4u; ++ks) {
+#pragma unroll
+      for (uint32_t c = 0; c < kGemmChains; ++c) {
+        const bf16x8 av = __builtin_bit_cast(
+            bf16x8, *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(
+                        a_addr + 16u * c * kGemmRowStride * 2u + ks * 64u));
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+          if (wave + (uint32_t)tt * (uint32_t)kWaves < tok_groups)
+            acc[c][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bc[tt][ks]),
+                                                                 acc[c][tt], 0, 0, 0);
+      }
+    }
+    ops_prev = ops;
+  }
+  // row ends
+#pragma unroll
+  for (uint32_t c = 0; c < kGemmChains; ++c) {
+    if (!live[c]) continue;
+    if (C[c].R.p4 != C[c].end4) flags |= C[c].R.p4 < C[c].end4 ? kFUnderrun : kFOverrun;
+    if (C[c].hi | C[c].lo) flags |= kFPadding;
+  }
+  // D of 16-row block c, token group g: lane holds rows 16c + 4 (lane / 16)
+  // + v for token 16 g + lane mod 16
+  float *y = static_cast<float *>(d.out);
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const uint32_t tok = (wave + (uint32_t)tt * (uint32_t)kWaves) * 16u + (lane & 15u);
+    if (tok < n_tokens) {
+#pragma unroll
+      for (uint32_t c = 0; c < kGemmChains; ++c)
+#pragma unroll
+        for (uint32_t v = 0; v < 4u; ++v) {
+          const uint32_t o = r0 + 16u * c + 4u * (lane >> 4) + v;
+          if (o < rows) y[(uint64_t)tok * rows + o] = acc[c][tt][v];
+        }
+    }
+  }
+  wait_lds_copy();   // copies past the rows' ends may still be in flight into the rings
+  lds_barrier();     // every wavefront is done with both slices before the next tile writes them
+  return flags;
+}
+
+template <int NT>
+__global__ __launch_bounds__(kBlockThreads) void ecw_gemm_ring_kernel(const StreamArgs a) {
+  // Set-up as in the matrix-core GEMV.  Dynamic LDS: the two-code table (at
+  // LDS address 0), the code table (lut_cap entries), the table-state word,
+  // the two 64-row slices, then four rings per wavefront.
+  const uint32_t lut_cap = a.lut_cap, flag_word = a.flag_word, ring_off = a.ring_off, n_tokens = a.batch;
+  const uint32_t slices_off = a.tile_a_off;
+  const uint32_t b = blockIdx.x;
+  uint32_t nwg, bl;
+  const uint32_t tw = wg_tensor(a, b, nwg, bl);
+  const TensorArg d = a.t[tw];
+  const uint32_t n_t = a.chunk_begin[tw + 1] - a.chunk_begin[tw];   // tiles of 64 rows
+  u32x2 *ptab = reinterpret_cast<u32x2 *>(dyn_lds);
+  uint32_t *lut = reinterpret_cast<uint32_t *>(dyn_lds) + (2u << kPairBitsWide);
+  uint32_t *state = reinterpret_cast<uint32_t *>(dyn_lds) + flag_word;
+  const uint32_t wave = rfl(threadIdx.x >> 6);
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t lds0 = lds_addr(dyn_lds);
+  const uint32_t ring0 = rfl(lds0 + ring_off + wave * (kGemmChains << (kGemmRingLog2 + 2u)));
+  const uint32_t slices = rfl(lds0 + slices_off);
+  const uint32_t t0 = bl * (n_t / nwg) + min(bl, n_t % nwg);
+  const uint32_t T = n_t / nwg + (bl < n_t % nwg ? 1u : 0u);
+  const bool hv = d.lut_words >= kLutHeaderWords;
+  const bool pt = d.plut != nullptr;
+  const uint32_t *const offs32 = reinterpret_cast<const uint32_t *>(d.offs);
+  const u32x4 hh = *(const __attribute__((address_space(4))) u32x4 *)(uintptr_t)(hv ? d.lut : offs32);
+  const u32x4 ph = *(const __attribute__((address_space(4))) u32x4 *)(uintptr_t)(pt ? d.plut : offs32);
+  const uint32_t h0 = hh[0], h1 = hh[1], hne = hh[2], hl1 = hh[3];
+  const uint32_t p0 = ph[0], p1 = ph[1], p2 = ph[2];
+  if (!lds_at_zero()) {   // the two-code table is addressed from LDS address 0
+    if (threadIdx.x == 0) atomicOr(d.status, kFLut);
+    return;
+  }
+  if (pt) ptab_copy(d.plut, wave, lane);   // nothing reads that LDS yet
+  const uint32_t ne_fetch = min(lut_cap, d.lut_words > kLutHeaderWords ? d.lut_words - kLutHeaderWords : 0u);
+  const uint32_t nv = ((uintptr_t)d.lut & 15u) == 0u ? ne_fetch >> 2 : 0u;
+  u32x4 lv = {0u, 0u, 0u, 0u};
+  if (threadIdx.x < nv) lv = reinterpret_cast<const u32x4 *>(d.lut + kLutHeaderWords)[threadIdx.x];
+  __syncthreads();
+  if (threadIdx.x == 0) *state = 0u;
+  if (threadIdx.x < nv)
+    reinterpret_cast<u32x4 *>(lut)[threadIdx.x] =
+        u32x4{kernel_entry<kModeGemv>(lv[0]), kernel_entry<kModeGemv>(lv[1]), kernel_entry<kModeGemv>(lv[2]),
+              kernel_entry<kModeGemv>(lv[3])};
+  for (uint32_t i = 4u * nv + threadIdx.x; i < ne_fetch; i += kBlockThreads)
+    lut[i] = kernel_entry<kModeGemv>(d.lut[kLutHeaderWords + i]);
+  uint32_t k = 0;
+  if (hv) {
+    const uint32_t kk = h1 & 0xFFu, lmin = h1 >> 24;
+    if (h0 == kLutMagic && (h1 & 0x00FFFF00u) == d.expect_hdr && kk >= 1 && kk <= kSingleLevelMax &&
+        hl1 == (1u << kk) && hne >= hl1 && hne <= lut_cap && hne <= d.lut_words - kLutHeaderWords &&
+        lmin >= 1u && lmin <= kMaxCodeLen)
+      k = kk | (lmin << 24);
+  }
+  if (pt && (p0 != kPairLutMagic || p2 != h1)) k = 0u;   // not this code's two-code table
+  k = rfl(k);
+  if (!k && threadIdx.x == 0) atomicOr(d.status, kFLut);
+  const uint32_t K = k & 0xFFu, l_min = k >> 24;
+  __syncthreads();
+  bool nofb = (p1 & kPairLutWhole) != 0u;
+  if (!pt) {
+    bool miss = false;
+    if (K) {
+      for (uint32_t i = threadIdx.x; i < (1u << kPairBitsWide); i += kBlockThreads) {
+        const u32x2 e = build_pair_entry<kModeGemv, kPairBitsWide>(lut, K, i);
+        ptab[i] = e;
+        miss |= (e.y & kPairFallback) != 0u;
+      }
+    }
+    if (__ballot(miss) && lane == 0) atomicOr(state, 1u);
+    __syncthreads();
+    nofb = rfl(*state) == 0u;
+  }
+  if (!K) return;
+  uint32_t flags = 0;
+  for (uint32_t t = t0; t < t0 + T; ++t) {
+    flags |= nofb ? gemm_tile<NT, true>(d, lut, K, l_min, t * kGemmTileRows, n_tokens, wave, lane, ring0, slices)
+                  : gemm_tile<NT, false>(d, lut, K, l_min, t * kGemmTileRows, n_tokens, wave, lane, ring0, slices);
+  }
+  if (flags && lane == 0) atomicOr(d.status, flags);
 }
 
 // ---------------------------------------------------------------------------
@@ -3163,6 +3460,96 @@ static hipError_t launch_gemm(GemmArgs &a, size_t dyn, hipStream_t s) {
   return hipGetLastError();
 }
 
+// decode + GEMM in 64-row tiles (ecw_gemm_ring_kernel): tensors of the
+// streamed layout (64 lanes, 4-bit codes, refill every two steps, one row per
+// chunk, 128 | cols, a stream below 4 GiB).  Prompts of kGemmRingMinTokens
+// to kGemmRingMaxTokens tokens take it (one token group per wavefront);
+// others the 16-row kernel, which stages shorter prompts' activations in LDS
+// and was as fast beyond 256 tokens.
+constexpr uint32_t kGemmRingMinTokens = 129;
+constexpr uint32_t kGemmRingMaxTokens = 16u * kWaves;
+
+// LDS bytes of a 64-row-tile launch (code table of lut_cap entries); sets
+// the layout fields of a if given.
+static size_t gemm_ring_lds_bytes(uint64_t lut_cap, StreamArgs *a = nullptr) {
+  size_t dyn = ((size_t)8u << kPairBitsWide) + (size_t)lut_cap * 4u;
+  if (a) a->flag_word = (uint32_t)(dyn / 4u);
+  dyn = (dyn + 16u + 15u) & ~(size_t)15u;
+  if (a) a->tile_a_off = (uint32_t)dyn;
+  dyn += 2u * (size_t)kGemmTileSliceBytes;
+  const size_t ring_bytes = (size_t)4u << kGemmRingLog2;
+  dyn = (dyn + ring_bytes - 1u) / ring_bytes * ring_bytes;
+  if (a) a->ring_off = (uint32_t)dyn, a->log2_ring = kGemmRingLog2;
+  return dyn + (size_t)kWaves * kGemmChains * ring_bytes;
+}
+
+static bool gemm_ring_fits(uint64_t lut_entries) {
+  return gemm_ring_lds_bytes((lut_entries + 3) & ~3ull) + kStaticLds <= kLdsPerCu - kLdsPlanReserve;
+}
+
+static bool gemm_ring_ok(const entro_tensor &t, const entro_gemv_item &g) {
+  if (t.lanes != 64u || t.sym_bits != 4u || t.refill_steps != 2u) return false;
+  if (g.cols == 0 || (g.cols % kGemmSliceCols) || t.chunk_symbols != g.cols) return false;
+  if (t.n_words >= (1ull << 30)) return false;
+  return gemm_ring_fits(stream_lut_entries(t));
+}
+
+static entro_status plan_gemm_ring(const entro_tensor *t, size_t n, const entro_gemv_item *g, uint32_t n_tokens,
+                                   uint32_t *d_status, std::vector<StreamPlan> &plans) {
+  size_t i = 0;
+  while (i < n) {
+    plans.emplace_back();
+    StreamPlan &pl = plans.back();
+    std::memset(&pl, 0, sizeof pl);
+    StreamArgs &a = pl.a;
+    a.batch = n_tokens;
+    uint32_t total = 0, k = 0;
+    uint64_t lut_need = 0;
+    for (; i < n && k < (uint32_t)kMaxStreamTensors; ++i) {
+      const entro_tensor &x = t[i];
+      if (x.n_symbols == 0) continue;
+      const uint64_t nc = (x.n_symbols + x.chunk_symbols - 1) / x.chunk_symbols;
+      const uint64_t tiles = (g[i].rows + kGemmTileRows - 1u) / kGemmTileRows;
+      if ((uint64_t)total + tiles > 0x7FFFFFFFull) break;
+      if (k && !gemm_ring_fits(std::max(lut_need, stream_lut_entries(x)))) break;
+      stream_tensor_arg(a.t[k], x, g[i], d_status + i, nc);
+      a.chunk_begin[k] = total;
+      total += (uint32_t)tiles;
+      lut_need = std::max<uint64_t>(lut_need, stream_lut_entries(x));
+      ++k;
+    }
+    if (k == 0) {
+      plans.pop_back();
+      continue;
+    }
+    a.n_tensors = k;
+    for (uint32_t r = k; r <= (uint32_t)kMaxStreamTensors; ++r) a.chunk_begin[r] = total;
+    a.lut_cap = (uint32_t)((lut_need + 3) & ~3ull);
+    pl.dyn = gemm_ring_lds_bytes(a.lut_cap, &a);
+    if (pl.dyn + kStaticLds > kLdsPerCu - kLdsPlanReserve) return ENTRO_E_UNSUPPORTED;   // not reached (gemm_ring_ok)
+    pl.total = total;
+  }
+  return ENTRO_OK;
+}
+
+static hipError_t launch_gemm_ring(StreamPlan &pl, hipStream_t s) {
+  auto kern = ecw_gemm_ring_kernel<1>;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBlockThreads, pl.dyn) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int lds_fit = (int)((kLdsPerCu - kLdsPlanReserve) / (pl.dyn + kStaticLds));
+  if (lds_fit >= 1 && per_cu > lds_fit) per_cu = lds_fit;
+  if (cus < 1) cus = 1;
+  // every workgroup resident at once, the tiles spread evenly
+  const uint32_t grid =
+      split_grid(pl.a, pl.total, cap_grid(std::min<uint64_t>((uint64_t)cus * (uint64_t)per_cu, pl.total)));
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlockThreads), pl.dyn, s, pl.a);
+  return hipGetLastError();
+}
+
 static entro_status run_gemm(const entro_tensor *t, size_t n, const entro_gemv_item *g, uint32_t n_tokens,
                              uint32_t *d_status, hipStream_t s) {
   if (n == 0) return ENTRO_OK;
@@ -3177,6 +3564,17 @@ static entro_status run_gemm(const entro_tensor *t, size_t n, const entro_gemv_i
     if (it.cols % kGemmSliceCols || t[i].chunk_symbols != it.cols) return ENTRO_E_FORMAT;
     if (t[i].lanes != 64u || t[i].sym_bits != 4u || t[i].refill_steps != 2u || t[i].max_chunk_words == 0u)
       return ENTRO_E_UNSUPPORTED;
+  }
+  bool ring = n_tokens >= kGemmRingMinTokens && n_tokens <= kGemmRingMaxTokens;
+  for (size_t i = 0; i < n && ring; ++i)
+    if (t[i].n_symbols && !gemm_ring_ok(t[i], g[i])) ring = false;
+  if (ring) {
+    std::vector<StreamPlan> rplans;
+    const entro_status st = plan_gemm_ring(t, n, g, n_tokens, d_status, rplans);
+    if (st != ENTRO_OK) return st;
+    for (auto &pl : rplans)
+      if (launch_gemm_ring(pl, s) != hipSuccess) return ENTRO_E_HIP;
+    return ENTRO_OK;
   }
   // plan every launch first (a row too long for the staging fails the call
   // before anything is enqueued), then launch

@@ -1,5 +1,6 @@
 """GPU parity of the fused decode + GEMM (prompt processing on the matrix
-cores) against the float64 oracle: token counts around the 16-token groups
+cores) against the float64 oracle: token counts around the 16-token groups,
+around the switch between the 16-row and the 64-row kernel (129..256 tokens)
 and up to the 512 maximum, row counts around the 16-row tiles, several
 matrices per call, streams with and without refilling ahead, a malformed
 stream, and a full-size Mistral-shaped matrix.  Streams and expected values
@@ -56,7 +57,7 @@ def run_gemm(cases, n_tokens, xs):
     return [y.cpu().numpy() for y in dy], status.cpu().numpy().view(np.uint32)
 
 
-@pytest.mark.parametrize("n_tokens", [1, 5, 16, 17, 64, 100, 256, 257, 512])
+@pytest.mark.parametrize("n_tokens", [1, 5, 16, 17, 64, 100, 128, 129, 200, 256, 257, 512])
 def test_gemm_matches_oracle(n_tokens):
     cases = [_case(16, 128, 1), _case(37, 256, 2, scheme="asymmetric"), _case(64, 512, 3, ahead=False),
              _case(100, 1024, 4, scheme="unsigned"), _case(5, 384, 5)]
@@ -82,7 +83,7 @@ def test_gemm_flags_a_malformed_stream():
     assert ogemv.rel_err(ys[0], ref) <= 1e-4
 
 
-@pytest.mark.parametrize("n_tokens", [64, 512])
+@pytest.mark.parametrize("n_tokens", [64, 256, 512])
 def test_gemm_mistral_o_full_size(n_tokens):
     """q/o-shaped 4096 x 4096 matrix of the Mistral-shaped stack (layer 0 weights)."""
     spec = TensorSpec("mistral_stack", 3, 0, "L0.o", 4096, 4096, "o")
@@ -97,7 +98,7 @@ def test_gemm_mistral_o_full_size(n_tokens):
     assert ogemv.rel_err(ys[0][toks], ref) <= 1e-4
 
 
-@pytest.mark.parametrize("n_tokens", [16, 64, 128])
+@pytest.mark.parametrize("n_tokens", [16, 64, 128, 200])
 def test_gemm_rows_too_long_to_stage_beside_the_activations(n_tokens):
     """14336-column rows of uniform 4-bit codes (~1790 words a row, as the
     down projection at 3.9 bits/weight): with x staged in LDS the staging
