@@ -3565,9 +3565,23 @@ static entro_status run_gemm(const entro_tensor *t, size_t n, const entro_gemv_i
     if (t[i].lanes != 64u || t[i].sym_bits != 4u || t[i].refill_steps != 2u || t[i].max_chunk_words == 0u)
       return ENTRO_E_UNSUPPORTED;
   }
+  // 64-row tiles where the call has enough of them: with fewer than 3/8 of
+  // the CUs busy (the 4096-row matrices of a Mistral-shaped layer at 64
+  // tiles on 256 CUs) the 16-row kernel, which keeps every CU busy, was
+  // faster; with 96 (q/k/v) or more, the 64-row kernel
   bool ring = n_tokens >= kGemmRingMinTokens && n_tokens <= kGemmRingMaxTokens;
-  for (size_t i = 0; i < n && ring; ++i)
+  uint64_t tiles64 = 0;
+  for (size_t i = 0; i < n && ring; ++i) {
     if (t[i].n_symbols && !gemm_ring_ok(t[i], g[i])) ring = false;
+    tiles64 += (g[i].rows + kGemmTileRows - 1u) / kGemmTileRows;
+  }
+  if (ring) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+    ring = 8u * tiles64 >= 3u * (uint64_t)cus;
+  }
   if (ring) {
     std::vector<StreamPlan> rplans;
     const entro_status st = plan_gemm_ring(t, n, g, n_tokens, d_status, rplans);

@@ -117,3 +117,33 @@ def test_gemm_rows_too_long_to_stage_beside_the_activations(n_tokens):
     # fp32 accumulation over 448 matrix-core steps of 32 columns: outputs
     # near zero (relative to the 1e-3 floor) show a few e-4
     assert err <= 1e-3, err
+
+
+@pytest.mark.parametrize("cap", [0, 7])
+@pytest.mark.parametrize("n_tokens", [129, 256])
+def test_gemm_64_row_tiles(n_tokens, cap):
+    """Calls of at least 96 tiles of 64 rows at 129..256 tokens take the
+    64-row kernel: rows not a multiple of 64, several matrices, streams with
+    and without refilling ahead, 14336-column rows; with a workgroup cap of 7
+    every workgroup decodes many tiles one after another."""
+    import entropy_coded_weight_canonical_amd as ent
+
+    rng = np.random.default_rng(12)
+    q = rng.integers(0, 16, size=(64, 14336), dtype=np.uint8)
+    cases = [_case(4000, 128, 21), _case(2100, 256, 22, scheme="unsigned", ahead=False), _case(37, 512, 23),
+             make_case(q, 4, 14336, 64, scale=0.01, zp=8, rows=64, cols=14336, refill_steps=2, ahead=True)]
+    assert sum((c.rows + 63) // 64 for c in cases) >= 96
+    xs = [activations_bf16("phi3_stack", 500 + i, c.cols, n_tokens) for i, c in enumerate(cases)]
+    say(f"decode+GEMM 64-row tiles, {n_tokens} tokens, cap {cap}")
+    prev = ent.set_max_workgroups(cap)
+    try:
+        ys, st = run_gemm(cases, n_tokens, xs)
+    finally:
+        ent.set_max_workgroups(prev)
+    assert (st == 0).all(), st
+    for c, x, y in zip(cases, xs, ys):
+        ref = ogemv.gemv_f64(c.expected_bf16().reshape(c.rows, c.cols), x)
+        assert not np.isnan(y).any()
+        err = ogemv.rel_err(y, ref)
+        assert err <= 1e-2
+        assert err <= (1e-3 if c.cols > 4096 else 1e-4), (c.rows, c.cols, err)   # fp32 sums; see the long-row test
