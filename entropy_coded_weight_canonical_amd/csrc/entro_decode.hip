@@ -2654,9 +2654,13 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_gemv_tile_kernel(const Stre
 // only for the copies (and x loads) issued before the previous slice.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kGemmRingLog2 = 8;       // rings of 256 words, blocks of 64
-constexpr uint32_t kGemmChains = 4;         // rows per wavefront in a tile
-constexpr uint32_t kGemmTileRows = kGemmChains * kWaves;
-constexpr uint32_t kGemmTileSliceBytes = kGemmTileRows * kGemmRowStride * 2u;
+
+// A tile of CH rows per wavefront (CH = 4: 64 rows; CH = 2: 32 rows).
+template <int CH>
+struct GemmTile {
+  static constexpr uint32_t rows = (uint32_t)CH * kWaves;
+  static constexpr uint32_t slice_bytes = rows * kGemmRowStride * 2u;
+};
 
 struct GemmChain {
   Run R;
@@ -2694,7 +2698,7 @@ __device__ __forceinline__ void gemm_b_load(u32x4 (&bo)[NT][4], const uint16_t *
 }
 
 // The tile of rows [r0, r0 + 64) (rows < d.rows): decode, multiply, write y.
-template <int NT, bool NOFB>
+template <int NT, int CH, bool NOFB>
 __device__ uint32_t gemm_tile(const TensorArg &d, const uint32_t *lut, uint32_t K, uint32_t l_min, uint32_t r0,
                               uint32_t n_tokens, uint32_t wave, uint32_t lane, uint32_t ring0, uint32_t slices) {
   const uint32_t cols = d.cols, rows = d.rows, q_n = cols / kGemmSliceCols;
@@ -2703,11 +2707,11 @@ __device__ uint32_t gemm_tile(const TensorArg &d, const uint32_t *lut, uint32_t 
   const uint32_t early_n = rfl(early_pairs(d.ahead, cols >> 6, l_min));
   uint32_t flags = 0;
   // the chains' runs (one row each) and their first four blocks
-  GemmChain C[kGemmChains];
-  bool live[kGemmChains];
-  uint32_t ring_b[kGemmChains], ring_vv[kGemmChains];
+  GemmChain C[CH];
+  bool live[CH];
+  uint32_t ring_b[CH], ring_vv[CH];
 #pragma unroll
-  for (uint32_t c = 0; c < kGemmChains; ++c) {
+  for (uint32_t c = 0; c < (uint32_t)CH; ++c) {
     const uint32_t row = r0 + 16u * c + wave;
     ring_b[c] = rfl(ring0 + c * (4u << kGemmRingLog2));
     asm volatile("v_mov_b32 %0, %1" : "=v"(ring_vv[c]) : "s"(ring_b[c]));
@@ -2729,7 +2733,7 @@ __device__ uint32_t gemm_tile(const TensorArg &d, const uint32_t *lut, uint32_t 
   wait_vm(0u);   // every ring's first four blocks
   // each row's first decision point: every lane takes one word
 #pragma unroll
-  for (uint32_t c = 0; c < kGemmChains; ++c) {
+  for (uint32_t c = 0; c < (uint32_t)CH; ++c) {
     if (!live[c]) continue;
     ring_fetch(~0ull, C[c].hi, C[c].lo, C[c].n, C[c].R.p4, ring_vv[c], rmask4);
     const uint32_t p_old = C[c].R.p4;
@@ -2737,9 +2741,9 @@ __device__ uint32_t gemm_tile(const TensorArg &d, const uint32_t *lut, uint32_t 
     if ((p_old ^ C[c].R.p4) >> kGemmRingLog2)
       ring_copy<kGemmRingLog2>(C[c].R, ring_b[c], (C[c].R.p4 >> kGemmRingLog2) + (kRingBlocks - 1u), lane);
   }
-  f32x4 acc[kGemmChains][NT];
+  f32x4 acc[CH][NT];
 #pragma unroll
-  for (uint32_t c = 0; c < kGemmChains; ++c)
+  for (uint32_t c = 0; c < (uint32_t)CH; ++c)
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) acc[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // x operands of slice q + 1 in flight (bn) while slice q is multiplied
@@ -2759,9 +2763,9 @@ __device__ uint32_t gemm_tile(const TensorArg &d, const uint32_t *lut, uint32_t 
       gemm_b_load<NT>(bn, d.x, cols, n_tokens, wave, lane, q + 1u);
       ops += 4u * NT;
     }
-    const uint32_t buf = slices + (q & 1u) * kGemmTileSliceBytes;
+    const uint32_t buf = slices + (q & 1u) * GemmTile<CH>::slice_bytes;
 #pragma unroll
-    for (uint32_t c = 0; c < kGemmChains; ++c) {
+    for (uint32_t c = 0; c < (uint32_t)CH; ++c) {
       const uint32_t ab = q < early_n
                               ? gemm_chain_pair<true, NOFB>(lut, K, C[c], live[c], ring_b[c], ring_vv[c], rmask4,
                                                             lane, ops)
@@ -2775,7 +2779,7 @@ __device__ uint32_t gemm_tile(const TensorArg &d, const uint32_t *lut, uint32_t 
 #pragma unroll
     for (uint32_t ks = 0; ks < 4u; ++ks) {
 #pragma unroll
-      for (uint32_t c = 0; c < kGemmChains; ++c) {
+      for (uint32_t c = 0; c < (uint32_t)CH; ++c) {
         const bf16x8 av = __builtin_bit_cast(
             bf16x8, *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(
                         a_addr + 16u * c * kGemmRowStride * 2u + ks * 64u));
@@ -2790,7 +2794,7 @@ __device__ uint32_t gemm_tile(const TensorArg &d, const uint32_t *lut, uint32_t 
   }
   // row ends
 #pragma unroll
-  for (uint32_t c = 0; c < kGemmChains; ++c) {
+  for (uint32_t c = 0; c < (uint32_t)CH; ++c) {
     if (!live[c]) continue;
     if (C[c].R.p4 != C[c].end4) flags |= C[c].R.p4 < C[c].end4 ? kFUnderrun : kFOverrun;
     if (C[c].hi | C[c].lo) flags |= kFPadding;
@@ -2803,7 +2807,7 @@ __device__ uint32_t gemm_tile(const TensorArg &d, const uint32_t *lut, uint32_t 
     const uint32_t tok = (wave + (uint32_t)tt * (uint32_t)kWaves) * 16u + (lane & 15u);
     if (tok < n_tokens) {
 #pragma unroll
-      for (uint32_t c = 0; c < kGemmChains; ++c)
+      for (uint32_t c = 0; c < (uint32_t)CH; ++c)
 #pragma unroll
         for (uint32_t v = 0; v < 4u; ++v) {
           const uint32_t o = r0 + 16u * c + 4u * (lane >> 4) + v;
@@ -2816,7 +2820,7 @@ __device__ uint32_t gemm_tile(const TensorArg &d, const uint32_t *lut, uint32_t 
   return flags;
 }
 
-template <int NT>
+template <int NT, int CH>
 __global__ __launch_bounds__(kBlockThreads) void ecw_gemm_ring_kernel(const StreamArgs a) {
   // Set-up as in the matrix-core GEMV.  Dynamic LDS: the two-code table (at
   // LDS address 0), the code table (lut_cap entries), the table-state word,
@@ -2827,14 +2831,14 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_gemm_ring_kernel(const Stre
   uint32_t nwg, bl;
   const uint32_t tw = wg_tensor(a, b, nwg, bl);
   const TensorArg d = a.t[tw];
-  const uint32_t n_t = a.chunk_begin[tw + 1] - a.chunk_begin[tw];   // tiles of 64 rows
+  const uint32_t n_t = a.chunk_begin[tw + 1] - a.chunk_begin[tw];   // tiles of 16 CH rows
   u32x2 *ptab = reinterpret_cast<u32x2 *>(dyn_lds);
   uint32_t *lut = reinterpret_cast<uint32_t *>(dyn_lds) + (2u << kPairBitsWide);
   uint32_t *state = reinterpret_cast<uint32_t *>(dyn_lds) + flag_word;
   const uint32_t wave = rfl(threadIdx.x >> 6);
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t lds0 = lds_addr(dyn_lds);
-  const uint32_t ring0 = rfl(lds0 + ring_off + wave * (kGemmChains << (kGemmRingLog2 + 2u)));
+  const uint32_t ring0 = rfl(lds0 + ring_off + wave * ((uint32_t)CH << (kGemmRingLog2 + 2u)));
   const uint32_t slices = rfl(lds0 + slices_off);
   const uint32_t t0 = bl * (n_t / nwg) + min(bl, n_t % nwg);
   const uint32_t T = n_t / nwg + (bl < n_t % nwg ? 1u : 0u);
@@ -2892,8 +2896,10 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_gemm_ring_kernel(const Stre
   if (!K) return;
   uint32_t flags = 0;
   for (uint32_t t = t0; t < t0 + T; ++t) {
-    flags |= nofb ? gemm_tile<NT, true>(d, lut, K, l_min, t * kGemmTileRows, n_tokens, wave, lane, ring0, slices)
-                  : gemm_tile<NT, false>(d, lut, K, l_min, t * kGemmTileRows, n_tokens, wave, lane, ring0, slices);
+    flags |= nofb ? gemm_tile<NT, CH, true>(d, lut, K, l_min, t * GemmTile<CH>::rows, n_tokens, wave, lane, ring0,
+                                            slices)
+                  : gemm_tile<NT, CH, false>(d, lut, K, l_min, t * GemmTile<CH>::rows, n_tokens, wave, lane, ring0,
+                                             slices);
   }
   if (flags && lane == 0) atomicOr(d.status, flags);
 }
@@ -3460,7 +3466,7 @@ static hipError_t launch_gemm(GemmArgs &a, size_t dyn, hipStream_t s) {
   return hipGetLastError();
 }
 
-// decode + GEMM in 64-row tiles (ecw_gemm_ring_kernel): tensors of the
+// decode + GEMM in 64- or 32-row tiles (ecw_gemm_ring_kernel): tensors of the
 // streamed layout (64 lanes, 4-bit codes, refill every two steps, one row per
 // chunk, 128 | cols, a stream below 4 GiB).  Prompts of kGemmRingMinTokens
 // to kGemmRingMaxTokens tokens take it (one token group per wavefront);
@@ -3469,22 +3475,22 @@ static hipError_t launch_gemm(GemmArgs &a, size_t dyn, hipStream_t s) {
 constexpr uint32_t kGemmRingMinTokens = 129;
 constexpr uint32_t kGemmRingMaxTokens = 16u * kWaves;
 
-// LDS bytes of a 64-row-tile launch (code table of lut_cap entries); sets
-// the layout fields of a if given.
-static size_t gemm_ring_lds_bytes(uint64_t lut_cap, StreamArgs *a = nullptr) {
+// LDS bytes of a launch of ch rows per wavefront (code table of lut_cap
+// entries); sets the layout fields of a if given.
+static size_t gemm_ring_lds_bytes(uint64_t lut_cap, uint32_t ch, StreamArgs *a = nullptr) {
   size_t dyn = ((size_t)8u << kPairBitsWide) + (size_t)lut_cap * 4u;
   if (a) a->flag_word = (uint32_t)(dyn / 4u);
   dyn = (dyn + 16u + 15u) & ~(size_t)15u;
   if (a) a->tile_a_off = (uint32_t)dyn;
-  dyn += 2u * (size_t)kGemmTileSliceBytes;
+  dyn += 2u * (size_t)ch * kWaves * kGemmRowStride * 2u;
   const size_t ring_bytes = (size_t)4u << kGemmRingLog2;
   dyn = (dyn + ring_bytes - 1u) / ring_bytes * ring_bytes;
   if (a) a->ring_off = (uint32_t)dyn, a->log2_ring = kGemmRingLog2;
-  return dyn + (size_t)kWaves * kGemmChains * ring_bytes;
+  return dyn + (size_t)kWaves * ch * ring_bytes;
 }
 
-static bool gemm_ring_fits(uint64_t lut_entries) {
-  return gemm_ring_lds_bytes((lut_entries + 3) & ~3ull) + kStaticLds <= kLdsPerCu - kLdsPlanReserve;
+static bool gemm_ring_fits(uint64_t lut_entries, uint32_t ch = 4) {
+  return gemm_ring_lds_bytes((lut_entries + 3) & ~3ull, ch) + kStaticLds <= kLdsPerCu - kLdsPlanReserve;
 }
 
 static bool gemm_ring_ok(const entro_tensor &t, const entro_gemv_item &g) {
@@ -3495,7 +3501,7 @@ static bool gemm_ring_ok(const entro_tensor &t, const entro_gemv_item &g) {
 }
 
 static entro_status plan_gemm_ring(const entro_tensor *t, size_t n, const entro_gemv_item *g, uint32_t n_tokens,
-                                   uint32_t *d_status, std::vector<StreamPlan> &plans) {
+                                   uint32_t ch, uint32_t *d_status, std::vector<StreamPlan> &plans) {
   size_t i = 0;
   while (i < n) {
     plans.emplace_back();
@@ -3509,9 +3515,9 @@ static entro_status plan_gemm_ring(const entro_tensor *t, size_t n, const entro_
       const entro_tensor &x = t[i];
       if (x.n_symbols == 0) continue;
       const uint64_t nc = (x.n_symbols + x.chunk_symbols - 1) / x.chunk_symbols;
-      const uint64_t tiles = (g[i].rows + kGemmTileRows - 1u) / kGemmTileRows;
+      const uint64_t tiles = (g[i].rows + 16u * ch - 1u) / (16u * ch);
       if ((uint64_t)total + tiles > 0x7FFFFFFFull) break;
-      if (k && !gemm_ring_fits(std::max(lut_need, stream_lut_entries(x)))) break;
+      if (k && !gemm_ring_fits(std::max(lut_need, stream_lut_entries(x)), ch)) break;
       stream_tensor_arg(a.t[k], x, g[i], d_status + i, nc);
       a.chunk_begin[k] = total;
       total += (uint32_t)tiles;
@@ -3525,15 +3531,15 @@ static entro_status plan_gemm_ring(const entro_tensor *t, size_t n, const entro_
     a.n_tensors = k;
     for (uint32_t r = k; r <= (uint32_t)kMaxStreamTensors; ++r) a.chunk_begin[r] = total;
     a.lut_cap = (uint32_t)((lut_need + 3) & ~3ull);
-    pl.dyn = gemm_ring_lds_bytes(a.lut_cap, &a);
+    pl.dyn = gemm_ring_lds_bytes(a.lut_cap, ch, &a);
     if (pl.dyn + kStaticLds > kLdsPerCu - kLdsPlanReserve) return ENTRO_E_UNSUPPORTED;   // not reached (gemm_ring_ok)
     pl.total = total;
   }
   return ENTRO_OK;
 }
 
-static hipError_t launch_gemm_ring(StreamPlan &pl, hipStream_t s) {
-  auto kern = ecw_gemm_ring_kernel<1>;
+static hipError_t launch_gemm_ring(StreamPlan &pl, uint32_t ch, hipStream_t s) {
+  auto kern = ch == 4u ? ecw_gemm_ring_kernel<1, 4> : ecw_gemm_ring_kernel<1, 2>;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
@@ -3565,29 +3571,31 @@ static entro_status run_gemm(const entro_tensor *t, size_t n, const entro_gemv_i
     if (t[i].lanes != 64u || t[i].sym_bits != 4u || t[i].refill_steps != 2u || t[i].max_chunk_words == 0u)
       return ENTRO_E_UNSUPPORTED;
   }
-  // 64-row tiles where the call has enough of them: with fewer than 3/8 of
-  // the CUs busy (the 4096-row matrices of a Mistral-shaped layer at 64
-  // tiles on 256 CUs) the 16-row kernel, which keeps every CU busy, was
-  // faster; with 96 (q/k/v) or more, the 64-row kernel
+  // the tallest tiles the call has enough of: with fewer than 3/8 of the
+  // CUs busy (the 4096-row matrices of a Mistral-shaped layer at 64 tiles
+  // of 64 rows on 256 CUs) smaller tiles that keep more CUs busy were
+  // faster; with 96 (q/k/v) or more, the taller ones
   bool ring = n_tokens >= kGemmRingMinTokens && n_tokens <= kGemmRingMaxTokens;
-  uint64_t tiles64 = 0;
+  uint64_t tiles64 = 0, tiles32 = 0;
   for (size_t i = 0; i < n && ring; ++i) {
     if (t[i].n_symbols && !gemm_ring_ok(t[i], g[i])) ring = false;
-    tiles64 += (g[i].rows + kGemmTileRows - 1u) / kGemmTileRows;
+    tiles64 += (g[i].rows + 63u) / 64u;
+    tiles32 += (g[i].rows + 31u) / 32u;
   }
+  uint32_t ch = 0;
   if (ring) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
-    ring = 8u * tiles64 >= 3u * (uint64_t)cus;
+    ch = 8u * tiles64 >= 3u * (uint64_t)cus ? 4u : 8u * tiles32 >= 3u * (uint64_t)cus ? 2u : 0u;
   }
-  if (ring) {
+  if (ch) {
     std::vector<StreamPlan> rplans;
-    const entro_status st = plan_gemm_ring(t, n, g, n_tokens, d_status, rplans);
+    const entro_status st = plan_gemm_ring(t, n, g, n_tokens, ch, d_status, rplans);
     if (st != ENTRO_OK) return st;
     for (auto &pl : rplans)
-      if (launch_gemm_ring(pl, s) != hipSuccess) return ENTRO_E_HIP;
+      if (launch_gemm_ring(pl, ch, s) != hipSuccess) return ENTRO_E_HIP;
     return ENTRO_OK;
   }
   // plan every launch first (a row too long for the staging fails the call

@@ -147,3 +147,32 @@ def test_gemm_64_row_tiles(n_tokens, cap):
         err = ogemv.rel_err(y, ref)
         assert err <= 1e-2
         assert err <= (1e-3 if c.cols > 4096 else 1e-4), (c.rows, c.cols, err)   # fp32 sums; see the long-row test
+
+
+@pytest.mark.parametrize("cap", [0, 5])
+@pytest.mark.parametrize("n_tokens", [129, 256])
+def test_gemm_32_row_tiles(n_tokens, cap):
+    """Calls of at least 96 tiles of 32 rows but fewer of 64 (the 4096-row
+    matrices of a Mistral-shaped layer) take the kernel with two rows per
+    wavefront."""
+    import entropy_coded_weight_canonical_amd as ent
+
+    rng = np.random.default_rng(13)
+    q = rng.integers(0, 16, size=(40, 14336), dtype=np.uint8)
+    cases = [_case(3100, 128, 31), _case(37, 512, 32, ahead=False),
+             make_case(q, 4, 14336, 64, scale=0.01, zp=8, rows=40, cols=14336, refill_steps=2, ahead=True)]
+    assert sum((c.rows + 63) // 64 for c in cases) < 96 <= sum((c.rows + 31) // 32 for c in cases)
+    xs = [activations_bf16("phi3_stack", 600 + i, c.cols, n_tokens) for i, c in enumerate(cases)]
+    say(f"decode+GEMM 32-row tiles, {n_tokens} tokens, cap {cap}")
+    prev = ent.set_max_workgroups(cap)
+    try:
+        ys, st = run_gemm(cases, n_tokens, xs)
+    finally:
+        ent.set_max_workgroups(prev)
+    assert (st == 0).all(), st
+    for c, x, y in zip(cases, xs, ys):
+        ref = ogemv.gemv_f64(c.expected_bf16().reshape(c.rows, c.cols), x)
+        assert not np.isnan(y).any()
+        err = ogemv.rel_err(y, ref)
+        assert err <= 1e-2
+        assert err <= (1e-3 if c.cols > 4096 else 1e-4), (c.rows, c.cols, err)
