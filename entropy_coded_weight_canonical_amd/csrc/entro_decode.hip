@@ -3470,9 +3470,9 @@ static hipError_t launch_gemm(GemmArgs &a, size_t dyn, hipStream_t s) {
 // streamed layout (64 lanes, 4-bit codes, refill every two steps, one row per
 // chunk, 128 | cols, a stream below 4 GiB).  Prompts of kGemmRingMinTokens
 // to kGemmRingMaxTokens tokens take it (one token group per wavefront);
-// others the 16-row kernel, which stages shorter prompts' activations in LDS
-// and was as fast beyond 256 tokens.
-constexpr uint32_t kGemmRingMinTokens = 129;
+// others the 16-row kernel: one token group keeps only one wavefront of a
+// tall tile multiplying, and beyond 256 tokens the 16-row kernel was as fast.
+constexpr uint32_t kGemmRingMinTokens = 17;
 constexpr uint32_t kGemmRingMaxTokens = 16u * kWaves;
 
 // LDS bytes of a launch of ch rows per wavefront (code table of lut_cap

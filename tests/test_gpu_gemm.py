@@ -1,7 +1,7 @@
 """GPU parity of the fused decode + GEMM (prompt processing on the matrix
-cores) against the float64 oracle: token counts around the 16-token groups,
-around the switch between the 16-row and the 64-row kernel (129..256 tokens)
-and up to the 512 maximum, row counts around the 16-row tiles, several
+cores) against the float64 oracle: token counts around the 16-token groups
+and up to the 512 maximum, calls that reach the 16-, 32- and 64-row tiles
+(17..256 tokens take the taller ones where a call has enough of them), row counts around the 16-row tiles, several
 matrices per call, streams with and without refilling ahead, a malformed
 stream, and a full-size Mistral-shaped matrix.  Streams and expected values
 come from the oracle only."""
@@ -120,9 +120,9 @@ def test_gemm_rows_too_long_to_stage_beside_the_activations(n_tokens):
 
 
 @pytest.mark.parametrize("cap", [0, 7])
-@pytest.mark.parametrize("n_tokens", [129, 256])
+@pytest.mark.parametrize("n_tokens", [17, 64, 129, 256])
 def test_gemm_64_row_tiles(n_tokens, cap):
-    """Calls of at least 96 tiles of 64 rows at 129..256 tokens take the
+    """Calls of at least 96 tiles of 64 rows at 17..256 tokens take the
     64-row kernel: rows not a multiple of 64, several matrices, streams with
     and without refilling ahead, 14336-column rows; with a workgroup cap of 7
     every workgroup decodes many tiles one after another."""
@@ -150,7 +150,7 @@ def test_gemm_64_row_tiles(n_tokens, cap):
 
 
 @pytest.mark.parametrize("cap", [0, 5])
-@pytest.mark.parametrize("n_tokens", [129, 256])
+@pytest.mark.parametrize("n_tokens", [17, 100, 256])
 def test_gemm_32_row_tiles(n_tokens, cap):
     """Calls of at least 96 tiles of 32 rows but fewer of 64 (the 4096-row
     matrices of a Mistral-shaped layer) take the kernel with two rows per
