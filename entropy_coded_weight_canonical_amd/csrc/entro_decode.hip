@@ -2030,48 +2030,11 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ---------------------------------------------------------------------------
-// decode + GEMM (prefill, n_tokens up to kGemmMaxTokens):
-//   y[t][o] = sum_k deq(W[o][k]) * x[t][k]
-// A workgroup owns kWaves consecutive rows of one matrix; wavefront w
-// decodes row w of the tile (its chunk: one row, W = 64, 4-bit codes in
-// pairs through the two-code table).  Each pair of steps gives a lane the
-// weights of columns 128q + j and 128q + 64 + j; the wavefronts write them
-// (packed like the decode outputs) into one of two LDS slices of
-// kWaves x 128 bf16, and after a workgroup barrier every wavefront that owns
-// 16-token groups multiplies the slice with them on the matrix cores
-// (v_mfma_f32_16x16x32_bf16: A = 16 rows x 32 columns of the slice,
-// B = 32 columns x 16 tokens of x, fp32 accumulation), while the next pair
-// is decoded into the other slice.  Every weight is decoded once.
+// Matrix-core operand types and the slice write shared by the decode + GEMM
+// and batched GEMV kernels.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// Decode the next pair of steps of a GEMM row (no arithmetic on it).
-__device__ __forceinline__ u32x2 gemm_pair(GemvLane<1> &g, const uint32_t *lut, uint32_t K, uint32_t early) {
-  u32x2 e2;
-  if (g.kk < early) {
-    e2 = early_pair64<kModeGemv>(lut, K, g.hi, g.lo, g.n, g.pa);
-  } else {
-    e2 = pair_lookup<kModeGemv>(lut, K, g.hi, g.lo);
-    const uint64_t m = need_mask(e2.y, g.n);
-    if (__builtin_amdgcn_inverse_ballot_w64(m)) {
-      const uint32_t idx =
-          __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      const uint32_t w = lds_word(g.pa, idx);
-      g.hi |= w >> g.n;
-      g.lo = __builtin_amdgcn_alignbit(w, 0u, g.n);
-      g.n += 32u;
-      e2 = pair_lookup<kModeGemv>(lut, K, g.hi, g.lo);
-    }
-    g.pa = lds_adv(g.pa, (uint32_t)__popcll(m));
-  }
-  ++g.kk;
-  const uint32_t nhi = __builtin_amdgcn_alignbit(g.hi, g.lo, e2.y);
-  g.lo = __builtin_amdgcn_alignbit(g.lo, 0u, e2.y);
-  g.hi = nhi;
-  g.n = sub_len(g.n, e2.y);
-  return e2;
-}
 
 // The pair's two bf16 weights of every lane into slice row `row` (byte
 // address): neighbouring lanes swap values (as for the packed decode
@@ -2082,206 +2045,6 @@ __device__ __forceinline__ void gemm_put(uint32_t row_addr, uint32_t lane, uint3
   const uint32_t v = __builtin_amdgcn_perm(nb, ab, pair_sel<kModeGemv>(lane));
   const uint32_t col = (lane & ~1u) + (lane & 1u) * 64u;
   *(__attribute__((address_space(3))) uint32_t *)(uintptr_t)(row_addr + col * 2u) = v;
-}
-
-// 16 consecutive bytes of x (8 bf16) as an MFMA operand; zero past the tokens.
-__device__ __forceinline__ bf16x8 gemm_x8(const uint16_t *x, uint32_t cols, uint32_t tok, uint32_t n_tokens,
-                                          uint32_t col) {
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (tok < n_tokens) v = *reinterpret_cast<const u32x4 *>(x + (uint64_t)tok * cols + col);
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// Activations of one slice (the tile's 128 columns of every token) staged in
-// LDS for prompts of at most kGemmXlTokens tokens: 16-byte units, unit u =
-// token u / 16, columns 8 (u % 16) .. +7; two units per thread at most.
-struct XSliceRegs { u32x4 v[2]; };
-
-__device__ __forceinline__ void gemm_x_load(XSliceRegs &r, const uint16_t *x, uint32_t cols, uint32_t n_tokens,
-                                            uint32_t units, uint32_t col0) {
-#pragma unroll
-  for (uint32_t h = 0; h < 2u; ++h) {
-    const uint32_t u = threadIdx.x + h * kBlockThreads;
-    const uint32_t tok = u >> 4;
-    r.v[h] = u32x4{0u, 0u, 0u, 0u};
-    if (u < units && tok < n_tokens)
-      r.v[h] = *reinterpret_cast<const u32x4 *>(x + (uint64_t)tok * cols + col0 + 8u * (u & 15u));
-  }
-}
-
-__device__ __forceinline__ void gemm_x_store(const XSliceRegs &r, uint32_t xs_addr, uint32_t units) {
-#pragma unroll
-  for (uint32_t h = 0; h < 2u; ++h) {
-    const uint32_t u = threadIdx.x + h * kBlockThreads;
-    if (u < units)
-      *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)(xs_addr + ((u >> 4) * kGemmRowStride + 8u * (u & 15u)) * 2u) =
-          r.v[h];
-  }
-}
-
-template <int NT, bool XL>
-__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_num_sgpr(kKernelSgprs))) void ecw_gemm_kernel(
-    const GemmArgs a) {
-  // dynamic LDS: two-code table (at 0), code table, the two weight slices,
-  // the table state word, one staging area per wavefront
-  u32x2 *ptab_area = reinterpret_cast<u32x2 *>(dyn_lds);
-  uint32_t *lut = reinterpret_cast<uint32_t *>(dyn_lds) + (2u << kPairBits);
-  const uint32_t slices = lds_addr(dyn_lds) + a.slice_byte;
-  const uint32_t xslices = slices + 2u * kGemmSliceBytes;   // two activation slices (XL)
-  if (!lds_at_zero()) {   // the two-code table is addressed from LDS address 0
-    if (threadIdx.x == 0)
-      for (uint32_t i = 0; i < a.n_tensors; ++i) atomicOr(a.t[i].status, kFLut);
-    return;
-  }
-  uint32_t &lut_state = reinterpret_cast<uint32_t *>(dyn_lds)[a.state_word];
-  const uint32_t wave = rfl(threadIdx.x >> 6);
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t stage_words = a.stage_words;
-  uint32_t *stage = reinterpret_cast<uint32_t *>(dyn_lds) + a.state_word + 4u + wave * (stage_words + kStageSlack);
-  const uint32_t tok_groups = (a.n_tokens + 15u) >> 4;
-  const uint32_t t0 = blockIdx.x * a.tiles_per_block;
-  const uint32_t t1 = min(t0 + a.tiles_per_block, a.total_tiles);
-  uint32_t cur = 0xFFFFFFFFu;
-  uint32_t K = 0, l_min = 1;
-  for (uint32_t tile = t0; tile < t1; ++tile) {
-    uint32_t ti = 0;
-    while (ti + 1 < a.n_tensors && a.tile_begin[ti + 1] <= tile) ++ti;
-    const TensorArg &d = a.t[ti];
-    if (ti != cur) {
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        uint32_t k = 0;
-        if (d.lut_words >= kLutHeaderWords) {
-          const uint32_t h0 = d.lut[0], h1 = d.lut[1], ne = d.lut[2], l1 = d.lut[3];
-          const uint32_t kk = h1 & 0xFFu;
-          const uint32_t lmin = h1 >> 24;
-          if (h0 == kLutMagic && (h1 & 0x00FFFF00u) == d.expect_hdr && kk >= 1 && kk <= kSingleLevelMax &&
-              l1 == (1u << kk) && ne >= l1 && ne <= a.lut_cap && ne <= d.lut_words - kLutHeaderWords &&
-              lmin >= 1u && lmin <= kMaxCodeLen)
-            k = kk | (ne << 8) | (lmin << 24);
-        }
-        if (!k) atomicOr(d.status, kFLut);
-        lut_state = k;
-      }
-      __syncthreads();
-      const uint32_t ne = (lut_state >> 8) & 0xFFFFu;
-      for (uint32_t i = threadIdx.x; i < ne; i += kBlockThreads) lut[i] = kernel_entry<kModeGemv>(d.lut[kLutHeaderWords + i]);
-      K = rfl(lut_state & 0xFFu);
-      l_min = rfl(lut_state >> 24);
-      cur = ti;
-      __syncthreads();
-      if (K)
-        for (uint32_t i = threadIdx.x; i < (1u << kPairBits); i += kBlockThreads)
-          ptab_area[i] = build_pair_entry<kModeGemv>(lut, K, i);
-      __syncthreads();
-    }
-    if (!K) continue;
-    const uint32_t r0 = (tile - a.tile_begin[ti]) * (uint32_t)kWaves;
-    const uint32_t row = r0 + wave;
-    const uint32_t cols = d.cols, rows = d.rows;
-    // this wavefront's row: chunk `row` (the host requires one row per chunk)
-    Staged st{0u, 0u, 0u};
-    const bool mine = row < rows;
-    const bool have = mine && stage_task<6>(d, row, stage, stage_words, st);
-    if (mine && !have && lane == 0u) atomicOr(d.status, kFOffsets);
-    GemvLane<1> g;
-    g.hi = g.lo = g.n = g.kk = 0u;
-    g.pa = lds_addr(stage + st.al);
-    const uint32_t early = rfl(early_pairs(d.ahead, cols >> 6, l_min));
-    const uint32_t q_n = cols / kGemmSliceCols;
-    const uint32_t my_row_addr = slices + wave * kGemmRowStride * 2u;
-    f32x4 acc[NT];
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // A operand: row lane % 16 of the slice, columns 8 * (lane / 16) + 32 ks
-    const uint32_t a_addr = slices + ((lane & 15u) * kGemmRowStride + 8u * (lane >> 4)) * 2u;
-    // staged activations (XL): B operand of group grp from token row
-    // grp * 16 + lane % 16 of the x slice, same column pattern as A
-    const uint32_t xunits = tok_groups * 256u;
-    const uint32_t b_addr = xslices + ((lane & 15u) * kGemmRowStride + 8u * (lane >> 4)) * 2u;
-    // Activations stay in flight across the slice barriers, which wait for
-    // LDS accesses only (a __syncthreads() would wait for every load in
-    // flight, a memory round trip per slice): staged prompts load slice
-    // q + 2 into registers while slice q is multiplied and store slice q + 1;
-    // longer prompts load the B operands of slice q + 1 into registers
-    // during slice q.
-    XSliceRegs xr, xr2;
-    if (XL) {
-      gemm_x_load(xr, d.x, cols, a.n_tokens, xunits, 0u);
-      gemm_x_store(xr, xslices, xunits);
-      if (q_n > 1u) gemm_x_load(xr, d.x, cols, a.n_tokens, xunits, kGemmSliceCols);
-    }
-    u32x4 bn[NT][4];
-    auto b_load = [&](u32x4 (&bo)[NT][4], uint32_t q) {
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt) {
-        const uint32_t tok = (wave + (uint32_t)tt * (uint32_t)kWaves) * 16u + (lane & 15u);
-#pragma unroll
-        for (uint32_t ks = 0; ks < 4u; ++ks)
-          bo[tt][ks] = __builtin_bit_cast(
-              u32x4, gemm_x8(d.x, cols, tok, a.n_tokens, q * kGemmSliceCols + ks * 32u + 8u * (lane >> 4)));
-      }
-    };
-    if (!XL) b_load(bn, 0u);
-    if (have) gemm_put(my_row_addr, lane, gemm_pair(g, lut, K, early).x);
-    lds_barrier();
-    for (uint32_t q = 0; q < q_n; ++q) {
-      const uint32_t buf = (q & 1u) * kGemmSliceBytes;
-      const bool next = q + 1u < q_n;
-      if (XL && q + 2u < q_n) gemm_x_load(xr2, d.x, cols, a.n_tokens, xunits, (q + 2u) * kGemmSliceCols);
-      u32x4 bc[NT][4];
-      if (!XL) {
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-          for (uint32_t ks = 0; ks < 4u; ++ks) bc[tt][ks] = bn[tt][ks];
-        if (next) b_load(bn, q + 1u);
-      }
-      if (have && next) gemm_put(my_row_addr + (kGemmSliceBytes - buf), lane, gemm_pair(g, lut, K, early).x);
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt) {
-        const uint32_t grp = wave + (uint32_t)tt * (uint32_t)kWaves;
-        if (grp < tok_groups) {
-#pragma unroll
-          for (uint32_t ks = 0; ks < 4u; ++ks) {
-            const bf16x8 av = __builtin_bit_cast(
-                bf16x8, *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(a_addr + buf + ks * 64u));
-            bf16x8 bv;
-            if (XL)
-              bv = __builtin_bit_cast(bf16x8, *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(
-                                                  b_addr + (q & 1u) * a.xslice_bytes + grp * 16u * kGemmRowStride * 2u +
-                                                  ks * 64u));
-            else
-              bv = __builtin_bit_cast(bf16x8, bc[tt][ks]);
-            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[tt], 0, 0, 0);
-          }
-        }
-      }
-      if (XL && next) {
-        gemm_x_store(xr, xslices + ((q + 1u) & 1u) * a.xslice_bytes, xunits);
-        xr = xr2;
-      }
-      lds_barrier();
-    }
-    if (have) {
-      const uint32_t flags = gemv_end_flags<1>(g, lds_addr(stage + st.al), rfl(st.nw));
-      if (flags && lane == 0u) atomicOr(d.status, flags);
-    }
-    // D of group grp: lane holds rows r0 + 4 (lane / 16) + v for token grp * 16 + lane % 16
-    float *y = static_cast<float *>(d.out);
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      const uint32_t grp = wave + (uint32_t)tt * (uint32_t)kWaves;
-      const uint32_t tok = grp * 16u + (lane & 15u);
-      if (grp < tok_groups && tok < a.n_tokens) {
-#pragma unroll
-        for (uint32_t v = 0; v < 4u; ++v) {
-          const uint32_t o = r0 + 4u * (lane >> 4) + v;
-          if (o < rows) y[(uint64_t)tok * rows + o] = acc[tt][v];
-        }
-      }
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -2635,23 +2398,32 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_gemv_tile_kernel(const Stre
 }
 
 // ---------------------------------------------------------------------------
-// decode + GEMM in 64-row tiles (prompts; y[t][o] = sum_k deq(W[o][k]) x[t][k])
+// decode + GEMM for prompts (y[t][o] = sum_k deq(W[o][k]) x[t][k], up to
+// 256 tokens per launch: one 16-token group per wavefront)
 //
-// A workgroup owns tiles of 64 consecutive rows.  Wavefront w decodes rows
-// w, 16 + w, 32 + w and 48 + w of a tile (chains 0..3), each streamed
-// through a ring of four 64-word blocks in LDS, one pair of steps (128
-// columns) per chain and slice, into a double-buffered LDS slice of 64 rows.
-// After an LDS-only barrier each wavefront multiplies the slice on the
-// matrix cores for its token groups (w and w + 16): its x operands are
-// loaded into registers one slice ahead, read once per workgroup and slice,
-// and reused by the four 16-row blocks of the tile.  A 16-row tile read x
-// four times as often, and that traffic bounded long prompts.
+// A workgroup owns tiles of 16 CH consecutive rows (CH = 1, 2 or 4).
+// Wavefront w decodes rows w, 16 + w, ... of a tile (chains 0..CH-1), each
+// streamed through a ring of four 64-word blocks in LDS, one pair of steps
+// (128 columns) per chain and slice, into a double-buffered LDS slice of the
+// tile's rows; after an LDS-only barrier it multiplies the slice on the
+// matrix cores (v_mfma_f32_16x16x32_bf16: A = 16 rows x 32 columns of the
+// slice, B = 32 columns x 16 tokens of x, fp32 accumulation) for its token
+// group, with x operands loaded into registers a slice ahead and reused by
+// the tile's CH 16-row blocks.  Every weight is decoded once per launch.
 //
 // Ring waits: a pair step reads at most 64 words, one block, so a chain
-// enters at most one new block per slice; the block after the one entered
-// was copied when the chain entered the block two before it, at least two
-// slices earlier.  At the start of each slice the wavefront therefore waits
-// only for the copies (and x loads) issued before the previous slice.
+// enters at most one new block per slice.  After its step in every slice a
+// chain copies the block three past P's into the slot of the block before
+// P's (again, while P stays in one block: the same bytes), so the last copy
+// of the block after P's was issued while P was two blocks back, at least
+// two slices earlier.  Before decoding a slice the wavefront therefore waits
+// only for the copies and x loads issued before the previous slice's.
+// Every slice issues the same memory operations, CH copies and 4 NT x
+// loads, whatever the data: the waits are constant and the compiler's own
+// waits for the x operands count exactly.  A chain without a row (past the
+// tensor's last row, or whose offsets were refused) copies the tensor's
+// first offsets instead, which lie inside their buffer; a copy wholly
+// outside its buffer could complete ahead of earlier loads.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kGemmRingLog2 = 8;       // rings of 256 words, blocks of 64
 
@@ -2668,32 +2440,52 @@ struct GemmChain {
   uint32_t end4;
 };
 
-// One pair step of chain C; returns the pair's packed weights (0 if the
-// chain has no row) and counts a ring copy in ops.
-template <bool EARLY, bool NOFB>
-__device__ __forceinline__ uint32_t gemm_chain_pair(const uint32_t *lut, uint32_t K, GemmChain &C, bool live,
-                                                    uint32_t ring_base, uint32_t ring_v, uint32_t rmask4,
-                                                    uint32_t lane, uint32_t &ops) {
-  if (!live) return 0u;
-  const uint32_t p_old = C.R.p4;
-  const u32x2 e2 = stream_pair<EARLY, NOFB>(lut, K, C.hi, C.lo, C.n, C.R.p4, ring_v, rmask4);
-  if ((p_old ^ C.R.p4) >> kGemmRingLog2) {
-    ring_copy<kGemmRingLog2>(C.R, ring_base, (C.R.p4 >> kGemmRingLog2) + (kRingBlocks - 1u), lane);
-    ops += RingCopies<kGemmRingLog2>::n;
+// One pair step of a chain whose two-code table holds whole pairs, as
+// stream_pair<EARLY, true> computes it, without branches: every lane reads
+// the ring word it would take and looks the pair up again, and the lanes
+// that take a word keep the results.  Steps of several chains written one
+// after another can then be interleaved.  (A lane that takes no word reads
+// a word of its own ring: the index is masked to the ring.)
+template <bool EARLY>
+__device__ __forceinline__ uint32_t gemm_pair_nofb(uint32_t &hi, uint32_t &lo, uint32_t &n, uint32_t &p4,
+                                                   uint32_t ring_v, uint32_t rmask4) {
+  u32x2 e2 = *(lds_u32x2 *)(uintptr_t)((hi >> (32u - kPairBitsWide)) << 3);
+  const bool take = EARLY ? n < 32u : ((e2.y >> 8) & 0xFFu) > n;
+  const uint64_t m = __builtin_amdgcn_ballot_w64(take);
+  const uint32_t idx = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  uint32_t a;
+  asm("v_lshl_add_u32 %0, %1, 2, %2\n\tv_and_or_b32 %0, %0, %3, %4"
+      : "=&v"(a) : "v"(idx), "s"(p4), "s"(rmask4), "v"(ring_v));
+  const uint32_t w = *(lds_u32 *)(uintptr_t)a;
+  const uint32_t hi2 = hi | (w >> (n & 31u));
+  const uint32_t lo2 = __builtin_amdgcn_alignbit(w, 0u, n);
+  if (!EARLY) {   // the pair is looked up again with the word merged in
+    const u32x2 e2b = *(lds_u32x2 *)(uintptr_t)((hi2 >> (32u - kPairBitsWide)) << 3);
+    e2.x = take ? e2b.x : e2.x;
+    e2.y = take ? e2b.y : e2.y;
   }
+  hi = take ? hi2 : hi;
+  lo = take ? lo2 : lo;
+  n = take ? n + 32u : n;
+  p4_add(p4, m);
+  const uint32_t nhi = __builtin_amdgcn_alignbit(hi, lo, e2.y);
+  lo = __builtin_amdgcn_alignbit(lo, 0u, e2.y);
+  hi = nhi;
+  n = sub_len(n, e2.y);
   return e2.x;
 }
 
+// x operands of slice q.  Every lane loads: a lane past the tokens reads the
+// last token's row, and the products of those columns are not stored.
 template <int NT>
 __device__ __forceinline__ void gemm_b_load(u32x4 (&bo)[NT][4], const uint16_t *x, uint32_t cols, uint32_t n_tokens,
                                             uint32_t wave, uint32_t lane, uint32_t q) {
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
-    const uint32_t tok = (wave + (uint32_t)tt * (uint32_t)kWaves) * 16u + (lane & 15u);
+    const uint32_t tok = min((wave + (uint32_t)tt * (uint32_t)kWaves) * 16u + (lane & 15u), n_tokens - 1u);
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(x + (uint64_t)tok * cols + q * kGemmSliceCols + 8u * (lane >> 4));
 #pragma unroll
-    for (uint32_t ks = 0; ks < 4u; ++ks)
-      bo[tt][ks] = __builtin_bit_cast(
-          u32x4, gemm_x8(x, cols, tok, n_tokens, q * kGemmSliceCols + ks * 32u + 8u * (lane >> 4)));
+    for (uint32_t ks = 0; ks < 4u; ++ks) bo[tt][ks] = p[ks * 4u];
   }
 }
 
@@ -2729,6 +2521,12 @@ __device__ uint32_t gemm_tile(const TensorArg &d, const uint32_t *lut, uint32_t 
         C[c].end4 = __builtin_amdgcn_readlane(C[c].R.ends, 0);
       }
     }
+    if (!live[c]) {   // copies read the first 16 bytes of the offsets (two of them exist)
+      C[c].R.r = __builtin_amdgcn_make_buffer_rsrc((void *)d.offs, (short)0, 16, 0x00020000);
+      C[c].R.klast = 0u;
+      C[c].R.bytes = 16u;
+      C[c].R.p4 = 0u;
+    }
   }
   wait_vm(0u);   // every ring's first four blocks
   // each row's first decision point: every lane takes one word
@@ -2746,52 +2544,91 @@ __device__ uint32_t gemm_tile(const TensorArg &d, const uint32_t *lut, uint32_t 
   for (uint32_t c = 0; c < (uint32_t)CH; ++c)
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) acc[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // x operands of slice q + 1 in flight (bn) while slice q is multiplied
-  // (two slices ahead measured slower)
-  u32x4 bn[NT][4];
-  gemm_b_load<NT>(bn, d.x, cols, n_tokens, wave, lane, 0u);
-  uint32_t ops_prev = 0;
-  for (uint32_t q = 0; q < q_n; ++q) {
-    wait_vm(ops_prev);   // copies and loads issued before the previous slice
-    u32x4 bc[NT][4];
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-      for (uint32_t ks = 0; ks < 4u; ++ks) bc[tt][ks] = bn[tt][ks];
-    uint32_t ops = 0;
-    if (q + 1u < q_n) {
-      gemm_b_load<NT>(bn, d.x, cols, n_tokens, wave, lane, q + 1u);
-      ops += 4u * NT;
-    }
+  // Slice 0 is decoded before the loop; between two barriers a wavefront
+  // then multiplies slice q - 1 and decodes slice q, in that order in half of
+  // the wavefronts of each SIMD and in the other order in the rest, so that
+  // each SIMD's matrix cores and vector ALUs run at once.  Right after its
+  // products a wavefront loads the x operands of the next slice into the
+  // same registers: a decode lies between those loads and their use, and the
+  // wavefronts' loads are spread over the interval (loading two slices ahead
+  // measured slower).  The last interval multiplies only.
+  constexpr uint32_t kOps = (uint32_t)CH * RingCopies<kGemmRingLog2>::n + 4u * NT;   // per interval
+  const bool decode_first = (wave & 4u) != 0u;
+  auto decode = [&](uint32_t q) {
     const uint32_t buf = slices + (q & 1u) * GemmTile<CH>::slice_bytes;
+    uint32_t ab[CH];
+    if (NOFB) {   // every chain steps (one without a row decodes its own ring), without branches
+      if (q < early_n) {
 #pragma unroll
-    for (uint32_t c = 0; c < (uint32_t)CH; ++c) {
-      const uint32_t ab = q < early_n
-                              ? gemm_chain_pair<true, NOFB>(lut, K, C[c], live[c], ring_b[c], ring_vv[c], rmask4,
-                                                            lane, ops)
-                              : gemm_chain_pair<false, NOFB>(lut, K, C[c], live[c], ring_b[c], ring_vv[c], rmask4,
-                                                             lane, ops);
-      gemm_put(buf + (16u * c + wave) * kGemmRowStride * 2u, lane, ab);
+        for (uint32_t c = 0; c < (uint32_t)CH; ++c)
+          ab[c] = gemm_pair_nofb<true>(C[c].hi, C[c].lo, C[c].n, C[c].R.p4, ring_vv[c], rmask4);
+      } else {
+#pragma unroll
+        for (uint32_t c = 0; c < (uint32_t)CH; ++c)
+          ab[c] = gemm_pair_nofb<false>(C[c].hi, C[c].lo, C[c].n, C[c].R.p4, ring_vv[c], rmask4);
+      }
+#pragma unroll
+      for (uint32_t c = 0; c < (uint32_t)CH; ++c) ab[c] = live[c] ? ab[c] : 0u;
+    } else if (q < early_n) {
+#pragma unroll
+      for (uint32_t c = 0; c < (uint32_t)CH; ++c)
+        ab[c] = live[c] ? stream_pair<true, NOFB>(lut, K, C[c].hi, C[c].lo, C[c].n, C[c].R.p4, ring_vv[c], rmask4).x
+                        : 0u;
+    } else {
+#pragma unroll
+      for (uint32_t c = 0; c < (uint32_t)CH; ++c)
+        ab[c] = live[c] ? stream_pair<false, NOFB>(lut, K, C[c].hi, C[c].lo, C[c].n, C[c].R.p4, ring_vv[c], rmask4).x
+                        : 0u;
     }
-    lds_barrier();
-    // A: rows 16c + lane mod 16 of the slice, columns 32 ks + 8 (lane / 16)
-    const uint32_t a_addr = buf + ((lane & 15u) * kGemmRowStride + 8u * (lane >> 4)) * 2u;
 #pragma unroll
-    for (uint32_t ks = 0; ks < 4u; ++ks) {
+    for (uint32_t c = 0; c < (uint32_t)CH; ++c) gemm_put(buf + (16u * c + wave) * kGemmRowStride * 2u, lane, ab[c]);
+    // every chain copies the block three past P's, whether or not P entered a new block
 #pragma unroll
-      for (uint32_t c = 0; c < (uint32_t)CH; ++c) {
-        const bf16x8 av = __builtin_bit_cast(
-            bf16x8, *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(
-                        a_addr + 16u * c * kGemmRowStride * 2u + ks * 64u));
+    for (uint32_t c = 0; c < (uint32_t)CH; ++c)
+      ring_copy<kGemmRingLog2>(C[c].R, ring_b[c], (C[c].R.p4 >> kGemmRingLog2) + (kRingBlocks - 1u), lane);
+  };
+  // A: rows 16c + lane mod 16 of the slice, columns 32 ks + 8 (lane / 16);
+  // a k step's fragments are all read before its products
+  auto multiply = [&](uint32_t q, const u32x4 (&b)[NT][4]) {
+    const uint32_t a_addr = slices + (q & 1u) * GemmTile<CH>::slice_bytes +
+                            ((lane & 15u) * kGemmRowStride + 8u * (lane >> 4)) * 2u;
+    auto a_frag = [&](uint32_t c, uint32_t ks) {
+      return __builtin_bit_cast(bf16x8, *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(
+                                            a_addr + 16u * c * kGemmRowStride * 2u + ks * 64u));
+    };
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
-          if (wave + (uint32_t)tt * (uint32_t)kWaves < tok_groups)
-            acc[c][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bc[tt][ks]),
-                                                                 acc[c][tt], 0, 0, 0);
+    for (int tt = 0; tt < NT; ++tt) {
+      if (wave + (uint32_t)tt * (uint32_t)kWaves >= tok_groups) continue;   // no tokens in this group
+#pragma unroll
+      for (uint32_t ks = 0; ks < 4u; ++ks) {
+        bf16x8 av[CH];
+#pragma unroll
+        for (uint32_t c = 0; c < (uint32_t)CH; ++c) av[c] = a_frag(c, ks);
+#pragma unroll
+        for (uint32_t c = 0; c < (uint32_t)CH; ++c)
+          acc[c][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[c], __builtin_bit_cast(bf16x8, b[tt][ks]), acc[c][tt],
+                                                               0, 0, 0);
       }
     }
-    ops_prev = ops;
+  };
+  u32x4 bx[NT][4];
+  gemm_b_load<NT>(bx, d.x, cols, n_tokens, wave, lane, 0u);
+  decode(0u);
+  lds_barrier();
+  for (uint32_t q = 1; q < q_n; ++q) {
+    wait_vm(kOps);   // copies and loads issued before the previous interval
+    if (!decode_first) {
+      multiply(q - 1u, bx);
+      gemm_b_load<NT>(bx, d.x, cols, n_tokens, wave, lane, q);
+    }
+    decode(q);
+    if (decode_first) {
+      multiply(q - 1u, bx);
+      gemm_b_load<NT>(bx, d.x, cols, n_tokens, wave, lane, q);
+    }
+    lds_barrier();
   }
+  multiply(q_n - 1u, bx);
   // row ends
 #pragma unroll
   for (uint32_t c = 0; c < (uint32_t)CH; ++c) {
@@ -2820,8 +2657,11 @@ __device__ uint32_t gemm_tile(const TensorArg &d, const uint32_t *lut, uint32_t 
   return flags;
 }
 
+// Four wavefronts per SIMD (one workgroup per CU), whatever the register
+// count below 128.
 template <int NT, int CH>
-__global__ __launch_bounds__(kBlockThreads) void ecw_gemm_ring_kernel(const StreamArgs a) {
+__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void ecw_gemm_ring_kernel(
+    const StreamArgs a) {
   // Set-up as in the matrix-core GEMV.  Dynamic LDS: the two-code table (at
   // LDS address 0), the code table (lut_cap entries), the table-state word,
   // the two 64-row slices, then four rings per wavefront.
@@ -3444,35 +3284,10 @@ static entro_status run(int mode, const entro_tensor *t, size_t n, void *const *
   return ENTRO_OK;
 }
 
-static hipError_t launch_gemm(GemmArgs &a, size_t dyn, hipStream_t s) {
-  auto kern = a.xslice_bytes ? ecw_gemm_kernel<1, true>
-                             : (a.n_tokens <= 16u * (uint32_t)kWaves ? ecw_gemm_kernel<1, false> : ecw_gemm_kernel<2, false>);
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBlockThreads, dyn) != hipSuccess || per_cu < 1)
-    per_cu = 1;
-  const int lds_fit = (int)((kLdsPerCu - kLdsPlanReserve) / (dyn + kStaticLds));
-  if (lds_fit >= 1 && per_cu > lds_fit) per_cu = lds_fit;
-  if (cus < 1) cus = 1;
-  const uint64_t slots = cap_grid((uint64_t)cus * (uint64_t)per_cu);
-  const uint32_t per_block = (uint32_t)((a.total_tiles + slots - 1) / slots);
-  a.tiles_per_block = per_block < 1 ? 1 : per_block;
-  const uint32_t grid = (a.total_tiles + a.tiles_per_block - 1) / a.tiles_per_block;
-  // clear an error left by an earlier call (ours, such as a failed occupancy
-  // query, or the caller's): the check below then sees this launch alone
-  (void)hipGetLastError();
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlockThreads), dyn, s, a);
-  return hipGetLastError();
-}
-
-// decode + GEMM in 64- or 32-row tiles (ecw_gemm_ring_kernel): tensors of the
-// streamed layout (64 lanes, 4-bit codes, refill every two steps, one row per
-// chunk, 128 | cols, a stream below 4 GiB).  Prompts of kGemmRingMinTokens
-// to kGemmRingMaxTokens tokens take it (one token group per wavefront);
-// others the 16-row kernel: one token group keeps only one wavefront of a
-// tall tile multiplying, and beyond 256 tokens the 16-row kernel was as fast.
-constexpr uint32_t kGemmRingMinTokens = 17;
+// decode + GEMM (ecw_gemm_ring_kernel): tensors of the streamed layout (64
+// lanes, 4-bit codes, refill every two steps, one row per chunk, 128 | cols,
+// a stream below 4 GiB).  A launch takes at most kGemmRingMaxTokens tokens
+// (one 16-token group per wavefront); longer prompts are split.
 constexpr uint32_t kGemmRingMaxTokens = 16u * kWaves;
 
 // LDS bytes of a launch of ch rows per wavefront (code table of lut_cap
@@ -3493,12 +3308,6 @@ static bool gemm_ring_fits(uint64_t lut_entries, uint32_t ch = 4) {
   return gemm_ring_lds_bytes((lut_entries + 3) & ~3ull, ch) + kStaticLds <= kLdsPerCu - kLdsPlanReserve;
 }
 
-static bool gemm_ring_ok(const entro_tensor &t, const entro_gemv_item &g) {
-  if (t.lanes != 64u || t.sym_bits != 4u || t.refill_steps != 2u) return false;
-  if (g.cols == 0 || (g.cols % kGemmSliceCols) || t.chunk_symbols != g.cols) return false;
-  if (t.n_words >= (1ull << 30)) return false;
-  return gemm_ring_fits(stream_lut_entries(t));
-}
 
 static entro_status plan_gemm_ring(const entro_tensor *t, size_t n, const entro_gemv_item *g, uint32_t n_tokens,
                                    uint32_t ch, uint32_t *d_status, std::vector<StreamPlan> &plans) {
@@ -3539,7 +3348,7 @@ static entro_status plan_gemm_ring(const entro_tensor *t, size_t n, const entro_
 }
 
 static hipError_t launch_gemm_ring(StreamPlan &pl, uint32_t ch, hipStream_t s) {
-  auto kern = ch == 4u ? ecw_gemm_ring_kernel<1, 4> : ecw_gemm_ring_kernel<1, 2>;
+  auto kern = ch == 4u ? ecw_gemm_ring_kernel<1, 4> : ch == 2u ? ecw_gemm_ring_kernel<1, 2> : ecw_gemm_ring_kernel<1, 1>;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
@@ -3568,112 +3377,46 @@ static entro_status run_gemm(const entro_tensor *t, size_t n, const entro_gemv_i
     if (t[i].n_symbols == 0) continue;
     if (!it.d_x || !it.d_y || (reinterpret_cast<uintptr_t>(it.d_x) & 15u)) return ENTRO_E_INVAL;
     if (it.cols % kGemmSliceCols || t[i].chunk_symbols != it.cols) return ENTRO_E_FORMAT;
-    if (t[i].lanes != 64u || t[i].sym_bits != 4u || t[i].refill_steps != 2u || t[i].max_chunk_words == 0u)
-      return ENTRO_E_UNSUPPORTED;
+    if (t[i].lanes != 64u || t[i].sym_bits != 4u || t[i].refill_steps != 2u) return ENTRO_E_UNSUPPORTED;
   }
-  // the tallest tiles the call has enough of: with fewer than 3/8 of the
-  // CUs busy (the 4096-row matrices of a Mistral-shaped layer at 64 tiles
-  // of 64 rows on 256 CUs) smaller tiles that keep more CUs busy were
-  // faster; with 96 (q/k/v) or more, the taller ones
-  bool ring = n_tokens >= kGemmRingMinTokens && n_tokens <= kGemmRingMaxTokens;
-  uint64_t tiles64 = 0, tiles32 = 0;
-  for (size_t i = 0; i < n && ring; ++i) {
-    if (t[i].n_symbols && !gemm_ring_ok(t[i], g[i])) ring = false;
+  // Tile height: 64 rows where the call has a 64-row tile for every CU, 32
+  // where its 32-row tiles fill three quarters of the CUs, else 16 (on a
+  // Mistral-shaped layer: gate/up, q/k/v and o/down respectively, each the
+  // fastest of the three at 1 to 256 tokens); lower if the tables do not
+  // fit the LDS beside the taller tiles.
+  uint64_t tiles64 = 0, tiles32 = 0, lut_need = 0;
+  for (size_t i = 0; i < n; ++i) {
+    if (t[i].n_symbols == 0) continue;
+    if (t[i].n_words >= (1ull << 30)) return ENTRO_E_UNSUPPORTED;
     tiles64 += (g[i].rows + 63u) / 64u;
     tiles32 += (g[i].rows + 31u) / 32u;
+    lut_need = std::max<uint64_t>(lut_need, stream_lut_entries(t[i]));
   }
-  uint32_t ch = 0;
-  if (ring) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-      cus = 256;
-    ch = 8u * tiles64 >= 3u * (uint64_t)cus ? 4u : 8u * tiles32 >= 3u * (uint64_t)cus ? 2u : 0u;
-  }
-  if (ch) {
-    std::vector<StreamPlan> rplans;
-    const entro_status st = plan_gemm_ring(t, n, g, n_tokens, ch, d_status, rplans);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  uint32_t ch = tiles64 >= (uint64_t)cus ? 4u : 4u * tiles32 >= 3u * (uint64_t)cus ? 2u : 1u;
+  while (ch > 1u && !gemm_ring_fits(lut_need, ch)) ch >>= 1;
+  if (!gemm_ring_fits(lut_need, ch)) return ENTRO_E_UNSUPPORTED;   // not reached: tables hold at most 4096 entries
+  // every launch planned before any is enqueued; prompts of more than
+  // kGemmRingMaxTokens tokens in parts of that many, each with its own x and
+  // y rows
+  std::vector<StreamPlan> plans;
+  std::vector<entro_gemv_item> part(n);
+  for (uint32_t t0 = 0; t0 < n_tokens; t0 += kGemmRingMaxTokens) {
+    const uint32_t nt = std::min(n_tokens - t0, kGemmRingMaxTokens);
+    for (size_t i = 0; i < n; ++i) {
+      part[i] = g[i];
+      if (t[i].n_symbols == 0) continue;
+      part[i].d_x = static_cast<const uint16_t *>(g[i].d_x) + (size_t)t0 * g[i].cols;
+      part[i].d_y = static_cast<float *>(g[i].d_y) + (size_t)t0 * g[i].rows;
+    }
+    const entro_status st = plan_gemm_ring(t, n, part.data(), nt, ch, d_status, plans);
     if (st != ENTRO_OK) return st;
-    for (auto &pl : rplans)
-      if (launch_gemm_ring(pl, ch, s) != hipSuccess) return ENTRO_E_HIP;
-    return ENTRO_OK;
-  }
-  // plan every launch first (a row too long for the staging fails the call
-  // before anything is enqueued), then launch
-  std::vector<std::pair<GemmArgs, size_t>> plans;
-  size_t i = 0;
-  while (i < n) {
-    plans.emplace_back();
-    GemmArgs &a = plans.back().first;
-    std::memset(&a, 0, sizeof a);
-    a.n_tokens = n_tokens;
-    uint32_t total = 0, k = 0;
-    uint64_t stage_need = 0, lut_need = 0;
-    for (; i < n && k < (uint32_t)kMaxTensorsPerLaunch; ++i) {
-      const entro_tensor &x = t[i];
-      if (x.n_symbols == 0) continue;
-      TensorArg &d = a.t[k];
-      d.lut = static_cast<const uint32_t *>(x.d_lut);
-      d.words = x.d_words;
-      d.offs = x.d_chunk_bit_off;
-      d.status = d_status + i;
-      d.n_words = x.n_words;
-      d.n_symbols = x.n_symbols;
-      d.chunk = x.chunk_symbols;
-      d.n_chunks = (uint32_t)((x.n_symbols + x.chunk_symbols - 1) / x.chunk_symbols);
-      d.expect_hdr = (x.sym_bits << 8) | (x.max_len << 16);
-      d.lut_words = (uint32_t)std::min<uint64_t>(x.lut_bytes / 4, kLutHeaderWords + kLutMaxEntries);
-      d.refill_steps = 2u;
-      d.ahead = x.refill_ahead;
-      d.out = g[i].d_y;
-      d.x = g[i].d_x;
-      d.rows = g[i].rows;
-      d.cols = g[i].cols;
-      d.n_tasks = d.n_chunks;
-      const uint64_t tiles = (d.rows + kWaves - 1) / kWaves;
-      if ((uint64_t)total + tiles > 0x7FFFFFFFull) return ENTRO_E_UNSUPPORTED;
-      a.tile_begin[k] = total;
-      total += (uint32_t)tiles;
-      lut_need = std::max<uint64_t>(lut_need, d.lut_words > kLutHeaderWords ? d.lut_words - kLutHeaderWords : 0);
-      stage_need = std::max<uint64_t>(stage_need, x.max_chunk_words);
-      ++k;
-    }
-    if (k == 0) {
-      plans.pop_back();
-      continue;
-    }
-    a.n_tensors = k;
-    a.total_tiles = total;
-    for (uint32_t r = k; r <= (uint32_t)kMaxTensorsPerLaunch; ++r) a.tile_begin[r] = total;
-    // LDS: two-code table, code table, two weight slices, state word, then
-    // one staging area per wavefront (the largest row plus alignment)
-    a.lut_cap = (uint32_t)((lut_need + 3) & ~3ull);
-    size_t dyn = ((size_t)8u << kPairBits) + (size_t)a.lut_cap * 4u;
-    dyn = (dyn + 15u) & ~(size_t)15u;
-    a.slice_byte = (uint32_t)dyn;
-    dyn += 2u * kGemmSliceBytes;
-    // short prompts: the activations of each slice staged in LDS as well,
-    // where the staging areas still hold the longest row (else x is read
-    // from L2 by every tile, as for long prompts)
-    const uint64_t sw = (stage_need + 3 + 3) & ~3ull;
-    auto stage_cap = [](size_t d) -> uint64_t {
-      const uint64_t words = (kLdsPerCu - kStaticLds) / 4u - (d + 16u) / 4u;
-      return words / kWaves > kStageSlack ? words / kWaves - kStageSlack : 0u;
-    };
-    const uint32_t tok_pad = (n_tokens + 15u) & ~15u;
-    if (n_tokens <= kGemmXlTokens && sw <= stage_cap(dyn + 2u * (size_t)tok_pad * kGemmRowStride * 2u)) {
-      a.xslice_bytes = tok_pad * kGemmRowStride * 2u;
-      dyn += 2u * (size_t)a.xslice_bytes;
-    }
-    a.state_word = (uint32_t)(dyn / 4u);
-    if (sw > stage_cap(dyn)) return ENTRO_E_UNSUPPORTED;
-    dyn += 16u;
-    a.stage_words = (uint32_t)sw;
-    dyn += (size_t)kWaves * (sw + kStageSlack) * 4u;
-    plans.back().second = dyn;
   }
   for (auto &pl : plans)
-    if (launch_gemm(pl.first, pl.second, s) != hipSuccess) return ENTRO_E_HIP;
+    if (launch_gemm_ring(pl, ch, s) != hipSuccess) return ENTRO_E_HIP;
   return ENTRO_OK;
 }
 

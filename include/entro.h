@@ -224,15 +224,13 @@ entro_status entro_decode_gemv(const entro_tensor *t, size_t n, const entro_gemv
  * 1..512; d_x[i] is bf16 [n_tokens][cols], 16-byte aligned; d_y[i] is fp32
  * [n_tokens][rows], overwritten.  Layouts decoded here: 4-bit codes, 64
  * lanes, refill every two steps, one row per chunk (chunk_symbols == cols,
- * cols a multiple of 128) and max_chunk_words stated; ENTRO_E_FORMAT or
- * ENTRO_E_UNSUPPORTED otherwise.  Calls of 17..256 tokens with enough rows
- * to fill the GPU with tiles of 32 or 64 rows stream rows of any length
- * through small on-chip rings; other calls stage each row whole, and return
- * ENTRO_E_UNSUPPORTED when the largest row (max_chunk_words) does not fit
- * that staging (about 2200 words).  The launch configuration does not
- * change the results beyond fp32 summation order.  Data faults set d_status
- * bits as for the other entry points (ENTRO_F_OFFSETS also when a row's
- * words cannot be staged). */
+ * cols a multiple of 128), rows of any length (streamed through small
+ * on-chip rings), a stream below 2^30 words; ENTRO_E_FORMAT or
+ * ENTRO_E_UNSUPPORTED otherwise.  Prompts of more than 256 tokens run as
+ * several launches, each decoding every weight again.  The tile height
+ * (16, 32 or 64 rows) follows the call's row count against the GPU's CU
+ * count and changes the results only in fp32 summation order.  Data faults
+ * set d_status bits as for the other entry points. */
 entro_status entro_decode_gemm(const entro_tensor *t, size_t n, const entro_gemv_item *g,
                                uint32_t n_tokens, uint32_t *d_status, hipStream_t stream);
 

@@ -304,8 +304,7 @@ def test_gemm_entry_point_validates_before_launch(lib):
     assert gemm(lanes=32) == 4                        # only 64 lanes
     assert gemm(sym_bits=8, max_len=16) == 4          # only 4-bit codes
     assert gemm(refill_steps=1) == 4                  # only pairs of steps
-    assert gemm(max_chunk_words=0) == 4               # staging size must be stated
-    assert gemm(max_chunk_words=1 << 20) == 4         # a row larger than the on-chip staging
+    assert gemm(n_words=1 << 30) == 4                 # a stream of 4 GiB or more
     assert lib.entro_decode_gemm((ent.Tensor * 1)(), 0, None, 16, st, None) == 0
 
 
@@ -318,7 +317,7 @@ def test_a_call_that_fails_planning_enqueues_nothing(lib):
     st = ctypes.c_void_p(1)
     good = [ent.Tensor(1, 1, 1, 10, 2 * 128, 128, 64, 4, 12, 64, 8, 2, 1) for _ in range(40)]
     bad = list(good)
-    bad[35] = ent.Tensor(1, 1, 1, 10, 2 * 128, 128, 64, 4, 12, 64, 1 << 20, 2, 1)   # row beyond the staging
+    bad[35] = ent.Tensor(1, 1, 1, 1 << 30, 2 * 128, 128, 64, 4, 12, 64, 8, 2, 1)   # a stream of 4 GiB
     g = (ent.GemvItem * 40)(*[ent.GemvItem(2, 128, 0x1000, 0x2000) for _ in range(40)])
     assert lib.entro_decode_gemm((ent.Tensor * 40)(*bad), 40, g, 16, st, None) == 4
     assert lib.entro_decode_gemm((ent.Tensor * 40)(*good), 40, g, 16, st, None) == 5

@@ -1,10 +1,11 @@
 """GPU parity of the fused decode + GEMM (prompt processing on the matrix
 cores) against the float64 oracle: token counts around the 16-token groups
-and up to the 512 maximum, calls that reach the 16-, 32- and 64-row tiles
-(17..256 tokens take the taller ones where a call has enough of them), row counts around the 16-row tiles, several
-matrices per call, streams with and without refilling ahead, a malformed
-stream, and a full-size Mistral-shaped matrix.  Streams and expected values
-come from the oracle only."""
+and up to the 512 maximum (more than 256 tokens run as several launches),
+calls that reach the 16-, 32- and 64-row tiles (the tile height follows the
+call's row count against the GPU's CU count), row counts around the tiles,
+several matrices per call, streams with and without refilling ahead, long
+rows, a malformed stream, and a full-size Mistral-shaped matrix.  Streams
+and expected values come from the oracle only."""
 import sys
 
 import numpy as np
@@ -30,6 +31,22 @@ def _gpu():
     import entropy_coded_weight_canonical_amd as ent
 
     ent.load()
+
+
+def _cus():
+    import torch
+
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def _check(cases, xs, ys, st):
+    assert (st == 0).all(), st
+    for c, x, y in zip(cases, xs, ys):
+        ref = ogemv.gemv_f64(c.expected_bf16().reshape(c.rows, c.cols), x)
+        assert not np.isnan(y).any()
+        err = ogemv.rel_err(y, ref)
+        assert err <= 1e-2
+        assert err <= (1e-3 if c.cols > 4096 else 1e-4), (c.rows, c.cols, err)   # fp32 sums; see the long-row test
 
 
 def _case(rows, cols, seed, scheme="mixed", ahead=True, w=None):
@@ -98,11 +115,10 @@ def test_gemm_mistral_o_full_size(n_tokens):
     assert ogemv.rel_err(ys[0][toks], ref) <= 1e-4
 
 
-@pytest.mark.parametrize("n_tokens", [16, 64, 128, 200])
-def test_gemm_rows_too_long_to_stage_beside_the_activations(n_tokens):
-    """14336-column rows of uniform 4-bit codes (~1790 words a row, as the
-    down projection at 3.9 bits/weight): with x staged in LDS the staging
-    area holds fewer words, so short prompts read x from L2 instead."""
+@pytest.mark.parametrize("n_tokens", [1, 16, 64, 128, 200])
+def test_gemm_long_rows(n_tokens):
+    """14336-column rows of uniform 4-bit codes (~1790 words a row, more than
+    the down projection at 3.9 bits/weight), streamed through the rings."""
     rng = np.random.default_rng(11)
     q = rng.integers(0, 16, size=(24, 14336), dtype=np.uint8)
     c = make_case(q, 4, 14336, 64, scale=0.01, zp=8, rows=24, cols=14336, refill_steps=2, ahead=True)
@@ -120,19 +136,20 @@ def test_gemm_rows_too_long_to_stage_beside_the_activations(n_tokens):
 
 
 @pytest.mark.parametrize("cap", [0, 7])
-@pytest.mark.parametrize("n_tokens", [17, 64, 129, 256])
+@pytest.mark.parametrize("n_tokens", [17, 64, 129, 256, 300])
 def test_gemm_64_row_tiles(n_tokens, cap):
-    """Calls of at least 96 tiles of 64 rows at 17..256 tokens take the
-    64-row kernel: rows not a multiple of 64, several matrices, streams with
-    and without refilling ahead, 14336-column rows; with a workgroup cap of 7
-    every workgroup decodes many tiles one after another."""
+    """Calls with at least one 64-row tile per CU take the 64-row tiles: rows
+    not a multiple of 64, several matrices, streams with and without
+    refilling ahead, 14336-column rows; with a workgroup cap of 7 every
+    workgroup decodes many tiles one after another."""
     import entropy_coded_weight_canonical_amd as ent
 
     rng = np.random.default_rng(12)
     q = rng.integers(0, 16, size=(64, 14336), dtype=np.uint8)
-    cases = [_case(4000, 128, 21), _case(2100, 256, 22, scheme="unsigned", ahead=False), _case(37, 512, 23),
-             make_case(q, 4, 14336, 64, scale=0.01, zp=8, rows=64, cols=14336, refill_steps=2, ahead=True)]
-    assert sum((c.rows + 63) // 64 for c in cases) >= 96
+    cases = [_case(64 * _cus() - 200, 128, 21), _case(130, 256, 22, scheme="unsigned", ahead=False),
+             _case(37, 512, 23), make_case(q, 4, 14336, 64, scale=0.01, zp=8, rows=64, cols=14336, refill_steps=2,
+                                           ahead=True)]
+    assert sum((c.rows + 63) // 64 for c in cases) >= _cus()
     xs = [activations_bf16("phi3_stack", 500 + i, c.cols, n_tokens) for i, c in enumerate(cases)]
     say(f"decode+GEMM 64-row tiles, {n_tokens} tokens, cap {cap}")
     prev = ent.set_max_workgroups(cap)
@@ -140,28 +157,22 @@ def test_gemm_64_row_tiles(n_tokens, cap):
         ys, st = run_gemm(cases, n_tokens, xs)
     finally:
         ent.set_max_workgroups(prev)
-    assert (st == 0).all(), st
-    for c, x, y in zip(cases, xs, ys):
-        ref = ogemv.gemv_f64(c.expected_bf16().reshape(c.rows, c.cols), x)
-        assert not np.isnan(y).any()
-        err = ogemv.rel_err(y, ref)
-        assert err <= 1e-2
-        assert err <= (1e-3 if c.cols > 4096 else 1e-4), (c.rows, c.cols, err)   # fp32 sums; see the long-row test
+    _check(cases, xs, ys, st)
 
 
 @pytest.mark.parametrize("cap", [0, 5])
-@pytest.mark.parametrize("n_tokens", [17, 100, 256])
+@pytest.mark.parametrize("n_tokens", [1, 17, 100, 256, 400])
 def test_gemm_32_row_tiles(n_tokens, cap):
-    """Calls of at least 96 tiles of 32 rows but fewer of 64 (the 4096-row
-    matrices of a Mistral-shaped layer) take the kernel with two rows per
-    wavefront."""
+    """Calls with 32-row tiles for three quarters of the CUs but fewer 64-row
+    tiles than CUs (a Mistral-shaped q/k/v group) take the 32-row tiles."""
     import entropy_coded_weight_canonical_amd as ent
 
     rng = np.random.default_rng(13)
     q = rng.integers(0, 16, size=(40, 14336), dtype=np.uint8)
-    cases = [_case(3100, 128, 31), _case(37, 512, 32, ahead=False),
+    cases = [_case(24 * _cus() + 7, 128, 31), _case(37, 512, 32, ahead=False),
              make_case(q, 4, 14336, 64, scale=0.01, zp=8, rows=40, cols=14336, refill_steps=2, ahead=True)]
-    assert sum((c.rows + 63) // 64 for c in cases) < 96 <= sum((c.rows + 31) // 32 for c in cases)
+    t64, t32 = sum((c.rows + 63) // 64 for c in cases), sum((c.rows + 31) // 32 for c in cases)
+    assert t64 < _cus() and 4 * t32 >= 3 * _cus()
     xs = [activations_bf16("phi3_stack", 600 + i, c.cols, n_tokens) for i, c in enumerate(cases)]
     say(f"decode+GEMM 32-row tiles, {n_tokens} tokens, cap {cap}")
     prev = ent.set_max_workgroups(cap)
@@ -169,10 +180,23 @@ def test_gemm_32_row_tiles(n_tokens, cap):
         ys, st = run_gemm(cases, n_tokens, xs)
     finally:
         ent.set_max_workgroups(prev)
-    assert (st == 0).all(), st
-    for c, x, y in zip(cases, xs, ys):
-        ref = ogemv.gemv_f64(c.expected_bf16().reshape(c.rows, c.cols), x)
-        assert not np.isnan(y).any()
-        err = ogemv.rel_err(y, ref)
-        assert err <= 1e-2
-        assert err <= (1e-3 if c.cols > 4096 else 1e-4), (c.rows, c.cols, err)
+    _check(cases, xs, ys, st)
+
+
+@pytest.mark.parametrize("cap", [0, 3])
+@pytest.mark.parametrize("n_tokens", [2, 33, 256])
+def test_gemm_16_row_tiles_many_per_workgroup(n_tokens, cap):
+    """Calls with few rows take the 16-row tiles; with a workgroup cap of 3
+    each workgroup decodes tiles of several matrices one after another."""
+    import entropy_coded_weight_canonical_amd as ent
+
+    cases = [_case(16 * 20 + 3, 384, 41), _case(16, 128, 42, ahead=False), _case(100, 1024, 43, scheme="unsigned")]
+    assert 4 * sum((c.rows + 31) // 32 for c in cases) < 3 * _cus()
+    xs = [activations_bf16("mistral_stack", 700 + i, c.cols, n_tokens) for i, c in enumerate(cases)]
+    say(f"decode+GEMM 16-row tiles, {n_tokens} tokens, cap {cap}")
+    prev = ent.set_max_workgroups(cap)
+    try:
+        ys, st = run_gemm(cases, n_tokens, xs)
+    finally:
+        ent.set_max_workgroups(prev)
+    _check(cases, xs, ys, st)
