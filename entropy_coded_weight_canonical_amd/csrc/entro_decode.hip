@@ -1639,7 +1639,10 @@ __device__ __forceinline__ void gemv_stream(const StreamArgs &a) {
     Run R;
     const bool have = cb < ce;
     const bool run_ok = have && run_begin<RL, 2u>(d, cb, ce, o0, o1, ring_base, lane, R);
-    __syncthreads();
+    // The table entries, the activations and the table-state word go to LDS
+    // before the workgroup's one set-up barrier: nothing reads them before
+    // it, and the direct-to-LDS copies in flight (two-code table, rings)
+    // write other LDS.
     if (threadIdx.x == 0) *state = 0u;
     if (threadIdx.x < nv)
       reinterpret_cast<u32x4 *>(lut)[threadIdx.x] =
@@ -2347,7 +2350,8 @@ __global__ __launch_bounds__(kBlockThreads) void ecw_gemv_tile_kernel(const Stre
     Run R;
     const bool have = cb < ce;
     const bool run_ok = have && run_begin<RL>(d, cb, ce, o0, o1, ring_base, lane, R);
-    __syncthreads();
+    // table entries and the table-state word before the one set-up barrier,
+    // as in the streamed kernel
     if (threadIdx.x == 0) *state = 0u;
     if (threadIdx.x < nv)
       reinterpret_cast<u32x4 *>(lut)[threadIdx.x] =
