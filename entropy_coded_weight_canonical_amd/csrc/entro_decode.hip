@@ -1499,6 +1499,13 @@ __device__ uint32_t stream_run(const TensorArg &d, const uint32_t *lut, uint32_t
 #pragma unroll
   for (uint32_t b = 0; b < SB; ++b) yv[b] = 0.f;
   ring_wait2<RL>();   // blocks 0 and 1 of the run
+  // A run of several rows takes issue priority 1 for its first half and 0
+  // for the rest: among wavefronts of equal priority the oldest is served
+  // first, so without this the ones that started last finish last.
+  const uint32_t run_rows =
+      ce > cb ? (uint32_t)(min((uint64_t)ce * rpc, (uint64_t)rows) - (uint64_t)cb * rpc) : 0u;
+  if (run_rows > 1u) set_prio(1u);
+  uint32_t rows_done = 0;
   for (uint32_t c = cb; c < ce; ++c) {
     if (c != cb && ((c - cb) & 63u) == 0u) {   // the next 64 chunk ends
       const uint64_t o_start = R.base * 32u + R.p4 * 8u;
@@ -1525,6 +1532,8 @@ __device__ uint32_t stream_run(const TensorArg &d, const uint32_t *lut, uint32_t
 #pragma unroll
       for (uint32_t b = 0; b < SB; ++b) acc[b] = 0.f;
       const uint32_t qe = early_n > kk ? min(early_n - kk, ppr) : 0u;
+      if (run_rows > 1u && rows_done == (run_rows >> 1)) set_prio(0u);
+      ++rows_done;
       stream_pairs<BATCH, true, NOFB, RL>(lut, K, 0u, qe, xl, lane, acc, hi, lo, n, R, ring_base, ring_v, rmask4);
       stream_pairs<BATCH, false, NOFB, RL>(lut, K, qe, ppr, xl, lane, acc, hi, lo, n, R, ring_base, ring_v, rmask4);
       // row end: the row's sums (lane 63 after the reduction) go to lane ycnt
